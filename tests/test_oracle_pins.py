@@ -1,0 +1,377 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test names what it pins.  Library routines used as independent
+references: torch's scaled_dot_product_attention and autograd (float64, CPU),
+torch's elu and sigmoid.  Brute force uses plain Python loops on tiny inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from compressive_linear_memory_amd import inputs as I
+from conftest import max_rel_err
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _problem(B=1, Hq=2, Hkv=2, N=12, d=4, seed=0, scale=1.0):
+    Q = _rand((B, Hq, N, d), seed, scale)
+    K = _rand((B, Hkv, N, d), seed + 1, scale)
+    V = _rand((B, Hkv, N, d), seed + 2, scale)
+    beta = _rand((Hq,), seed + 3)
+    return Q, K, V, beta
+
+
+def _prefix_state(B, Hkv, d, T=5, seed=50):
+    """A consistent carried state, as an earlier call over T tokens would leave it."""
+    Kp = _rand((B, Hkv, T, d), seed)
+    Vp = _rand((B, Hkv, T, d), seed + 1)
+    _, _, M0, z0 = O.state_sweep(Kp, Vp, T)
+    return M0, z0
+
+
+# ----------------------------------------------------------- elementwise maps
+
+def test_sigma_is_elu_plus_one():
+    """R4: sigma = ELU(alpha=1) + 1, checked against torch's elu."""
+    x = np.linspace(-6, 6, 1001)
+    ref = torch.nn.functional.elu(torch.tensor(x, dtype=torch.float64), alpha=1.0).numpy() + 1.0
+    assert np.max(np.abs(O.sigma(x) - ref)) < 1e-15
+    assert np.all(O.sigma(x) > 0)
+
+
+def test_sigma_grad_against_autograd():
+    x = torch.tensor(np.linspace(-6, 6, 1000) + 1e-3, dtype=torch.float64, requires_grad=True)
+    (torch.nn.functional.elu(x) + 1).sum().backward()
+    assert np.max(np.abs(O.sigma_grad(x.detach().numpy()) - x.grad.numpy())) < 1e-15
+
+
+def test_gate_is_sigmoid_with_exact_limits():
+    b = np.array([-np.inf, -30.0, -1.0, 0.0, 2.5, 30.0, np.inf])
+    ref = torch.sigmoid(torch.tensor(b, dtype=torch.float64)).numpy()
+    assert np.max(np.abs(O.gate(b) - ref)) < 1e-15
+    assert O.gate(-np.inf) == 0.0 and O.gate(np.inf) == 1.0
+
+
+# ----------------------------------------------------------- closed forms
+
+def test_closed_form_scalar_heads():
+    """d = 1, seg_len = 1: every quantity has a closed form.
+
+    Segment 0 has an empty memory, so A_mem = 0 and O_0 = (1-g) v_0; later
+    segments read the memory of all earlier tokens; A_dot is the token's own v."""
+    q = np.array([0.5, -1.0, 2.0])
+    k = np.array([-0.5, 1.0, 0.0])
+    v = np.array([2.0, -3.0, 0.25])
+    beta = 0.3
+    g = 1 / (1 + math.exp(-beta))
+    sq = [1.5, math.exp(-1.0), 3.0]
+    sk = [math.exp(-0.5), 2.0, 1.0]
+    eps = O.EPS
+    exp_o = [
+        (1 - g) * v[0],
+        g * (sq[1] * sk[0] * v[0]) / (sq[1] * sk[0] + eps) + (1 - g) * v[1],
+        g * (sq[2] * (sk[0] * v[0] + sk[1] * v[1])) / (sq[2] * (sk[0] + sk[1]) + eps) + (1 - g) * v[2],
+    ]
+    exp_M = sk[0] * v[0] + sk[1] * v[1] + sk[2] * v[2]
+    exp_z = sum(sk)
+    sh = (1, 1, 3, 1)
+    out, M, z = O.forward(q.reshape(sh), k.reshape(sh), v.reshape(sh), np.array([beta]), 1)
+    assert np.allclose(out.ravel(), exp_o, rtol=1e-14, atol=1e-14)
+    assert abs(M.item() - exp_M) < 1e-14 and abs(z.item() - exp_z) < 1e-14
+
+
+def test_closed_form_two_token_segment():
+    """d = 1, one segment of two tokens: row 0 sees only key 0, row 1 sees
+    keys 0 and 1 with weights exp(q1 k_j) / sum (scale 1/sqrt(1) = 1)."""
+    q = np.array([0.3, -0.7]); k = np.array([1.2, 0.4]); v = np.array([5.0, -1.0])
+    sh = (1, 1, 2, 1)
+    out, _, _ = O.forward(q.reshape(sh), k.reshape(sh), v.reshape(sh), np.array([-np.inf]), 2)
+    w0, w1 = math.exp(-0.7 * 1.2), math.exp(-0.7 * 0.4)
+    assert np.allclose(out.ravel(), [5.0, (w0 * 5.0 + w1 * -1.0) / (w0 + w1)], rtol=1e-14)
+
+
+# ----------------------------------------------------------- I1: beta = -inf
+
+def _brute_segment_attention(Q, K, V, L):
+    """Per-segment causal softmax attention with scalar loops (tiny only)."""
+    B, Hq, N, d = Q.shape
+    G = Hq // K.shape[1]
+    out = np.zeros_like(Q)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(N):
+                st = (i // L) * L
+                sc = [sum(Q[b, h, i, c] * K[b, h // G, j, c] for c in range(d)) / math.sqrt(d)
+                      for j in range(st, i + 1)]
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                for t, j in enumerate(range(st, i + 1)):
+                    out[b, h, i] += w[t] / sum(w) * V[b, h // G, j]
+    return out
+
+
+@pytest.mark.parametrize("Hq,Hkv,L", [(2, 2, 4), (4, 2, 3), (3, 1, 12)])
+def test_I1_gate_closed_is_segment_causal_attention_bruteforce(Hq, Hkv, L):
+    Q, K, V, _ = _problem(B=2, Hq=Hq, Hkv=Hkv, N=12, d=4, seed=11)
+    M0, z0 = _prefix_state(2, Hkv, 4)
+    beta = np.full(Hq, -np.inf)
+    out, _, _ = O.forward(Q, K, V, beta, L, M0, z0)
+    assert np.max(np.abs(out - _brute_segment_attention(Q, K, V, L))) < 1e-13
+
+
+def test_I1_gate_closed_matches_torch_sdpa():
+    """Library reference: torch SDPA (float64, is_causal, default scale 1/sqrt(d))
+    per segment, K/V repeat-interleaved for grouped-query heads."""
+    B, Hq, Hkv, N, d, L = 2, 8, 2, 96, 16, 32
+    Q, K, V, _ = _problem(B, Hq, Hkv, N, d, seed=21)
+    out, _, _ = O.forward(Q, K, V, np.full(Hq, -np.inf), L)
+    Kr = np.repeat(K, Hq // Hkv, axis=1)
+    Vr = np.repeat(V, Hq // Hkv, axis=1)
+    ref = np.zeros_like(Q)
+    for s in range(N // L):
+        r = slice(s * L, (s + 1) * L)
+        ref[:, :, r] = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(Q[:, :, r]), torch.tensor(Kr[:, :, r]), torch.tensor(Vr[:, :, r]),
+            is_causal=True).numpy()
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+# ----------------------------------------------------------- I2, I3: the gate
+
+def test_I2_gate_open_first_segment_empty_memory_is_zero():
+    Q, K, V, _ = _problem(N=12, seed=31)
+    out, _, _ = O.forward(Q, K, V, np.full(2, np.inf), 4)
+    assert np.all(out[:, :, :4] == 0.0)
+    assert np.all(np.abs(out[:, :, 4:]) > 0)
+
+
+def test_I3_output_is_affine_in_gate():
+    """O(beta) = g O(+inf) + (1-g) O(-inf) for every beta."""
+    Q, K, V, beta = _problem(Hq=4, Hkv=2, N=16, seed=41)
+    M0, z0 = _prefix_state(1, 2, 4)
+    o, _, _ = O.forward(Q, K, V, beta, 4, M0, z0)
+    o_mem, _, _ = O.forward(Q, K, V, np.full(4, np.inf), 4, M0, z0)
+    o_dot, _, _ = O.forward(Q, K, V, np.full(4, -np.inf), 4, M0, z0)
+    g = (1 / (1 + np.exp(-beta)))[None, :, None, None]
+    assert np.max(np.abs(o - (g * o_mem + (1 - g) * o_dot))) < 1e-13
+
+
+# ----------------------------------------------------------- I4, I5, I6: state
+
+def test_I4_state_equals_one_shot_sum():
+    """M_S = M0 + sigma(K_all)^T V_all and z_S = z0 + column sums of sigma(K_all),
+    formed in one product over all tokens (torch elu used for sigma)."""
+    Q, K, V, beta = _problem(B=2, Hq=4, Hkv=2, N=24, d=5, seed=51)
+    M0, z0 = _prefix_state(2, 2, 5)
+    _, M, z = O.forward(Q, K, V, beta, 6, M0, z0)
+    sK = torch.nn.functional.elu(torch.tensor(K)).numpy() + 1
+    M1 = M0 + np.einsum("bhna,bhnc->bhac", sK, V)
+    z1 = z0 + sK.sum(axis=2)
+    assert np.max(np.abs(M - M1)) < 1e-12 and np.max(np.abs(z - z1)) < 1e-12
+
+
+def test_I5_state_independent_of_segment_length():
+    Q, K, V, beta = _problem(N=16, seed=61)
+    states = [O.forward(Q, K, V, beta, L)[1:] for L in (1, 2, 4, 8, 16)]
+    for M, z in states[1:]:
+        assert np.max(np.abs(M - states[0][0])) < 1e-12
+        assert np.max(np.abs(z - states[0][1])) < 1e-12
+
+
+def test_I6_chaining_single_segment_calls_equals_one_call():
+    Q, K, V, beta = _problem(Hq=4, Hkv=2, N=20, seed=71)
+    L = 5
+    o_all, M_all, z_all = O.forward(Q, K, V, beta, L)
+    M = z = None
+    for s in range(4):
+        r = slice(s * L, (s + 1) * L)
+        o, M, z = O.forward(Q[:, :, r], K[:, :, r], V[:, :, r], beta, L, M, z)
+        assert np.array_equal(o, o_all[:, :, r])
+    assert np.array_equal(M, M_all) and np.array_equal(z, z_all)
+
+
+# ----------------------------------------------------------- I7: direct form
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_I7_per_token_form_agrees(with_state):
+    Q, K, V, beta = _problem(B=1, Hq=4, Hkv=2, N=12, d=3, seed=81)
+    M0, z0 = _prefix_state(1, 2, 3) if with_state else (None, None)
+    a, _, _ = O.forward(Q, K, V, beta, 4, M0, z0)
+    b = O.forward_per_token(Q, K, V, beta, 4, M0, z0)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+# ----------------------------------------------------------- I8, I9, I10
+
+def test_I8_output_in_hull_of_zero_and_values():
+    Q, K, V, beta = _problem(B=1, Hq=2, Hkv=2, N=24, d=4, seed=91)
+    out, _, _ = O.forward(Q, K, V, beta, 6)
+    for h in range(2):
+        for i in range(24):
+            lo = np.minimum(0.0, V[0, h, :i + 1].min(axis=0))
+            hi = np.maximum(0.0, V[0, h, :i + 1].max(axis=0))
+            assert np.all(out[0, h, i] >= lo - 1e-12) and np.all(out[0, h, i] <= hi + 1e-12)
+
+
+def test_I9_permuting_an_earlier_segment_changes_nothing_later():
+    Q, K, V, beta = _problem(Hq=2, Hkv=1, N=16, seed=101)
+    o1, M1, z1 = O.forward(Q, K, V, beta, 4)
+    perm = np.random.default_rng(5).permutation(4) + 4           # segment 1
+    K2, V2 = K.copy(), V.copy()
+    K2[:, :, 4:8] = K[:, :, perm]; V2[:, :, 4:8] = V[:, :, perm]
+    o2, M2, z2 = O.forward(Q, K2, V2, beta, 4)
+    assert np.max(np.abs(o1[:, :, 8:] - o2[:, :, 8:])) < 1e-13
+    assert np.max(np.abs(M1 - M2)) < 1e-13 and np.max(np.abs(z1 - z2)) < 1e-13
+    assert np.max(np.abs(o1[:, :, 4:8] - o2[:, :, 4:8])) > 1e-3   # the segment itself does change
+
+
+def test_I10_grouped_query_heads_equal_repeated_kv():
+    Q, K, V, beta = _problem(B=2, Hq=6, Hkv=2, N=12, d=4, seed=111)
+    M0, z0 = _prefix_state(2, 2, 4)
+    og, Mg, zg = O.forward(Q, K, V, beta, 4, M0, z0)
+    rep = lambda x: np.repeat(x, 3, axis=1)
+    om, Mm, zm = O.forward(Q, rep(K), rep(V), beta, 4, rep(M0), rep(z0))
+    assert np.max(np.abs(og - om)) < 1e-13
+    assert np.max(np.abs(rep(Mg) - Mm)) < 1e-13 and np.max(np.abs(rep(zg) - zm)) < 1e-13
+
+
+# ----------------------------------------------------------- I11: bounded state
+
+def test_I11_state_size_independent_of_sequence_length():
+    sizes = set()
+    for N in (8, 32, 128):
+        Q, K, V, beta = _problem(B=2, Hq=4, Hkv=2, N=N, d=4, seed=N)
+        _, M, z = O.forward(Q, K, V, beta, 8)
+        M32, z32 = M.astype(np.float32), z.astype(np.float32)
+        sizes.add(M32.nbytes + z32.nbytes)
+        assert M32.nbytes + z32.nbytes == O.state_bytes(2, 2, 4, N)
+    assert len(sizes) == 1
+
+
+# ----------------------------------------------------------- I13: epsilon
+
+def test_I13_epsilon_perturbs_nonempty_memory_negligibly():
+    w = I.WORKLOADS["tiny_fp32"]
+    Q, K, V = I.qkv(w)
+    beta = I.beta(w)
+    L = w.seg_len
+    a, _, _ = O.forward(Q, K, V, beta, L, eps=O.EPS)
+    # eps = 0 is undefined in segment 0 (0/0); compare retrieval in segments >= 1.
+    Msnap, zsnap, _, _ = O.state_sweep(K, V, L)
+    worst = 0.0
+    for h in range(w.q_heads):
+        for s in range(1, w.segments):
+            r = slice(s * L, (s + 1) * L)
+            am1, _, den1, _ = O.memory_retrieval(Q[0, h, r], Msnap[0, h, s], zsnap[0, h, s], O.EPS)
+            am0, _, den0, _ = O.memory_retrieval(Q[0, h, r], Msnap[0, h, s], zsnap[0, h, s], 0.0)
+            worst = max(worst, np.max(np.abs(am1 - am0)) / np.max(np.abs(am0)))
+            assert np.min(den0) > 100.0
+    assert worst < 1e-8
+    assert np.all(np.isfinite(a))
+
+
+# ----------------------------------------------------------- sampled units
+
+def test_segment_unit_matches_forward_rows():
+    Q, K, V, beta = _problem(B=2, Hq=4, Hkv=2, N=24, d=4, seed=121)
+    M0, z0 = _prefix_state(2, 2, 4)
+    L = 6
+    out, _, _ = O.forward(Q, K, V, beta, L, M0, z0)
+    Msnap, zsnap, _, _ = O.state_sweep(K, V, L, M0, z0)
+    for (b, h, s) in [(0, 0, 0), (1, 3, 3), (0, 2, 2)]:
+        r = slice(s * L, (s + 1) * L)
+        rows = np.array([0, 3, 5])
+        u = O.segment_unit(Q[b, h, r], K[b, h // 2, r], V[b, h // 2, r],
+                           Msnap[b, h // 2, s], zsnap[b, h // 2, s], beta[h], rows)
+        assert np.max(np.abs(u - out[b, h, r][rows])) < 1e-13
+
+
+# ----------------------------------------------------------- I12: backward
+
+def _loss(params, dO, dMS, dzS, L):
+    o, M, z = O.forward(params["Q"], params["K"], params["V"], params["beta"], L,
+                        params["M0"], params["z0"])
+    return np.sum(dO * o) + np.sum(dMS * M) + np.sum(dzS * z)
+
+
+def test_I12_backward_matches_central_differences():
+    B, Hq, Hkv, N, d, L = 1, 4, 2, 6, 3, 2
+    Q, K, V, beta = _problem(B, Hq, Hkv, N, d, seed=131)
+    M0, z0 = _prefix_state(B, Hkv, d)
+    dO = _rand(Q.shape, 140)
+    dMS = _rand(M0.shape, 141, 0.1)
+    dzS = _rand(z0.shape, 142, 0.1)
+    g = O.backward(Q, K, V, beta, L, dO, M0, z0, dMS, dzS)
+    params = dict(Q=Q, K=K, V=V, beta=beta, M0=M0, z0=z0)
+    names = dict(Q="dQ", K="dK", V="dV", beta="dbeta", M0="dM0", z0="dz0")
+    h = 1e-6
+    for p, gname in names.items():
+        fd = np.zeros_like(params[p])
+        it = np.nditer(params[p], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = {k: v.copy() for k, v in params.items()}
+            minus = {k: v.copy() for k, v in params.items()}
+            plus[p][idx] += h
+            minus[p][idx] -= h
+            fd[idx] = (_loss(plus, dO, dMS, dzS, L) - _loss(minus, dO, dMS, dzS, L)) / (2 * h)
+        assert max_rel_err(g[gname], fd) < 1e-6, p
+
+
+def test_I12_gate_closed_gradients_match_torch_autograd_sdpa():
+    """With beta = -inf and no upstream state gradient the backward is plain
+    per-segment causal attention backward: compare with torch autograd."""
+    B, Hq, Hkv, N, d, L = 1, 4, 2, 16, 8, 8
+    Q, K, V, _ = _problem(B, Hq, Hkv, N, d, seed=151)
+    dO = _rand(Q.shape, 152)
+    g = O.backward(Q, K, V, np.full(Hq, -np.inf), L, dO)
+    q = torch.tensor(Q, requires_grad=True)
+    k = torch.tensor(K, requires_grad=True)
+    v = torch.tensor(V, requires_grad=True)
+    outs = []
+    for s in range(N // L):
+        r = slice(s * L, (s + 1) * L)
+        outs.append(torch.nn.functional.scaled_dot_product_attention(
+            q[:, :, r], k[:, :, r].repeat_interleave(Hq // Hkv, 1),
+            v[:, :, r].repeat_interleave(Hq // Hkv, 1), is_causal=True))
+    (torch.cat(outs, dim=2) * torch.tensor(dO)).sum().backward()
+    assert np.max(np.abs(g["dQ"] - q.grad.numpy())) < 1e-12
+    assert np.max(np.abs(g["dK"] - k.grad.numpy())) < 1e-12
+    assert np.max(np.abs(g["dV"] - v.grad.numpy())) < 1e-12
+    assert np.all(g["dbeta"] == 0.0)
+
+
+def test_I12_dbeta_from_forward_calls_only():
+    """dbeta_h = g_h * sum dO * (O(beta=+inf) - O(beta)): two forward calls, no backward code."""
+    Q, K, V, beta = _problem(B=2, Hq=4, Hkv=2, N=16, d=4, seed=161)
+    dO = _rand(Q.shape, 162)
+    o, _, _ = O.forward(Q, K, V, beta, 4)
+    o_mem, _, _ = O.forward(Q, K, V, np.full(4, np.inf), 4)
+    gg = 1 / (1 + np.exp(-beta))
+    ref = gg * np.sum(dO * (o_mem - o), axis=(0, 2, 3))
+    got = O.backward(Q, K, V, beta, 4, dO)["dbeta"]
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_backward_chains_across_calls():
+    """dM0 / dz0 of a later call fed as dM_S / dz_S of the earlier call equals
+    one backward over both halves."""
+    Q, K, V, beta = _problem(B=1, Hq=2, Hkv=1, N=16, d=4, seed=171)
+    dO = _rand(Q.shape, 172)
+    L = 4
+    full = O.backward(Q, K, V, beta, L, dO)
+    a, b = slice(0, 8), slice(8, 16)
+    _, M1, z1 = O.forward(Q[:, :, a], K[:, :, a], V[:, :, a], beta, L)
+    g2 = O.backward(Q[:, :, b], K[:, :, b], V[:, :, b], beta, L, dO[:, :, b], M1, z1)
+    g1 = O.backward(Q[:, :, a], K[:, :, a], V[:, :, a], beta, L, dO[:, :, a],
+                    dM_S=g2["dM0"], dz_S=g2["dz0"])
+    assert np.max(np.abs(np.concatenate([g1["dQ"], g2["dQ"]], 2) - full["dQ"])) < 1e-12
+    assert np.max(np.abs(np.concatenate([g1["dK"], g2["dK"]], 2) - full["dK"])) < 1e-12
+    assert np.max(np.abs(np.concatenate([g1["dV"], g2["dV"]], 2) - full["dV"])) < 1e-12
+    assert np.max(np.abs(g1["dbeta"] + g2["dbeta"] - full["dbeta"])) < 1e-12
