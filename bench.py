@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Infini-attention forward throughput on one MI355X.
+
+Workload (default): the Llama-3-8B head shape — B=4, 32 query heads sharing
+8 K/V heads, head_dim 128, segments of 2048 tokens, 16 segments (32768
+tokens), bf16 Q/K/V ~ N(0,1)/sqrt(128), beta ~ N(0,1), fp32 memory state;
+seeded synthetic inputs (no dataset or trained weights exist for it here).
+
+One step is one whole forward call over the batch: the memory phase
+(infini_fwd_memory: sigma(K)^T V and sum sigma(K) per segment, exclusive
+prefix over segments) followed by the attention phase (infini_fwd_attend:
+causal softmax attention inside each segment, retrieval from the memory,
+sigmoid gate).  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from compressive_linear_memory_amd import inputs as I  # noqa: E402
+
+PEAK_BF16_MFMA_TFLOPS = 2500.0
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "Infini-attention fwd tokens/s at Llama-3-8B head shape; % bf16 MFMA peak"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w: I.Workload):
+    """Algorithmic work of one forward call (the method's own arithmetic and a
+    single pass over every tensor; no masked-out upper triangle, no recompute)."""
+    B, Hq, Hkv, L, S, d = w.batch, w.q_heads, w.kv_heads, w.seg_len, w.segments, w.head_dim
+    eb = 4 if w.dtype == "fp32" else 2
+    uq, ukv = B * Hq * S, B * Hkv * S
+    local = 2 * 2 * d * L * (L + 1) / 2            # QK^T and PV over the causal lower triangle
+    retrieval = 2 * L * d * d + 2 * L * d           # sigma(Q) M and sigma(Q) z
+    update = 2 * L * d * d + L * d                  # sigma(K)^T V and sum sigma(K)
+    n_q = B * Hq * w.seq_len * d
+    n_kv = B * Hkv * w.seq_len * d
+    state = B * Hkv * (d * d + d) * 4
+    snaps = ukv * (d * d + d) * 4                   # per-segment state handed from phase 1 to phase 2
+    return dict(
+        attend_flop=uq * (local + retrieval),
+        attend_bytes=eb * (2 * n_q + 2 * n_kv) + snaps,
+        memory_flop=ukv * update,
+        memory_bytes=eb * 2 * n_kv + snaps + state,
+        step_flop=uq * (local + retrieval) + ukv * update,
+        step_bytes=eb * (2 * n_q + 2 * n_kv) + 2 * state,
+    )
+
+
+def cpu_baseline(w, Q, K, V, beta, o_gpu_host_rows, budget_s=12.0):
+    """Time the fp64 oracle on a bounded sample of the same workload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    L = w.seg_len
+    G = w.q_heads // w.kv_heads
+    t0 = time.perf_counter()
+    Msnap, zsnap, _, _ = O.state_sweep(K, V, L)
+    t_sweep = time.perf_counter() - t0
+    rng = np.random.default_rng(1234)
+    units, t_units = 0, 0.0
+    errs = []
+    while t_units < budget_s and units < 1024:
+        b = int(rng.integers(0, w.batch)); h = int(rng.integers(0, w.q_heads)); s = units % w.segments
+        r = slice(s * L, (s + 1) * L)
+        t1 = time.perf_counter()
+        ref = O.segment_unit(Q[b, h, r], K[b, h // G, r], V[b, h // G, r], Msnap[b, h // G, s],
+                             zsnap[b, h // G, s], beta[h])
+        t_units += time.perf_counter() - t1
+        units += 1
+        got = o_gpu_host_rows(b, h, s)
+        errs.append((np.max(np.abs(got - ref)), np.max(np.abs(ref))))
+    per_unit = t_units / units
+    total_units = w.batch * w.q_heads * w.segments
+    est = t_sweep + per_unit * total_units
+    tok = w.batch * w.seq_len
+    err = max(e for e, _ in errs) / max(m for _, m in errs)
+    return dict(value=tok / est, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=(f"full fp64 state sweep ({t_sweep:.2f} s) + {units} of {total_units} "
+                        f"(batch, head, segment) units in full ({t_units:.2f} s); "
+                        f"whole-workload time extrapolated as sweep + per-unit x units = {est:.1f} s")), err
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="fwd_llama3_8b", choices=sorted(I.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the sequence-parallel "
+              "multi-GPU path is a design note, not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from compressive_linear_memory_amd import binding as Bi
+    Bi.lib()                                    # fail loudly if the HIP library is missing
+    w = I.WORKLOADS[args.workload]
+    if w.launches != 1:
+        w = w.with_(launches=1)
+    if w.segments > 16:
+        raise SystemExit("bench times single-chunk workloads")
+    say(f"[bench] generating {w.name} inputs")
+    Q, K, V = I.qkv(w)
+    beta = I.beta(w)
+    tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(Q).to(dev).to(tdt)
+    k = torch.from_numpy(K).to(dev).to(tdt)
+    v = torch.from_numpy(V).to(dev).to(tdt)
+    b = torch.from_numpy(beta).to(dev)
+    p = Bi.problem(q, k, w.seg_len)
+    path = Bi.fwd_path(p)
+    ws = torch.empty(Bi.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    O_ = torch.empty_like(q)
+    B_, Hkv, d = w.batch, w.kv_heads, w.head_dim
+    M_S = torch.empty((B_, Hkv, d, d), dtype=torch.float32, device=dev)
+    z_S = torch.empty((B_, Hkv, d), dtype=torch.float32, device=dev)
+
+    def step():
+        Bi.fwd_memory(p, k, v, None, None, M_S, z_S, ws)
+        Bi.fwd_attend(p, q, k, v, b, O_, None, ws)
+
+    say(f"[bench] path {path}; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        Bi.fwd_memory(p, k, v, None, None, M_S, z_S, ws)
+        ev[i][1].record()
+        Bi.fwd_attend(p, q, k, v, b, O_, None, ws)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev[0][0].elapsed_time(ev[-1][2])
+    mem_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_step = total_ms / args.steps
+    tokens = w.batch * w.seq_len
+    value = tokens * args.steps / (total_ms / 1e3)
+    say(f"[bench] {ms_step:.3f} ms/step (memory {mem_ms:.3f} ms, attend {att_ms:.3f} ms); wall {wall:.2f} s")
+
+    alg = algorithmic(w)
+    if path == "mfma_bf16":
+        roof = dict(bound="mfma", peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s")
+        dtype = "bf16"
+    else:
+        roof = dict(bound="alu", peak=PEAK_FP32_VECTOR_TFLOPS, unit="TFLOP/s")
+        dtype = "fp32"
+    achieved = alg["attend_flop"] / (att_ms / 1e3) / 1e12
+    roof.update(achieved=round(achieved, 3), frac=round(achieved / roof["peak"], 5), traffic=None,
+                kernel="infini_fwd_attend", flop_per_launch=alg["attend_flop"],
+                launch_ms=round(att_ms, 4))
+    step_tflops = alg["step_flop"] / (ms_step / 1e3) / 1e12
+    out = {
+        "metric": METRIC if w.name == "fwd_llama3_8b" else f"Infini-attention fwd tokens/s ({w.name})",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "head_dim": w.head_dim, "seg_len": w.seg_len, "segments": w.segments,
+                   "seq_len": w.seq_len, "io_dtype": w.dtype, "kernel_path": path},
+        "pct_bf16_mfma_peak": round(100 * step_tflops / PEAK_BF16_MFMA_TFLOPS, 3),
+        "step_tflops": round(step_tflops, 3),
+        "phases_ms": {"memory": round(mem_ms, 4), "attend": round(att_ms, 4)},
+        "memory_phase_gbs": round(alg["memory_bytes"] / (mem_ms / 1e3) / 1e9, 1),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        say("[bench] timing the CPU oracle on a bounded sample")
+        o_cpu = None
+
+        def rows(bb, hh, ss):
+            nonlocal o_cpu
+            L = w.seg_len
+            return O_[bb, hh, ss * L:(ss + 1) * L].float().cpu().numpy().astype(np.float64)
+
+        cb, err = cpu_baseline(w, Q, K, V, beta, rows)
+        out["cpu_baseline"] = cb
+        out["parity_sampled_max_rel_err"] = float(err)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+"""ctypes binding of libinfini (argument marshalling only).
+
+Every step of the computation runs in the HIP library; this module checks
+tensor properties, allocates outputs and workspace with torch on the GPU and
+passes raw device pointers plus torch's current stream.  There is no other
+implementation to fall back to: if libinfini.so is missing or fails to load,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libinfini.so")
+
+INFINI_FP32, INFINI_BF16 = 0, 1
+_DTYPES = {torch.float32: INFINI_FP32, torch.bfloat16: INFINI_BF16}
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("seg_len", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class InfiniError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {lib().infini_status_string(code).decode()} (status {code})")
+        self.code = code
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load libinfini.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.infini_status_string.restype = ctypes.c_char_p
+        L.infini_status_string.argtypes = [ctypes.c_int]
+        L.infini_version.restype = ctypes.c_int
+        L.infini_version.argtypes = []
+        for fn in ("infini_fwd_workspace_bytes", "infini_bwd_workspace_bytes"):
+            getattr(L, fn).restype = ctypes.c_size_t
+            getattr(L, fn).argtypes = [ctypes.POINTER(Problem)]
+        L.infini_attn_fwd.restype = ctypes.c_int
+        L.infini_attn_fwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 11 + [ctypes.c_size_t, _P]
+        L.infini_attn_bwd.restype = ctypes.c_int
+        L.infini_attn_bwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 17 + [ctypes.c_size_t, _P]
+        L.infini_fwd_path.restype = ctypes.c_char_p
+        L.infini_fwd_path.argtypes = [ctypes.POINTER(Problem)]
+        L.infini_fwd_memory.restype = ctypes.c_int
+        L.infini_fwd_memory.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_size_t, _P]
+        L.infini_fwd_attend.restype = ctypes.c_int
+        L.infini_fwd_attend.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_size_t, _P]
+        _lib = L
+    return _lib
+
+
+def problem(q: torch.Tensor, k: torch.Tensor, seg_len: int) -> Problem:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [batch, heads, seq_len, head_dim]")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, Hq, N, d = q.shape
+    return Problem(B, Hq, k.shape[1], N, d, int(seg_len), _DTYPES[q.dtype])
+
+
+def workspace_bytes(p: Problem, backward: bool = False) -> int:
+    fn = lib().infini_bwd_workspace_bytes if backward else lib().infini_fwd_workspace_bytes
+    return int(fn(ctypes.byref(p)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(name, t, dtype, shape, device):
+    if t is None:
+        return
+    if t.device != device or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: need contiguous {dtype} {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def attn_fwd(q, k, v, beta, seg_len, M0=None, z0=None, want_lse=False, out=None, ws=None):
+    """O, M_S, z_S (and lse if want_lse) of one call; see include/infini.h.
+
+    `out` may hold preallocated (O, M_S, z_S, lse) tensors and `ws` a uint8
+    workspace tensor, so that a timed loop allocates nothing."""
+    p = problem(q, k, seg_len)
+    dev = q.device
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    for name, t, dt, shp in (("k", k, q.dtype, (B, Hkv, N, d)), ("v", v, q.dtype, (B, Hkv, N, d)),
+                             ("beta", beta, torch.float32, (Hq,)),
+                             ("M0", M0, torch.float32, (B, Hkv, d, d)), ("z0", z0, torch.float32, (B, Hkv, d))):
+        _check(name, t, dt, shp, dev)
+    _check("q", q, q.dtype, q.shape, dev)
+    if out is None:
+        O = torch.empty_like(q)
+        M_S = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=dev)
+        z_S = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if want_lse else None
+    else:
+        O, M_S, z_S, lse = out
+    if ws is None:
+        ws = torch.empty(max(workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
+    rc = lib().infini_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
+                               _ptr(O), _ptr(M_S), _ptr(z_S), _ptr(lse), _ptr(ws), ws.numel(), _stream())
+    if rc != 0:
+        raise InfiniError(rc, "infini_attn_fwd")
+    return (O, M_S, z_S, lse) if want_lse else (O, M_S, z_S)
+
+
+def attn_bwd(q, k, v, beta, seg_len, dO, M0=None, z0=None, lse=None, dM_S=None, dz_S=None,
+             want_state_grads=False, ws=None):
+    """dQ, dK, dV, dbeta (and dM0, dz0 if want_state_grads); see include/infini.h."""
+    p = problem(q, k, seg_len)
+    dev = q.device
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    for name, t, dt, shp in (("k", k, q.dtype, (B, Hkv, N, d)), ("v", v, q.dtype, (B, Hkv, N, d)),
+                             ("dO", dO, q.dtype, (B, Hq, N, d)), ("beta", beta, torch.float32, (Hq,)),
+                             ("M0", M0, torch.float32, (B, Hkv, d, d)), ("z0", z0, torch.float32, (B, Hkv, d)),
+                             ("lse", lse, torch.float32, (B, Hq, N)),
+                             ("dM_S", dM_S, torch.float32, (B, Hkv, d, d)),
+                             ("dz_S", dz_S, torch.float32, (B, Hkv, d))):
+        _check(name, t, dt, shp, dev)
+    dQ = torch.empty_like(q)
+    dK = torch.empty_like(k)
+    dV = torch.empty_like(v)
+    dbeta = torch.empty((Hq,), dtype=torch.float32, device=dev)
+    dM0 = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=dev) if want_state_grads else None
+    dz0 = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev) if want_state_grads else None
+    if ws is None:
+        ws = torch.empty(max(workspace_bytes(p, backward=True), 1), dtype=torch.uint8, device=dev)
+    rc = lib().infini_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
+                               _ptr(lse), _ptr(dO), _ptr(dM_S), _ptr(dz_S), _ptr(dQ), _ptr(dK), _ptr(dV),
+                               _ptr(dbeta), _ptr(dM0), _ptr(dz0), _ptr(ws), ws.numel(), _stream())
+    if rc != 0:
+        raise InfiniError(rc, "infini_attn_bwd")
+    if want_state_grads:
+        return dQ, dK, dV, dbeta, dM0, dz0
+    return dQ, dK, dV, dbeta
+
+
+def fwd_memory(p: Problem, k, v, M0, z0, M_S, z_S, ws):
+    """Phase 1 of the forward (memory path only) on preallocated buffers."""
+    rc = lib().infini_fwd_memory(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(M0), _ptr(z0), _ptr(M_S), _ptr(z_S),
+                                 _ptr(ws), ws.numel(), _stream())
+    if rc != 0:
+        raise InfiniError(rc, "infini_fwd_memory")
+
+
+def fwd_attend(p: Problem, q, k, v, beta, O, lse, ws):
+    """Phase 2 of the forward (attention, retrieval, gate) on preallocated buffers."""
+    rc = lib().infini_fwd_attend(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(O), _ptr(lse),
+                                 _ptr(ws), ws.numel(), _stream())
+    if rc != 0:
+        raise InfiniError(rc, "infini_fwd_attend")
+
+
+def fwd_path(p: Problem) -> str:
+    """Kernel family the forward runs for this problem."""
+    r = lib().infini_fwd_path(ctypes.byref(p))
+    return r.decode() if r else ""

@@ -1,0 +1,299 @@
+// libinfini C ABI: validation, workspace layout and launch order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/infini.h"
+#include "kernels.h"
+
+namespace {
+
+using infini::Geometry;
+
+constexpr int kMaxChunkSegments = INFINI_CHUNK_SEGMENTS;   // segments whose snapshots live in the workspace at once
+
+bool valid_problem(const infini_problem_t* p, infini_status_t* why) {
+  if (!p) { *why = INFINI_ERR_NULL; return false; }
+  if (p->batch <= 0 || p->q_heads <= 0 || p->kv_heads <= 0 || p->seq_len <= 0 ||
+      p->head_dim <= 0 || p->seg_len <= 0) { *why = INFINI_ERR_SHAPE; return false; }
+  if (p->seq_len % p->seg_len != 0 || p->q_heads % p->kv_heads != 0) {
+    *why = INFINI_ERR_SHAPE; return false;
+  }
+  if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) {
+    *why = INFINI_ERR_UNSUPPORTED; return false;
+  }
+  if (p->dtype != INFINI_FP32 && p->dtype != INFINI_BF16) { *why = INFINI_ERR_UNSUPPORTED; return false; }
+  // Every index the kernels form must fit comfortably in 64 bits and every
+  // per-call count in 32 bits.
+  const double elems = (double)p->batch * p->q_heads * p->seq_len * p->head_dim;
+  if (elems > 9.0e15 || (double)p->batch * p->q_heads > 2147483647.0) { *why = INFINI_ERR_SHAPE; return false; }
+  return true;
+}
+
+Geometry geometry(const infini_problem_t* p) {
+  Geometry g;
+  g.B = p->batch; g.Hq = p->q_heads; g.Hkv = p->kv_heads; g.N = p->seq_len;
+  g.D = p->head_dim; g.L = p->seg_len; g.S = p->seq_len / p->seg_len; g.dtype = p->dtype;
+  return g;
+}
+
+int chunk_segments(const Geometry& g) {
+  int c = kMaxChunkSegments;
+  if (const char* e = getenv("INFINI_CHUNK_SEGMENTS")) {   // test hook: force multi-chunk paths
+    const int v = atoi(e);
+    if (v >= 1 && v < c) c = v;
+  }
+  return g.S < c ? g.S : c;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t elem_bytes(const Geometry& g) { return g.dtype == INFINI_FP32 ? 4 : 2; }
+
+// ---- workspace layouts (byte offsets, 256-aligned)
+
+struct FwdWs { size_t Msnap, zsnap, total; };
+FwdWs fwd_layout(const Geometry& g) {
+  const size_t C = (size_t)(g.S < kMaxChunkSegments ? g.S : kMaxChunkSegments);
+  const size_t bk = (size_t)g.B * g.Hkv;
+  FwdWs w;
+  size_t off = 0;
+  w.Msnap = off; off = align_up(off + bk * C * g.D * g.D * 4);
+  w.zsnap = off; off = align_up(off + bk * C * g.D * 4);
+  w.total = off;
+  return w;
+}
+
+struct BwdWs { size_t Mst, zst, Msnap, zsnap, dMc, dzc, dMsnap, dzsnap, lse, Dd, dden, dnum, dbp, dbacc, total; };
+BwdWs bwd_layout(const Geometry& g) {
+  const size_t C = (size_t)(g.S < kMaxChunkSegments ? g.S : kMaxChunkSegments);
+  const size_t bk = (size_t)g.B * g.Hkv;
+  const size_t rows = (size_t)g.B * g.Hq * C * g.L;
+  const size_t D = g.D;
+  BwdWs w;
+  size_t off = 0;
+  w.Mst = off;    off = align_up(off + bk * D * D * 4);
+  w.zst = off;    off = align_up(off + bk * D * 4);
+  w.Msnap = off;  off = align_up(off + bk * C * D * D * 4);
+  w.zsnap = off;  off = align_up(off + bk * C * D * 4);
+  w.dMc = off;    off = align_up(off + bk * D * D * 4);
+  w.dzc = off;    off = align_up(off + bk * D * 4);
+  w.dMsnap = off; off = align_up(off + bk * C * D * D * 4);
+  w.dzsnap = off; off = align_up(off + bk * C * D * 4);
+  w.lse = off;    off = align_up(off + rows * 4);
+  w.Dd = off;     off = align_up(off + rows * 4);
+  w.dden = off;   off = align_up(off + rows * 4);
+  w.dnum = off;   off = align_up(off + rows * D * 4);
+  w.dbp = off;    off = align_up(off + (size_t)g.B * g.Hq * C * infini::bwd_q_row_blocks(g) * 4);
+  w.dbacc = off;  off = align_up(off + (size_t)g.Hq * 4);
+  w.total = off;
+  return w;
+}
+
+// ---- aliasing
+
+struct Span { const void* p; size_t n; };
+bool overlap(Span a, Span b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
+  for (int i = 0; i < no; ++i) {
+    for (int j = 0; j < ni; ++j) if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < no; ++j) if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+infini_status_t hip_status(hipError_t e) { return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP; }
+
+#define TRY(expr)                                       \
+  do {                                                  \
+    hipError_t e_ = (expr);                             \
+    if (e_ != hipSuccess) return hip_status(e_);        \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* infini_status_string(infini_status_t s) {
+  switch (s) {
+    case INFINI_OK: return "ok";
+    case INFINI_ERR_NULL: return "a required pointer is NULL";
+    case INFINI_ERR_SHAPE: return "invalid shape (dims must be > 0, seq_len % seg_len == 0, q_heads % kv_heads == 0)";
+    case INFINI_ERR_UNSUPPORTED: return "unsupported head_dim (32, 64, 128) or dtype";
+    case INFINI_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+    case INFINI_ERR_WORKSPACE: return "workspace is NULL or too small";
+    case INFINI_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+int infini_version(void) { return INFINI_VERSION; }
+
+const char* infini_fwd_path(const infini_problem_t* p) {
+  infini_status_t why;
+  if (!valid_problem(p, &why)) return nullptr;
+  return "generic_fp32";
+}
+
+size_t infini_fwd_workspace_bytes(const infini_problem_t* p) {
+  infini_status_t why;
+  if (!valid_problem(p, &why)) return 0;
+  return fwd_layout(geometry(p)).total;
+}
+
+size_t infini_bwd_workspace_bytes(const infini_problem_t* p) {
+  infini_status_t why;
+  if (!valid_problem(p, &why)) return 0;
+  return bwd_layout(geometry(p)).total;
+}
+
+infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const void* K,
+                                const void* V, const float* beta, const float* M0, const float* z0,
+                                void* O, float* M_S, float* z_S, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
+  infini_status_t why;
+  if (!valid_problem(p, &why)) return why;
+  if (!Q || !K || !V || !beta || !O || !M_S || !z_S) return INFINI_ERR_NULL;
+  if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
+  const Geometry g = geometry(p);
+  const FwdWs lay = fwd_layout(g);
+  if (!ws || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
+  const size_t eb = elem_bytes(g);
+  const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
+  const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
+  const Span outs[] = {{O, nq * eb}, {M_S, nM}, {z_S, nz}, {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0},
+                       {ws, lay.total}};
+  const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
+                      {M0, M0 ? nM : 0}, {z0, z0 ? nz : 0}};
+  if (any_overlap(outs, 5, ins, 6)) return INFINI_ERR_ALIAS;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* Msnap = reinterpret_cast<float*>(base + lay.Msnap);
+  float* zsnap = reinterpret_cast<float*>(base + lay.zsnap);
+  const int C = chunk_segments(g);
+  for (int s0 = 0; s0 < g.S; s0 += C) {
+    const int s1 = s0 + C < g.S ? s0 + C : g.S;
+    const float* Min = s0 == 0 ? M0 : M_S;
+    const float* zin = s0 == 0 ? z0 : z_S;
+    TRY(infini::launch_sweep(g, K, V, Min, zin, M_S, z_S, Msnap, zsnap, s0, s1, st));
+    TRY(infini::launch_fwd_generic(g, Q, K, V, beta, Msnap, zsnap, O, lse, s0, s1, st));
+  }
+  return INFINI_OK;
+}
+
+infini_status_t infini_fwd_memory(const infini_problem_t* p, const void* K, const void* V,
+                                  const float* M0, const float* z0, float* M_S, float* z_S,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  infini_status_t why;
+  if (!valid_problem(p, &why)) return why;
+  if (!K || !V || !M_S || !z_S) return INFINI_ERR_NULL;
+  if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
+  const Geometry g = geometry(p);
+  if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
+  const FwdWs lay = fwd_layout(g);
+  if (!ws || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
+  const size_t eb = elem_bytes(g);
+  const size_t nkv = (size_t)g.B * g.Hkv * g.N * g.D;
+  const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
+  const Span outs[] = {{M_S, nM}, {z_S, nz}, {ws, lay.total}};
+  const Span ins[] = {{K, nkv * eb}, {V, nkv * eb}, {M0, M0 ? nM : 0}, {z0, z0 ? nz : 0}};
+  if (any_overlap(outs, 3, ins, 4)) return INFINI_ERR_ALIAS;
+  char* base = static_cast<char*>(ws);
+  TRY(infini::launch_sweep(g, K, V, M0, z0, M_S, z_S, reinterpret_cast<float*>(base + lay.Msnap),
+                           reinterpret_cast<float*>(base + lay.zsnap), 0, g.S,
+                           static_cast<hipStream_t>(stream)));
+  return INFINI_OK;
+}
+
+infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, const void* K,
+                                  const void* V, const float* beta, void* O, float* lse,
+                                  const void* ws, size_t ws_bytes, void* stream) {
+  infini_status_t why;
+  if (!valid_problem(p, &why)) return why;
+  if (!Q || !K || !V || !beta || !O) return INFINI_ERR_NULL;
+  const Geometry g = geometry(p);
+  if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
+  const FwdWs lay = fwd_layout(g);
+  if (!ws || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
+  const size_t eb = elem_bytes(g);
+  const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
+  const Span outs[] = {{O, nq * eb}, {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0}};
+  const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
+                      {ws, lay.total}};
+  if (any_overlap(outs, 2, ins, 5)) return INFINI_ERR_ALIAS;
+  const char* base = static_cast<const char*>(ws);
+  TRY(infini::launch_fwd_generic(g, Q, K, V, beta, reinterpret_cast<const float*>(base + lay.Msnap),
+                                 reinterpret_cast<const float*>(base + lay.zsnap), O, lse, 0, g.S,
+                                 static_cast<hipStream_t>(stream)));
+  return INFINI_OK;
+}
+
+infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const void* K,
+                                const void* V, const float* beta, const float* M0, const float* z0,
+                                const float* lse, const void* dO, const float* dM_S,
+                                const float* dz_S, void* dQ, void* dK, void* dV, float* dbeta,
+                                float* dM0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
+  (void)lse;  // the generic backward recomputes the row statistics
+  infini_status_t why;
+  if (!valid_problem(p, &why)) return why;
+  if (!Q || !K || !V || !beta || !dO || !dQ || !dK || !dV || !dbeta) return INFINI_ERR_NULL;
+  if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
+  if ((dM_S == nullptr) != (dz_S == nullptr)) return INFINI_ERR_NULL;
+  if ((dM0 == nullptr) != (dz0 == nullptr)) return INFINI_ERR_NULL;
+  const Geometry g = geometry(p);
+  const BwdWs lay = bwd_layout(g);
+  if (!ws || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
+  const size_t eb = elem_bytes(g);
+  const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
+  const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
+  const Span outs[] = {{dQ, nq * eb}, {dK, nkv * eb}, {dV, nkv * eb}, {dbeta, (size_t)g.Hq * 4},
+                       {dM0, dM0 ? nM : 0}, {dz0, dz0 ? nz : 0}, {ws, lay.total}};
+  const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
+                      {M0, M0 ? nM : 0}, {z0, z0 ? nz : 0}, {dO, nq * eb},
+                      {dM_S, dM_S ? nM : 0}, {dz_S, dz_S ? nz : 0},
+                      {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0}};
+  if (any_overlap(outs, 7, ins, 10)) return INFINI_ERR_ALIAS;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  infini::BwdChunkWs w;
+  w.lse = F(lay.lse); w.Dd = F(lay.Dd); w.dden = F(lay.dden); w.dnum = F(lay.dnum);
+  w.dbeta_part = F(lay.dbp); w.dMsnap = F(lay.dMsnap); w.dzsnap = F(lay.dzsnap);
+  float* Mst = F(lay.Mst); float* zst = F(lay.zst);
+  float* Msnap = F(lay.Msnap); float* zsnap = F(lay.zsnap);
+  float* dMc = F(lay.dMc); float* dzc = F(lay.dzc);
+  float* dbacc = F(lay.dbacc);
+
+  const int C = chunk_segments(g);
+  const int nchunks = (g.S + C - 1) / C;
+  for (int ci = nchunks - 1; ci >= 0; --ci) {
+    const int s0 = ci * C;
+    const int s1 = s0 + C < g.S ? s0 + C : g.S;
+    const float* Mstart = M0;
+    const float* zstart = z0;
+    if (s0 > 0) {   // state at the chunk start: replay the memory path from M0
+      TRY(infini::launch_sweep(g, K, V, M0, z0, Mst, zst, nullptr, nullptr, 0, s0, st));
+      Mstart = Mst; zstart = zst;
+    }
+    TRY(infini::launch_sweep(g, K, V, Mstart, zstart, nullptr, nullptr, Msnap, zsnap, s0, s1, st));
+    TRY(infini::launch_bwd_q(g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, s0, s1, st));
+    const bool first = ci == nchunks - 1, last = ci == 0;
+    TRY(infini::launch_dbeta_reduce(g, beta, w, dbacc, dbeta, s1 - s0, first, last, st));
+    const float* dMin = first ? dM_S : dMc;
+    const float* dzin = first ? dz_S : dzc;
+    float* dMout = last ? dM0 : dMc;
+    float* dzout = last ? dz0 : dzc;
+    TRY(infini::launch_rscan(g, Q, w, dMin, dzin, dMout, dzout, s0, s1, st));
+    TRY(infini::launch_bwd_kv(g, Q, K, V, beta, dO, w, dK, dV, s0, s1, st));
+  }
+  return INFINI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Host-side launch interface between api.cpp and the HIP kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace infini {
+
+// One call's geometry, after validation.
+struct Geometry {
+  int B, Hq, Hkv, N, D, L, S;   // S = N / L segments
+  int dtype;                    // 0 fp32, 1 bf16
+  int G() const { return Hq / Hkv; }
+};
+
+// Memory path over segments [s_begin, s_end) of the call.
+//   M_in/z_in: state before segment s_begin (NULL = empty memory).
+//   M_out/z_out: state after segment s_end - 1 (NULL = not written; may equal M_in).
+//   Msnap/zsnap: per-segment state before each segment, [B*Hkv][s_end-s_begin][D][D]
+//   (NULL = not written).
+hipError_t launch_sweep(const Geometry& g, const void* K, const void* V,
+                        const float* M_in, const float* z_in, float* M_out, float* z_out,
+                        float* Msnap, float* zsnap, int s_begin, int s_end, hipStream_t st);
+
+// Generic forward (fp32 vector arithmetic) over segments [s_begin, s_end),
+// reading the per-segment snapshots written by launch_sweep.
+hipError_t launch_fwd_generic(const Geometry& g, const void* Q, const void* K, const void* V,
+                              const float* beta, const float* Msnap, const float* zsnap,
+                              void* O, float* lse, int s_begin, int s_end, hipStream_t st);
+
+// Generic backward pieces, over segments [s_begin, s_end) (one chunk).
+struct BwdChunkWs {
+  float* lse;      // [B][Hq][C*L]
+  float* Dd;       // [B][Hq][C*L]   rowsum(dA_dot * A_dot)
+  float* dden;     // [B][Hq][C*L]
+  float* dnum;     // [B][Hq][C*L][D]
+  float* dbeta_part;  // [B][Hq][C][row blocks]
+  float* dMsnap;   // [B*Hkv][C][D][D]   gradient w.r.t. M_s
+  float* dzsnap;   // [B*Hkv][C][D]
+};
+
+int bwd_q_row_blocks(const Geometry& g);
+
+hipError_t launch_bwd_q(const Geometry& g, const void* Q, const void* K, const void* V,
+                        const float* beta, const float* Msnap, const float* zsnap,
+                        const void* dO, void* dQ, const BwdChunkWs& w,
+                        int s_begin, int s_end, hipStream_t st);
+
+hipError_t launch_rscan(const Geometry& g, const void* Q, const BwdChunkWs& w,
+                        const float* dM_in, const float* dz_in, float* dM_out, float* dz_out,
+                        int s_begin, int s_end, hipStream_t st);
+
+hipError_t launch_bwd_kv(const Geometry& g, const void* Q, const void* K, const void* V,
+                         const float* beta, const void* dO, const BwdChunkWs& w,
+                         void* dK, void* dV, int s_begin, int s_end, hipStream_t st);
+
+// dbeta_acc[h] (=, or += unless first) sum of the chunk's partials; when last,
+// dbeta[h] = g(1-g) * dbeta_acc[h].
+hipError_t launch_dbeta_reduce(const Geometry& g, const float* beta, const BwdChunkWs& w,
+                               float* dbeta_acc, float* dbeta, int nseg, bool first, bool last,
+                               hipStream_t st);
+
+}  // namespace infini

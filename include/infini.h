@@ -1,0 +1,175 @@
+/*
+ * libinfini — Infini-attention segment kernel for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes; no C++ or framework types.
+ *
+ * What is computed (per batch b, query head h, K/V head k = h / (Hq/Hkv)):
+ * the sequence is cut into fixed-length segments of seg_len tokens (page
+ * "Hugging Face Infini-Attention 재현 분석", section "Infini-Attention
+ * 메커니즘", step Segmentation).  For segment s, with rows r:
+ *
+ *   A_dot = softmax(mask(Q_r K_r^T / sqrt(d))) V_r     causal, inside the segment
+ *                                                       (same section, Local Attention)
+ *   A_mem = sigma(Q_r) M_{s-1} / (sigma(Q_r) z_{s-1} + INFINI_MEM_EPS)
+ *           sigma(x) = ELU(x) + 1 = x + 1 (x > 0), exp(x) (x <= 0)
+ *                                                       (Memory Retrieval)
+ *   O_r   = g_h A_mem + (1 - g_h) A_dot,  g_h = sigmoid(beta_h)   (Integration)
+ *   M_s   = M_{s-1} + sigma(K_r)^T V_r,   z_s = z_{s-1} + sum_rows sigma(K_r)
+ *                                                       (Memory Update)
+ *
+ * and only (M, z) is carried to the next segment (State Transfer).  The
+ * normalised linear-attention form of A_mem follows the page
+ * "[정보] KV선형 덧셈연산 인피니 어텐션에 대한 정보" (summary of "Leave No
+ * Context Behind"), which calls the memory path long-term linear attention
+ * that reuses the standard attention's query, key and value states.
+ *
+ * Layouts (all row-major, contiguous, device memory):
+ *   Q, O, dQ, dO : [batch][q_heads][seq_len][head_dim]     dtype of the problem
+ *   K, V, dK, dV : [batch][kv_heads][seq_len][head_dim]    dtype of the problem
+ *   beta, dbeta  : [q_heads]                                float32
+ *   M*, dM*      : [batch][kv_heads][head_dim][head_dim]    float32, M[a][c] = key-feature a, value c
+ *   z*, dz*      : [batch][kv_heads][head_dim]              float32
+ *   lse          : [batch][q_heads][seq_len]                float32, natural-log
+ *                  log-sum-exp of each row's scaled local scores
+ *
+ * Ownership: the caller allocates and frees every buffer (inputs, outputs,
+ * workspace).  The library never allocates, frees or synchronises; calls are
+ * asynchronous on `stream` (a hipStream_t, NULL = the default stream).  The
+ * library keeps no mutable global state, so concurrent calls on different
+ * streams with disjoint buffers are safe; calls sharing a workspace must be
+ * ordered by the caller.
+ *
+ * Errors: arguments are validated on the host before anything is launched;
+ * on any error nothing is written.  INFINI_ERR_HIP reports a failed launch.
+ */
+#ifndef INFINI_H
+#define INFINI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Added to sigma(Q) z in the retrieval denominator.  With an empty memory
+ * (M0 = z0 = 0) it makes A_mem exactly 0 in the first segment instead of 0/0. */
+#define INFINI_MEM_EPS 1e-6f
+
+#define INFINI_VERSION 1
+
+typedef enum {
+  INFINI_OK = 0,
+  INFINI_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+  INFINI_ERR_SHAPE = 2,       /* a dim <= 0, seq_len % seg_len != 0 or q_heads % kv_heads != 0 */
+  INFINI_ERR_UNSUPPORTED = 3, /* head_dim not 32, 64 or 128, or unknown dtype                   */
+  INFINI_ERR_ALIAS = 4,       /* an output buffer overlaps an input or another output          */
+  INFINI_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns          */
+  INFINI_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed                      */
+} infini_status_t;
+
+typedef enum { INFINI_FP32 = 0, INFINI_BF16 = 1 } infini_dtype_t;
+
+/* One call's problem.  The carried state is always float32. */
+typedef struct {
+  int32_t batch;
+  int32_t q_heads;
+  int32_t kv_heads;   /* q_heads % kv_heads == 0; query head h reads K/V head h / (q_heads/kv_heads) */
+  int32_t seq_len;    /* tokens in this call; a multiple of seg_len                                 */
+  int32_t head_dim;   /* 32, 64 or 128; keys, queries and values share it                            */
+  int32_t seg_len;    /* tokens per segment                                                          */
+  int32_t dtype;      /* infini_dtype_t of Q, K, V, O, dO, dQ, dK, dV                                */
+} infini_problem_t;
+
+/* Workspace bytes for infini_attn_fwd.  Bounded by a constant times
+ * batch*kv_heads*head_dim^2 that does not grow with seq_len (segments are
+ * processed in chunks of at most a fixed number).  Returns 0 for an invalid
+ * problem. */
+size_t infini_fwd_workspace_bytes(const infini_problem_t* p);
+
+/* Workspace bytes for infini_attn_bwd (does not grow with seq_len either). */
+size_t infini_bwd_workspace_bytes(const infini_problem_t* p);
+
+/* Forward.
+ *   Q, K, V   inputs (layouts above)
+ *   beta      [q_heads] gate parameters
+ *   M0, z0    carried state from an earlier call, or both NULL for an empty
+ *             memory.  Precondition: either both zero/NULL or produced by an
+ *             earlier call (or a consistent sum sigma(K)^T V, sum sigma(K));
+ *             z0 = 0 with M0 != 0 gives unspecified results.
+ *   O         [batch][q_heads][seq_len][head_dim] output
+ *   M_S, z_S  state after the last segment (must not alias M0 / z0: chained
+ *             calls ping-pong between two state buffers)
+ *   lse       optional [batch][q_heads][seq_len] float32 output, for the
+ *             backward; NULL to skip
+ *   ws        device workspace of at least infini_fwd_workspace_bytes(p)
+ */
+infini_status_t infini_attn_fwd(const infini_problem_t* p,
+                                const void* Q, const void* K, const void* V,
+                                const float* beta, const float* M0, const float* z0,
+                                void* O, float* M_S, float* z_S, float* lse,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Backward: the exact gradient of infini_attn_fwd for
+ *   loss = <dO, O> + <dM_S, M_S> + <dz_S, z_S>.
+ *   Q, K, V, beta, M0, z0   the forward's inputs (M0, z0 both NULL = empty memory)
+ *   lse        the forward's lse output, or NULL (then recomputed)
+ *   dO         upstream gradient of O (dtype of the problem)
+ *   dM_S, dz_S upstream gradients of the final state, or NULL for zero
+ *   dQ, dK, dV gradients (dtype of the problem), overwritten
+ *   dbeta      [q_heads] float32, overwritten
+ *   dM0, dz0   gradients of the state passed in, or NULL to skip; chaining
+ *              them as dM_S, dz_S of the previous call backpropagates through
+ *              a sequence of calls
+ *   ws         device workspace of at least infini_bwd_workspace_bytes(p)
+ */
+infini_status_t infini_attn_bwd(const infini_problem_t* p,
+                                const void* Q, const void* K, const void* V,
+                                const float* beta, const float* M0, const float* z0,
+                                const float* lse, const void* dO,
+                                const float* dM_S, const float* dz_S,
+                                void* dQ, void* dK, void* dV, float* dbeta,
+                                float* dM0, float* dz0,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Segments whose per-segment state a workspace holds at once.  Longer calls
+ * are processed in chunks of this many segments. */
+#define INFINI_CHUNK_SEGMENTS 16
+
+/* The forward in its two phases, for callers that schedule them separately
+ * (for example to overlap the memory phase of one layer with the attention
+ * phase of another, or to time each phase).  Only for calls with at most
+ * INFINI_CHUNK_SEGMENTS segments (seq_len / seg_len); longer calls return
+ * INFINI_ERR_SHAPE and must use infini_attn_fwd.
+ *
+ * infini_fwd_memory runs the memory path alone (same page and section,
+ * steps Memory Update and State Transfer): it writes M_S, z_S and leaves in
+ * `ws` the state each segment retrieves from.  infini_fwd_attend then runs
+ * local attention, retrieval and the gate for every segment, reading that
+ * state from `ws`; between the two calls the caller must not touch `ws`.
+ * Running both with the same arguments as infini_attn_fwd gives bit-identical
+ * results.  Argument meanings, layouts and errors are those of
+ * infini_attn_fwd. */
+infini_status_t infini_fwd_memory(const infini_problem_t* p, const void* K, const void* V,
+                                  const float* M0, const float* z0, float* M_S, float* z_S,
+                                  void* ws, size_t ws_bytes, void* stream);
+infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, const void* K,
+                                  const void* V, const float* beta, void* O, float* lse,
+                                  const void* ws, size_t ws_bytes, void* stream);
+
+/* Name of the kernel family infini_attn_fwd / infini_fwd_attend runs for this
+ * problem ("generic_fp32": fp32 vector-ALU path; "mfma_bf16": bf16 matrix-core
+ * path).  NULL for an invalid problem.  Static storage. */
+const char* infini_fwd_path(const infini_problem_t* p);
+
+/* Static description of a status code. */
+const char* infini_status_string(infini_status_t s);
+
+/* INFINI_VERSION of the loaded library. */
+int infini_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFINI_H */

@@ -1,0 +1,131 @@
+"""C ABI checks that need no GPU: symbols, status codes, validation, workspace sizes.
+
+Only calls that fail validation are made (validation runs on the host before
+any HIP call), so nothing here touches a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "infini.h")
+
+binding = pytest.importorskip("compressive_linear_memory_amd.binding")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libinfini.so not built")
+    return binding.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(infini_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    fns = header_functions()
+    for f in ("infini_attn_fwd", "infini_attn_bwd", "infini_fwd_workspace_bytes",
+              "infini_bwd_workspace_bytes", "infini_status_string", "infini_version"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(L):
+    for f in header_functions():
+        assert hasattr(L, f), f
+
+
+def test_version_and_status_strings(L):
+    assert L.infini_version() == 1
+    for code in range(7):
+        assert len(L.infini_status_string(code)) > 0
+    assert L.infini_status_string(0) == b"ok"
+
+
+def P(B=1, Hq=2, Hkv=2, N=64, d=32, L=16, dtype=0):
+    return binding.Problem(B, Hq, Hkv, N, d, L, dtype)
+
+
+FAKE = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(20)]   # never dereferenced
+
+
+def fwd(L, p, ptrs=None, ws_bytes=1 << 40, null=()):
+    a = list(ptrs or FAKE[:11])
+    for i in null:
+        a[i] = None
+    # order: Q K V beta M0 z0 O M_S z_S lse ws
+    return L.infini_attn_fwd(ctypes.byref(p), *a[:10], a[10], ws_bytes, None)
+
+
+def test_workspace_sizes(L):
+    assert L.infini_fwd_workspace_bytes(ctypes.byref(P())) > 0
+    assert L.infini_bwd_workspace_bytes(ctypes.byref(P())) > 0
+    assert L.infini_fwd_workspace_bytes(None) == 0
+    assert L.infini_fwd_workspace_bytes(ctypes.byref(P(N=60))) == 0   # 60 % 16 != 0
+    assert L.infini_fwd_workspace_bytes(ctypes.byref(P(d=48))) == 0
+
+
+def test_workspace_does_not_grow_with_sequence_length(L):
+    """Bounded state: once a call has more segments than one chunk holds, the
+    workspace stops growing with seq_len."""
+    sizes_f = {L.infini_fwd_workspace_bytes(ctypes.byref(P(N=16 * s))) for s in (16, 32, 512, 4096)}
+    sizes_b = {L.infini_bwd_workspace_bytes(ctypes.byref(P(N=16 * s))) for s in (16, 32, 512, 4096)}
+    assert len(sizes_f) == 1 and len(sizes_b) == 1
+    # and it never exceeds the 16-segment bound for short calls either
+    big = L.infini_fwd_workspace_bytes(ctypes.byref(P(N=16 * 16)))
+    for s in (1, 2, 7, 15):
+        assert L.infini_fwd_workspace_bytes(ctypes.byref(P(N=16 * s))) <= big
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 6, 7, 8])
+def test_fwd_null_required_pointer(L, idx):
+    assert fwd(L, P(), null=(idx,)) == 1
+
+
+def test_fwd_half_state_is_null_error(L):
+    assert fwd(L, P(), null=(4,)) == 1     # M0 NULL but z0 not
+    assert fwd(L, P(), null=(5,)) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=60), 2), (dict(Hq=3, Hkv=2), 2), (dict(B=0), 2), (dict(L=0), 2), (dict(N=-16), 2),
+    (dict(d=48), 3), (dict(d=256), 3), (dict(dtype=7), 3),
+])
+def test_fwd_shape_errors(L, kw, code):
+    assert fwd(L, P(**kw)) == code
+
+
+def test_fwd_workspace_too_small(L):
+    need = L.infini_fwd_workspace_bytes(ctypes.byref(P()))
+    assert fwd(L, P(), ws_bytes=need - 1) == 5
+    assert fwd(L, P(), null=(10,)) == 5
+
+
+def test_fwd_alias_output_overlaps_input(L):
+    a = list(FAKE[:11])
+    a[6] = ctypes.c_void_p(FAKE[0].value + 64)        # O inside Q
+    assert fwd(L, P(), a) == 4
+    a = list(FAKE[:11])
+    a[7] = a[4]                                       # M_S == M0 (in-place state is refused)
+    assert fwd(L, P(), a) == 4
+
+
+def test_bwd_validation(L):
+    p = P()
+    a = list(FAKE[:17])
+    # Q K V beta M0 z0 lse dO dM_S dz_S dQ dK dV dbeta dM0 dz0 ws
+    def call(args, ws_bytes=1 << 40):
+        return L.infini_attn_bwd(ctypes.byref(p), *args[:16], args[16], ws_bytes, None)
+    b = list(a); b[7] = None
+    assert call(b) == 1                               # dO missing
+    b = list(a); b[14] = None
+    assert call(b) == 1                               # dM0 without dz0
+    b = list(a); b[10] = b[7]
+    assert call(b) == 4                               # dQ aliases dO
+    need = L.infini_bwd_workspace_bytes(ctypes.byref(p))
+    assert call(a, need - 1) == 5

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP library against the fp64 CPU oracle, element by element.
+
+Tolerance: normwise max relative error ||x - ref||_inf / ||ref||_inf per output
+tensor, 1e-4 for fp32 problems and 2e-2 for bf16 problems.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from compressive_linear_memory_amd import inputs as I
+from gpu_util import TOL, dev, host, log, rel
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from compressive_linear_memory_amd import binding
+    binding.lib()
+
+
+def B():
+    from compressive_linear_memory_amd import binding
+    return binding
+
+
+def rnd(shape, seed, scale, dtype):
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32) * np.float32(scale)
+    return I.storage(x, dtype)
+
+
+def make(Bn, Hq, Hkv, N, d, dtype, seed, scale=None, with_state=False):
+    sc = (1.0 / np.sqrt(d)) if scale is None else scale
+    Q = rnd((Bn, Hq, N, d), seed, sc, dtype)
+    K = rnd((Bn, Hkv, N, d), seed + 1, sc, dtype)
+    V = rnd((Bn, Hkv, N, d), seed + 2, sc, dtype)
+    beta = np.random.default_rng(seed + 3).standard_normal(Hq).astype(np.float32)
+    M0 = z0 = None
+    if with_state:
+        Kp = rnd((Bn, Hkv, 48, d), seed + 4, sc, dtype)
+        Vp = rnd((Bn, Hkv, 48, d), seed + 5, sc, dtype)
+        _, _, M0, z0 = O.state_sweep(Kp, Vp, 48)
+        M0, z0 = M0.astype(np.float32), z0.astype(np.float32)
+    return Q, K, V, beta, M0, z0
+
+
+def run_fwd(Q, K, V, beta, L, M0, z0, dtype, want_lse=False):
+    return B().attn_fwd(dev(Q, dtype), dev(K, dtype), dev(V, dtype), dev(beta), L,
+                        dev(M0), dev(z0), want_lse=want_lse)
+
+
+def check_fwd(Q, K, V, beta, L, M0, z0, dtype, tag=""):
+    log(f"fwd {tag} Q{Q.shape} K{K.shape} L={L} {dtype} state={M0 is not None}")
+    o, M, z = run_fwd(Q, K, V, beta, L, M0, z0, dtype)
+    torch.cuda.synchronize()
+    ro, rM, rz = O.forward(Q, K, V, beta, L, M0, z0)
+    eo, eM, ez = rel(host(o), ro), rel(host(M), rM), rel(host(z), rz)
+    log(f"   err O {eo:.2e} M {eM:.2e} z {ez:.2e}")
+    tol = TOL[dtype]
+    assert eo < tol and eM < tol and ez < tol, (eo, eM, ez)
+    return o, M, z
+
+
+# ------------------------------------------------------------------ fp32 workload
+
+def test_tiny_fp32_forward():
+    w = I.WORKLOADS["tiny_fp32"]
+    Q, K, V = I.qkv(w)
+    check_fwd(Q, K, V, I.beta(w), w.seg_len, None, None, "fp32", "tiny_fp32")
+
+
+def _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, tag=""):
+    log(f"bwd {tag} Q{Q.shape} K{K.shape} L={L} {dtype} state={M0 is not None} dstate={dMS is not None}")
+    want_sg = True
+    g = B().attn_bwd(dev(Q, dtype), dev(K, dtype), dev(V, dtype), dev(beta), L, dev(dO, dtype),
+                     dev(M0), dev(z0), None, dev(dMS), dev(dzS), want_state_grads=want_sg)
+    torch.cuda.synchronize()
+    ref = O.backward(Q, K, V, beta, L, dO, M0, z0, dMS, dzS)
+    errs = {}
+    for name, t in zip(("dQ", "dK", "dV", "dbeta", "dM0", "dz0"), g):
+        errs[name] = rel(host(t), ref[name])
+    log("   " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    tol = TOL[dtype]
+    assert all(v < tol for v in errs.values()), errs
+
+
+def test_tiny_fp32_backward():
+    w = I.WORKLOADS["tiny_fp32"]
+    Q, K, V = I.qkv(w)
+    _check_bwd(Q, K, V, I.beta(w), w.seg_len, None, None, I.d_out(w), None, None, "fp32", "tiny_fp32")
+
+
+def test_tiny_fp32_backward_with_state_and_upstream_state_grads():
+    w = I.WORKLOADS["tiny_fp32"]
+    Q, K, V = I.qkv(w)
+    Kp, Vp = I.random_state(w, tokens=40)
+    _, _, M0, z0 = O.state_sweep(Kp, Vp, 40)
+    dMS, dzS = I.upstream_state_grads(w)
+    _check_bwd(Q, K, V, I.beta(w), w.seg_len, M0.astype(np.float32), z0.astype(np.float32),
+               I.d_out(w), dMS, dzS, "fp32", "tiny_fp32+state")
+
+
+# ------------------------------------------------------------------ shape sweep
+
+FWD_CASES = [
+    # B, Hq, Hkv, N, d, L, dtype, state
+    (1, 2, 2, 64, 32, 16, "fp32", True),
+    (2, 4, 2, 96, 64, 32, "fp32", False),
+    (1, 4, 1, 120, 128, 40, "fp32", True),     # ragged row and key tiles
+    (2, 3, 3, 9, 32, 3, "fp32", True),         # tiny segments
+    (1, 2, 2, 8, 64, 1, "fp32", False),        # one token per segment
+    (1, 2, 2, 300, 64, 300, "fp32", True),     # one long segment, ragged tiles
+    (2, 8, 2, 256, 128, 64, "bf16", True),
+    (1, 6, 3, 390, 64, 130, "bf16", False),
+    (1, 4, 4, 128, 32, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_forward_shapes(case):
+    Bn, Hq, Hkv, N, d, L, dtype, st = case
+    Q, K, V, beta, M0, z0 = make(Bn, Hq, Hkv, N, d, dtype, seed=N + d, with_state=st)
+    check_fwd(Q, K, V, beta, L, M0, z0, dtype)
+
+
+BWD_CASES = [
+    (1, 2, 2, 64, 32, 16, "fp32", True),
+    (1, 4, 2, 96, 64, 48, "fp32", True),
+    (1, 2, 1, 80, 128, 40, "fp32", False),
+    (2, 2, 2, 12, 32, 3, "fp32", True),
+    (2, 4, 2, 256, 128, 64, "bf16", True),
+    (1, 3, 3, 130, 64, 65, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_shapes(case):
+    Bn, Hq, Hkv, N, d, L, dtype, st = case
+    Q, K, V, beta, M0, z0 = make(Bn, Hq, Hkv, N, d, dtype, seed=3 * N + d, with_state=st)
+    dO = rnd(Q.shape, 99, 1.0, dtype)
+    dMS = dzS = None
+    if st:
+        dMS = np.random.default_rng(7).standard_normal(M0.shape).astype(np.float32) * 1e-2
+        dzS = np.random.default_rng(8).standard_normal(z0.shape).astype(np.float32) * 1e-2
+    _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype)
+
+
+# ------------------------------------------------------------------ gate limits
+
+@pytest.mark.parametrize("bval", [-np.inf, np.inf])
+def test_gate_limits(bval):
+    Q, K, V, beta, M0, z0 = make(1, 4, 2, 64, 64, "fp32", seed=5)
+    beta = np.full(4, bval, dtype=np.float32)
+    o, _, _ = check_fwd(Q, K, V, beta, 16, None, None, "fp32", f"beta={bval}")
+    oh = host(o)
+    assert np.all(np.isfinite(oh))
+    if bval > 0:
+        assert np.all(oh[:, :, :16] == 0.0)      # empty memory retrieves exactly nothing
+
+
+# ------------------------------------------------------------------ chaining, chunks, determinism
+
+def test_chained_calls_equal_one_call():
+    Q, K, V, beta, M0, z0 = make(2, 4, 2, 128, 64, "bf16", seed=17, with_state=True)
+    L = 32
+    o_all, M_all, z_all = run_fwd(Q, K, V, beta, L, M0, z0, "bf16")
+    Ms, zs = dev(M0), dev(z0)
+    outs = []
+    for s in range(4):
+        r = slice(s * L, (s + 1) * L)
+        o, Ms, zs = B().attn_fwd(dev(Q[:, :, r], "bf16"), dev(K[:, :, r], "bf16"), dev(V[:, :, r], "bf16"),
+                                 dev(beta), L, Ms, zs)
+        outs.append(o)
+    o_chain = torch.cat(outs, dim=2)
+    assert rel(host(o_chain), host(o_all)) < 1e-6
+    assert rel(host(Ms), host(M_all)) < 1e-6
+
+
+def test_multi_chunk_matches_single_chunk(monkeypatch):
+    Q, K, V, beta, M0, z0 = make(1, 4, 2, 20 * 16, 64, "fp32", seed=23, with_state=True)
+    dO = rnd(Q.shape, 24, 1.0, "fp32")
+    ref_f = run_fwd(Q, K, V, beta, 16, M0, z0, "fp32")
+    ref_b = B().attn_bwd(dev(Q), dev(K), dev(V), dev(beta), 16, dev(dO), dev(M0), dev(z0),
+                         want_state_grads=True)
+    monkeypatch.setenv("INFINI_CHUNK_SEGMENTS", "3")
+    got_f = run_fwd(Q, K, V, beta, 16, M0, z0, "fp32")
+    got_b = B().attn_bwd(dev(Q), dev(K), dev(V), dev(beta), 16, dev(dO), dev(M0), dev(z0),
+                         want_state_grads=True)
+    for a, b in zip(ref_f, got_f):
+        assert rel(host(a), host(b)) < 1e-5
+    for a, b in zip(ref_b, got_b):
+        assert rel(host(a), host(b)) < 1e-5
+    ro, rM, rz = O.forward(Q, K, V, beta, 16, M0, z0)
+    assert rel(host(got_f[0]), ro) < 1e-4
+
+
+def test_run_twice_bitwise_identical():
+    Q, K, V, beta, M0, z0 = make(2, 8, 2, 256, 128, "bf16", seed=29, with_state=True)
+    a = run_fwd(Q, K, V, beta, 64, M0, z0, "bf16")
+    b = run_fwd(Q, K, V, beta, 64, M0, z0, "bf16")
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    dO = rnd(Q.shape, 30, 1.0, "bf16")
+    args = (dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), dev(beta), 64, dev(dO, "bf16"), dev(M0), dev(z0))
+    g1 = B().attn_bwd(*args)
+    g2 = B().attn_bwd(*args)
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
+
+
+def test_errors_raise_with_real_tensors():
+    Q, K, V, beta, _, _ = make(1, 2, 2, 64, 32, "fp32", seed=31)
+    q = dev(Q)
+    with pytest.raises(B().InfiniError) as e:
+        B().attn_fwd(q, dev(K), dev(V), dev(beta), 48)          # 64 % 48 != 0
+    assert e.value.code == 2
+    o = torch.empty_like(q)
+    Ms = torch.empty((1, 2, 32, 32), device="cuda")
+    zs = torch.empty((1, 2, 32), device="cuda")
+    with pytest.raises(B().InfiniError) as e:
+        B().attn_fwd(q, dev(K), dev(V), dev(beta), 16, out=(q, Ms, zs, None))   # O aliases Q
+    assert e.value.code == 4
+    del o
+
+
+# ------------------------------------------------------------------ the five workloads at full size
+
+def test_fwd_200m_full():
+    w = I.WORKLOADS["fwd_200m"]
+    Q, K, V = I.qkv(w)
+    check_fwd(Q, K, V, I.beta(w), w.seg_len, None, None, "bf16", w.name)
+
+
+def test_train_llama3_8b_full():
+    w = I.WORKLOADS["train_llama3_8b"]
+    Q, K, V = I.qkv(w)
+    beta = I.beta(w)
+    check_fwd(Q, K, V, beta, w.seg_len, None, None, "bf16", w.name)
+    _check_bwd(Q, K, V, beta, w.seg_len, None, None, I.d_out(w), None, None, "bf16", w.name)
+
+
+def sampled_units(w, n_units, seed):
+    """(b, h, s) units covering every segment index and K/V group, plus row picks."""
+    g = np.random.default_rng(seed)
+    units = []
+    for u in range(n_units):
+        s = u % w.segments
+        h = (u * 7 + g.integers(0, w.q_heads)) % w.q_heads
+        b = int(g.integers(0, w.batch))
+        rows = np.unique(np.concatenate([[0, w.seg_len - 1], g.integers(0, w.seg_len, 30)]))
+        units.append((b, int(h), s, rows))
+    return units
+
+
+def test_fwd_llama3_8b_full_sampled():
+    w = I.WORKLOADS["fwd_llama3_8b"]
+    log("generating fwd_llama3_8b inputs")
+    Q, K, V = I.qkv(w)
+    beta = I.beta(w)
+    o, M, z = run_fwd(Q, K, V, beta, w.seg_len, None, None, "bf16")
+    torch.cuda.synchronize()
+    Msnap, zsnap, rM, rz = O.state_sweep(K, V, w.seg_len)
+    eM, ez = rel(host(M), rM), rel(host(z), rz)
+    G = w.q_heads // w.kv_heads
+    L = w.seg_len
+    got, ref = [], []
+    for (b, h, s, rows) in sampled_units(w, 48, 3):
+        r = slice(s * L, (s + 1) * L)
+        ref.append(O.segment_unit(Q[b, h, r], K[b, h // G, r], V[b, h // G, r],
+                                  Msnap[b, h // G, s], zsnap[b, h // G, s], beta[h], rows))
+        got.append(host(o[b, h, s * L + rows]))
+    eo = rel(np.concatenate(got), np.concatenate(ref))
+    log(f"   fwd_llama3_8b err O(sampled) {eo:.2e} M {eM:.2e} z {ez:.2e}")
+    assert eo < 2e-2 and eM < 2e-2 and ez < 2e-2
+
+
+def test_stream_1m_launch_shape_chained():
+    """Streaming workload's launch shape (one 2048-token segment per call),
+    state carried across calls; the first launches of the 512-launch stream."""
+    w = I.WORKLOADS["stream_1m"]
+    beta = I.beta(w)
+    n_launch = int(os.environ.get("INFINI_TEST_STREAM_LAUNCHES", "6"))
+    Ms = zs = None
+    rM = rz = None
+    for t in range(n_launch):
+        Q, K, V = I.qkv(w, launch=t)
+        o, Ms, zs = B().attn_fwd(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), dev(beta), w.seg_len, Ms, zs)
+        Msnap, zsnap, rM1, rz1 = O.state_sweep(K, V, w.seg_len, rM, rz)
+        ref = []
+        got = []
+        for h in range(0, w.q_heads, 5):
+            rows = np.array([0, 1, 777, 2047])
+            ref.append(O.segment_unit(Q[0, h], K[0, h], V[0, h], Msnap[0, h, 0], zsnap[0, h, 0], beta[h], rows))
+            got.append(host(o[0, h, rows]))
+        eo = rel(np.concatenate(got), np.concatenate(ref))
+        rM, rz = rM1, rz1
+        eM, ez = rel(host(Ms), rM), rel(host(zs), rz)
+        log(f"   launch {t}: err O {eo:.2e} M {eM:.2e} z {ez:.2e}")
+        assert eo < 2e-2 and eM < 2e-2 and ez < 2e-2
