@@ -53,7 +53,7 @@ size_t elem_bytes(const Geometry& g) { return g.dtype == INFINI_FP32 ? 4 : 2; }
 
 // ---- workspace layouts (byte offsets, 256-aligned)
 
-struct FwdWs { size_t Msnap, zsnap, total; };
+struct FwdWs { size_t Msnap, zsnap, MsnapT, total; };
 FwdWs fwd_layout(const Geometry& g) {
   const size_t C = (size_t)(g.S < kMaxChunkSegments ? g.S : kMaxChunkSegments);
   const size_t bk = (size_t)g.B * g.Hkv;
@@ -61,8 +61,29 @@ FwdWs fwd_layout(const Geometry& g) {
   size_t off = 0;
   w.Msnap = off; off = align_up(off + bk * C * g.D * g.D * 4);
   w.zsnap = off; off = align_up(off + bk * C * g.D * 4);
+  w.MsnapT = off; off = align_up(off + (infini::fwd_mfma_supported(g) ? bk * C * g.D * g.D * 2 : 0));
   w.total = off;
   return w;
+}
+
+// Memory phase + attention phase over segments [s0, s1), kernel family by problem.
+hipError_t run_fwd_chunk(const Geometry& g, const FwdWs& lay, char* base, const void* Q,
+                         const void* K, const void* V, const float* beta, const float* Min,
+                         const float* zin, void* O, float* M_S, float* z_S, float* lse, int s0,
+                         int s1, hipStream_t st, bool memory, bool attend) {
+  float* Msnap = reinterpret_cast<float*>(base + lay.Msnap);
+  float* zsnap = reinterpret_cast<float*>(base + lay.zsnap);
+  const bool mfma = infini::fwd_mfma_supported(g);
+  void* MsnapT = mfma ? base + lay.MsnapT : nullptr;
+  if (memory) {
+    hipError_t e = infini::launch_sweep(g, K, V, Min, zin, M_S, z_S, Msnap, zsnap, s0, s1, st, MsnapT);
+    if (e != hipSuccess) return e;
+  }
+  if (attend) {
+    if (mfma) return infini::launch_fwd_mfma(g, Q, K, V, beta, MsnapT, zsnap, O, lse, s0, s1, st);
+    return infini::launch_fwd_generic(g, Q, K, V, beta, Msnap, zsnap, O, lse, s0, s1, st);
+  }
+  return hipSuccess;
 }
 
 struct BwdWs { size_t Mst, zst, Msnap, zsnap, dMc, dzc, dMsnap, dzsnap, lse, Dd, dden, dnum, dbp, dbacc, total; };
@@ -137,7 +158,7 @@ int infini_version(void) { return INFINI_VERSION; }
 const char* infini_fwd_path(const infini_problem_t* p) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return nullptr;
-  return "generic_fp32";
+  return infini::fwd_mfma_supported(geometry(p)) ? "mfma_bf16" : "generic_fp32";
 }
 
 size_t infini_fwd_workspace_bytes(const infini_problem_t* p) {
@@ -174,15 +195,12 @@ infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const 
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  float* Msnap = reinterpret_cast<float*>(base + lay.Msnap);
-  float* zsnap = reinterpret_cast<float*>(base + lay.zsnap);
   const int C = chunk_segments(g);
   for (int s0 = 0; s0 < g.S; s0 += C) {
     const int s1 = s0 + C < g.S ? s0 + C : g.S;
     const float* Min = s0 == 0 ? M0 : M_S;
     const float* zin = s0 == 0 ? z0 : z_S;
-    TRY(infini::launch_sweep(g, K, V, Min, zin, M_S, z_S, Msnap, zsnap, s0, s1, st));
-    TRY(infini::launch_fwd_generic(g, Q, K, V, beta, Msnap, zsnap, O, lse, s0, s1, st));
+    TRY(run_fwd_chunk(g, lay, base, Q, K, V, beta, Min, zin, O, M_S, z_S, lse, s0, s1, st, true, true));
   }
   return INFINI_OK;
 }
@@ -204,10 +222,8 @@ infini_status_t infini_fwd_memory(const infini_problem_t* p, const void* K, cons
   const Span outs[] = {{M_S, nM}, {z_S, nz}, {ws, lay.total}};
   const Span ins[] = {{K, nkv * eb}, {V, nkv * eb}, {M0, M0 ? nM : 0}, {z0, z0 ? nz : 0}};
   if (any_overlap(outs, 3, ins, 4)) return INFINI_ERR_ALIAS;
-  char* base = static_cast<char*>(ws);
-  TRY(infini::launch_sweep(g, K, V, M0, z0, M_S, z_S, reinterpret_cast<float*>(base + lay.Msnap),
-                           reinterpret_cast<float*>(base + lay.zsnap), 0, g.S,
-                           static_cast<hipStream_t>(stream)));
+  TRY(run_fwd_chunk(g, lay, static_cast<char*>(ws), nullptr, K, V, nullptr, M0, z0, nullptr, M_S, z_S,
+                    nullptr, 0, g.S, static_cast<hipStream_t>(stream), true, false));
   return INFINI_OK;
 }
 
@@ -227,10 +243,8 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
   const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
                       {ws, lay.total}};
   if (any_overlap(outs, 2, ins, 5)) return INFINI_ERR_ALIAS;
-  const char* base = static_cast<const char*>(ws);
-  TRY(infini::launch_fwd_generic(g, Q, K, V, beta, reinterpret_cast<const float*>(base + lay.Msnap),
-                                 reinterpret_cast<const float*>(base + lay.zsnap), O, lse, 0, g.S,
-                                 static_cast<hipStream_t>(stream)));
+  TRY(run_fwd_chunk(g, lay, static_cast<char*>(const_cast<void*>(ws)), Q, K, V, beta, nullptr, nullptr, O,
+                    nullptr, nullptr, lse, 0, g.S, static_cast<hipStream_t>(stream), false, true));
   return INFINI_OK;
 }
 

@@ -1,0 +1,316 @@
+// bf16 matrix-core forward of the Infini-attention segment kernel (gfx950).
+//
+// One workgroup = 4 waves = 128 query rows of one (batch, query head,
+// segment); each wave owns 32 query rows.  Per 64-key tile:
+//   S^T = K Q^T          v_mfma_f32_32x32x16_bf16, K from LDS, Q^T in registers
+//   online softmax       base-2, row max/sum inside the lane plus one swap with
+//                        the lane 32 apart (page "Context Memorization for
+//                        Efficient Long Context Generation", section "방법론":
+//                        attention states over key sub-blocks merge exactly)
+//   O^T += V^T P^T       P^T straight from the S^T accumulators (no LDS trip);
+//                        V^T staged transposed in LDS
+// Working on the transposed products makes every lane own one query row, so
+// the softmax statistics need no cross-lane reduction beyond one exchange.
+//
+// Epilogue (page "Hugging Face Infini-Attention 재현 분석", section
+// "Infini-Attention 메커니즘", steps Memory Retrieval and Integration):
+//   A_mem^T = M_{s-1}^T sigma(Q)^T   on the matrix cores, M^T staged in LDS (bf16)
+//   den     = sigma(Q) z_{s-1} + eps  fp32 dot per lane
+//   O       = g A_mem + (1 - g) A_dot, rounded once to bf16
+//
+// Layout of the per-lane MFMA operands (gfx950, 32x32x16 bf16): A lane l holds
+// row l%32, k = 8(l/32)..+7; B lane l holds column l%32, same k; the C/D lane l
+// holds column l%32, rows 8(r/4) + 4(l/32) + r%4 for r = 0..15.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace infini {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int D>
+struct FwdCfg {
+  static constexpr int BM = 128;          // query rows per workgroup
+  static constexpr int WM = 32;           // query rows per wave
+  static constexpr int BN = 64;           // keys per tile
+  static constexpr int KS = D / 16;       // MFMA k-steps over head_dim
+  static constexpr int DB = D / 32;       // 32-row blocks of head_dim
+  static constexpr int KSTR = D + 8;      // K tile row stride (elements); 16-byte aligned rows
+  static constexpr int VSTR = BN + 4;     // V^T tile row stride; 8-byte aligned rows
+  static constexpr int KTILE = BN * KSTR;
+  static constexpr int VTILE = D * VSTR;
+  static constexpr int KPT = D / 32;      // keys per thread when staging V^T
+  static constexpr int CPT = D / 32;      // 16-byte chunks per thread per tile
+  static constexpr int MSTR = D + 8;      // M^T stage row stride
+  static constexpr int BUF = KTILE + VTILE;
+  static constexpr int LDS_ELEMS = (2 * BUF > D * MSTR) ? 2 * BUF : D * MSTR;
+};
+
+__device__ __forceinline__ float wave_swap32(float x) {
+  return __shfl_xor(x, 32);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                     const __bf16* __restrict__ V, const float* __restrict__ beta,
+                     const __bf16* __restrict__ MsnapT, const float* __restrict__ zsnap,
+                     __bf16* __restrict__ O, float* __restrict__ lse,
+                     int Hq, int Hkv, int N, int L, int s_begin, int nseg, int nqt, float sl2) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[C::LDS_ELEMS];
+  __shared__ float zs[D];
+
+  // ---- work decode: each XCD (workgroups are dealt round-robin to 8 XCDs)
+  // takes a contiguous range of work so that the query heads and tiles that
+  // share one K/V segment run on the same L2.
+  const int nwg = gridDim.x;
+  int work = blockIdx.x;
+  if ((nwg & 7) == 0) work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  const int G = Hq / Hkv;
+  const int per_group = G * nqt;
+  const int grp = work / per_group;
+  const int rem = work % per_group;
+  const int qt = nqt - 1 - rem / G;           // longest (most keys) tiles first
+  const int h_in = rem % G;
+  const int sl = grp % nseg;
+  const int bk = grp / nseg;                  // b * Hkv + kvh
+  const int b = bk / Hkv, kvh = bk % Hkv;
+  const int h = kvh * G + h_in;
+  const int s = s_begin + sl;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hh = lane >> 5;
+  const int q0 = qt * C::BM + wave * C::WM;   // wave's first row (segment-relative)
+  const int qrow = q0 + lq;                   // this lane's query row
+  const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
+  const size_t kvbase = (((size_t)b * Hkv + kvh) * N + (size_t)s * L) * D;
+
+  // ---- Q^T operand in registers for the whole key loop
+  bf16x8_t qreg[C::KS];
+  {
+    const bool ok = qrow < L;
+    const __bf16* qp = Q + qbase + (size_t)(ok ? qrow : 0) * D + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
+      qreg[ks] = ok ? v : bf16x8_t{};
+    }
+  }
+
+  const int kend = min(L, qt * C::BM + C::BM);
+  const int ntiles = (kend + C::BN - 1) / C::BN;
+
+  // ---- global -> register staging of one K/V tile
+  bf16x8_t kst[C::CPT], vst[C::KPT];
+  const int vdc = tid % (D / 8), vkg = tid / (D / 8);
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int key = k0 + row;
+      bf16x8_t v = {};
+      if (key < L) v = *reinterpret_cast<const bf16x8_t*>(K + kvbase + (size_t)key * D + col);
+      kst[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int key = k0 + vkg * C::KPT + i;
+      bf16x8_t v = {};
+      if (key < L) v = *reinterpret_cast<const bf16x8_t*>(V + kvbase + (size_t)key * D + vdc * 8);
+      vst[i] = v;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    __bf16* Ks = smem + buf * C::BUF;
+    __bf16* Vt = Ks + C::KTILE;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *reinterpret_cast<bf16x8_t*>(Ks + row * C::KSTR + col) = kst[i];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16* dst = Vt + (vdc * 8 + e) * C::VSTR + vkg * C::KPT;
+      if constexpr (C::KPT == 4) {
+        bf16x4_t w = {vst[0][e], vst[1][e], vst[2][e], vst[3][e]};
+        *reinterpret_cast<bf16x4_t*>(dst) = w;
+      } else {
+        bf16x2_t w = {vst[0][e], vst[1][e]};
+        *reinterpret_cast<bf16x2_t*>(dst) = w;
+      }
+    }
+  };
+
+  f32x16_t oacc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16_t{};
+  float m = -INFINITY, lpart = 0.f;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int k0 = j * C::BN;
+    if (j + 1 < ntiles) load_tile(k0 + C::BN);
+    const __bf16* Ks = smem + (j & 1) * C::BUF;
+    const __bf16* Vt = Ks + C::KTILE;
+
+    if (k0 <= q0 + C::WM - 1 && q0 < L) {
+      // S^T = K Q^T for 2 blocks of 32 keys
+      f32x16_t sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 32 + lq) * C::KSTR + ks * 16 + hh * 8);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[kb], 0, 0, 0);
+        }
+      }
+      const bool need_mask = (k0 + C::BN - 1 > q0) || (k0 + C::BN > L);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = sacc[kb][r] * sl2;
+          if (need_mask) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key > qrow || key >= L) v = -INFINITY;
+          }
+          sacc[kb][r] = v;
+          mt = fmaxf(mt, v);
+        }
+      }
+      mt = fmaxf(mt, wave_swap32(mt));
+      const float mn = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      float psum = 0.f;
+      bf16x8_t pb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - mn);
+          psum += p;
+          pb[kb][r >> 3][r & 7] = (__bf16)p;
+        }
+      }
+      lpart = lpart * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      // O^T += V^T P^T: k-slot q of half hh <-> key 16t + 8(q/4) + 4hh + q%4
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const __bf16* vp = Vt + (db * 32 + lq) * C::VSTR + kb * 32 + 16 * t + 4 * hh;
+            const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vp);
+            const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vp + 8);
+            const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], oacc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (j + 1 < ntiles) store_tile((j + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- retrieval from M_{s-1}, z_{s-1} and the gate
+  const float l = lpart + wave_swap32(lpart);
+  {
+    const __bf16* src = MsnapT + ((size_t)bk * nseg + sl) * D * D;
+    for (int c = tid; c < D * D / 8; c += 256) {
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *reinterpret_cast<bf16x8_t*>(smem + row * C::MSTR + col) =
+          *reinterpret_cast<const bf16x8_t*>(src + (size_t)row * D + col);
+    }
+    const float* zsrc = zsnap + ((size_t)bk * nseg + sl) * D;
+    for (int c = tid; c < D; c += 256) zs[c] = zsrc[c];
+  }
+  __syncthreads();
+
+  bf16x8_t sq[C::KS];
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 v = (__bf16)elu1((float)qreg[ks][e]);
+      sq[ks][e] = v;
+      dpart += (float)v * zs[ks * 16 + hh * 8 + e];
+    }
+  }
+  const float den = dpart + wave_swap32(dpart) + 1e-6f;
+  f32x16_t nacc[C::DB];
+#pragma unroll
+  for (int cb = 0; cb < C::DB; ++cb) {
+    nacc[cb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(smem + (cb * 32 + lq) * C::MSTR + ks * 16 + hh * 8);
+      nacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sq[ks], nacc[cb], 0, 0, 0);
+    }
+  }
+  const float gt = sigmoid(beta[h]);
+  const float wm = gt / den;
+  const float wd = (1.f - gt) / l;
+  if (qrow < L) {
+    __bf16* op = O + qbase + (size_t)qrow * D;
+#pragma unroll
+    for (int cb = 0; cb < C::DB; ++cb) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bf16x4_t w;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) w[x] = (__bf16)(wm * nacc[cb][4 * u + x] + wd * oacc[cb][4 * u + x]);
+        *reinterpret_cast<bf16x4_t*>(op + cb * 32 + 8 * u + 4 * hh) = w;
+      }
+    }
+    if (lse && hh == 0)
+      lse[((size_t)b * Hq + h) * N + (size_t)s * L + qrow] = (m + __log2f(l)) * 0.69314718055994531f;
+  }
+}
+
+template <int D>
+static hipError_t fwd_mfma_t(const Geometry& g, const void* Q, const void* K, const void* V,
+                             const float* beta, const void* MsnapT, const float* zsnap, void* O,
+                             float* lse, int s_begin, int s_end, hipStream_t st) {
+  const int nseg = s_end - s_begin;
+  const int nqt = (g.L + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
+  const long long nwg = (long long)g.B * g.Hq * nseg * nqt;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3((unsigned)nwg), dim3(256), 0, st,
+                     static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
+                     static_cast<const __bf16*>(V), beta, static_cast<const __bf16*>(MsnapT), zsnap,
+                     static_cast<__bf16*>(O), lse, g.Hq, g.Hkv, g.N, g.L, s_begin, nseg, nqt, sl2);
+  return hipGetLastError();
+}
+
+bool fwd_mfma_supported(const Geometry& g) { return g.dtype == 1 && (g.D == 64 || g.D == 128); }
+
+hipError_t launch_fwd_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
+                           const float* beta, const void* MsnapT, const float* zsnap, void* O,
+                           float* lse, int s_begin, int s_end, hipStream_t st) {
+  if (g.dtype != 1) return hipErrorInvalidValue;
+  if (g.D == 128) return fwd_mfma_t<128>(g, Q, K, V, beta, MsnapT, zsnap, O, lse, s_begin, s_end, st);
+  if (g.D == 64) return fwd_mfma_t<64>(g, Q, K, V, beta, MsnapT, zsnap, O, lse, s_begin, s_end, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace infini

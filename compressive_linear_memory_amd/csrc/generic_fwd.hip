@@ -29,7 +29,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void sweep_kernel(
     const T* __restrict__ K, const T* __restrict__ V,
     const float* M_in, const float* z_in, float* M_out, float* z_out,
-    float* __restrict__ Msnap, float* __restrict__ zsnap,
+    float* __restrict__ Msnap, float* __restrict__ zsnap, bf16_t* __restrict__ MsnapT,
     int N, int L, int s_begin, int s_end) {
   constexpr int TPR = D / SW_TILE;                 // tiles per row of M
   const int tile = blockIdx.x;
@@ -57,6 +57,10 @@ __global__ __launch_bounds__(256) void sweep_kernel(
       const size_t sb = (bh * nseg + (s - s_begin)) * (size_t)D * D + (size_t)(a0 + ta) * D + c0 + tc;
       for (int c = 0; c < 4; ++c) Msnap[sb + c] = acc[c];
       if (z_lane) zsnap[(bh * nseg + (s - s_begin)) * D + a0 + t] = zacc;
+    }
+    if (MsnapT) {
+      const size_t tb = (bh * nseg + (s - s_begin)) * (size_t)D * D;
+      for (int c = 0; c < 4; ++c) MsnapT[tb + (size_t)(c0 + tc + c) * D + a0 + ta] = f32_to_bf16(acc[c]);
     }
     const size_t rowbase = (bh * N + (size_t)s * L) * D;
     for (int j0 = 0; j0 < L; j0 += SW_KEYS) {
@@ -90,18 +94,18 @@ __global__ __launch_bounds__(256) void sweep_kernel(
 template <typename T, int D>
 static hipError_t sweep_t(const Geometry& g, const void* K, const void* V, const float* M_in,
                           const float* z_in, float* M_out, float* z_out, float* Msnap, float* zsnap,
-                          int s_begin, int s_end, hipStream_t st) {
+                          int s_begin, int s_end, hipStream_t st, void* MsnapT) {
   dim3 grid((D / SW_TILE) * (D / SW_TILE), g.B * g.Hkv);
   hipLaunchKernelGGL((sweep_kernel<T, D>), grid, dim3(256), 0, st,
                      static_cast<const T*>(K), static_cast<const T*>(V), M_in, z_in, M_out, z_out,
-                     Msnap, zsnap, g.N, g.L, s_begin, s_end);
+                     Msnap, zsnap, static_cast<bf16_t*>(MsnapT), g.N, g.L, s_begin, s_end);
   return hipGetLastError();
 }
 
 hipError_t launch_sweep(const Geometry& g, const void* K, const void* V, const float* M_in,
                         const float* z_in, float* M_out, float* z_out, float* Msnap, float* zsnap,
-                        int s_begin, int s_end, hipStream_t st) {
-#define SW_CASE(T, DD) return sweep_t<T, DD>(g, K, V, M_in, z_in, M_out, z_out, Msnap, zsnap, s_begin, s_end, st)
+                        int s_begin, int s_end, hipStream_t st, void* MsnapT) {
+#define SW_CASE(T, DD) return sweep_t<T, DD>(g, K, V, M_in, z_in, M_out, z_out, Msnap, zsnap, s_begin, s_end, st, MsnapT)
   if (g.dtype == 0) {
     if (g.D == 32) SW_CASE(float, 32);
     if (g.D == 64) SW_CASE(float, 64);

@@ -19,9 +19,18 @@ struct Geometry {
 //   M_out/z_out: state after segment s_end - 1 (NULL = not written; may equal M_in).
 //   Msnap/zsnap: per-segment state before each segment, [B*Hkv][s_end-s_begin][D][D]
 //   (NULL = not written).
+//   MsnapT: optional bf16 copy of each snapshot, transposed ([c][a]), for the
+//   matrix-core forward (NULL = not written).
 hipError_t launch_sweep(const Geometry& g, const void* K, const void* V,
                         const float* M_in, const float* z_in, float* M_out, float* z_out,
-                        float* Msnap, float* zsnap, int s_begin, int s_end, hipStream_t st);
+                        float* Msnap, float* zsnap, int s_begin, int s_end, hipStream_t st,
+                        void* MsnapT = nullptr);
+
+// bf16 matrix-core forward (head_dim 64 or 128), reading MsnapT / zsnap.
+bool fwd_mfma_supported(const Geometry& g);
+hipError_t launch_fwd_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
+                           const float* beta, const void* MsnapT, const float* zsnap, void* O,
+                           float* lse, int s_begin, int s_end, hipStream_t st);
 
 // Generic forward (fp32 vector arithmetic) over segments [s_begin, s_end),
 // reading the per-segment snapshots written by launch_sweep.

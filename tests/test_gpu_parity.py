@@ -119,6 +119,12 @@ FWD_CASES = [
     (2, 8, 2, 256, 128, 64, "bf16", True),
     (1, 6, 3, 390, 64, 130, "bf16", False),
     (1, 4, 4, 128, 32, 128, "bf16", True),
+    # bf16 head_dim 64 / 128 take the matrix-core path: tails of query and key tiles
+    (1, 2, 2, 8, 64, 1, "bf16", True),
+    (2, 4, 2, 48, 128, 16, "bf16", False),
+    (1, 4, 1, 200, 128, 100, "bf16", True),
+    (1, 2, 2, 600, 64, 300, "bf16", True),
+    (1, 8, 2, 1024, 128, 512, "bf16", True),
 ]
 
 
@@ -152,6 +158,25 @@ def test_backward_shapes(case):
 
 
 # ------------------------------------------------------------------ gate limits
+
+def test_kernel_path_selection():
+    from compressive_linear_memory_amd import binding as Bi
+    assert Bi.fwd_path(Bi.Problem(1, 2, 2, 64, 128, 16, 1)) == "mfma_bf16"
+    assert Bi.fwd_path(Bi.Problem(1, 2, 2, 64, 64, 16, 1)) == "mfma_bf16"
+    assert Bi.fwd_path(Bi.Problem(1, 2, 2, 64, 32, 16, 1)) == "generic_fp32"
+    assert Bi.fwd_path(Bi.Problem(1, 2, 2, 64, 128, 16, 0)) == "generic_fp32"
+
+
+@pytest.mark.parametrize("bval", [-np.inf, np.inf])
+def test_gate_limits_bf16_mfma(bval):
+    Q, K, V, beta, M0, z0 = make(1, 4, 2, 256, 128, "bf16", seed=6)
+    beta = np.full(4, bval, dtype=np.float32)
+    o, _, _ = check_fwd(Q, K, V, beta, 64, None, None, "bf16", f"beta={bval}")
+    oh = host(o)
+    assert np.all(np.isfinite(oh))
+    if bval > 0:
+        assert np.all(oh[:, :, :64] == 0.0)
+
 
 @pytest.mark.parametrize("bval", [-np.inf, np.inf])
 def test_gate_limits(bval):
