@@ -53,7 +53,7 @@ size_t elem_bytes(const Geometry& g) { return g.dtype == INFINI_FP32 ? 4 : 2; }
 
 // ---- workspace layouts (byte offsets, 256-aligned)
 
-struct FwdWs { size_t Msnap, zsnap, MsnapT, total; };
+struct FwdWs { size_t Msnap, zsnap, MsnapT, dz, total; };
 FwdWs fwd_layout(const Geometry& g) {
   const size_t C = (size_t)(g.S < kMaxChunkSegments ? g.S : kMaxChunkSegments);
   const size_t bk = (size_t)g.B * g.Hkv;
@@ -62,6 +62,7 @@ FwdWs fwd_layout(const Geometry& g) {
   w.Msnap = off; off = align_up(off + bk * C * g.D * g.D * 4);
   w.zsnap = off; off = align_up(off + bk * C * g.D * 4);
   w.MsnapT = off; off = align_up(off + (infini::fwd_mfma_supported(g) ? bk * C * g.D * g.D * 2 : 0));
+  w.dz = off;     off = align_up(off + (infini::fwd_mfma_supported(g) ? bk * C * g.D * 4 : 0));
   w.total = off;
   return w;
 }
@@ -76,7 +77,12 @@ hipError_t run_fwd_chunk(const Geometry& g, const FwdWs& lay, char* base, const 
   const bool mfma = infini::fwd_mfma_supported(g);
   void* MsnapT = mfma ? base + lay.MsnapT : nullptr;
   if (memory) {
-    hipError_t e = infini::launch_sweep(g, K, V, Min, zin, M_S, z_S, Msnap, zsnap, s0, s1, st, MsnapT);
+    // The matrix-core path keeps per-segment dM in the fp32 snapshot area
+    // (it reads only the bf16 transposed snapshots).
+    hipError_t e = mfma ? infini::launch_sweep_mfma(g, K, V, Min, zin, M_S, z_S, Msnap,
+                                                    reinterpret_cast<float*>(base + lay.dz), MsnapT,
+                                                    zsnap, s0, s1, st)
+                        : infini::launch_sweep(g, K, V, Min, zin, M_S, z_S, Msnap, zsnap, s0, s1, st);
     if (e != hipSuccess) return e;
   }
   if (attend) {

@@ -26,6 +26,14 @@ hipError_t launch_sweep(const Geometry& g, const void* K, const void* V,
                         float* Msnap, float* zsnap, int s_begin, int s_end, hipStream_t st,
                         void* MsnapT = nullptr);
 
+// bf16 matrix-core memory phase (head_dim 64 or 128): per-segment dM, dz into
+// the scratch buffers dM [B*Hkv][nseg][D][D] and dz [B*Hkv][nseg][D], then the
+// prefix over segments into MsnapT (bf16, transposed) and zsnap, and the state
+// after the last segment into M_out / z_out (may equal M_in / z_in).
+hipError_t launch_sweep_mfma(const Geometry& g, const void* K, const void* V, const float* M_in,
+                             const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
+                             void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st);
+
 // bf16 matrix-core forward (head_dim 64 or 128), reading MsnapT / zsnap.
 bool fwd_mfma_supported(const Geometry& g);
 hipError_t launch_fwd_mfma(const Geometry& g, const void* Q, const void* K, const void* V,

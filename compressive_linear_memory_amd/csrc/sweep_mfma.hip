@@ -1,0 +1,249 @@
+// Memory phase of the bf16 forward on the matrix cores (gfx950).
+//
+// The memory path (page "Hugging Face Infini-Attention 재현 분석", section
+// "Infini-Attention 메커니즘", steps Memory Update and State Transfer) is a
+// prefix sum over segments of per-segment terms that depend only on K and V:
+//   dM_s = sigma(K_s)^T V_s        dz_s = sum_rows sigma(K_s)
+//   M_{s-1} = M0 + sum_{t<s} dM_t  (the state segment s retrieves from)
+// so it runs in two launches:
+//   delta_mfma_kernel  one workgroup per (batch, K/V head, segment): dM_s on
+//                      v_mfma_f32_32x32x16_bf16 with sigma(K)^T and V^T staged
+//                      key-contiguous in LDS; dz_s in fp32 from the unrounded
+//                      sigma(K)
+//   scan_kernel        one workgroup per 64x64 tile of M per (batch, K/V head):
+//                      walks the segments in order with the tile resident in
+//                      registers, publishes each M_{s-1} as a transposed bf16
+//                      copy (the operand layout the attention kernel reads) and
+//                      z_{s-1} in fp32, and writes the final state.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace infini {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct DeltaCfg {
+  static constexpr int BK = 64;            // keys per staged chunk
+  static constexpr int TSTR = BK + 8;      // row stride of the key-contiguous tiles
+  static constexpr int WT = D / 2;         // wave tile edge (4 waves in 2 x 2)
+  static constexpr int WB = WT / 32;       // 32x32 blocks per wave tile edge
+  static constexpr int KPT = D / 32;       // keys per thread in staging
+  static constexpr int TILE = D * TSTR;    // one transposed tile (elements)
+  static constexpr int NKG = 256 / (D / 8);   // key groups
+};
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                       float* __restrict__ dM, float* __restrict__ dz,
+                       int N, int L, int s_begin, int nseg) {
+  using C = DeltaCfg<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[4 * C::TILE];   // 2 buffers x (K^T, V^T)
+  static_assert(C::NKG * (D + 1) * 4 <= 4 * C::TILE * 2, "dz reduction must fit the tile buffers");
+  float (*zred)[D + 1] = reinterpret_cast<float (*)[D + 1]>(smem);     // reused after the key loop
+
+  const int unit = blockIdx.x;               // (b * Hkv + kvh) * nseg + sl
+  const int sl = unit % nseg;
+  const size_t bk = unit / nseg;
+  const int s = s_begin + sl;
+  const size_t base = (bk * N + (size_t)s * L) * D;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hh = lane >> 5;
+  const int wa = wave >> 1, wc = wave & 1;
+  const int dc = tid % (D / 8), kg = tid / (D / 8);
+
+  float zp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zp[e] = 0.f;
+  bf16x8_t kst[C::KPT], vst[C::KPT];
+
+  auto load_chunk = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int key = j0 + kg * C::KPT + i;
+      bf16x8_t kv = {}, vv = {};
+      if (key < L) {
+        kv = *reinterpret_cast<const bf16x8_t*>(K + base + (size_t)key * D + dc * 8);
+        vv = *reinterpret_cast<const bf16x8_t*>(V + base + (size_t)key * D + dc * 8);
+      }
+      kst[i] = kv;
+      vst[i] = vv;
+    }
+  };
+  auto store_chunk = [&](int buf, int j0) {
+    __bf16* Kt = smem + buf * 2 * C::TILE;
+    __bf16* Vt = Kt + C::TILE;
+    float sk[C::KPT][8];
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const bool in = j0 + kg * C::KPT + i < L;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = in ? elu1((float)kst[i][e]) : 0.f;
+        sk[i][e] = f;
+        zp[e] += f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16* kd = Kt + (dc * 8 + e) * C::TSTR + kg * C::KPT;
+      __bf16* vd = Vt + (dc * 8 + e) * C::TSTR + kg * C::KPT;
+      if constexpr (C::KPT == 4) {
+        *reinterpret_cast<bf16x4_t*>(kd) = bf16x4_t{(__bf16)sk[0][e], (__bf16)sk[1][e], (__bf16)sk[2][e], (__bf16)sk[3][e]};
+        *reinterpret_cast<bf16x4_t*>(vd) = bf16x4_t{vst[0][e], vst[1][e], vst[2][e], vst[3][e]};
+      } else {
+        *reinterpret_cast<bf16x2_t*>(kd) = bf16x2_t{(__bf16)sk[0][e], (__bf16)sk[1][e]};
+        *reinterpret_cast<bf16x2_t*>(vd) = bf16x2_t{vst[0][e], vst[1][e]};
+      }
+    }
+  };
+
+  f32x16_t acc[C::WB][C::WB];
+#pragma unroll
+  for (int x = 0; x < C::WB; ++x)
+#pragma unroll
+    for (int y = 0; y < C::WB; ++y) acc[x][y] = f32x16_t{};
+
+  const int nch = (L + C::BK - 1) / C::BK;
+  load_chunk(0);
+  store_chunk(0, 0);
+  __syncthreads();
+  for (int j = 0; j < nch; ++j) {
+    if (j + 1 < nch) load_chunk((j + 1) * C::BK);
+    const __bf16* Kt = smem + (j & 1) * 2 * C::TILE;
+    const __bf16* Vt = Kt + C::TILE;
+#pragma unroll
+    for (int ks = 0; ks < C::BK / 16; ++ks) {
+      bf16x8_t a[C::WB], bb[C::WB];
+#pragma unroll
+      for (int x = 0; x < C::WB; ++x) {
+        a[x] = *reinterpret_cast<const bf16x8_t*>(Kt + (wa * C::WT + x * 32 + lq) * C::TSTR + ks * 16 + hh * 8);
+        bb[x] = *reinterpret_cast<const bf16x8_t*>(Vt + (wc * C::WT + x * 32 + lq) * C::TSTR + ks * 16 + hh * 8);
+      }
+#pragma unroll
+      for (int x = 0; x < C::WB; ++x)
+#pragma unroll
+        for (int y = 0; y < C::WB; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], bb[y], acc[x][y], 0, 0, 0);
+    }
+    if (j + 1 < nch) store_chunk((j + 1) & 1, (j + 1) * C::BK);
+    __syncthreads();
+  }
+
+  // dM[a][c]: lane holds column c = lq, rows 8(r/4) + 4hh + r%4 of each block.
+  float* out = dM + (size_t)unit * D * D;
+#pragma unroll
+  for (int x = 0; x < C::WB; ++x)
+#pragma unroll
+    for (int y = 0; y < C::WB; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int a = wa * C::WT + x * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int c = wc * C::WT + y * 32 + lq;
+        out[(size_t)a * D + c] = acc[x][y][r];
+      }
+  // dz: reduce the per-thread partial sums over key groups.
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zred[kg][dc * 8 + e] = zp[e];
+  __syncthreads();
+  for (int a = tid; a < D; a += 256) {
+    float t = 0.f;
+    for (int g = 0; g < C::NKG; ++g) t += zred[g][a];
+    dz[(size_t)unit * D + a] = t;
+  }
+}
+
+// ---------------------------------------------------------------- scan
+
+constexpr int SC_T = 64;   // tile edge
+
+template <int D>
+__global__ __launch_bounds__(256) void scan_kernel(
+    const float* __restrict__ dM, const float* __restrict__ dz, const float* M_in, const float* z_in,
+    float* M_out, float* z_out, __bf16* __restrict__ MsnapT, float* __restrict__ zsnap, int nseg) {
+  constexpr int TPR = D / SC_T;
+  __shared__ float tr[SC_T][SC_T + 1];
+  const int a0 = (blockIdx.x / TPR) * SC_T, c0 = (blockIdx.x % TPR) * SC_T;
+  const bool do_z = (blockIdx.x % TPR) == 0;
+  const size_t bk = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int ra = tid >> 2, rc = (tid & 3) * 16;       // row a0+ra, columns c0+rc..+15
+  const size_t eoff = (size_t)(a0 + ra) * D + c0 + rc;
+
+  float run[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) run[x] = M_in ? M_in[bk * D * D + eoff + x] : 0.f;
+  float zr = 0.f;
+  if (do_z && tid < SC_T) zr = z_in ? z_in[bk * D + a0 + tid] : 0.f;
+
+  for (int sl = 0; sl < nseg; ++sl) {
+    const size_t unit = bk * nseg + sl;
+    // publish M_{s-1} transposed in bf16: stage the fp32 tile, read columns
+#pragma unroll
+    for (int x = 0; x < 16; ++x) tr[ra][rc + x] = run[x];
+    if (do_z && tid < SC_T) zsnap[unit * D + a0 + tid] = zr;
+    __syncthreads();
+    {
+      const int cc = tid >> 2, aa = (tid & 3) * 16;    // output row c0+cc, columns a0+aa..+15
+      __bf16* dst = MsnapT + unit * D * D + (size_t)(c0 + cc) * D + a0 + aa;
+#pragma unroll
+      for (int x = 0; x < 16; x += 8) {
+        bf16x8_t w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (__bf16)tr[aa + x + e][cc];
+        *reinterpret_cast<bf16x8_t*>(dst + x) = w;
+      }
+    }
+    __syncthreads();
+    const float* src = dM + unit * D * D + eoff;
+#pragma unroll
+    for (int x = 0; x < 16; x += 4) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + x);
+      run[x] += v[0]; run[x + 1] += v[1]; run[x + 2] += v[2]; run[x + 3] += v[3];
+    }
+    if (do_z && tid < SC_T) zr += dz[unit * D + a0 + tid];
+  }
+  if (M_out) {
+#pragma unroll
+    for (int x = 0; x < 16; ++x) M_out[bk * D * D + eoff + x] = run[x];
+    if (do_z && tid < SC_T) z_out[bk * D + a0 + tid] = zr;
+  }
+}
+
+template <int D>
+static hipError_t sweep_mfma_t(const Geometry& g, const void* K, const void* V, const float* M_in,
+                               const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
+                               void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st) {
+  const int nseg = s_end - s_begin;
+  const long long units = (long long)g.B * g.Hkv * nseg;
+  if (units > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((delta_mfma_kernel<D>), dim3((unsigned)units), dim3(256), 0, st,
+                     static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), dM, dz, g.N, g.L,
+                     s_begin, nseg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((D / SC_T) * (D / SC_T), g.B * g.Hkv);
+  hipLaunchKernelGGL((scan_kernel<D>), grid, dim3(256), 0, st, dM, dz, M_in, z_in, M_out, z_out,
+                     static_cast<__bf16*>(MsnapT), zsnap, nseg);
+  return hipGetLastError();
+}
+
+hipError_t launch_sweep_mfma(const Geometry& g, const void* K, const void* V, const float* M_in,
+                             const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
+                             void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st) {
+  if (g.dtype != 1) return hipErrorInvalidValue;
+  if (g.D == 128) return sweep_mfma_t<128>(g, K, V, M_in, z_in, M_out, z_out, dM, dz, MsnapT, zsnap, s_begin, s_end, st);
+  if (g.D == 64) return sweep_mfma_t<64>(g, K, V, M_in, z_in, M_out, z_out, dM, dz, MsnapT, zsnap, s_begin, s_end, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace infini
