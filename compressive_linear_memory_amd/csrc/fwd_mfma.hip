@@ -23,6 +23,8 @@
 // holds column l%32, rows 8(r/4) + 4(l/32) + r%4 for r = 0..15.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -51,8 +53,15 @@ struct FwdCfg {
   static constexpr int LDS_ELEMS = (2 * BUF > D * MSTR) ? 2 * BUF : D * MSTR;
 };
 
-__device__ __forceinline__ float wave_swap32(float x) {
-  return __shfl_xor(x, 32);
+// max / sum of x over lanes l and l^32 (v_permlane32_swap exchanges the two
+// wave halves; the pair it returns holds both values in every lane).
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D>
@@ -107,36 +116,71 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int kend = min(L, qt * C::BM + C::BM);
   const int ntiles = (kend + C::BN - 1) / C::BN;
 
-  // ---- global -> register staging of one K/V tile
+  // ---- global -> register staging of K and V tiles
+  //
+  // LDS holds two K tiles and two V^T tiles.  Iteration j of the key loop
+  // reads K(j+1) (scores of the next tile, computed under this tile's
+  // softmax) and V(j) (this tile's PV product); at its end it stores K(j+2)
+  // into the K buffer K(j) used and V(j+1) into the other V buffer, then one
+  // barrier.  Global loads run one iteration ahead of their LDS store.
   bf16x8_t kst[C::CPT], vst[C::KPT];
-  const int vdc = tid % (D / 8), vkg = tid / (D / 8);
-  auto load_tile = [&](int k0) {
+  // V^T staging: consecutive lanes take consecutive key groups so that the
+  // transposed LDS stores of a 16-lane group hit distinct banks.
+  constexpr int NKG = 64 / C::KPT;
+  const int vkg = tid % NKG, vdc = tid / NKG;
+  // Per-lane element offsets inside a tile are fixed; each tile adds a
+  // workgroup-uniform row offset.  Keys past the segment end (only in the last
+  // tile of a ragged segment) are clamped to its last row: finite values that
+  // the score mask removes (K) or that meet a zero probability (V).
+  const __bf16* Kseg = K + kvbase;
+  const __bf16* Vseg = V + kvbase;
+  int koff[C::CPT], krow[C::CPT];
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = k0 + row;
-      bf16x8_t v = {};
-      if (key < L) v = *reinterpret_cast<const bf16x8_t*>(K + kvbase + (size_t)key * D + col);
-      kst[i] = v;
-    }
+  for (int i = 0; i < C::CPT; ++i) {
+    const int c = tid + 256 * i;
+    krow[i] = c / (D / 8);
+    koff[i] = krow[i] * D + (c % (D / 8)) * 8;
+  }
+  auto load_k = [&](int k0) {
+    const __bf16* kt = Kseg + (size_t)k0 * D;
+    if (k0 + C::BN <= L) {
 #pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-      const int key = k0 + vkg * C::KPT + i;
-      bf16x8_t v = {};
-      if (key < L) v = *reinterpret_cast<const bf16x8_t*>(V + kvbase + (size_t)key * D + vdc * 8);
-      vst[i] = v;
+      for (int i = 0; i < C::CPT; ++i) kst[i] = *reinterpret_cast<const bf16x8_t*>(kt + koff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::CPT; ++i) {
+        const int key = min(k0 + krow[i], L - 1);
+        kst[i] = *reinterpret_cast<const bf16x8_t*>(Kseg + (size_t)key * D + (koff[i] - krow[i] * D));
+      }
     }
   };
-  auto store_tile = [&](int buf) {
-    __bf16* Ks = smem + buf * C::BUF;
-    __bf16* Vt = Ks + C::KTILE;
+  auto load_v = [&](int k0) {
+    const __bf16* vt = Vseg + (size_t)k0 * D;
+    if (k0 + C::BN <= L) {
+#pragma unroll
+      for (int i = 0; i < C::KPT; ++i)
+        vst[i] = *reinterpret_cast<const bf16x8_t*>(vt + (vkg * C::KPT + i) * D + vdc * 8);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::KPT; ++i) {
+        const int key = min(k0 + vkg * C::KPT + i, L - 1);
+        vst[i] = *reinterpret_cast<const bf16x8_t*>(Vseg + (size_t)key * D + vdc * 8);
+      }
+    }
+  };
+  __bf16* const kbuf0 = smem;
+  __bf16* const vbuf0 = smem + 2 * C::KTILE;
+  auto store_k = [&](int buf) {
+    __bf16* Ks = kbuf0 + buf * C::KTILE;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int c = tid + 256 * i;
       const int row = c / (D / 8), col = (c % (D / 8)) * 8;
       *reinterpret_cast<bf16x8_t*>(Ks + row * C::KSTR + col) = kst[i];
     }
+  };
+  auto store_v = [&](int buf) {
+    __bf16* Vt = vbuf0 + buf * C::VTILE;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       __bf16* dst = Vt + (vdc * 8 + e) * C::VSTR + vkg * C::KPT;
@@ -155,83 +199,132 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16_t{};
   float m = -INFINITY, lpart = 0.f;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int k0 = j * C::BN;
-    if (j + 1 < ntiles) load_tile(k0 + C::BN);
-    const __bf16* Ks = smem + (j & 1) * C::BUF;
-    const __bf16* Vt = Ks + C::KTILE;
-
-    if (k0 <= q0 + C::WM - 1 && q0 < L) {
-      // S^T = K Q^T for 2 blocks of 32 keys
-      f32x16_t sacc[2];
+  // S^T = K Q^T for one 64-key tile (two 32-key blocks).
+  auto scores = [&](const __bf16* Ks, f32x16_t (&sa)[2]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16_t{};
+    for (int kb = 0; kb < 2; ++kb) {
+      sa[kb] = f32x16_t{};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 32 + lq) * C::KSTR + ks * 16 + hh * 8);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[kb], 0, 0, 0);
-        }
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 32 + lq) * C::KSTR + ks * 16 + hh * 8);
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sa[kb], 0, 0, 0);
       }
-      const bool need_mask = (k0 + C::BN - 1 > q0) || (k0 + C::BN > L);
-      float mt = -INFINITY;
+    }
+  };
+
+  // Online softmax over one tile's scores.  Scores stay in the raw domain until
+  // one FMA per element forms (s * scale * log2 e - m); the running max m
+  // (scaled, base 2) only moves when a row's tile max exceeds it by more than
+  // kRescaleSlack, so the accumulator rescale is skipped on almost every tile.
+  // Any reference value gives the same normalised result; the slack bounds the
+  // unnormalised terms by 2^kRescaleSlack.
+  constexpr float kRescaleSlack = 8.f;
+  auto softmax_max = [&](f32x16_t (&sa)[2], int k0, bool masked) {
+    if (masked) {
+      // element (kb, r) holds key k0 + 4hh + kb*32 + 8(r/4) + r%4
+      const int lim = min(qrow, L - 1) - (k0 + 4 * hh);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = sacc[kb][r] * sl2;
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > qrow || key >= L) v = -INFINITY;
-          }
-          sacc[kb][r] = v;
-          mt = fmaxf(mt, v);
-        }
-      }
-      mt = fmaxf(mt, wave_swap32(mt));
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sa[kb][r] = -INFINITY;
+    }
+    float mt = sa[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sa[kb][r]);
+    mt = pair_max32(mt) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack)) {
       const float mn = fmaxf(m, mt);
       const float alpha = __builtin_amdgcn_exp2f(m - mn);
       m = mn;
-      float psum = 0.f;
-      bf16x8_t pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - mn);
-          psum += p;
-          pb[kb][r >> 3][r & 7] = (__bf16)p;
-        }
-      }
-      lpart = lpart * alpha + psum;
+      lpart *= alpha;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
-      // O^T += V^T P^T: k-slot q of half hh <-> key 16t + 8(q/4) + 4hh + q%4
+    }
+  };
+  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+  auto softmax_exp = [&](const f32x16_t (&sa)[2], bf16x8_t (&pb)[2][2]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+      for (int r = 0; r < 16; ++r)
+        pb[kb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sa[kb][r], sl2, -m));
+    // Row sum of the bf16 probabilities the PV product uses, two per v_dot2.
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const __bf16* vp = Vt + (db * 32 + lq) * C::VSTR + kb * 32 + 16 * t + 4 * hh;
-            const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vp);
-            const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vp + 8);
-            const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], oacc[db], 0, 0, 0);
-          }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          lpart = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[kb][t][2 * x], pb[kb][t][2 * x + 1]}, ones, lpart, false);
+  };
+  // O^T += V^T P^T: k-slot q of half hh <-> key 16t + 8(q/4) + 4hh + q%4.
+  auto pv = [&](const __bf16* Vt, const bf16x8_t (&pb)[2][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const __bf16* vp = Vt + (db * 32 + lq) * C::VSTR + kb * 32 + 16 * t + 4 * hh;
+          const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vp);
+          const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vp + 8);
+          const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], oacc[db], 0, 0, 0);
         }
       }
     }
-    if (j + 1 < ntiles) store_tile((j + 1) & 1);
+  };
+
+  // Tiles this wave attends to: k0 <= q0 + 31 (its other tiles lie above the diagonal).
+  const int n_act = q0 < L ? min(ntiles, (q0 + C::WM - 1) / C::BN + 1) : 0;
+
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  if (ntiles > 1) {
+    load_k(C::BN);
+    store_k(1);
+  }
+  __syncthreads();
+  if (ntiles > 2) load_k(2 * C::BN);
+  if (ntiles > 1) load_v(C::BN);
+
+  f32x16_t scur[2];
+  if (n_act > 0) scores(kbuf0, scur);
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int k0 = j * C::BN;
+    if (j < n_act) {
+      const bool masked = (k0 + C::BN - 1 > q0) || (k0 + C::BN > L);
+      softmax_max(scur, k0, masked);
+      bf16x8_t pb[2][2];
+      if (j + 1 < n_act) {
+        // next tile's scores on the matrix cores while this tile's
+        // exponentials run on the vector ALUs
+        f32x16_t snext[2];
+        scores(kbuf0 + ((j + 1) & 1) * C::KTILE, snext);
+        softmax_exp(scur, pb);
+        pv(vbuf0 + (j & 1) * C::VTILE, pb);
+        scur[0] = snext[0];
+        scur[1] = snext[1];
+      } else {
+        softmax_exp(scur, pb);
+        pv(vbuf0 + (j & 1) * C::VTILE, pb);
+      }
+    }
+    if (j + 2 < ntiles) store_k(j & 1);
+    if (j + 1 < ntiles) store_v((j + 1) & 1);
     __syncthreads();
+    if (j + 3 < ntiles) load_k((j + 3) * C::BN);
+    if (j + 2 < ntiles) load_v((j + 2) * C::BN);
   }
 
   // ---- retrieval from M_{s-1}, z_{s-1} and the gate
-  const float l = lpart + wave_swap32(lpart);
+  const float l = pair_sum32(lpart);
   {
     const __bf16* src = MsnapT + ((size_t)bk * nseg + sl) * D * D;
     for (int c = tid; c < D * D / 8; c += 256) {
@@ -255,7 +348,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       dpart += (float)v * zs[ks * 16 + hh * 8 + e];
     }
   }
-  const float den = dpart + wave_swap32(dpart) + 1e-6f;
+  const float den = pair_sum32(dpart) + 1e-6f;
   f32x16_t nacc[C::DB];
 #pragma unroll
   for (int cb = 0; cb < C::DB; ++cb) {
