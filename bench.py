@@ -106,11 +106,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fwd_llama3_8b", choices=sorted(I.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="fwd", choices=["fwd", "train", "stream"],
+                    help="fwd: forward throughput (default, the headline line); train: forward + "
+                         "backward step; stream: chained single-segment launches carrying the state")
+    ap.add_argument("--launches", type=int, default=512, help="stream mode: chained launches per step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the sequence-parallel "
               "multi-GPU path is a design note, not built", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "train":
+        return bench_train(args)
+    if args.mode == "stream":
+        return bench_stream(args)
 
     import torch
     from compressive_linear_memory_amd import binding as Bi
@@ -203,6 +211,106 @@ def main():
         out["cpu_baseline"] = cb
         out["parity_sampled_max_rel_err"] = float(err)
     print(json.dumps(out), flush=True)
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def bench_train(args):
+    """Forward (with row log-sum-exp saved) + backward per step on the training workload."""
+    import torch
+    from compressive_linear_memory_amd import binding as Bi
+    Bi.lib()
+    w = I.WORKLOADS["train_llama3_8b"] if args.workload == "fwd_llama3_8b" else I.WORKLOADS[args.workload]
+    say(f"[bench] generating {w.name} inputs")
+    Q, K, V = I.qkv(w)
+    dO = I.d_out(w)
+    tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    t = lambda x: torch.from_numpy(x).to(dev).to(tdt)
+    q, k, v, do = t(Q), t(K), t(V), t(dO)
+    b = torch.from_numpy(I.beta(w)).to(dev)
+    p = Bi.problem(q, k, w.seg_len)
+    wsf = torch.empty(Bi.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(Bi.workspace_bytes(p, backward=True), dtype=torch.uint8, device=dev)
+    B_, Hq, Hkv, N, d = w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim
+    out = (torch.empty_like(q), torch.empty((B_, Hkv, d, d), device=dev), torch.empty((B_, Hkv, d), device=dev),
+           torch.empty((B_, Hq, N), device=dev))
+
+    def step(evs=None):
+        if evs: evs[0].record()
+        Bi.attn_fwd(q, k, v, b, w.seg_len, want_lse=True, out=out, ws=wsf)
+        if evs: evs[1].record()
+        Bi.attn_bwd(q, k, v, b, w.seg_len, do, lse=out[3], ws=wsb)
+        if evs: evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [_events(3) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    total = ev[0][0].elapsed_time(ev[-1][2])
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    tok = w.batch * w.seq_len
+    print(json.dumps({"metric": f"Infini-attention fwd+bwd tokens/s ({w.name})", "value": round(tok * args.steps / (total / 1e3), 1),
+                      "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(total / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+                      "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+                      "config": {"workload": w.name, "mode": "train", "kernel_path": Bi.fwd_path(p)},
+                      "phases_ms": {"fwd": round(fwd, 4), "bwd": round(bwd, 4)}}), flush=True)
+
+
+def bench_stream(args):
+    """Chained single-segment launches carrying (M, z) between two state buffers.
+    Inputs for 8 distinct launches are generated and cycled (same shapes and
+    traffic as distinct inputs; the state still chains through every launch)."""
+    import torch
+    from compressive_linear_memory_amd import binding as Bi
+    Bi.lib()
+    w = I.WORKLOADS["stream_1m"]
+    dev = torch.device("cuda:0")
+    say("[bench] generating stream_1m launch inputs (8 distinct launches, cycled)")
+    nd = 8
+    ins = []
+    for t_ in range(nd):
+        Q, K, V = I.qkv(w, launch=t_)
+        ins.append(tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (Q, K, V)))
+    b = torch.from_numpy(I.beta(w)).to(dev)
+    p = Bi.problem(ins[0][0], ins[0][1], w.seg_len)
+    ws = torch.empty(Bi.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    d, H = w.head_dim, w.kv_heads
+    st = [(torch.zeros((1, H, d, d), device=dev), torch.zeros((1, H, d), device=dev)) for _ in range(2)]
+    O_ = torch.empty_like(ins[0][0])
+    nl = args.launches
+
+    def run():
+        for i in range(nl):
+            q, k, v = ins[i % nd]
+            src, dst = st[i & 1], st[(i + 1) & 1]
+            Bi.attn_fwd(q, k, v, b, w.seg_len, M0=src[0], z0=src[1], out=(O_, dst[0], dst[1], None), ws=ws)
+
+    for _ in range(max(1, args.warmup // 3)):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tok = w.seq_len * nl
+    print(json.dumps({"metric": "Infini-attention streaming fwd tokens/s (stream_1m)", "value": round(tok / (ms / 1e3), 1),
+                      "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(ms, 4), "us_per_launch": round(1e3 * ms / nl, 2), "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "stream_1m", "mode": "stream", "launches": nl,
+                                 "kernel_path": Bi.fwd_path(p)}}), flush=True)
 
 
 if __name__ == "__main__":

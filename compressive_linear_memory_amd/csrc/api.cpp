@@ -92,7 +92,7 @@ hipError_t run_fwd_chunk(const Geometry& g, const FwdWs& lay, char* base, const 
   return hipSuccess;
 }
 
-struct BwdWs { size_t Mst, zst, Msnap, zsnap, dMc, dzc, dMsnap, dzsnap, lse, Dd, dden, dnum, dbp, dbacc, total; };
+struct BwdWs { size_t Mst, zst, Msnap, zsnap, dMc, dzc, dMsnap, dzsnap, lse, Dd, dden, dnum, dbp, dbacc, dbs, total; };
 BwdWs bwd_layout(const Geometry& g) {
   const size_t C = (size_t)(g.S < kMaxChunkSegments ? g.S : kMaxChunkSegments);
   const size_t bk = (size_t)g.B * g.Hkv;
@@ -114,6 +114,7 @@ BwdWs bwd_layout(const Geometry& g) {
   w.dnum = off;   off = align_up(off + rows * D * 4);
   w.dbp = off;    off = align_up(off + (size_t)g.B * g.Hq * C * infini::bwd_q_row_blocks(g) * 4);
   w.dbacc = off;  off = align_up(off + (size_t)g.Hq * 4);
+  w.dbs = off;    off = align_up(off + (size_t)g.B * g.Hq * 4);
   w.total = off;
   return w;
 }
@@ -164,7 +165,9 @@ int infini_version(void) { return INFINI_VERSION; }
 const char* infini_fwd_path(const infini_problem_t* p) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return nullptr;
-  return infini::fwd_mfma_supported(geometry(p)) ? "mfma_bf16" : "generic_fp32";
+  const Geometry g = geometry(p);
+  if (infini::fwd_short_supported(g)) return "mfma_bf16_short";
+  return infini::fwd_mfma_supported(g) ? "mfma_bf16" : "generic_fp32";
 }
 
 size_t infini_fwd_workspace_bytes(const infini_problem_t* p) {
@@ -200,6 +203,10 @@ infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const 
   if (any_overlap(outs, 5, ins, 6)) return INFINI_ERR_ALIAS;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (infini::fwd_short_supported(g)) {   // state stays on chip for the whole call
+    TRY(infini::launch_fwd_short(g, Q, K, V, beta, M0, z0, O, M_S, z_S, lse, st));
+    return INFINI_OK;
+  }
   char* base = static_cast<char*>(ws);
   const int C = chunk_segments(g);
   for (int s0 = 0; s0 < g.S; s0 += C) {
@@ -283,6 +290,11 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  if (infini::bwd_short_supported(g)) {   // state and its gradient stay on chip
+    TRY(infini::launch_bwd_short(g, Q, K, V, beta, M0, z0, dO, dM_S, dz_S, dQ, dK, dV, dbeta, dM0, dz0,
+                                 F(lay.dbs), st));
+    return INFINI_OK;
+  }
   infini::BwdChunkWs w;
   w.lse = F(lay.lse); w.Dd = F(lay.Dd); w.dden = F(lay.dden); w.dnum = F(lay.dnum);
   w.dbeta_part = F(lay.dbp); w.dMsnap = F(lay.dMsnap); w.dzsnap = F(lay.dzsnap);

@@ -40,6 +40,21 @@ hipError_t launch_fwd_mfma(const Geometry& g, const void* Q, const void* K, cons
                            const float* beta, const void* MsnapT, const float* zsnap, void* O,
                            float* lse, int s_begin, int s_end, hipStream_t st);
 
+// Fused short-segment forward (bf16, head_dim 64 or 128, seg_len <= 64): one
+// workgroup per (batch, K/V head) walks all segments with (M, z) on chip.
+bool fwd_short_supported(const Geometry& g);
+hipError_t launch_fwd_short(const Geometry& g, const void* Q, const void* K, const void* V,
+                            const float* beta, const float* M0, const float* z0, void* O,
+                            float* M_S, float* z_S, float* lse, hipStream_t st);
+
+// Fused short-segment backward (bf16, head_dim 64 or 128, seg_len <= 64,
+// at most 16 query heads per K/V head).  dbeta_part: [B][Hq] scratch.
+bool bwd_short_supported(const Geometry& g);
+hipError_t launch_bwd_short(const Geometry& g, const void* Q, const void* K, const void* V,
+                            const float* beta, const float* M0, const float* z0, const void* dO,
+                            const float* dM_S, const float* dz_S, void* dQ, void* dK, void* dV,
+                            float* dbeta, float* dM0, float* dz0, float* dbeta_part, hipStream_t st);
+
 // Generic forward (fp32 vector arithmetic) over segments [s_begin, s_end),
 // reading the per-segment snapshots written by launch_sweep.
 hipError_t launch_fwd_generic(const Geometry& g, const void* Q, const void* K, const void* V,

@@ -157,9 +157,11 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
                                   const void* V, const float* beta, void* O, float* lse,
                                   const void* ws, size_t ws_bytes, void* stream);
 
-/* Name of the kernel family infini_attn_fwd / infini_fwd_attend runs for this
- * problem ("generic_fp32": fp32 vector-ALU path; "mfma_bf16": bf16 matrix-core
- * path).  NULL for an invalid problem.  Static storage. */
+/* Name of the kernel family infini_attn_fwd runs for this problem
+ * ("generic_fp32": fp32 vector-ALU path; "mfma_bf16": bf16 matrix-core
+ * path, memory phase then attention phase; "mfma_bf16_short": bf16
+ * matrix-core path for seg_len <= 64 that keeps the memory on chip in one
+ * fused kernel).  NULL for an invalid problem.  Static storage. */
 const char* infini_fwd_path(const infini_problem_t* p);
 
 /* Static description of a status code. */

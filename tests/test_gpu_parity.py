@@ -142,6 +142,11 @@ BWD_CASES = [
     (2, 2, 2, 12, 32, 3, "fp32", True),
     (2, 4, 2, 256, 128, 64, "bf16", True),
     (1, 3, 3, 130, 64, 65, "bf16", False),
+    # bf16 head_dim 64/128 with seg_len <= 64 take the fused matrix-core backward
+    (1, 2, 2, 192, 64, 64, "bf16", True),
+    (2, 8, 2, 96, 128, 48, "bf16", True),      # ragged segment tile, 4 heads per K/V head
+    (1, 2, 1, 40, 128, 8, "bf16", False),
+    (1, 2, 2, 5, 64, 1, "bf16", True),
 ]
 
 
@@ -161,8 +166,10 @@ def test_backward_shapes(case):
 
 def test_kernel_path_selection():
     from compressive_linear_memory_amd import binding as Bi
-    assert Bi.fwd_path(Bi.Problem(1, 2, 2, 64, 128, 16, 1)) == "mfma_bf16"
-    assert Bi.fwd_path(Bi.Problem(1, 2, 2, 64, 64, 16, 1)) == "mfma_bf16"
+    assert Bi.fwd_path(Bi.Problem(1, 2, 2, 64, 128, 16, 1)) == "mfma_bf16_short"
+    assert Bi.fwd_path(Bi.Problem(1, 2, 2, 64, 64, 64, 1)) == "mfma_bf16_short"
+    assert Bi.fwd_path(Bi.Problem(1, 2, 2, 130, 64, 65, 1)) == "mfma_bf16"
+    assert Bi.fwd_path(Bi.Problem(1, 2, 2, 256, 128, 128, 1)) == "mfma_bf16"
     assert Bi.fwd_path(Bi.Problem(1, 2, 2, 64, 32, 16, 1)) == "generic_fp32"
     assert Bi.fwd_path(Bi.Problem(1, 2, 2, 64, 128, 16, 0)) == "generic_fp32"
 
