@@ -62,6 +62,27 @@ def algorithmic(w: I.Workload):
     )
 
 
+def recorded_traffic(w, path):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary, or None if there is none for this workload or the kernel source
+    changed since the counters were taken."""
+    import hashlib
+    if w.name != "fwd_llama3_8b" or path != "mfma_bf16":
+        return None
+    prof = os.path.join(ROOT, "profiles", "fwd_llama3_8b_traffic.md")
+    src = os.path.join(ROOT, "compressive_linear_memory_amd", "csrc", "fwd_mfma.hip")
+    try:
+        text = open(prof).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    vals = dict(line.split(": ", 1) for line in text.splitlines()
+                if line.startswith(("traffic_bytes_per_launch:", "kernel_source_sha256:")))
+    if vals.get("kernel_source_sha256", "").strip() != sha:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(w, Q, K, V, beta, o_gpu_host_rows, budget_s=12.0):
     """Time the fp64 oracle on a bounded sample of the same workload."""
     import oracle as O
@@ -106,9 +127,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fwd_llama3_8b", choices=sorted(I.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="fwd", choices=["fwd", "train", "stream"],
+    ap.add_argument("--mode", default="fwd", choices=["fwd", "train", "stream", "copy"],
                     help="fwd: forward throughput (default, the headline line); train: forward + "
-                         "backward step; stream: chained single-segment launches carrying the state")
+                         "backward step; stream: chained single-segment launches carrying the state; "
+                         "copy: a plain device copy of known size (calibrates HBM byte counters)")
     ap.add_argument("--launches", type=int, default=512, help="stream mode: chained launches per step")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -119,6 +141,8 @@ def main():
         return bench_train(args)
     if args.mode == "stream":
         return bench_stream(args)
+    if args.mode == "copy":
+        return bench_copy(args)
 
     import torch
     from compressive_linear_memory_amd import binding as Bi
@@ -145,7 +169,12 @@ def main():
     M_S = torch.empty((B_, Hkv, d, d), dtype=torch.float32, device=dev)
     z_S = torch.empty((B_, Hkv, d), dtype=torch.float32, device=dev)
 
+    fused = path == "mfma_bf16_short"      # short segments: one fused kernel, no phases
+
     def step():
+        if fused:
+            Bi.attn_fwd(q, k, v, b, w.seg_len, out=(O_, M_S, z_S, None), ws=ws)
+            return
         Bi.fwd_memory(p, k, v, None, None, M_S, z_S, ws)
         Bi.fwd_attend(p, q, k, v, b, O_, None, ws)
 
@@ -158,9 +187,13 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record()
-        Bi.fwd_memory(p, k, v, None, None, M_S, z_S, ws)
+        if not fused:
+            Bi.fwd_memory(p, k, v, None, None, M_S, z_S, ws)
         ev[i][1].record()
-        Bi.fwd_attend(p, q, k, v, b, O_, None, ws)
+        if fused:
+            Bi.attn_fwd(q, k, v, b, w.seg_len, out=(O_, M_S, z_S, None), ws=ws)
+        else:
+            Bi.fwd_attend(p, q, k, v, b, O_, None, ws)
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -173,16 +206,22 @@ def main():
     say(f"[bench] {ms_step:.3f} ms/step (memory {mem_ms:.3f} ms, attend {att_ms:.3f} ms); wall {wall:.2f} s")
 
     alg = algorithmic(w)
-    if path == "mfma_bf16":
+    if fused:   # the one kernel does the whole step
+        alg["attend_flop"] = alg["step_flop"]
+    if path.startswith("mfma_bf16"):
         roof = dict(bound="mfma", peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s")
         dtype = "bf16"
     else:
         roof = dict(bound="alu", peak=PEAK_FP32_VECTOR_TFLOPS, unit="TFLOP/s")
         dtype = "fp32"
     achieved = alg["attend_flop"] / (att_ms / 1e3) / 1e12
-    roof.update(achieved=round(achieved, 3), frac=round(achieved / roof["peak"], 5), traffic=None,
-                kernel="infini_fwd_attend", flop_per_launch=alg["attend_flop"],
-                launch_ms=round(att_ms, 4))
+    if fused:   # short segments stream every tensor once at low arithmetic intensity
+        roof = dict(bound="hbm", peak=PEAK_HBM_GBS, unit="GB/s")
+        achieved = alg["step_bytes"] / (att_ms / 1e3) / 1e9
+    roof.update(achieved=round(achieved, 3), frac=round(achieved / roof["peak"], 5),
+                traffic=recorded_traffic(w, path), traffic_unit="HBM bytes per launch",
+                kernel="infini_attn_fwd (fused)" if fused else "infini_fwd_attend",
+                flop_per_launch=alg["attend_flop"], launch_ms=round(att_ms, 4))
     step_tflops = alg["step_flop"] / (ms_step / 1e3) / 1e12
     out = {
         "metric": METRIC if w.name == "fwd_llama3_8b" else f"Infini-attention fwd tokens/s ({w.name})",
@@ -311,6 +350,28 @@ def bench_stream(args):
                       "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": "stream_1m", "mode": "stream", "launches": nl,
                                  "kernel_path": Bi.fwd_path(p)}}), flush=True)
+
+
+def bench_copy(args):
+    """A plain 1 GiB device-to-device copy per step: the reference for scaling
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = 1 << 28                      # float32 elements = 1 GiB
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"metric": "device copy GB/s", "value": round(2 * n * 4 / (ms / 1e3) / 1e9, 1), "unit": "GB/s",
+                      "bytes_read_per_step": n * 4, "bytes_written_per_step": n * 4, "ms_per_step": round(ms, 4),
+                      "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
 if __name__ == "__main__":
