@@ -73,7 +73,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      int Hq, int Hkv, int N, int L, int s_begin, int nseg, int nqt, float sl2) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[C::LDS_ELEMS];
-  __shared__ float zs[D];
+  __shared__ __attribute__((aligned(16))) float zs[D];
 
   // ---- work decode: each XCD (workgroups are dealt round-robin to 8 XCDs)
   // takes a contiguous range of work so that the query heads and tiles that
@@ -118,11 +118,9 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // ---- global -> register staging of K and V tiles
   //
-  // LDS holds two K tiles and two V^T tiles.  Iteration j of the key loop
-  // reads K(j+1) (scores of the next tile, computed under this tile's
-  // softmax) and V(j) (this tile's PV product); at its end it stores K(j+2)
-  // into the K buffer K(j) used and V(j+1) into the other V buffer, then one
-  // barrier.  Global loads run one iteration ahead of their LDS store.
+  // LDS holds two (K, V^T) buffers; tile j computes from buffer j & 1 while
+  // tile j + 1, loaded into registers during tile j, is stored into the other
+  // buffer at its end (one barrier per tile).
   bf16x8_t kst[C::CPT], vst[C::KPT];
   // V^T staging: consecutive lanes take consecutive key groups so that the
   // transposed LDS stores of a 16-lane group hit distinct banks.
@@ -134,33 +132,24 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // the score mask removes (K) or that meet a zero probability (V).
   const __bf16* Kseg = K + kvbase;
   const __bf16* Vseg = V + kvbase;
-  int koff[C::CPT], krow[C::CPT];
-#pragma unroll
-  for (int i = 0; i < C::CPT; ++i) {
-    const int c = tid + 256 * i;
-    krow[i] = c / (D / 8);
-    koff[i] = krow[i] * D + (c % (D / 8)) * 8;
-  }
-  auto load_k = [&](int k0) {
-    const __bf16* kt = Kseg + (size_t)k0 * D;
-    if (k0 + C::BN <= L) {
-#pragma unroll
-      for (int i = 0; i < C::CPT; ++i) kst[i] = *reinterpret_cast<const bf16x8_t*>(kt + koff[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::CPT; ++i) {
-        const int key = min(k0 + krow[i], L - 1);
-        kst[i] = *reinterpret_cast<const bf16x8_t*>(Kseg + (size_t)key * D + (koff[i] - krow[i] * D));
-      }
-    }
-  };
-  auto load_v = [&](int k0) {
+  // K chunk i of this thread: row krow0 + i * KRS, columns kcol .. kcol + 7
+  constexpr int KRS = 256 / (D / 8);
+  const int krow0 = tid / (D / 8), kcol = (tid % (D / 8)) * 8;
+  auto load_tile = [&](int k0) {
+    const __bf16* kt = Kseg + (size_t)k0 * D + krow0 * D + kcol;
     const __bf16* vt = Vseg + (size_t)k0 * D;
     if (k0 + C::BN <= L) {
+#pragma unroll
+      for (int i = 0; i < C::CPT; ++i) kst[i] = *reinterpret_cast<const bf16x8_t*>(kt + i * KRS * D);
 #pragma unroll
       for (int i = 0; i < C::KPT; ++i)
         vst[i] = *reinterpret_cast<const bf16x8_t*>(vt + (vkg * C::KPT + i) * D + vdc * 8);
     } else {
+#pragma unroll
+      for (int i = 0; i < C::CPT; ++i) {
+        const int key = min(k0 + krow0 + i * KRS, L - 1);
+        kst[i] = *reinterpret_cast<const bf16x8_t*>(Kseg + (size_t)key * D + kcol);
+      }
 #pragma unroll
       for (int i = 0; i < C::KPT; ++i) {
         const int key = min(k0 + vkg * C::KPT + i, L - 1);
@@ -168,19 +157,12 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       }
     }
   };
-  __bf16* const kbuf0 = smem;
-  __bf16* const vbuf0 = smem + 2 * C::KTILE;
-  auto store_k = [&](int buf) {
-    __bf16* Ks = kbuf0 + buf * C::KTILE;
+  auto store_tile = [&](int buf) {
+    __bf16* Ks = smem + buf * C::BUF;
+    __bf16* Vt = Ks + C::KTILE;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<bf16x8_t*>(Ks + row * C::KSTR + col) = kst[i];
-    }
-  };
-  auto store_v = [&](int buf) {
-    __bf16* Vt = vbuf0 + buf * C::VTILE;
+    for (int i = 0; i < C::CPT; ++i)
+      *reinterpret_cast<bf16x8_t*>(Ks + (krow0 + i * KRS) * C::KSTR + kcol) = kst[i];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       __bf16* dst = Vt + (vdc * 8 + e) * C::VSTR + vkg * C::KPT;
@@ -194,46 +176,71 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   };
 
+  // The retrieval operands (bf16 M_{s-1}^T, fp32 z_{s-1}) go straight from
+  // global memory into the tile buffer the last tile does not use
+  // (global_load_lds_dwordx4: lane l of a wave's load lands at base + 16 l), so
+  // the epilogue neither waits on them nor spends staging registers.  M^T rows
+  // are unpadded; 16-byte chunk c of row r sits at chunk c ^ (r & 7), which
+  // keeps the epilogue's row reads conflict-free.
+  constexpr int MPT = D * D / 8 / 256;    // 16-byte chunks of M^T per thread
+  static_assert(D * D <= C::BUF, "M^T stage must fit one tile buffer");
+  const __bf16* msrc = MsnapT + ((size_t)bk * nseg + sl) * D * D;
+  const float* zsrc = zsnap + ((size_t)bk * nseg + sl) * D;
+  // Wave load i of wave w covers 1 KB block i*4 + w, i.e. rows
+  // (i*4 + w) * RPB + lane / (D/8); (row & 7) does not depend on i, so every
+  // load of a lane is one base address plus a constant.
+  constexpr int RPB = 64 / (D / 8);               // M^T rows per 1 KB block
+  const int mrow0 = wave * RPB + lane / (D / 8);
+  const __bf16* msrc0 = msrc + (size_t)mrow0 * D + (((lane % (D / 8)) ^ (mrow0 & 7)) * 8);
+  auto load_m = [&](__bf16* dst) {
+#pragma unroll
+    for (int i = 0; i < MPT; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(msrc0 + (size_t)i * 4 * RPB * D),
+                                       (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 512), 16, 0, 0);
+    if (wave < D / 64)
+      __builtin_amdgcn_global_load_lds((const void*)(zsrc + wave * 64 + lane),
+                                       (__attribute__((address_space(3))) void*)(zs + wave * 64), 4, 0, 0);
+  };
+
   f32x16_t oacc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16_t{};
   float m = -INFINITY, lpart = 0.f;
 
-  // S^T = K Q^T for one 64-key tile (two 32-key blocks).
-  auto scores = [&](const __bf16* Ks, f32x16_t (&sa)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sa[kb] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 32 + lq) * C::KSTR + ks * 16 + hh * 8);
-        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sa[kb], 0, 0, 0);
-      }
-    }
-  };
-
-  // Online softmax over one tile's scores.  Scores stay in the raw domain until
-  // one FMA per element forms (s * scale * log2 e - m); the running max m
+  // One 64-key tile for this wave's 32 rows.  Scores stay in the raw domain
+  // until one FMA per element forms (s * scale * log2 e - m); the running max m
   // (scaled, base 2) only moves when a row's tile max exceeds it by more than
   // kRescaleSlack, so the accumulator rescale is skipped on almost every tile.
   // Any reference value gives the same normalised result; the slack bounds the
   // unnormalised terms by 2^kRescaleSlack.
   constexpr float kRescaleSlack = 8.f;
-  auto softmax_max = [&](f32x16_t (&sa)[2], int k0, bool masked) {
-    if (masked) {
+  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+  auto tile_step = [&](const __bf16* Ks, const __bf16* Vt, int k0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 32 + lq) * C::KSTR + ks * 16 + hh * 8);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[kb], 0, 0, 0);
+      }
+    }
+    if constexpr (MASK) {
       // element (kb, r) holds key k0 + 4hh + kb*32 + 8(r/4) + r%4
       const int lim = min(qrow, L - 1) - (k0 + 4 * hh);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sa[kb][r] = -INFINITY;
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
     }
-    float mt = sa[0][0];
+    float mt = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sa[kb][r]);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
     mt = pair_max32(mt) * sl2;
     if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack)) {
       const float mn = fmaxf(m, mt);
@@ -243,14 +250,12 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
     }
-  };
-  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
-  auto softmax_exp = [&](const f32x16_t (&sa)[2], bf16x8_t (&pb)[2][2]) {
+    bf16x8_t pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        pb[kb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sa[kb][r], sl2, -m));
+        pb[kb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -m));
     // Row sum of the bf16 probabilities the PV product uses, two per v_dot2.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -259,9 +264,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int x = 0; x < 4; ++x)
           lpart = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[kb][t][2 * x], pb[kb][t][2 * x + 1]}, ones, lpart, false);
-  };
-  // O^T += V^T P^T: k-slot q of half hh <-> key 16t + 8(q/4) + 4hh + q%4.
-  auto pv = [&](const __bf16* Vt, const bf16x8_t (&pb)[2][2]) {
+    // O^T += V^T P^T: k-slot q of half hh <-> key 16t + 8(q/4) + 4hh + q%4
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -278,64 +281,31 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   };
 
-  // Tiles this wave attends to: k0 <= q0 + 31 (its other tiles lie above the diagonal).
-  const int n_act = q0 < L ? min(ntiles, (q0 + C::WM - 1) / C::BN + 1) : 0;
-
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  if (ntiles > 1) {
-    load_k(C::BN);
-    store_k(1);
-  }
+  load_tile(0);
+  store_tile(0);
   __syncthreads();
-  if (ntiles > 2) load_k(2 * C::BN);
-  if (ntiles > 1) load_v(C::BN);
-
-  f32x16_t scur[2];
-  if (n_act > 0) scores(kbuf0, scur);
+  if (ntiles > 1) load_tile(C::BN);
+  else load_m(smem + C::BUF);
 
   for (int j = 0; j < ntiles; ++j) {
     const int k0 = j * C::BN;
-    if (j < n_act) {
-      const bool masked = (k0 + C::BN - 1 > q0) || (k0 + C::BN > L);
-      softmax_max(scur, k0, masked);
-      bf16x8_t pb[2][2];
-      if (j + 1 < n_act) {
-        // next tile's scores on the matrix cores while this tile's
-        // exponentials run on the vector ALUs
-        f32x16_t snext[2];
-        scores(kbuf0 + ((j + 1) & 1) * C::KTILE, snext);
-        softmax_exp(scur, pb);
-        pv(vbuf0 + (j & 1) * C::VTILE, pb);
-        scur[0] = snext[0];
-        scur[1] = snext[1];
-      } else {
-        softmax_exp(scur, pb);
-        pv(vbuf0 + (j & 1) * C::VTILE, pb);
-      }
+    const __bf16* Ks = smem + (j & 1) * C::BUF;
+    const __bf16* Vt = Ks + C::KTILE;
+    const bool active = k0 <= q0 + C::WM - 1 && q0 < L;
+    const bool masked = (k0 + C::BN - 1 > q0) || (k0 + C::BN > L);
+    if (active) {
+      if (masked) tile_step(Ks, Vt, k0, std::true_type{});
+      else tile_step(Ks, Vt, k0, std::false_type{});
     }
-    if (j + 2 < ntiles) store_k(j & 1);
-    if (j + 1 < ntiles) store_v((j + 1) & 1);
+    if (j + 1 < ntiles) store_tile((j + 1) & 1);
     __syncthreads();
-    if (j + 3 < ntiles) load_k((j + 3) * C::BN);
-    if (j + 2 < ntiles) load_v((j + 2) * C::BN);
+    if (j + 2 < ntiles) load_tile((j + 2) * C::BN);
+    else if (j + 2 == ntiles) load_m(smem + (ntiles & 1) * C::BUF);
   }
+  const __bf16* Mts = smem + (ntiles & 1) * C::BUF;   // where load_m put M^T
 
-  // ---- retrieval from M_{s-1}, z_{s-1} and the gate
+  // ---- retrieval from M_{s-1}, z_{s-1} (staged in the K buffers) and the gate
   const float l = pair_sum32(lpart);
-  {
-    const __bf16* src = MsnapT + ((size_t)bk * nseg + sl) * D * D;
-    for (int c = tid; c < D * D / 8; c += 256) {
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<bf16x8_t*>(smem + row * C::MSTR + col) =
-          *reinterpret_cast<const bf16x8_t*>(src + (size_t)row * D + col);
-    }
-    const float* zsrc = zsnap + ((size_t)bk * nseg + sl) * D;
-    for (int c = tid; c < D; c += 256) zs[c] = zsrc[c];
-  }
-  __syncthreads();
 
   bf16x8_t sq[C::KS];
   float dpart = 0.f;
@@ -355,7 +325,8 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     nacc[cb] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(smem + (cb * 32 + lq) * C::MSTR + ks * 16 + hh * 8);
+      const int r = cb * 32 + lq;
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Mts + r * D + (((ks * 2 + hh) ^ (r & 7)) * 8));
       nacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sq[ks], nacc[cb], 0, 0, 0);
     }
   }
