@@ -132,6 +132,8 @@ def main():
                          "backward step; stream: chained single-segment launches carrying the state; "
                          "copy: a plain device copy of known size (calibrates HBM byte counters)")
     ap.add_argument("--launches", type=int, default=512, help="stream mode: chained launches per step")
+    ap.add_argument("--graph", action="store_true",
+                    help="stream mode: capture the chained launches of one step in a HIP graph and replay it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the sequence-parallel "
@@ -336,10 +338,21 @@ def bench_stream(args):
     for _ in range(max(1, args.warmup // 3)):
         run()
     torch.cuda.synchronize()
+    step = run
+    if args.graph:
+        # One step's launches recorded once and replayed: the host issues one
+        # graph launch per step instead of two kernel launches per segment.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        torch.cuda.synchronize()
+        step = graph.replay
+        step()
+        torch.cuda.synchronize()
     e0, e1 = _events(2)
     e0.record()
     for _ in range(args.steps):
-        run()
+        step()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -349,7 +362,7 @@ def bench_stream(args):
                       "ms_per_step": round(ms, 4), "us_per_launch": round(1e3 * ms / nl, 2), "higher_is_better": True,
                       "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": "stream_1m", "mode": "stream", "launches": nl,
-                                 "kernel_path": Bi.fwd_path(p)}}), flush=True)
+                                 "graph": bool(args.graph), "kernel_path": Bi.fwd_path(p)}}), flush=True)
 
 
 def bench_copy(args):

@@ -59,10 +59,14 @@ FwdWs fwd_layout(const Geometry& g) {
   const size_t bk = (size_t)g.B * g.Hkv;
   FwdWs w;
   size_t off = 0;
-  w.Msnap = off; off = align_up(off + bk * C * g.D * g.D * 4);
+  // The matrix-core path keeps its per-segment dM parts (one per key split)
+  // where the generic path keeps fp32 snapshots.
+  const bool mfma = infini::fwd_mfma_supported(g);
+  const size_t parts = mfma ? (size_t)infini::delta_splits(g) : 1;
+  w.Msnap = off; off = align_up(off + bk * C * parts * g.D * g.D * 4);
   w.zsnap = off; off = align_up(off + bk * C * g.D * 4);
-  w.MsnapT = off; off = align_up(off + (infini::fwd_mfma_supported(g) ? bk * C * g.D * g.D * 2 : 0));
-  w.dz = off;     off = align_up(off + (infini::fwd_mfma_supported(g) ? bk * C * g.D * 4 : 0));
+  w.MsnapT = off; off = align_up(off + (mfma ? bk * C * g.D * g.D * 2 : 0));
+  w.dz = off;     off = align_up(off + (mfma ? bk * C * parts * g.D * 4 : 0));
   w.total = off;
   return w;
 }

@@ -30,6 +30,9 @@ hipError_t launch_sweep(const Geometry& g, const void* K, const void* V,
 // the scratch buffers dM [B*Hkv][nseg][D][D] and dz [B*Hkv][nseg][D], then the
 // prefix over segments into MsnapT (bf16, transposed) and zsnap, and the state
 // after the last segment into M_out / z_out (may equal M_in / z_in).
+// Key splits per segment of the bf16 memory phase (dM and dz hold that many
+// parts per segment).
+int delta_splits(const Geometry& g);
 hipError_t launch_sweep_mfma(const Geometry& g, const void* K, const void* V, const float* M_in,
                              const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
                              void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st);

@@ -6,10 +6,13 @@
 //   dM_s = sigma(K_s)^T V_s        dz_s = sum_rows sigma(K_s)
 //   M_{s-1} = M0 + sum_{t<s} dM_t  (the state segment s retrieves from)
 // so it runs in two launches:
-//   delta_mfma_kernel  one workgroup per (batch, K/V head, segment): dM_s on
+//   delta_mfma_kernel  one workgroup per (batch, K/V head, segment, key
+//                      split): the split's part of dM_s on
 //                      v_mfma_f32_32x32x16_bf16 with sigma(K)^T and V^T staged
 //                      key-contiguous in LDS; dz_s in fp32 from the unrounded
-//                      sigma(K)
+//                      sigma(K).  Grids with few segments split each segment's
+//                      keys over several workgroups so that the whole chip
+//                      takes part; the scan adds the parts in a fixed order.
 //   scan_kernel        one workgroup per 64x64 tile of M per (batch, K/V head):
 //                      walks the segments in order with the tile resident in
 //                      registers, publishes each M_{s-1} as a transposed bf16
@@ -18,6 +21,7 @@
 #include <hip/hip_runtime.h>
 
 #include "common.h"
+#include "infini.h"
 #include "kernels.h"
 
 namespace infini {
@@ -43,17 +47,20 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                        float* __restrict__ dM, float* __restrict__ dz,
-                       int N, int L, int s_begin, int nseg) {
+                       int N, int L, int s_begin, int nseg, int nsplit, int split_keys) {
   using C = DeltaCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[4 * C::TILE];   // 2 buffers x (K^T, V^T)
   static_assert(C::NKG * (D + 1) * 4 <= 4 * C::TILE * 2, "dz reduction must fit the tile buffers");
   float (*zred)[D + 1] = reinterpret_cast<float (*)[D + 1]>(smem);     // reused after the key loop
 
-  const int unit = blockIdx.x;               // (b * Hkv + kvh) * nseg + sl
+  const int part = blockIdx.x;               // unit * nsplit + split
+  const int unit = part / nsplit;            // (b * Hkv + kvh) * nseg + sl
+  const int k_begin = (part % nsplit) * split_keys;
   const int sl = unit % nseg;
   const size_t bk = unit / nseg;
   const int s = s_begin + sl;
-  const size_t base = (bk * N + (size_t)s * L) * D;
+  const size_t base = (bk * N + (size_t)s * L + k_begin) * D;
+  L = max(0, min(L - k_begin, split_keys));   // keys of this split (may be none)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -114,8 +121,10 @@ void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ 
     for (int y = 0; y < C::WB; ++y) acc[x][y] = f32x16_t{};
 
   const int nch = (L + C::BK - 1) / C::BK;
-  load_chunk(0);
-  store_chunk(0, 0);
+  if (nch > 0) {
+    load_chunk(0);
+    store_chunk(0, 0);
+  }
   __syncthreads();
   for (int j = 0; j < nch; ++j) {
     if (j + 1 < nch) load_chunk((j + 1) * C::BK);
@@ -140,7 +149,7 @@ void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ 
   }
 
   // dM[a][c]: lane holds column c = lq, rows 8(r/4) + 4hh + r%4 of each block.
-  float* out = dM + (size_t)unit * D * D;
+  float* out = dM + (size_t)part * D * D;
 #pragma unroll
   for (int x = 0; x < C::WB; ++x)
 #pragma unroll
@@ -158,7 +167,7 @@ void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ 
   for (int a = tid; a < D; a += 256) {
     float t = 0.f;
     for (int g = 0; g < C::NKG; ++g) t += zred[g][a];
-    dz[(size_t)unit * D + a] = t;
+    dz[(size_t)part * D + a] = t;
   }
 }
 
@@ -169,7 +178,8 @@ constexpr int SC_T = 64;   // tile edge
 template <int D>
 __global__ __launch_bounds__(256) void scan_kernel(
     const float* __restrict__ dM, const float* __restrict__ dz, const float* M_in, const float* z_in,
-    float* M_out, float* z_out, __bf16* __restrict__ MsnapT, float* __restrict__ zsnap, int nseg) {
+    float* M_out, float* z_out, __bf16* __restrict__ MsnapT, float* __restrict__ zsnap, int nseg,
+    int nsplit) {
   constexpr int TPR = D / SC_T;
   __shared__ float tr[SC_T][SC_T + 1];
   const int a0 = (blockIdx.x / TPR) * SC_T, c0 = (blockIdx.x % TPR) * SC_T;
@@ -204,13 +214,27 @@ __global__ __launch_bounds__(256) void scan_kernel(
       }
     }
     __syncthreads();
-    const float* src = dM + unit * D * D + eoff;
+    // dM_s = sum of its key-split parts, added in split order
+    float part[16];
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float* src = dM + (unit * nsplit + sp) * D * D + eoff;
 #pragma unroll
-    for (int x = 0; x < 16; x += 4) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + x);
-      run[x] += v[0]; run[x + 1] += v[1]; run[x + 2] += v[2]; run[x + 3] += v[3];
+      for (int x = 0; x < 16; x += 4) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + x);
+        if (sp == 0) {
+          part[x] = v[0]; part[x + 1] = v[1]; part[x + 2] = v[2]; part[x + 3] = v[3];
+        } else {
+          part[x] += v[0]; part[x + 1] += v[1]; part[x + 2] += v[2]; part[x + 3] += v[3];
+        }
+      }
     }
-    if (do_z && tid < SC_T) zr += dz[unit * D + a0 + tid];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) run[x] += part[x];
+    if (do_z && tid < SC_T) {
+      float zpart = dz[(unit * nsplit) * D + a0 + tid];
+      for (int sp = 1; sp < nsplit; ++sp) zpart += dz[(unit * nsplit + sp) * D + a0 + tid];
+      zr += zpart;
+    }
   }
   if (M_out) {
 #pragma unroll
@@ -224,17 +248,31 @@ static hipError_t sweep_mfma_t(const Geometry& g, const void* K, const void* V, 
                                const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
                                void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st) {
   const int nseg = s_end - s_begin;
-  const long long units = (long long)g.B * g.Hkv * nseg;
-  if (units > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((delta_mfma_kernel<D>), dim3((unsigned)units), dim3(256), 0, st,
+  const int nsplit = delta_splits(g);
+  const int split_keys = (((g.L + nsplit - 1) / nsplit + 63) / 64) * 64;
+  const long long parts = (long long)g.B * g.Hkv * nseg * nsplit;
+  if (parts > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((delta_mfma_kernel<D>), dim3((unsigned)parts), dim3(256), 0, st,
                      static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), dM, dz, g.N, g.L,
-                     s_begin, nseg);
+                     s_begin, nseg, nsplit, split_keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((D / SC_T) * (D / SC_T), g.B * g.Hkv);
   hipLaunchKernelGGL((scan_kernel<D>), grid, dim3(256), 0, st, dM, dz, M_in, z_in, M_out, z_out,
-                     static_cast<__bf16*>(MsnapT), zsnap, nseg);
+                     static_cast<__bf16*>(MsnapT), zsnap, nseg, nsplit);
   return hipGetLastError();
+}
+
+// Key splits per segment for the delta kernel: 1 when a chunk of segments
+// already gives every compute unit work, else enough splits of at least 128
+// keys to reach about 512 workgroups.
+int delta_splits(const Geometry& g) {
+  const long long units = (long long)g.B * g.Hkv * (g.S < INFINI_CHUNK_SEGMENTS ? g.S : INFINI_CHUNK_SEGMENTS);
+  if (units >= 256) return 1;
+  const long long want = (512 + units - 1) / units;
+  const long long most = g.L / 128 > 1 ? g.L / 128 : 1;
+  const long long n = want < most ? want : most;
+  return (int)(n < 16 ? n : 16);
 }
 
 hipError_t launch_sweep_mfma(const Geometry& g, const void* K, const void* V, const float* M_in,

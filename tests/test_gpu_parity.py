@@ -125,6 +125,8 @@ FWD_CASES = [
     (1, 4, 1, 200, 128, 100, "bf16", True),
     (1, 2, 2, 600, 64, 300, "bf16", True),
     (1, 8, 2, 1024, 128, 512, "bf16", True),
+    (1, 4, 2, 1540, 128, 770, "bf16", True),   # 2-row last query tile
+    (1, 2, 1, 1000, 64, 1000, "bf16", False),
 ]
 
 
@@ -230,6 +232,47 @@ def test_multi_chunk_matches_single_chunk(monkeypatch):
         assert rel(host(a), host(b)) < 1e-5
     ro, rM, rz = O.forward(Q, K, V, beta, 16, M0, z0)
     assert rel(host(got_f[0]), ro) < 1e-4
+
+
+@pytest.mark.parametrize("L", [256, 64], ids=["long_path", "fused_short_path"])
+def test_graph_replay_matches_eager(L):
+    """Chained forward calls recorded once in a HIP graph: every replay equals
+    the eager run bit for bit, with eager work and synchronisation between the
+    replays (the library issues no memset or allocation inside the calls)."""
+    Bi = B()
+    Bn, Hq, Hkv, N, d = 1, 4, 2, 512, 64
+    Q, K, V, beta, M0, z0 = make(Bn, Hq, Hkv, N, d, "bf16", seed=91, with_state=True)
+    q, k, v, b, m0, s0 = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), dev(beta), dev(M0), dev(z0)
+    p = Bi.problem(q, k, L)
+    ws = torch.empty(max(Bi.workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
+    n = 3
+    outs = [(torch.empty_like(q), torch.empty_like(m0), torch.empty_like(s0)) for _ in range(n)]
+
+    def chain():
+        m, z = m0, s0
+        for i in range(n):
+            Bi.attn_fwd(q, k, v, b, L, m, z, out=(outs[i][0], outs[i][1], outs[i][2], None), ws=ws)
+            m, z = outs[i][1], outs[i][2]
+
+    chain()
+    torch.cuda.synchronize()
+    eager = [tuple(t.clone() for t in o) for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for o in outs:
+            for t in o:
+                t.fill_(float("nan"))
+        Bi.attn_fwd(q, k, v, b, L, m0, s0, ws=ws)      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(n):
+            for a, e in zip(outs[i], eager[i]):
+                assert torch.equal(a, e), (r, i)
+    log(f"   graph L={L}: 3 replays of {n} chained calls equal the eager run")
 
 
 def test_run_twice_bitwise_identical():
