@@ -123,8 +123,9 @@ def cpu_baseline(w, Q, K, V, beta, o_gpu_host_rows, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="untimed steps; the first few launches run slower while the GPU clocks ramp up")
     ap.add_argument("--workload", default="fwd_llama3_8b", choices=sorted(I.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="fwd", choices=["fwd", "train", "stream", "copy"],
@@ -298,12 +299,24 @@ def bench_train(args):
     fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     tok = w.batch * w.seq_len
+    # Short training segments stream every tensor a few times at low arithmetic
+    # intensity: the HBM roofline binds.  Algorithmic bytes: the forward's
+    # (Q, K, V in, O out, state) plus the backward's (Q, K, V, dO, row LSE in;
+    # dQ, dK, dV out; state).
+    alg = algorithmic(w)
+    eb = 4 if w.dtype == "fp32" else 2
+    n_q, n_kv = B_ * Hq * N * d, B_ * Hkv * N * d
+    bwd_bytes = eb * (2 * n_q + 2 * n_kv) + 4 * B_ * Hq * N + eb * (n_q + 2 * n_kv) + 2 * B_ * Hkv * (d * d + d) * 4
+    step_bytes = alg["step_bytes"] + 4 * B_ * Hq * N + bwd_bytes
+    ach = step_bytes / (total / args.steps / 1e3) / 1e9
+    roof = dict(bound="hbm", peak=PEAK_HBM_GBS, unit="GB/s", achieved=round(ach, 1), frac=round(ach / PEAK_HBM_GBS, 5),
+                traffic=None, kernel="infini_attn_fwd + infini_attn_bwd", bytes_per_step=step_bytes)
     print(json.dumps({"metric": f"Infini-attention fwd+bwd tokens/s ({w.name})", "value": round(tok * args.steps / (total / 1e3), 1),
                       "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "ms_per_step": round(total / args.steps, 4), "higher_is_better": True, "scaling": "weak",
                       "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
                       "config": {"workload": w.name, "mode": "train", "kernel_path": Bi.fwd_path(p)},
-                      "phases_ms": {"fwd": round(fwd, 4), "bwd": round(bwd, 4)}}), flush=True)
+                      "phases_ms": {"fwd": round(fwd, 4), "bwd": round(bwd, 4)}, "roofline": roof}), flush=True)
 
 
 def bench_stream(args):
@@ -357,12 +370,19 @@ def bench_stream(args):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     tok = w.seq_len * nl
+    # Each launch is one 2048-token segment per head: matrix-core bound in
+    # principle (arithmetic intensity ~545 flop/byte).
+    alg = algorithmic(w.with_(launches=1))
+    ach = alg["step_flop"] / (ms / nl / 1e3) / 1e12
+    roof = dict(bound="mfma", peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s", achieved=round(ach, 3),
+                frac=round(ach / PEAK_BF16_MFMA_TFLOPS, 5), traffic=None,
+                kernel="infini_attn_fwd (memory + attention) per launch", flop_per_launch=alg["step_flop"])
     print(json.dumps({"metric": "Infini-attention streaming fwd tokens/s (stream_1m)", "value": round(tok / (ms / 1e3), 1),
                       "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "ms_per_step": round(ms, 4), "us_per_launch": round(1e3 * ms / nl, 2), "higher_is_better": True,
                       "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": "stream_1m", "mode": "stream", "launches": nl,
-                                 "graph": bool(args.graph), "kernel_path": Bi.fwd_path(p)}}), flush=True)
+                                 "graph": bool(args.graph), "kernel_path": Bi.fwd_path(p)}, "roofline": roof}), flush=True)
 
 
 def bench_copy(args):
