@@ -49,6 +49,12 @@ Readings where the pages leave a step open (each is stated where it is used):
       the method is trainable end to end); dM_S, dz_S are optional upstream
       gradients of the carried state and dM0, dz0 the gradients of the state
       passed in, so backward chains across calls like the forward.
+  R10 A sequence whose length is not a multiple of the segment length ends in
+      one shorter segment ([HF] Segmentation fixes the segment length but not
+      what happens to a remainder).  It is processed like every other segment:
+      causal attention among its own tokens, retrieval from the state before
+      it, and an update with its keys.  So segments are the slices
+      [s L, min((s+1) L, N)) for s = 0 .. ceil(N / L) - 1.
 
 Parity pins: every public function is pinned by tests in tests/test_oracle_pins.py
 against brute force, closed forms, invariants, a library attention routine
@@ -93,8 +99,18 @@ def _dims(Q, K, seg_len):
     Bk, Hkv, Nk, dk = K.shape
     assert (B, N, d) == (Bk, Nk, dk), "Q and K disagree in batch, length or head_dim"
     assert Hq % Hkv == 0, "query heads must be a multiple of K/V heads"
-    assert N % seg_len == 0, "sequence length must be a multiple of seg_len"
-    return B, Hq, Hkv, N, d, Hq // Hkv, N // seg_len
+    return B, Hq, Hkv, N, d, Hq // Hkv, num_segments(N, seg_len)
+
+
+def num_segments(N, seg_len):
+    """Segments of a call: ceil(N / seg_len), the last one possibly shorter (R10)."""
+    assert N > 0 and seg_len > 0
+    return -(-N // seg_len)
+
+
+def seg_rows(s, seg_len, N):
+    """Token rows of segment s: [s L, min((s+1) L, N)) ([HF] Segmentation; R10)."""
+    return slice(s * seg_len, min((s + 1) * seg_len, N))
 
 
 def _state_or_zero(M0, z0, B, Hkv, d):
@@ -156,14 +172,14 @@ def state_sweep(K, V, seg_len, M0=None, z0=None):
     that segment s retrieves from (R6), and M_S the state after the last segment."""
     K, V = f64(K), f64(V)
     B, Hkv, N, d = K.shape
-    S = N // seg_len
+    S = num_segments(N, seg_len)
     M, z = _state_or_zero(M0, z0, B, Hkv, d)
     Msnap = np.empty((B, Hkv, S, d, d))
     zsnap = np.empty((B, Hkv, S, d))
     for b in range(B):
         for k in range(Hkv):
             for s in range(S):
-                r = slice(s * seg_len, (s + 1) * seg_len)
+                r = seg_rows(s, seg_len, N)
                 Msnap[b, k, s] = M[b, k]
                 zsnap[b, k, s] = z[b, k]
                 M[b, k], z[b, k] = memory_update(M[b, k], z[b, k], K[b, k, r], V[b, k, r])
@@ -198,7 +214,7 @@ def forward(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS, want_lse=False):
     for b in range(B):
         for k in range(Hkv):
             for s in range(S):                                  # Segmentation
-                r = slice(s * seg_len, (s + 1) * seg_len)
+                r = seg_rows(s, seg_len, N)
                 Ks, Vs = K[b, k, r], V[b, k, r]
                 for h in range(k * G, (k + 1) * G):             # R7
                     Qs = Q[b, h, r]
@@ -280,7 +296,7 @@ def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None,
     for b in range(B):
         for k in range(Hkv):
             for s in reversed(range(S)):
-                r = slice(s * seg_len, (s + 1) * seg_len)
+                r = seg_rows(s, seg_len, N)
                 Ks, Vs = K[b, k, r], V[b, k, r]
                 sK = sigma(Ks)
                 # memory update of segment s: M_s = M_{s-1} + sK^T V_s

@@ -375,3 +375,86 @@ def test_backward_chains_across_calls():
     assert np.max(np.abs(np.concatenate([g1["dK"], g2["dK"]], 2) - full["dK"])) < 1e-12
     assert np.max(np.abs(np.concatenate([g1["dV"], g2["dV"]], 2) - full["dV"])) < 1e-12
     assert np.max(np.abs(g1["dbeta"] + g2["dbeta"] - full["dbeta"])) < 1e-12
+
+
+# ----------------------------------------------------------- R10: ragged final segment
+
+def test_R10_segments_cover_the_sequence_once():
+    for N, L in [(1, 1), (7, 3), (12, 4), (100, 32), (5, 64)]:
+        S = O.num_segments(N, L)
+        rows = [O.seg_rows(s, L, N) for s in range(S)]
+        cover = np.concatenate([np.arange(N)[r] for r in rows])
+        assert np.array_equal(cover, np.arange(N))
+        assert all(r.stop - r.start == L for r in rows[:-1]) and 0 < rows[-1].stop - rows[-1].start <= L
+
+
+def test_R10_ragged_gate_closed_matches_torch_sdpa():
+    """beta = -inf with a short final segment: torch SDPA (float64, causal) on
+    each slice [s L, min((s+1) L, N)), K/V repeat-interleaved for GQA."""
+    B, Hq, Hkv, N, d, L = 2, 4, 2, 100, 8, 32
+    Q, K, V, _ = _problem(B, Hq, Hkv, N, d, seed=221)
+    M0, z0 = _prefix_state(B, Hkv, d)
+    out, _, _ = O.forward(Q, K, V, np.full(Hq, -np.inf), L, M0, z0)
+    Kr = np.repeat(K, Hq // Hkv, axis=1)
+    Vr = np.repeat(V, Hq // Hkv, axis=1)
+    ref = np.zeros_like(Q)
+    for s0 in range(0, N, L):
+        r = slice(s0, min(s0 + L, N))
+        ref[:, :, r] = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(Q[:, :, r]), torch.tensor(Kr[:, :, r]), torch.tensor(Vr[:, :, r]),
+            is_causal=True).numpy()
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_R10_ragged_state_equals_one_shot_sum():
+    Q, K, V, beta = _problem(B=2, Hq=4, Hkv=2, N=23, d=5, seed=231)
+    M0, z0 = _prefix_state(2, 2, 5)
+    _, M, z = O.forward(Q, K, V, beta, 6, M0, z0)
+    sK = torch.nn.functional.elu(torch.tensor(K)).numpy() + 1
+    assert np.max(np.abs(M - (M0 + np.einsum("bhna,bhnc->bhac", sK, V)))) < 1e-12
+    assert np.max(np.abs(z - (z0 + sK.sum(axis=2)))) < 1e-12
+
+
+@pytest.mark.parametrize("N,L", [(11, 4), (9, 8), (5, 2)])
+def test_R10_ragged_per_token_form_agrees(N, L):
+    Q, K, V, beta = _problem(B=1, Hq=4, Hkv=2, N=N, d=3, seed=241)
+    M0, z0 = _prefix_state(1, 2, 3)
+    o, _, _ = O.forward(Q, K, V, beta, L, M0, z0)
+    assert np.max(np.abs(o - O.forward_per_token(Q, K, V, beta, L, M0, z0))) < 1e-12
+
+
+def test_R10_ragged_call_equals_full_segments_then_remainder():
+    """N = 3 L + 2: one call equals a call over 3 L tokens followed by a call
+    over the last 2 tokens (one segment shorter than L) carrying the state."""
+    Q, K, V, beta = _problem(Hq=2, Hkv=1, N=14, d=4, seed=251)
+    L = 4
+    o_all, M_all, z_all = O.forward(Q, K, V, beta, L)
+    a, b = slice(0, 12), slice(12, 14)
+    o1, M1, z1 = O.forward(Q[:, :, a], K[:, :, a], V[:, :, a], beta, L)
+    o2, M2, z2 = O.forward(Q[:, :, b], K[:, :, b], V[:, :, b], beta, L, M1, z1)
+    assert np.max(np.abs(np.concatenate([o1, o2], 2) - o_all)) < 1e-13
+    assert np.max(np.abs(M2 - M_all)) < 1e-12 and np.max(np.abs(z2 - z_all)) < 1e-12
+
+
+def test_R10_ragged_backward_matches_central_differences():
+    B, Hq, Hkv, N, d, L = 1, 2, 1, 7, 3, 3
+    Q, K, V, beta = _problem(B, Hq, Hkv, N, d, seed=261)
+    M0, z0 = _prefix_state(B, Hkv, d)
+    dO = _rand(Q.shape, 262)
+    dMS = _rand(M0.shape, 263, 0.1)
+    dzS = _rand(z0.shape, 264, 0.1)
+    g = O.backward(Q, K, V, beta, L, dO, M0, z0, dMS, dzS)
+    params = dict(Q=Q, K=K, V=V, beta=beta, M0=M0, z0=z0)
+    names = dict(Q="dQ", K="dK", V="dV", beta="dbeta", M0="dM0", z0="dz0")
+    h = 1e-6
+    for p, gname in names.items():
+        fd = np.zeros_like(params[p])
+        it = np.nditer(params[p], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = {k: v.copy() for k, v in params.items()}
+            minus = {k: v.copy() for k, v in params.items()}
+            plus[p][idx] += h
+            minus[p][idx] -= h
+            fd[idx] = (_loss(plus, dO, dMS, dzS, L) - _loss(minus, dO, dMS, dzS, L)) / (2 * h)
+        assert max_rel_err(g[gname], fd) < 1e-6, p
