@@ -17,9 +17,7 @@ bool valid_problem(const infini_problem_t* p, infini_status_t* why) {
   if (!p) { *why = INFINI_ERR_NULL; return false; }
   if (p->batch <= 0 || p->q_heads <= 0 || p->kv_heads <= 0 || p->seq_len <= 0 ||
       p->head_dim <= 0 || p->seg_len <= 0) { *why = INFINI_ERR_SHAPE; return false; }
-  if (p->seq_len % p->seg_len != 0 || p->q_heads % p->kv_heads != 0) {
-    *why = INFINI_ERR_SHAPE; return false;
-  }
+  if (p->q_heads % p->kv_heads != 0) { *why = INFINI_ERR_SHAPE; return false; }
   if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) {
     *why = INFINI_ERR_UNSUPPORTED; return false;
   }
@@ -34,7 +32,8 @@ bool valid_problem(const infini_problem_t* p, infini_status_t* why) {
 Geometry geometry(const infini_problem_t* p) {
   Geometry g;
   g.B = p->batch; g.Hq = p->q_heads; g.Hkv = p->kv_heads; g.N = p->seq_len;
-  g.D = p->head_dim; g.L = p->seg_len; g.S = p->seq_len / p->seg_len; g.dtype = p->dtype;
+  g.D = p->head_dim; g.L = p->seg_len; g.dtype = p->dtype;
+  g.S = (p->seq_len + p->seg_len - 1) / p->seg_len;   // the last segment may be shorter
   return g;
 }
 
@@ -155,7 +154,7 @@ const char* infini_status_string(infini_status_t s) {
   switch (s) {
     case INFINI_OK: return "ok";
     case INFINI_ERR_NULL: return "a required pointer is NULL";
-    case INFINI_ERR_SHAPE: return "invalid shape (dims must be > 0, seq_len % seg_len == 0, q_heads % kv_heads == 0)";
+    case INFINI_ERR_SHAPE: return "invalid shape (dims must be > 0, q_heads % kv_heads == 0)";
     case INFINI_ERR_UNSUPPORTED: return "unsupported head_dim (32, 64, 128) or dtype";
     case INFINI_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case INFINI_ERR_WORKSPACE: return "workspace is NULL or too small";

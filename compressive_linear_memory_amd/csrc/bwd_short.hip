@@ -119,7 +119,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int bk = blockIdx.x;
   const int b = bk / Hkv, kvh = bk % Hkv;
   const int G = Hq / Hkv;
-  const int S = N / L;
+  const int S = (N + L - 1) / L;            // the last segment may be short
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lc = lane & 15, g = lane >> 4;
@@ -149,11 +149,12 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     float zp[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) zp[e] = 0.f;
+    const int Lk = min(L, N - s * L);      // keys of this segment
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int key = kg * C::KPT + i;
-      const bool in = key < L;
-      const size_t off = kvbase + ((size_t)s * L + min(key, L - 1)) * D + dc * 8;
+      const bool in = key < Lk;
+      const size_t off = kvbase + ((size_t)s * L + min(key, Lk - 1)) * D + dc * 8;
       const bbf16x8 kv = *reinterpret_cast<const bbf16x8*>(K + off);
       const bbf16x8 vv = *reinterpret_cast<const bbf16x8*>(V + off);
       *reinterpret_cast<bbf16x8*>(Ks + key * RS + dc * 8) = kv;
@@ -217,6 +218,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
   // ---- 2. segments in reverse
   for (int s = S - 1; s >= 0; --s) {
+    const int Ls = min(L, N - s * L);      // rows and keys of this segment
     stage_kv(s);
     __syncthreads();
     if (s > 0) {
@@ -290,11 +292,11 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       for (int c = tid; c < C::BL * D / 8; c += 256) {
         const int row = c / (D / 8), col = (c % (D / 8)) * 8;
         *reinterpret_cast<bbf16x8*>(Qs + row * RS + col) =
-            *reinterpret_cast<const bbf16x8*>(Q + qb + (size_t)min(row, L - 1) * D + col);
+            *reinterpret_cast<const bbf16x8*>(Q + qb + (size_t)min(row, Ls - 1) * D + col);
       }
       __syncthreads();
 
-      const bool qok = q < L;
+      const bool qok = q < Ls;
       const float gt = sigmoid(beta[h]);
       bbf16x8 qreg[C::KS];
 #pragma unroll
@@ -310,7 +312,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           pacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], pacc[kb], 0, 0, 0);
         }
       }
-      const int lim = min(q, L - 1);
+      const int lim = min(q, Ls - 1);
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -363,7 +365,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       // gate and retrieval gradients per (q, c = cb*16 + 4g + i)
       float bsum = 0.f, ddot = 0.f, dmem = 0.f;
       bbf16x8 dnp[C::KS], dap[C::KS];     // dnum, dA_dot packed like pb (c in place of keys)
-      const __bf16* dop = dO + qb + (size_t)min(q, L - 1) * D;
+      const __bf16* dop = dO + qb + (size_t)min(q, Ls - 1) * D;
 #pragma unroll
       for (int cb = 0; cb < C::DB; ++cb) {
         bf32x4 nacc = {};
@@ -511,7 +513,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     }
 
     // dK, dV of this segment's keys
-    if (jk < L) {
+    if (jk < Ls) {
       const size_t kr = kvbase + ((size_t)s * L + jk) * D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {

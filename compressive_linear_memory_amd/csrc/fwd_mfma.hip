@@ -100,11 +100,13 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int qrow = q0 + lq;                   // this lane's query row
   const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
   const size_t kvbase = (((size_t)b * Hkv + kvh) * N + (size_t)s * L) * D;
+  const int Ls = min(L, N - s * L);           // rows and keys of this segment (the last may be short)
+  if (qt * C::BM >= Ls) return;               // a query tile past the end of a short segment
 
   // ---- Q^T operand in registers for the whole key loop
   bf16x8_t qreg[C::KS];
   {
-    const bool ok = qrow < L;
+    const bool ok = qrow < Ls;
     const __bf16* qp = Q + qbase + (size_t)(ok ? qrow : 0) * D + hh * 8;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -113,7 +115,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   }
 
-  const int kend = min(L, qt * C::BM + C::BM);
+  const int kend = min(Ls, qt * C::BM + C::BM);
   const int ntiles = (kend + C::BN - 1) / C::BN;
 
   // ---- global -> register staging of K and V tiles
@@ -138,7 +140,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   auto load_tile = [&](int k0) {
     const __bf16* kt = Kseg + (size_t)k0 * D + krow0 * D + kcol;
     const __bf16* vt = Vseg + (size_t)k0 * D;
-    if (k0 + C::BN <= L) {
+    if (k0 + C::BN <= Ls) {
 #pragma unroll
       for (int i = 0; i < C::CPT; ++i) kst[i] = *reinterpret_cast<const bf16x8_t*>(kt + i * KRS * D);
 #pragma unroll
@@ -147,12 +149,12 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     } else {
 #pragma unroll
       for (int i = 0; i < C::CPT; ++i) {
-        const int key = min(k0 + krow0 + i * KRS, L - 1);
+        const int key = min(k0 + krow0 + i * KRS, Ls - 1);
         kst[i] = *reinterpret_cast<const bf16x8_t*>(Kseg + (size_t)key * D + kcol);
       }
 #pragma unroll
       for (int i = 0; i < C::KPT; ++i) {
-        const int key = min(k0 + vkg * C::KPT + i, L - 1);
+        const int key = min(k0 + vkg * C::KPT + i, Ls - 1);
         vst[i] = *reinterpret_cast<const bf16x8_t*>(Vseg + (size_t)key * D + vdc * 8);
       }
     }
@@ -229,7 +231,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     if constexpr (MASK) {
       // element (kb, r) holds key k0 + 4hh + kb*32 + 8(r/4) + r%4
-      const int lim = min(qrow, L - 1) - (k0 + 4 * hh);
+      const int lim = min(qrow, Ls - 1) - (k0 + 4 * hh);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -291,8 +293,8 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int k0 = j * C::BN;
     const __bf16* Ks = smem + (j & 1) * C::BUF;
     const __bf16* Vt = Ks + C::KTILE;
-    const bool active = k0 <= q0 + C::WM - 1 && q0 < L;
-    const bool masked = (k0 + C::BN - 1 > q0) || (k0 + C::BN > L);
+    const bool active = k0 <= q0 + C::WM - 1 && q0 < Ls;
+    const bool masked = (k0 + C::BN - 1 > q0) || (k0 + C::BN > Ls);
     if (active) {
       if (masked) tile_step(Ks, Vt, k0, std::true_type{});
       else tile_step(Ks, Vt, k0, std::false_type{});
@@ -333,7 +335,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const float gt = sigmoid(beta[h]);
   const float wm = gt / den;
   const float wd = (1.f - gt) / l;
-  if (qrow < L) {
+  if (qrow < Ls) {
     __bf16* op = O + qbase + (size_t)qrow * D;
 #pragma unroll
     for (int cb = 0; cb < C::DB; ++cb) {

@@ -65,7 +65,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int bk = blockIdx.x;                       // b * Hkv + kvh
   const int b = bk / Hkv, kvh = bk % Hkv;
   const int G = Hq / Hkv;
-  const int S = N / L;
+  const int S = (N + L - 1) / L;            // the last segment may be short
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lc = lane & 15, g = lane >> 4;
@@ -101,10 +101,12 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   // ---- staging of one segment's K and V: KPT keys x 8 columns per thread
   const int kg = tid % C::NKG, dc = tid / C::NKG;
   sbf16x8 kst[C::KPT], vst[C::KPT];
+  int Lst = L;                             // keys of the staged segment
   auto load_seg = [&](int s) {
+    Lst = min(L, N - s * L);
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
-      const int key = min(kg * C::KPT + i, L - 1);
+      const int key = min(kg * C::KPT + i, Lst - 1);
       const size_t off = kvbase + ((size_t)s * L + key) * D + dc * 8;
       kst[i] = *reinterpret_cast<const sbf16x8*>(K + off);
       vst[i] = *reinterpret_cast<const sbf16x8*>(V + off);
@@ -117,7 +119,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     float sk[C::KPT][8];
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
-      const bool in = kg * C::KPT + i < L;
+      const bool in = kg * C::KPT + i < Lst;
       *reinterpret_cast<sbf16x8*>(Ks + (kg * C::KPT + i) * C::KSTR + dc * 8) = kst[i];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -133,12 +135,12 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       if constexpr (C::KPT == 4) {
         // keys past the segment end carry zero V (they meet zero probability
         // and must not enter the memory update)
-        const bool in0 = kg * 4 + 0 < L, in1 = kg * 4 + 1 < L, in2 = kg * 4 + 2 < L, in3 = kg * 4 + 3 < L;
+        const bool in0 = kg * 4 + 0 < Lst, in1 = kg * 4 + 1 < Lst, in2 = kg * 4 + 2 < Lst, in3 = kg * 4 + 3 < Lst;
         *reinterpret_cast<sbf16x4*>(vd) = sbf16x4{in0 ? vst[0][e] : (__bf16)0.f, in1 ? vst[1][e] : (__bf16)0.f,
                                                   in2 ? vst[2][e] : (__bf16)0.f, in3 ? vst[3][e] : (__bf16)0.f};
         *reinterpret_cast<sbf16x4*>(kd) = sbf16x4{(__bf16)sk[0][e], (__bf16)sk[1][e], (__bf16)sk[2][e], (__bf16)sk[3][e]};
       } else {
-        const bool in0 = kg * 2 + 0 < L, in1 = kg * 2 + 1 < L;
+        const bool in0 = kg * 2 + 0 < Lst, in1 = kg * 2 + 1 < Lst;
         *reinterpret_cast<sbf16x2*>(vd) = sbf16x2{in0 ? vst[0][e] : (__bf16)0.f, in1 ? vst[1][e] : (__bf16)0.f};
         *reinterpret_cast<sbf16x2*>(kd) = sbf16x2{(__bf16)sk[0][e], (__bf16)sk[1][e]};
       }
@@ -156,6 +158,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int qrow = q0 + lc;                // this lane's query row
 
   for (int s = 0; s < S; ++s) {
+    const int Ls = min(L, N - s * L);      // rows and keys of this segment
     if (s + 1 < S) load_seg(s + 1);        // in flight while this segment computes
 
     for (int h = kvh * G; h < (kvh + 1) * G; ++h) {
@@ -163,7 +166,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       // Q^T operand: lane holds query qrow, k = 32ks + 8g .. +7
       sbf16x8 qreg[C::KS];
       {
-        const int qr = min(qrow, L - 1);
+        const int qr = min(qrow, Ls - 1);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
           qreg[ks] = *reinterpret_cast<const sbf16x8*>(Q + qb + (size_t)qr * D + ks * 32 + g * 8);
@@ -180,7 +183,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         }
       }
       // exact softmax over the segment's keys: element (kb, i) is key 16kb + 4g + i
-      const int lim = min(qrow, L - 1);
+      const int lim = min(qrow, Ls - 1);
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -244,14 +247,14 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           const sbf16x8 a = *reinterpret_cast<const sbf16x8*>(Mt + (cb * 16 + lc) * C::MSTR + ks * 32 + g * 8);
           nacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, sq[ks], nacc, 0, 0, 0);
         }
-        if (qrow < L) {
+        if (qrow < Ls) {
           sbf16x4 w;
 #pragma unroll
           for (int i = 0; i < 4; ++i) w[i] = (__bf16)(wm * nacc[i] + wd * oacc[cb][i]);
           *reinterpret_cast<sbf16x4*>(op + cb * 16 + 4 * g) = w;
         }
       }
-      if (lse && g == 0 && qrow < L)
+      if (lse && g == 0 && qrow < Ls)
         lse[((size_t)b * Hq + h) * N + (size_t)s * L + qrow] = (mref + __log2f(lsum)) * 0.69314718055994531f;
     }
     __syncthreads();   // every read of M_{s-1}, z_{s-1} and this segment's tiles is done

@@ -76,9 +76,10 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_q_kernel(
   const int b = blockIdx.z / nseg;
   const int s = s_begin + sl;
   const int kvh = h / (Hq / Hkv);
+  const int Ls = min(L, N - s * L);           // rows of this segment (the last may be short)
   const int i_raw = blockIdx.x * ROWS + r;
-  const bool valid = i_raw < L;
-  const int i = valid ? i_raw : L - 1;
+  const bool valid = i_raw < Ls;
+  const int i = valid ? i_raw : Ls - 1;
   const size_t qrow = (((size_t)b * Hq + h) * N + (size_t)s * L + i) * D + part * DL;
   const size_t kvbase = (((size_t)b * Hkv + kvh) * N + (size_t)s * L) * D;
   const size_t crow = ((size_t)b * Hq + h) * ((size_t)nseg * L) + (size_t)sl * L + i;  // chunk row
@@ -87,12 +88,12 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_q_kernel(
 #pragma unroll
   for (int c = 0; c < DL; ++c) { q[c] = io<T>::load(Q, qrow + c); o[c] = 0.f; }
   float m = -INFINITY, l = 0.f;
-  const int kend = min(L, (int)(blockIdx.x + 1) * ROWS);
+  const int kend = min(Ls, (int)(blockIdx.x + 1) * ROWS);
 
   // Pass 1: recompute A_dot and the row log-sum-exp.
   for (int j0 = 0; j0 < kend; j0 += GB_KT) {
     for (int e = t; e < GB_KT * D; e += GB_THREADS) {
-      const bool in = j0 + e / D < L;
+      const bool in = j0 + e / D < Ls;
       sK[e] = in ? io<T>::load(K, kvbase + (size_t)j0 * D + e) : 0.f;
       sV[e] = in ? io<T>::load(V, kvbase + (size_t)j0 * D + e) : 0.f;
     }
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_q_kernel(
   for (int c = 0; c < DL; ++c) dql[c] = 0.f;
   for (int j0 = 0; j0 < kend; j0 += GB_KT) {
     for (int e = t; e < GB_KT * D; e += GB_THREADS) {
-      const bool in = j0 + e / D < L;
+      const bool in = j0 + e / D < Ls;
       sK[e] = in ? io<T>::load(K, kvbase + (size_t)j0 * D + e) : 0.f;
       sV[e] = in ? io<T>::load(V, kvbase + (size_t)j0 * D + e) : 0.f;
     }
@@ -284,19 +285,20 @@ __global__ __launch_bounds__(256) void rscan_kernel(
     const size_t sb = ((size_t)bk * nseg + sl) * D * D + (size_t)(a0 + ta) * D + c0 + tc;
     for (int c = 0; c < 4; ++c) dMsnap[sb + c] = acc[c];
     if (z_lane) dzsnap[((size_t)bk * nseg + sl) * D + a0 + t] = zacc;
+    const int Ls = min(L, N - s * L);         // rows of this segment (the last may be short)
     for (int h = kvh * G; h < (kvh + 1) * G; ++h) {
       const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
       const size_t cbase = ((size_t)b * Hq + h) * ((size_t)nseg * L) + (size_t)sl * L;
-      for (int i0 = 0; i0 < L; i0 += RS_ROWS) {
+      for (int i0 = 0; i0 < Ls; i0 += RS_ROWS) {
         for (int e = t; e < RS_ROWS * RS_TILE; e += 256) {
           const int i = e / RS_TILE, x = e % RS_TILE;
-          const bool in = i0 + i < L;
+          const bool in = i0 + i < Ls;
           sQ[i][x] = in ? elu1(io<T>::load(Q, qbase + (size_t)(i0 + i) * D + a0 + x)) : 0.f;
           sN[i][x] = in ? dnum[(cbase + i0 + i) * D + c0 + x] : 0.f;
         }
-        for (int e = t; e < RS_ROWS; e += 256) sD[e] = (i0 + e < L) ? dden[cbase + i0 + e] : 0.f;
+        for (int e = t; e < RS_ROWS; e += 256) sD[e] = (i0 + e < Ls) ? dden[cbase + i0 + e] : 0.f;
         __syncthreads();
-        const int in_n = min(RS_ROWS, L - i0);
+        const int in_n = min(RS_ROWS, Ls - i0);
         for (int i = 0; i < in_n; ++i) {
           const float sq = sQ[i][ta];
           for (int c = 0; c < 4; ++c) acc[c] += sq * sN[i][tc + c];
@@ -353,9 +355,10 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_kv_kernel(
   const int b = blockIdx.z / nseg;
   const int s = s_begin + sl;
   const int G = Hq / Hkv;
+  const int Ls = min(L, N - s * L);           // keys of this segment (the last may be short)
   const int j_raw = blockIdx.x * ROWS + r;
-  const bool valid = j_raw < L;
-  const int j = valid ? j_raw : L - 1;
+  const bool valid = j_raw < Ls;
+  const int j = valid ? j_raw : Ls - 1;
   const size_t krow = (((size_t)b * Hkv + kvh) * N + (size_t)s * L + j) * D + part * DL;
 
   float k[DL], v[DL], dk[DL], dv[DL];
@@ -373,19 +376,19 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_kv_kernel(
     const float og = 1.f - gt;
     const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
     const size_t cbase = ((size_t)b * Hq + h) * ((size_t)nseg * L) + (size_t)sl * L;
-    for (int i0 = i_start; i0 < L; i0 += GB_QT) {
+    for (int i0 = i_start; i0 < Ls; i0 += GB_QT) {
       for (int e = t; e < GB_QT * D; e += GB_THREADS) {
-        const bool in = i0 + e / D < L;
+        const bool in = i0 + e / D < Ls;
         sQ[e] = in ? io<T>::load(Q, qbase + (size_t)i0 * D + e) : 0.f;
         sO[e] = in ? io<T>::load(dO, qbase + (size_t)i0 * D + e) : 0.f;
       }
       for (int e = t; e < GB_QT; e += GB_THREADS) {
-        const bool in = i0 + e < L;
+        const bool in = i0 + e < Ls;
         sL[e] = in ? ws_lse[cbase + i0 + e] : 0.f;
         sDd[e] = in ? ws_Dd[cbase + i0 + e] : 0.f;
       }
       __syncthreads();
-      const int qn = min(GB_QT, L - i0);
+      const int qn = min(GB_QT, Ls - i0);
       for (int ii = 0; ii < qn; ++ii) {
         const float* qr = sQ + ii * D + part * DL;
         const float* orow = sO + ii * D + part * DL;

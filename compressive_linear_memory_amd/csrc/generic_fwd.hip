@@ -63,20 +63,21 @@ __global__ __launch_bounds__(256) void sweep_kernel(
       for (int c = 0; c < 4; ++c) MsnapT[tb + (size_t)(c0 + tc + c) * D + a0 + ta] = f32_to_bf16(acc[c]);
     }
     const size_t rowbase = (bh * N + (size_t)s * L) * D;
-    for (int j0 = 0; j0 < L; j0 += SW_KEYS) {
+    const int Ls = min(L, N - s * L);              // keys of this segment (the last may be short)
+    for (int j0 = 0; j0 < Ls; j0 += SW_KEYS) {
       for (int e = t; e < SW_KEYS * SW_TILE; e += 256) {
         const int j = e / SW_TILE, x = e % SW_TILE;
         float kv = 0.f, vv = 0.f;
-        if (j0 + j < L) {
+        if (j0 + j < Ls) {
           const size_t gi = rowbase + (size_t)(j0 + j) * D;
           kv = elu1(io<T>::load(K, gi + a0 + x));
           vv = io<T>::load(V, gi + c0 + x);
         }
-        sK[j][x] = (j0 + j < L) ? kv : 0.f;
+        sK[j][x] = (j0 + j < Ls) ? kv : 0.f;
         sV[j][x] = vv;
       }
       __syncthreads();
-      const int jn = min(SW_KEYS, L - j0);
+      const int jn = min(SW_KEYS, Ls - j0);
       for (int j = 0; j < jn; ++j) {
         const float k = sK[j][ta];
         for (int c = 0; c < 4; ++c) acc[c] += k * sV[j][tc + c];
@@ -158,9 +159,10 @@ __global__ __launch_bounds__(GF_THREADS) void fwd_generic_kernel(
   const int b = blockIdx.z / nseg;
   const int s = s_begin + sl;
   const int kvh = h / (Hq / Hkv);
+  const int Ls = min(L, N - s * L);           // rows of this segment (the last may be short)
   const int i_raw = blockIdx.x * ROWS + r;
-  const bool valid = i_raw < L;
-  const int i = valid ? i_raw : L - 1;
+  const bool valid = i_raw < Ls;
+  const int i = valid ? i_raw : Ls - 1;
   const size_t qrow = (((size_t)b * Hq + h) * N + (size_t)s * L + i) * D + part * DL;
   const size_t kvbase = (((size_t)b * Hkv + kvh) * N + (size_t)s * L) * D;
 
@@ -169,11 +171,11 @@ __global__ __launch_bounds__(GF_THREADS) void fwd_generic_kernel(
   for (int c = 0; c < DL; ++c) { q[c] = io<T>::load(Q, qrow + c) * scale; o[c] = 0.f; }
   float m = -INFINITY, l = 0.f;
 
-  const int kend = min(L, (int)(blockIdx.x + 1) * ROWS);   // causal limit of this block
+  const int kend = min(Ls, (int)(blockIdx.x + 1) * ROWS);   // causal limit of this block
   for (int j0 = 0; j0 < kend; j0 += GF_KT) {
     for (int e = t; e < GF_KT * D; e += GF_THREADS) {
       const int j = e / D;
-      const bool in = j0 + j < L;
+      const bool in = j0 + j < Ls;
       sK[e] = in ? io<T>::load(K, kvbase + (size_t)j0 * D + e) : 0.f;
       sV[e] = in ? io<T>::load(V, kvbase + (size_t)j0 * D + e) : 0.f;
     }

@@ -60,7 +60,8 @@ void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ 
   const size_t bk = unit / nseg;
   const int s = s_begin + sl;
   const size_t base = (bk * N + (size_t)s * L + k_begin) * D;
-  L = max(0, min(L - k_begin, split_keys));   // keys of this split (may be none)
+  // keys of this split (may be none); the last segment may be short
+  L = max(0, min(min(L, N - s * L) - k_begin, split_keys));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;

@@ -17,7 +17,11 @@
  *   M_s   = M_{s-1} + sigma(K_r)^T V_r,   z_s = z_{s-1} + sum_rows sigma(K_r)
  *                                                       (Memory Update)
  *
- * and only (M, z) is carried to the next segment (State Transfer).  The
+ * and only (M, z) is carried to the next segment (State Transfer).  When
+ * seq_len is not a multiple of seg_len the last segment is shorter
+ * (seq_len - (S-1) seg_len tokens, S = ceil(seq_len / seg_len)) and is
+ * processed like the others; the pages fix the segment length but not what
+ * happens to a remainder, so this is the reading taken.  The
  * normalised linear-attention form of A_mem follows the page
  * "[정보] KV선형 덧셈연산 인피니 어텐션에 대한 정보" (summary of "Leave No
  * Context Behind"), which calls the memory path long-term linear attention
@@ -61,7 +65,7 @@ extern "C" {
 typedef enum {
   INFINI_OK = 0,
   INFINI_ERR_NULL = 1,        /* a required pointer is NULL                                   */
-  INFINI_ERR_SHAPE = 2,       /* a dim <= 0, seq_len % seg_len != 0 or q_heads % kv_heads != 0 */
+  INFINI_ERR_SHAPE = 2,       /* a dim <= 0 or q_heads % kv_heads != 0                      */
   INFINI_ERR_UNSUPPORTED = 3, /* head_dim not 32, 64 or 128, or unknown dtype                   */
   INFINI_ERR_ALIAS = 4,       /* an output buffer overlaps an input or another output          */
   INFINI_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns          */
@@ -75,7 +79,7 @@ typedef struct {
   int32_t batch;
   int32_t q_heads;
   int32_t kv_heads;   /* q_heads % kv_heads == 0; query head h reads K/V head h / (q_heads/kv_heads) */
-  int32_t seq_len;    /* tokens in this call; a multiple of seg_len                                 */
+  int32_t seq_len;    /* tokens in this call; the last segment may be shorter than seg_len         */
   int32_t head_dim;   /* 32, 64 or 128; keys, queries and values share it                            */
   int32_t seg_len;    /* tokens per segment                                                          */
   int32_t dtype;      /* infini_dtype_t of Q, K, V, O, dO, dQ, dK, dV                                */
@@ -139,7 +143,7 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p,
 /* The forward in its two phases, for callers that schedule them separately
  * (for example to overlap the memory phase of one layer with the attention
  * phase of another, or to time each phase).  Only for calls with at most
- * INFINI_CHUNK_SEGMENTS segments (seq_len / seg_len); longer calls return
+ * INFINI_CHUNK_SEGMENTS segments (ceil(seq_len / seg_len)); longer calls return
  * INFINI_ERR_SHAPE and must use infini_attn_fwd.
  *
  * infini_fwd_memory runs the memory path alone (same page and section,

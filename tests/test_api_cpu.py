@@ -66,7 +66,7 @@ def test_workspace_sizes(L):
     assert L.infini_fwd_workspace_bytes(ctypes.byref(P())) > 0
     assert L.infini_bwd_workspace_bytes(ctypes.byref(P())) > 0
     assert L.infini_fwd_workspace_bytes(None) == 0
-    assert L.infini_fwd_workspace_bytes(ctypes.byref(P(N=60))) == 0   # 60 % 16 != 0
+    assert L.infini_fwd_workspace_bytes(ctypes.byref(P(Hq=3, Hkv=2))) == 0
     assert L.infini_fwd_workspace_bytes(ctypes.byref(P(d=48))) == 0
 
 
@@ -93,7 +93,7 @@ def test_fwd_half_state_is_null_error(L):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(N=60), 2), (dict(Hq=3, Hkv=2), 2), (dict(B=0), 2), (dict(L=0), 2), (dict(N=-16), 2),
+    (dict(Hkv=0), 2), (dict(Hq=3, Hkv=2), 2), (dict(B=0), 2), (dict(L=0), 2), (dict(N=-16), 2),
     (dict(d=48), 3), (dict(d=256), 3), (dict(dtype=7), 3),
 ])
 def test_fwd_shape_errors(L, kw, code):
@@ -129,3 +129,13 @@ def test_bwd_validation(L):
     assert call(b) == 4                               # dQ aliases dO
     need = L.infini_bwd_workspace_bytes(ctypes.byref(p))
     assert call(a, need - 1) == 5
+
+
+def test_ragged_final_segment_is_a_valid_shape(L):
+    """A sequence that is not a multiple of seg_len ends in one shorter segment:
+    accepted, and sized like the call with that segment full."""
+    for N in (60, 49, 17, 1, 255):
+        full = -(-N // 16) * 16
+        for bwd in (False, True):
+            f = L.infini_bwd_workspace_bytes if bwd else L.infini_fwd_workspace_bytes
+            assert f(ctypes.byref(P(N=N))) == f(ctypes.byref(P(N=full))) > 0

@@ -127,6 +127,15 @@ FWD_CASES = [
     (1, 8, 2, 1024, 128, 512, "bf16", True),
     (1, 4, 2, 1540, 128, 770, "bf16", True),   # 2-row last query tile
     (1, 2, 1, 1000, 64, 1000, "bf16", False),
+    # sequence not a multiple of seg_len: the last segment is shorter
+    (1, 2, 2, 70, 32, 16, "fp32", True),       # generic path, 6-token tail
+    (1, 3, 3, 101, 64, 48, "fp32", False),
+    (1, 4, 2, 1000, 128, 384, "bf16", True),   # long path, 232-token tail
+    (1, 2, 2, 300, 64, 128, "bf16", False),    # long path, 44-token tail
+    (1, 2, 1, 2049, 128, 1024, "bf16", True),  # long path, 1-token tail
+    (2, 4, 2, 100, 64, 64, "bf16", True),      # fused short path, 36-token tail
+    (1, 4, 4, 70, 128, 16, "bf16", True),      # fused short path, 6-token tail
+    (1, 2, 2, 9, 64, 8, "bf16", False),        # fused short path, 1-token tail
 ]
 
 
@@ -149,6 +158,12 @@ BWD_CASES = [
     (2, 8, 2, 96, 128, 48, "bf16", True),      # ragged segment tile, 4 heads per K/V head
     (1, 2, 1, 40, 128, 8, "bf16", False),
     (1, 2, 2, 5, 64, 1, "bf16", True),
+    # sequence not a multiple of seg_len
+    (1, 2, 2, 70, 32, 16, "fp32", True),       # generic backward, 6-token tail
+    (1, 3, 3, 150, 64, 65, "bf16", True),      # generic backward (bf16, seg_len > 64), 20-token tail
+    (2, 4, 2, 100, 64, 64, "bf16", True),      # fused short backward, 36-token tail
+    (1, 4, 4, 70, 128, 16, "bf16", True),      # fused short backward, 6-token tail
+    (1, 2, 1, 41, 128, 8, "bf16", False),      # fused short backward, 1-token tail
 ]
 
 
@@ -292,8 +307,9 @@ def test_run_twice_bitwise_identical():
 def test_errors_raise_with_real_tensors():
     Q, K, V, beta, _, _ = make(1, 2, 2, 64, 32, "fp32", seed=31)
     q = dev(Q)
+    Q3, K3, V3, beta3, _, _ = make(1, 3, 2, 64, 32, "fp32", seed=32)
     with pytest.raises(B().InfiniError) as e:
-        B().attn_fwd(q, dev(K), dev(V), dev(beta), 48)          # 64 % 48 != 0
+        B().attn_fwd(dev(Q3), dev(K3), dev(V3), dev(beta3), 16)   # 3 query heads over 2 K/V heads
     assert e.value.code == 2
     o = torch.empty_like(q)
     Ms = torch.empty((1, 2, 32, 32), device="cuda")
