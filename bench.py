@@ -17,6 +17,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -128,9 +129,10 @@ def main():
                     help="untimed steps; the first few launches run slower while the GPU clocks ramp up")
     ap.add_argument("--workload", default="fwd_llama3_8b", choices=sorted(I.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="fwd", choices=["fwd", "train", "stream", "copy"],
+    ap.add_argument("--mode", default="fwd", choices=["fwd", "train", "stream", "decode", "copy"],
                     help="fwd: forward throughput (default, the headline line); train: forward + "
                          "backward step; stream: chained single-segment launches carrying the state; "
+                         "decode: token-by-token streaming decode through one segment; "
                          "copy: a plain device copy of known size (calibrates HBM byte counters)")
     ap.add_argument("--launches", type=int, default=512, help="stream mode: chained launches per step")
     ap.add_argument("--graph", action="store_true",
@@ -146,6 +148,8 @@ def main():
         return bench_stream(args)
     if args.mode == "copy":
         return bench_copy(args)
+    if args.mode == "decode":
+        return bench_decode(args)
 
     import torch
     from compressive_linear_memory_amd import binding as Bi
@@ -383,6 +387,87 @@ def bench_stream(args):
                       "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": "stream_1m", "mode": "stream", "launches": nl,
                                  "graph": bool(args.graph), "kernel_path": Bi.fwd_path(p)}, "roofline": roof}), flush=True)
+
+
+def bench_decode(args):
+    """Token-by-token decode through one whole segment of the streaming
+    workload's shape (B=1, 32 heads, d=64, seg_len 2048), starting from a
+    carried state; the last token completes the segment and folds it into the
+    memory.  One step = the 2048 single-token calls, recorded once in a HIP
+    graph and replayed (the eager per-token time is reported beside it)."""
+    import torch
+    from compressive_linear_memory_amd import binding as Bi
+    Bi.lib()
+    w = I.WORKLOADS["stream_1m"]
+    dev = torch.device("cuda:0")
+    say("[bench] generating decode inputs (one 2048-token segment of stream_1m)")
+    Q, K, V = I.qkv(w, launch=1)
+    Kp, Vp = I.qkv(w, launch=0)[1:]
+    t = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    q, k, v = t(Q), t(K), t(V)
+    b = torch.from_numpy(I.beta(w)).to(dev)
+    B_, H, L, d = w.batch, w.kv_heads, w.seg_len, w.head_dim
+    # the state after the previous segment, from the library itself
+    M = torch.empty((B_, H, d, d), device=dev)
+    z = torch.empty((B_, H, d), device=dev)
+    Bi.attn_fwd(t(Kp), t(Kp), t(Vp), b, L, out=(torch.empty_like(q), M, z, None))
+    kc = torch.zeros((B_, H, L, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    O_ = torch.empty((L, B_, w.q_heads, 1, d), dtype=torch.bfloat16, device=dev)   # one contiguous row block per token
+    Mn = torch.empty_like(M)
+    zn = torch.empty_like(z)
+    p1 = Bi.problem(q[:, :, :1], k[:, :, :1], L)
+    ws = torch.empty(max(Bi.lib().infini_decode_workspace_bytes(ctypes.byref(p1)), 1), dtype=torch.uint8,
+                     device=dev)
+    rows = [(q[:, :, i:i + 1].contiguous(), k[:, :, i:i + 1].contiguous(), v[:, :, i:i + 1].contiguous(),
+             O_[i]) for i in range(L)]
+
+    def run():
+        for i in range(L):
+            qi, ki, vi, oi = rows[i]
+            Bi.decode(qi, ki, vi, b, L, i, kc, vc, M, z, out=oi, state_out=(Mn, zn), ws=ws)
+
+    for _ in range(max(1, args.warmup // 5)):
+        run()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0, e1 = _events(2)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_eager = timed(run)
+    # The same 2048 calls recorded once in a HIP graph: the GPU time of the
+    # decode loop without the host's per-call cost.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ms = timed(graph.replay)
+    say(f"[bench] decode: {1e3 * ms_eager / L:.2f} us/token eager, {1e3 * ms / L:.2f} us/token graph-replayed")
+    # Algorithmic bytes of one segment decoded token by token: for token i the
+    # cached rows 0..i of K and V, its own Q/K/V/O rows and the state read once;
+    # the closing update reads the cache once and writes the state.
+    eb = 2
+    kv_rows = B_ * H * L * (L + 1) // 2
+    step_bytes = (eb * 2 * d * kv_rows + L * (eb * d * (2 * w.q_heads + 2 * H) + B_ * H * (d * d + d) * 4)
+                  + eb * 2 * B_ * H * L * d + 2 * B_ * H * (d * d + d) * 4)
+    ach = step_bytes / (ms / 1e3) / 1e9
+    roof = dict(bound="hbm", peak=PEAK_HBM_GBS, unit="GB/s", achieved=round(ach, 1), frac=round(ach / PEAK_HBM_GBS, 5),
+                traffic=None, kernel="infini_decode, one token per call", bytes_per_step=step_bytes)
+    print(json.dumps({"metric": "Infini-attention streaming decode tokens/s (stream_1m shape, one token per call)",
+                      "value": round(L / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": round(ms, 4), "us_per_token": round(1e3 * ms / L, 2),
+                      "us_per_token_eager": round(1e3 * ms_eager / L, 2), "graph": True,
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                      "data": "synthetic", "config": {"workload": "stream_1m", "mode": "decode", "tokens": L},
+                      "roofline": roof}), flush=True)
 
 
 def bench_copy(args):

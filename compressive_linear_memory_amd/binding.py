@@ -48,7 +48,7 @@ def lib() -> ctypes.CDLL:
         L.infini_status_string.argtypes = [ctypes.c_int]
         L.infini_version.restype = ctypes.c_int
         L.infini_version.argtypes = []
-        for fn in ("infini_fwd_workspace_bytes", "infini_bwd_workspace_bytes"):
+        for fn in ("infini_fwd_workspace_bytes", "infini_bwd_workspace_bytes", "infini_decode_workspace_bytes"):
             getattr(L, fn).restype = ctypes.c_size_t
             getattr(L, fn).argtypes = [ctypes.POINTER(Problem)]
         L.infini_attn_fwd.restype = ctypes.c_int
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.infini_fwd_memory.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_size_t, _P]
         L.infini_fwd_attend.restype = ctypes.c_int
         L.infini_fwd_attend.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_size_t, _P]
+        L.infini_decode.restype = ctypes.c_int
+        L.infini_decode.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32] + [_P] * 12 + [ctypes.c_size_t, _P]
         _lib = L
     return _lib
 
@@ -171,6 +173,44 @@ def fwd_attend(p: Problem, q, k, v, beta, O, lse, ws):
                                  _ptr(ws), ws.numel(), _stream())
     if rc != 0:
         raise InfiniError(rc, "infini_fwd_attend")
+
+
+def decode(q, k, v, beta, seg_len, pos, kcache, vcache, M=None, z=None, out=None, state_out=None, ws=None):
+    """Streaming decode (see include/infini.h, infini_decode): T = q.shape[2]
+    new tokens at positions pos.. of the current segment.  Writes the new K/V
+    rows into kcache/vcache ([B, Hkv, seg_len, d]) and returns O [B, Hq, T, d];
+    when pos + T == seg_len it also returns the state after the segment,
+    (O, M_next, z_next)."""
+    p = problem(q, k, seg_len)
+    p.seq_len = q.shape[2]
+    dev = q.device
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    for name, t, dt, shp in (("k", k, q.dtype, (B, Hkv, T, d)), ("v", v, q.dtype, (B, Hkv, T, d)),
+                             ("beta", beta, torch.float32, (Hq,)),
+                             ("kcache", kcache, q.dtype, (B, Hkv, seg_len, d)),
+                             ("vcache", vcache, q.dtype, (B, Hkv, seg_len, d)),
+                             ("M", M, torch.float32, (B, Hkv, d, d)), ("z", z, torch.float32, (B, Hkv, d))):
+        _check(name, t, dt, shp, dev)
+    _check("q", q, q.dtype, q.shape, dev)
+    closes = pos + T == seg_len
+    O = torch.empty_like(q) if out is None else out
+    M_next = z_next = None
+    if closes:
+        if state_out is None:
+            M_next = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=dev)
+            z_next = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
+        else:
+            M_next, z_next = state_out
+    if ws is None:
+        ws = torch.empty(max(lib().infini_decode_workspace_bytes(ctypes.byref(p)), 1), dtype=torch.uint8,
+                         device=dev)
+    rc = lib().infini_decode(ctypes.byref(p), int(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(kcache),
+                             _ptr(vcache), _ptr(M), _ptr(z), _ptr(O), _ptr(M_next), _ptr(z_next), _ptr(ws),
+                             ws.numel(), _stream())
+    if rc != 0:
+        raise InfiniError(rc, "infini_decode")
+    return (O, M_next, z_next) if closes else O
 
 
 def fwd_path(p: Problem) -> str:

@@ -331,4 +331,66 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
   return INFINI_OK;
 }
 
+// ---- streaming decode
+
+// The geometry of one full segment of the decode problem (the shape of the
+// caches and of the memory update that closes the segment).
+static bool decode_problem(const infini_problem_t* p, int32_t pos, Geometry* seg, infini_status_t* why) {
+  if (!valid_problem(p, why)) return false;
+  if (pos < 0 || (int64_t)pos + p->seq_len > p->seg_len) { *why = INFINI_ERR_SHAPE; return false; }
+  infini_problem_t q = *p;
+  q.seq_len = p->seg_len;
+  *seg = geometry(&q);
+  return true;
+}
+
+// The memory update that closes a segment and the key-split partials of the
+// rows are never live together (same stream, one after the other), so they
+// share the workspace.
+static size_t decode_ws_bytes(const Geometry& seg, int Tn) {
+  const size_t a = fwd_layout(seg).total, b = align_up(infini::decode_partial_bytes(seg, Tn));
+  return a > b ? a : b;
+}
+
+size_t infini_decode_workspace_bytes(const infini_problem_t* p) {
+  infini_status_t why;
+  Geometry seg;
+  if (!decode_problem(p, 0, &seg, &why)) return 0;
+  return decode_ws_bytes(seg, p->seq_len);
+}
+
+infini_status_t infini_decode(const infini_problem_t* p, int32_t pos, const void* Q, const void* K,
+                              const void* V, const float* beta, void* Kcache, void* Vcache,
+                              const float* M, const float* z, void* O, float* M_next, float* z_next,
+                              void* ws, size_t ws_bytes, void* stream) {
+  infini_status_t why;
+  Geometry seg;
+  if (!decode_problem(p, pos, &seg, &why)) return why;
+  if (!Q || !K || !V || !beta || !Kcache || !Vcache || !O) return INFINI_ERR_NULL;
+  if ((M == nullptr) != (z == nullptr)) return INFINI_ERR_NULL;
+  const bool closes = pos + p->seq_len == p->seg_len;
+  if (closes && (!M_next || !z_next)) return INFINI_ERR_NULL;
+  const FwdWs lay = fwd_layout(seg);
+  const size_t need = decode_ws_bytes(seg, p->seq_len);
+  if (!ws || ws_bytes < need) return INFINI_ERR_WORKSPACE;
+  const size_t eb = elem_bytes(seg);
+  const size_t Tn = (size_t)p->seq_len;
+  const size_t nq = (size_t)seg.B * seg.Hq * Tn * seg.D, nkv = (size_t)seg.B * seg.Hkv * Tn * seg.D;
+  const size_t nc = (size_t)seg.B * seg.Hkv * seg.L * seg.D;
+  const size_t nM = (size_t)seg.B * seg.Hkv * seg.D * seg.D * 4, nz = (size_t)seg.B * seg.Hkv * seg.D * 4;
+  const Span outs[] = {{O, nq * eb}, {Kcache, nc * eb}, {Vcache, nc * eb},
+                       {M_next, closes ? nM : 0}, {z_next, closes ? nz : 0}, {ws, need}};
+  const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)seg.Hq * 4},
+                      {M, M ? nM : 0}, {z, z ? nz : 0}};
+  if (any_overlap(outs, 6, ins, 6)) return INFINI_ERR_ALIAS;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY(infini::launch_decode(seg, (int)Tn, pos, Q, K, V, beta, Kcache, Vcache, M, z, O,
+                            static_cast<float*>(ws), st));
+  if (closes)   // the segment is complete: fold it into the memory
+    TRY(run_fwd_chunk(seg, lay, static_cast<char*>(ws), nullptr, Kcache, Vcache, nullptr, M, z, nullptr,
+                      M_next, z_next, nullptr, 0, 1, st, true, false));
+  return INFINI_OK;
+}
+
 }  // extern "C"

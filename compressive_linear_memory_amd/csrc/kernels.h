@@ -96,4 +96,13 @@ hipError_t launch_dbeta_reduce(const Geometry& g, const float* beta, const BwdCh
                                float* dbeta_acc, float* dbeta, int nseg, bool first, bool last,
                                hipStream_t st);
 
+// Streaming decode: Tn new rows at positions pos.. of the current segment;
+// appends them to the caches Kc/Vc ([B*Hkv][L][D]) and writes O ([B][Hq][Tn][D]).
+// `part` holds decode_partial_bytes(g, Tn) bytes for the key-split partials.
+constexpr int kDecodeMaxSplits = 16;
+size_t decode_partial_bytes(const Geometry& g, int Tn);
+hipError_t launch_decode(const Geometry& g, int Tn, int pos, const void* Q, const void* K, const void* V,
+                         const float* beta, void* Kc, void* Vc, const float* M, const float* z, void* O,
+                         float* part, hipStream_t st);
+
 }  // namespace infini

@@ -161,6 +161,46 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
                                   const void* V, const float* beta, void* O, float* lse,
                                   const void* ws, size_t ws_bytes, void* stream);
 
+/* Streaming decode: a few new tokens of the segment that is being filled.
+ *
+ * The same computation as infini_attn_fwd, evaluated for the tokens a
+ * generation loop produces one (or a few) at a time (page "Hugging Face
+ * Infini-Attention 재현 분석", section "Infini-Attention 메커니즘": Local
+ * Attention, Memory Retrieval, Integration, and Memory Update once the
+ * segment is complete).  Feeding a sequence through infini_decode in pieces
+ * gives the outputs and the state of one infini_attn_fwd call over it.
+ *
+ *   p->seq_len   T, the new tokens of this call (>= 1)
+ *   p->seg_len   L; other fields as for infini_attn_fwd
+ *   pos          tokens of the current segment already in the caches,
+ *                0 <= pos and pos + T <= L
+ *   Q            [B][Hq][T][d] new query rows
+ *   K, V         [B][Hkv][T][d] new key and value rows
+ *   Kcache, Vcache  [B][Hkv][L][d], caller-owned, in/out: rows [0, pos) hold
+ *                the segment's earlier tokens; this call writes rows
+ *                [pos, pos + T).  Rows past pos + T are not read.
+ *   M, z         state before the current segment ([B][Hkv][d][d],
+ *                [B][Hkv][d] fp32; both NULL = empty memory)
+ *   O            [B][Hq][T][d] output rows (row t is token pos + t)
+ *   M_next, z_next  written only when pos + T == L (the call completes the
+ *                segment): the state after it, M + sigma(Kcache)^T Vcache
+ *                and z + sum_rows sigma(Kcache); may be NULL otherwise
+ *   ws, ws_bytes    infini_decode_workspace_bytes(p) bytes of scratch, on
+ *                every call (key-split partials of the rows, and the memory
+ *                update when the call completes the segment); it depends on
+ *                T and the shape, not on pos
+ *
+ * Errors: INFINI_ERR_SHAPE for pos < 0 or pos + T > L (and the shape checks
+ * of infini_attn_fwd); INFINI_ERR_NULL for a missing pointer, a half-given
+ * state, or a missing M_next/z_next on the completing call;
+ * INFINI_ERR_WORKSPACE; INFINI_ERR_ALIAS when O, the caches, M_next, z_next
+ * or ws overlap an input or each other.  Calls are asynchronous on stream. */
+size_t infini_decode_workspace_bytes(const infini_problem_t* p);
+infini_status_t infini_decode(const infini_problem_t* p, int32_t pos, const void* Q, const void* K,
+                              const void* V, const float* beta, void* Kcache, void* Vcache,
+                              const float* M, const float* z, void* O, float* M_next, float* z_next,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* Name of the kernel family infini_attn_fwd runs for this problem
  * ("generic_fp32": fp32 vector-ALU path; "mfma_bf16": bf16 matrix-core
  * path, memory phase then attention phase; "mfma_bf16_short": bf16

@@ -139,3 +139,29 @@ def test_ragged_final_segment_is_a_valid_shape(L):
         for bwd in (False, True):
             f = L.infini_bwd_workspace_bytes if bwd else L.infini_fwd_workspace_bytes
             assert f(ctypes.byref(P(N=N))) == f(ctypes.byref(P(N=full))) > 0
+
+
+def test_decode_validation(L):
+    """Streaming decode: shape, pointer and workspace checks (no launch)."""
+    P1 = P(N=3)                         # three new tokens, seg_len 16
+    # Q K V beta Kcache Vcache M z O M_next z_next
+    a = [FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], FAKE[5], None, None, FAKE[6], FAKE[7], FAKE[8]]
+
+    def dec(p, pos, args, ws=FAKE[10], ws_bytes=1 << 30):
+        return L.infini_decode(ctypes.byref(p), pos, *args, ws, ws_bytes, None)
+
+    assert dec(P1, 14, a) == 2                               # 14 + 3 > 16
+    assert dec(P1, -1, a) == 2
+    b = list(a); b[0] = None
+    assert dec(P1, 0, b) == 1                                # Q missing
+    b = list(a); b[6] = FAKE[9]
+    assert dec(P1, 0, b) == 1                                # M without z
+    b = list(a); b[9] = None
+    assert dec(P1, 13, b) == 1                               # completing call without M_next
+    need = L.infini_decode_workspace_bytes(ctypes.byref(P1))
+    assert need >= L.infini_fwd_workspace_bytes(ctypes.byref(P(N=16))) > 0
+    assert dec(P1, 13, a, ws_bytes=need - 1) == 5
+    assert dec(P1, 0, a, ws_bytes=need - 1) == 5            # key-split partials need it on every call
+    assert dec(P1, 0, a, ws=None) == 5
+    b = list(a); b[8] = FAKE[0]
+    assert dec(P1, 0, b) == 4                                # O overlaps Q

@@ -394,3 +394,76 @@ def test_stream_1m_launch_shape_chained():
         eM, ez = rel(host(Ms), rM), rel(host(zs), rz)
         log(f"   launch {t}: err O {eo:.2e} M {eM:.2e} z {ez:.2e}")
         assert eo < 2e-2 and eM < 2e-2 and ez < 2e-2
+
+
+# ------------------------------------------------------------------ streaming decode
+
+DECODE_CASES = [
+    # B, Hq, Hkv, N, d, L, dtype, state, pieces (tokens per call, cycled)
+    (1, 4, 2, 40, 32, 16, "fp32", True, (1, 3, 1, 5)),
+    (2, 2, 2, 150, 64, 64, "bf16", False, (1, 7, 2)),
+    (1, 8, 2, 300, 128, 128, "bf16", True, (5, 1, 16)),
+    (1, 2, 2, 2100, 64, 2048, "bf16", True, (1, 64, 1, 300)),   # rows past one 1024-key chunk
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "-".join(map(str, c[:8])))
+def test_decode_in_pieces_equals_one_forward(case):
+    """Feeding a sequence through infini_decode a few tokens at a time gives
+    the oracle's forward over the whole sequence: every output row, and the
+    state after every completed segment."""
+    Bn, Hq, Hkv, N, d, L, dtype, st, pieces = case
+    Q, K, V, beta, M0, z0 = make(Bn, Hq, Hkv, N, d, dtype, seed=N + 7 * d, with_state=st)
+    ro, rM, rz = O.forward(Q, K, V, beta, L, M0, z0)
+    log(f"decode Q{Q.shape} L={L} {dtype} pieces={pieces}")
+    Bi = B()
+    td = torch.float32 if dtype == "fp32" else torch.bfloat16
+    kc = torch.zeros((Bn, Hkv, L, d), dtype=td, device="cuda")
+    vc = torch.zeros_like(kc)
+    M, z = dev(M0), dev(z0)
+    b = dev(beta)
+    outs = []
+    n, k, closed = 0, 0, 0
+    while n < N:
+        pos = n % L
+        T = min(pieces[k % len(pieces)], L - pos, N - n)
+        r = slice(n, n + T)
+        res = Bi.decode(dev(Q[:, :, r], dtype), dev(K[:, :, r], dtype), dev(V[:, :, r], dtype), b, L, pos,
+                        kc, vc, M, z)
+        if pos + T == L:
+            o, M, z = res
+            closed += 1
+        else:
+            o = res
+        outs.append(o)
+        n += T
+        k += 1
+    torch.cuda.synchronize()
+    got = torch.cat(outs, dim=2)
+    eo = rel(host(got), ro)
+    log(f"   {k} calls, {closed} completed segments: err O {eo:.2e}")
+    assert eo < TOL[dtype]
+    if N % L == 0:      # the state after the last completed segment is the forward's final state
+        assert rel(host(M), rM) < TOL[dtype] and rel(host(z), rz) < TOL[dtype]
+    else:
+        _, _, sM, sz = O.state_sweep(K[:, :, : (N // L) * L], V[:, :, : (N // L) * L], L, M0, z0)
+        if closed:
+            assert rel(host(M), sM) < TOL[dtype] and rel(host(z), sz) < TOL[dtype]
+
+
+def test_decode_argument_errors():
+    """Rejected before any launch: a piece past the segment end, a negative
+    position, an output overlapping the cache."""
+    Bi = B()
+    q = torch.zeros((1, 2, 3, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 2, 3, 64), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((1, 2, 16, 64), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    b = torch.zeros(2, device="cuda")
+    for pos in (14, -1):
+        with pytest.raises(Bi.InfiniError) as e:
+            Bi.decode(q, k, k, b, 16, pos, kc, vc)
+        assert e.value.code == 2
+    with pytest.raises(Bi.InfiniError) as e:
+        Bi.decode(q, k, k, b, 16, 0, kc, vc, out=kc[:, :, :3])
+    assert e.value.code == 4
