@@ -67,7 +67,9 @@ void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ 
   const int lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 31, hh = lane >> 5;
   const int wa = wave >> 1, wc = wave & 1;
-  const int dc = tid % (D / 8), kg = tid / (D / 8);
+  // Staging: consecutive lanes take consecutive key groups, so the transposed
+  // LDS stores of a 16-lane group fall in one row, in distinct banks.
+  const int kg = tid % C::NKG, dc = tid / C::NKG;
 
   float zp[8];
 #pragma unroll
