@@ -179,6 +179,25 @@ def test_backward_shapes(case):
     _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype)
 
 
+
+@pytest.mark.parametrize("case", [
+    (1, 2, 2, 64, 32, 16, "fp32"),           # generic path
+    (1, 4, 2, 600, 64, 256, "bf16"),         # long path, ragged tail
+    (1, 16, 2, 512, 64, 256, "bf16"),        # long path, 8 query heads per K/V head
+    (2, 4, 2, 100, 128, 64, "bf16"),         # fused short path, ragged tail
+], ids=lambda c: "-".join(map(str, c)))
+def test_forward_row_logsumexp(case):
+    """The optional per-row log-sum-exp output (natural log of the causal
+    softmax normaliser of the scaled scores) against the oracle's."""
+    Bn, Hq, Hkv, N, d, L, dtype = case
+    Q, K, V, beta, M0, z0 = make(Bn, Hq, Hkv, N, d, dtype, seed=5 * N + d, with_state=True)
+    o, M, z, lse = run_fwd(Q, K, V, beta, L, M0, z0, dtype, want_lse=True)
+    torch.cuda.synchronize()
+    ro, rM, rz, rl = O.forward(Q, K, V, beta, L, M0, z0, want_lse=True)
+    el = rel(host(lse), rl)
+    log(f"   lse {case}: err {el:.2e} O {rel(host(o), ro):.2e}")
+    assert el < TOL[dtype] and rel(host(o), ro) < TOL[dtype]
+
 # ------------------------------------------------------------------ gate limits
 
 def test_kernel_path_selection():
