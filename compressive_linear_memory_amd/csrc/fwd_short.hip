@@ -16,6 +16,15 @@
 // Nothing but (M, z) crosses segments and nothing but the final state leaves
 // the chip.
 //
+// When few (batch, K/V head) pairs are in flight the segments of a pair are
+// dealt to `parts` workgroups in consecutive ranges; part p first replays the
+// memory update alone (no attention) over the segments before its range to
+// reach its starting state, then processes its range fully.  A replayed
+// segment costs about kReplayCost of a full one (measured at the 200M-model
+// shape), so later parts get shorter ranges: part p starts at
+// b_p = c (1 - (1 - r)^p) / r with c chosen so that b_parts = S, which gives
+// every part the same cost.  Only the last part writes the final state.
+//
 // 16x16x32 bf16 operand layout (gfx950): A lane l holds row l%16, k = 8(l/16)..+7;
 // B lane l holds column l%16, same k; C/D lane l holds column l%16,
 // rows 4(l/16) + i, i = 0..3.
@@ -30,6 +39,8 @@ typedef __bf16 sbf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 sbf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 sbf16x2 __attribute__((ext_vector_type(2)));
 typedef float sf32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kReplayCost = 0.45f;      // replayed segment / fully processed segment
 
 template <int D>
 struct ShortCfg {
@@ -53,7 +64,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       const __bf16* __restrict__ V, const float* __restrict__ beta,
                       const float* __restrict__ M0, const float* __restrict__ z0,
                       __bf16* __restrict__ O, float* __restrict__ M_S, float* __restrict__ z_S,
-                      float* __restrict__ lse, int Hq, int Hkv, int N, int L, float sl2) {
+                      float* __restrict__ lse, int Hq, int Hkv, int N, int L, int parts, float sl2) {
   using C = ShortCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[C::KTILE];
   __shared__ __attribute__((aligned(16))) __bf16 Vt[C::TTILE];
@@ -62,10 +73,18 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   __shared__ float zs[D];
   __shared__ float zred[C::NKG][D + 1];
 
-  const int bk = blockIdx.x;                       // b * Hkv + kvh
+  const int bk = blockIdx.x / parts;               // b * Hkv + kvh
+  const int part = blockIdx.x % parts;
   const int b = bk / Hkv, kvh = bk % Hkv;
   const int G = Hq / Hkv;
   const int S = (N + L - 1) / L;            // the last segment may be short
+  auto bound = [&](int p) {                // first segment of part p
+    if (p >= parts) return S;
+    const float q = 1.f - kReplayCost;
+    return (int)rintf((float)S * (1.f - __powf(q, (float)p)) / (1.f - __powf(q, (float)parts)));
+  };
+  const int s_att = bound(part);            // this part attends segments [s_att, s_end)
+  const int s_end = bound(part + 1);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lc = lane & 15, g = lane >> 4;
@@ -157,11 +176,11 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int q0 = wave * 16;                // this wave's query rows inside the segment
   const int qrow = q0 + lc;                // this lane's query row
 
-  for (int s = 0; s < S; ++s) {
+  for (int s = 0; s < s_end; ++s) {
     const int Ls = min(L, N - s * L);      // rows and keys of this segment
-    if (s + 1 < S) load_seg(s + 1);        // in flight while this segment computes
+    if (s + 1 < s_end) load_seg(s + 1);    // in flight while this segment computes
 
-    for (int h = kvh * G; h < (kvh + 1) * G; ++h) {
+    for (int h = kvh * G; s >= s_att && h < (kvh + 1) * G; ++h) {
       const size_t qb = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
       // Q^T operand: lane holds query qrow, k = 32ks + 8g .. +7
       sbf16x8 qreg[C::KS];
@@ -279,10 +298,11 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       zs[tid] += t;
     }
     __syncthreads();   // tiles and the z partials are consumed
-    if (s + 1 < S) store_seg();
+    if (s + 1 < s_end) store_seg();
     publish_mt();
     __syncthreads();
   }
+  if (part != parts - 1) return;           // the last part holds the final state
 
   // final state
 #pragma unroll
@@ -307,9 +327,15 @@ hipError_t launch_fwd_short(const Geometry& g, const void* Q, const void* K, con
                             float* M_S, float* z_S, float* lse, hipStream_t st) {
   if (!fwd_short_supported(g)) return hipErrorInvalidValue;
   const float sl2 = 1.4426950408889634f / sqrtf((float)g.D);
-  dim3 grid(g.B * g.Hkv);
+  // Split each pair's segments over up to 4 workgroups (at least 2 segments
+  // each on average) when the pairs alone would leave most of the 256
+  // compute units idle.
+  const int units = g.B * g.Hkv;
+  int parts = 1;
+  while (parts < 4 && parts * 4 <= g.S && units * parts * 2 <= 256) parts *= 2;
+  dim3 grid(units * parts);
 #define FS_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), \
-                beta, M0, z0, static_cast<__bf16*>(O), M_S, z_S, lse, g.Hq, g.Hkv, g.N, g.L, sl2
+                beta, M0, z0, static_cast<__bf16*>(O), M_S, z_S, lse, g.Hq, g.Hkv, g.N, g.L, parts, sl2
   if (g.D == 128) hipLaunchKernelGGL(fwd_short_kernel<128>, grid, dim3(256), 0, st, FS_ARGS);
   else hipLaunchKernelGGL(fwd_short_kernel<64>, grid, dim3(256), 0, st, FS_ARGS);
 #undef FS_ARGS
