@@ -30,19 +30,23 @@ namespace infini {
 
 constexpr int DC_THREADS = 256;
 constexpr int DC_CHUNK = 1024;                 // keys scored per pass (4 per thread)
+constexpr int PB = 4;                          // V rows per thread in flight in the P V pass
 
-template <typename T> struct vec16;            // one 16-byte load as floats
+template <typename T> struct vec16;            // one 16-byte load, then as floats
 template <> struct vec16<float> {
   static constexpr int N = 4;
-  __device__ __forceinline__ static void load(const float* p, float (&x)[4]) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
+  using R = float4;
+  __device__ __forceinline__ static R raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ static void cvt(const R& v, float (&x)[4]) {
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
   }
+  __device__ __forceinline__ static void load(const float* p, float (&x)[4]) { cvt(raw(p), x); }
 };
 template <> struct vec16<bf16_t> {
   static constexpr int N = 8;
-  __device__ __forceinline__ static void load(const bf16_t* p, float (&x)[8]) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+  using R = uint4;
+  __device__ __forceinline__ static R raw(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static void cvt(const R& v, float (&x)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -50,6 +54,7 @@ template <> struct vec16<bf16_t> {
       x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  __device__ __forceinline__ static void load(const bf16_t* p, float (&x)[8]) { cvt(raw(p), x); }
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -101,8 +106,18 @@ __global__ __launch_bounds__(DC_THREADS) void decode_kernel(
     for (int t = 0; t < Tn; ++t) {
       const int i = pos + t;                   // row inside the segment
       const size_t qrow = (((size_t)b * Hq + h) * Tn + t) * D;
+      // every thread holds the query row itself, so the key loads below do
+      // not wait for a barrier; sq (read by the retrieval, after the chunk
+      // loop's barriers) is written beside it
+      float qv[D];
+#pragma unroll
+      for (int a0 = 0; a0 < D; a0 += VW) {
+        float x[VW];
+        vec16<T>::load(Q + qrow + a0, x);
+#pragma unroll
+        for (int e = 0; e < VW; ++e) qv[a0 + e] = x[e];
+      }
       for (int a = tid; a < D; a += DC_THREADS) sq[a] = io<T>::load(Q, qrow + a);
-      __syncthreads();
 
       float m = -INFINITY, l = 0.f;
       float oc[VW];
@@ -125,13 +140,18 @@ __global__ __launch_bounds__(DC_THREADS) void decode_kernel(
               float x[VW];
               vec16<T>::load(kr + a0, x);
 #pragma unroll
-              for (int e = 0; e < VW; ++e) acc = fmaf(sq[a0 + e], x[e], acc);
+              for (int e = 0; e < VW; ++e) acc = fmaf(qv[a0 + e], x[e], acc);
             }
             s = acc * scale;
           }
           sp[jj] = s;
           cm = fmaxf(cm, s);
         }
+        // the first P V batch of V rows is loaded while the scores reduce
+        // (indexes past the chunk repeat its last key and get weight 0)
+        typename vec16<T>::R vr[PB];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) vr[u] = vec16<T>::raw(vrow(j0 + min(kgp + NKG * u, jn - 1)) + ch * VW);
         cm = wave_max(cm);
         if ((tid & 63) == 0) sred[0][wave] = cm;
         __syncthreads();
@@ -159,13 +179,27 @@ __global__ __launch_bounds__(DC_THREADS) void decode_kernel(
         __syncthreads();
 #pragma unroll
         for (int w = 0; w < DC_THREADS / 64; ++w) l += sred[1][w];
-#pragma unroll 4
-        for (int jj = kgp; jj < jn; jj += NKG) {
-          float x[VW];
-          vec16<T>::load(vrow(j0 + jj) + ch * VW, x);
-          const float pj = sp[jj];
+        for (int jb = kgp; jb < jn; jb += NKG * PB) {
+          const bool more = jb + NKG * PB < jn;
+          typename vec16<T>::R nx[PB];
+          if (more) {
 #pragma unroll
-          for (int e = 0; e < VW; ++e) oc[e] = fmaf(pj, x[e], oc[e]);
+            for (int u = 0; u < PB; ++u)
+              nx[u] = vec16<T>::raw(vrow(j0 + min(jb + NKG * (PB + u), jn - 1)) + ch * VW);
+          }
+#pragma unroll
+          for (int u = 0; u < PB; ++u) {
+            const int jj = jb + NKG * u;
+            const float pj = jj < jn ? sp[jj] : 0.f;
+            float x[VW];
+            vec16<T>::cvt(vr[u], x);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) oc[e] = fmaf(pj, x[e], oc[e]);
+          }
+          if (more) {
+#pragma unroll
+            for (int u = 0; u < PB; ++u) vr[u] = nx[u];
+          }
         }
         __syncthreads();                       // sp and sred are reused
       }
@@ -190,6 +224,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_kernel(
         if (M) {
           const float* Mb = M + (size_t)bk * D * D;
           const float* zb = z + (size_t)bk * D;
+#pragma unroll 16
           for (int a = 0; a < D; ++a) {
             const float sa = elu1(sq[a]);
             num = fmaf(sa, Mb[(size_t)a * D + tid], num);
@@ -206,43 +241,79 @@ __global__ __launch_bounds__(DC_THREADS) void decode_kernel(
 
 // Merge the key splits of one query row (max, sum and P V row of each),
 // then retrieval from the state before the segment and the gate.  One
-// workgroup per (batch, query head, new row); thread c owns output column c.
+// workgroup of 256 threads per (batch, query head, new row): thread (g, c)
+// owns output column c for split group g (splits g, g + NG, ...) and state
+// rows g*RA .. g*RA+RA-1, so that every load the row needs is issued at once
+// and waited for once; the groups' partial sums meet in LDS.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(
+__global__ __launch_bounds__(DC_THREADS) void decode_combine_kernel(
     const T* __restrict__ Q, const float* __restrict__ beta, const float* __restrict__ M,
     const float* __restrict__ z, const float* __restrict__ part, T* __restrict__ O,
     int Hq, int Hkv, int Tn, int nsplit) {
-  __shared__ float sq[D];
+  constexpr int NG = DC_THREADS / D;           // thread groups
+  constexpr int RA = D / NG;                   // state rows per group
+  constexpr int NS = (kDecodeMaxSplits + NG - 1) / NG;   // splits per group, at most
+  __shared__ float rsum[4][NG][D];             // num, den, P V, sum
+  __shared__ float rmax[NG];
   const int row = blockIdx.x;                  // (b * Hq + h) * Tn + t
   const int h = (row / Tn) % Hq, b = row / (Tn * Hq);
   const int bk = b * Hkv + h / (Hq / Hkv);
-  const int c = threadIdx.x;
-  sq[c] = io<T>::load(Q, (size_t)row * D + c);
+  const int c = threadIdx.x % D, g = threadIdx.x / D;
   const float* pr = part + (size_t)row * nsplit * (D + 2);
-  float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pr[s * (D + 2)]);
-  float l = 0.f, od = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = pr[s * (D + 2)];
-    if (ms == -INFINITY) continue;             // no keys in that split
-    const float w = __expf(ms - mx);
-    l = fmaf(w, pr[s * (D + 2) + 1], l);
-    od = fmaf(w, pr[s * (D + 2) + 2 + c], od);
+  // split parts: indexes past nsplit repeat the last split and get weight 0
+  float pm[NS], pl[NS], po[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    const int s = min(g + NG * n, nsplit - 1);
+    pm[n] = pr[s * (D + 2)];
+    pl[n] = pr[s * (D + 2) + 1];
+    po[n] = pr[s * (D + 2) + 2 + c];
   }
-  __syncthreads();
   float num = 0.f, den = 0.f;
   if (M) {
     const float* Mb = M + (size_t)bk * D * D;
     const float* zb = z + (size_t)bk * D;
-    for (int a = 0; a < D; ++a) {
-      const float sa = elu1(sq[a]);
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      const int a = g * RA + i;
+      const float sa = elu1(io<T>::load(Q, (size_t)row * D + a));
       num = fmaf(sa, Mb[(size_t)a * D + c], num);
       den = fmaf(sa, zb[a], den);
     }
   }
-  den += 1e-6f;
-  const float gt = sigmoid(beta[h]);
-  io<T>::store(O, (size_t)row * D + c, gt * (num / den) + (1.f - gt) * (od / l));
+  float gm = pm[0];
+#pragma unroll
+  for (int n = 1; n < NS; ++n) gm = fmaxf(gm, pm[n]);
+  if (c == 0) rmax[g] = gm;
+  __syncthreads();
+  float mx = rmax[0];                          // finite: split 0 holds key 0 of every row
+#pragma unroll
+  for (int i = 1; i < NG; ++i) mx = fmaxf(mx, rmax[i]);
+  float l = 0.f, od = 0.f;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    // a split with no keys for this row holds (-inf, 0, 0): weight 0
+    const float w = g + NG * n < nsplit ? __expf(pm[n] - mx) : 0.f;
+    l = fmaf(w, pl[n], l);
+    od = fmaf(w, po[n], od);
+  }
+  rsum[0][g][c] = num;
+  rsum[1][g][c] = den;
+  rsum[2][g][c] = od;
+  rsum[3][g][c] = l;
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int i = 1; i < NG; ++i) {
+      num += rsum[0][i][c];
+      den += rsum[1][i][c];
+      od += rsum[2][i][c];
+      l += rsum[3][i][c];
+    }
+    den += 1e-6f;
+    const float gt = sigmoid(beta[h]);
+    io<T>::store(O, (size_t)row * D + c, gt * (num / den) + (1.f - gt) * (od / l));
+  }
 }
 
 // Key splits per row: 1 when the (batch, K/V head) pairs already fill the
@@ -274,7 +345,7 @@ static hipError_t decode_t(const Geometry& g, int Tn, int pos, const void* Q, co
                      Tn, g.L, pos, nsplit, split_keys, 1.f / sqrtf((float)D));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(g.B * g.Hq * Tn), dim3(D), 0, st,
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(g.B * g.Hq * Tn), dim3(DC_THREADS), 0, st,
                      static_cast<const T*>(Q), beta, M, z, part, static_cast<T*>(O), g.Hq, g.Hkv, Tn, nsplit);
   return hipGetLastError();
 }

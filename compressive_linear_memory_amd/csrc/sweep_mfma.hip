@@ -200,6 +200,28 @@ __global__ __launch_bounds__(256) void scan_kernel(
 
   for (int sl = 0; sl < nseg; ++sl) {
     const size_t unit = bk * nseg + sl;
+    // dM_s = sum of its key-split parts, added in split order.  The loads are
+    // issued before M_{s-1} is published so that they overlap the transpose.
+    float part[16];
+#pragma unroll 4
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float* src = dM + (unit * nsplit + sp) * D * D + eoff;
+#pragma unroll
+      for (int x = 0; x < 16; x += 4) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + x);
+        if (sp == 0) {
+          part[x] = v[0]; part[x + 1] = v[1]; part[x + 2] = v[2]; part[x + 3] = v[3];
+        } else {
+          part[x] += v[0]; part[x + 1] += v[1]; part[x + 2] += v[2]; part[x + 3] += v[3];
+        }
+      }
+    }
+    float zpart = 0.f;
+    if (do_z && tid < SC_T) {
+      zpart = dz[(unit * nsplit) * D + a0 + tid];
+#pragma unroll 4
+      for (int sp = 1; sp < nsplit; ++sp) zpart += dz[(unit * nsplit + sp) * D + a0 + tid];
+    }
     // publish M_{s-1} transposed in bf16: stage the fp32 tile, read columns
 #pragma unroll
     for (int x = 0; x < 16; ++x) tr[ra][rc + x] = run[x];
@@ -217,27 +239,9 @@ __global__ __launch_bounds__(256) void scan_kernel(
       }
     }
     __syncthreads();
-    // dM_s = sum of its key-split parts, added in split order
-    float part[16];
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float* src = dM + (unit * nsplit + sp) * D * D + eoff;
-#pragma unroll
-      for (int x = 0; x < 16; x += 4) {
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + x);
-        if (sp == 0) {
-          part[x] = v[0]; part[x + 1] = v[1]; part[x + 2] = v[2]; part[x + 3] = v[3];
-        } else {
-          part[x] += v[0]; part[x + 1] += v[1]; part[x + 2] += v[2]; part[x + 3] += v[3];
-        }
-      }
-    }
 #pragma unroll
     for (int x = 0; x < 16; ++x) run[x] += part[x];
-    if (do_z && tid < SC_T) {
-      float zpart = dz[(unit * nsplit) * D + a0 + tid];
-      for (int sp = 1; sp < nsplit; ++sp) zpart += dz[(unit * nsplit + sp) * D + a0 + tid];
-      zr += zpart;
-    }
+    if (do_z && tid < SC_T) zr += zpart;
   }
   if (M_out) {
 #pragma unroll
