@@ -178,30 +178,37 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   };
 
-  // The retrieval operands (bf16 M_{s-1}^T, fp32 z_{s-1}) go straight from
-  // global memory into the tile buffer the last tile does not use
-  // (global_load_lds_dwordx4: lane l of a wave's load lands at base + 16 l), so
-  // the epilogue neither waits on them nor spends staging registers.  M^T rows
-  // are unpadded; 16-byte chunk c of row r sits at chunk c ^ (r & 7), which
-  // keeps the epilogue's row reads conflict-free.
+  // The retrieval operand M_{s-1}^T (bf16) is loaded into registers while
+  // the last tile computes (the staging registers are free by
+  // then) and stored after the key loop into the tile buffer the last tile
+  // does not use.  M^T rows are unpadded; 16-byte chunk c of row r sits at
+  // chunk c ^ (r & 7), which keeps the epilogue's row reads conflict-free.
+  // (Loads straight into LDS would make the compiler wait for every
+  // outstanding global load before each tile's LDS reads.)
   constexpr int MPT = D * D / 8 / 256;    // 16-byte chunks of M^T per thread
   static_assert(D * D <= C::BUF, "M^T stage must fit one tile buffer");
   const __bf16* msrc = MsnapT + ((size_t)bk * nseg + sl) * D * D;
   const float* zsrc = zsnap + ((size_t)bk * nseg + sl) * D;
-  // Wave load i of wave w covers 1 KB block i*4 + w, i.e. rows
+  // Chunk i of a thread in wave w covers 1 KB block i*4 + w, i.e. rows
   // (i*4 + w) * RPB + lane / (D/8); (row & 7) does not depend on i, so every
   // load of a lane is one base address plus a constant.
   constexpr int RPB = 64 / (D / 8);               // M^T rows per 1 KB block
   const int mrow0 = wave * RPB + lane / (D / 8);
   const __bf16* msrc0 = msrc + (size_t)mrow0 * D + (((lane % (D / 8)) ^ (mrow0 & 7)) * 8);
-  auto load_m = [&](__bf16* dst) {
+  // The chunks live in the K/V staging registers (kst, then vst).
+  static_assert(MPT <= C::CPT + C::KPT, "M^T chunks must fit the staging registers");
+  auto load_m = [&]() {
+#pragma unroll
+    for (int i = 0; i < MPT; ++i) {
+      const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(msrc0 + (size_t)i * 4 * RPB * D);
+      if (i < C::CPT) kst[i] = v;
+      else vst[i - C::CPT] = v;
+    }
+  };
+  auto store_m = [&](__bf16* dst) {
 #pragma unroll
     for (int i = 0; i < MPT; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(msrc0 + (size_t)i * 4 * RPB * D),
-                                       (__attribute__((address_space(3))) void*)(dst + (i * 4 + wave) * 512), 16, 0, 0);
-    if (wave < D / 64)
-      __builtin_amdgcn_global_load_lds((const void*)(zsrc + wave * 64 + lane),
-                                       (__attribute__((address_space(3))) void*)(zs + wave * 64), 4, 0, 0);
+      *reinterpret_cast<bf16x8_t*>(dst + (i * 4 + wave) * 512 + lane * 8) = i < C::CPT ? kst[i] : vst[i - C::CPT];
   };
 
   f32x16_t oacc[C::DB];
@@ -284,10 +291,12 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   };
 
   load_tile(0);
+  // z_{s-1} has an LDS array of its own, written once before the first barrier
+  if (wave < D / 64) zs[wave * 64 + lane] = zsrc[wave * 64 + lane];
   store_tile(0);
   __syncthreads();
   if (ntiles > 1) load_tile(C::BN);
-  else load_m(smem + C::BUF);
+  else load_m();
 
   for (int j = 0; j < ntiles; ++j) {
     const int k0 = j * C::BN;
@@ -302,11 +311,15 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     if (j + 1 < ntiles) store_tile((j + 1) & 1);
     __syncthreads();
     if (j + 2 < ntiles) load_tile((j + 2) * C::BN);
-    else if (j + 2 == ntiles) load_m(smem + (ntiles & 1) * C::BUF);
+    else if (j + 2 == ntiles) load_m();
   }
-  const __bf16* Mts = smem + (ntiles & 1) * C::BUF;   // where load_m put M^T
+  // M^T goes to the buffer the last tile did not use: every wave has passed
+  // the barrier after the tile that used it last.
+  __bf16* Mts = smem + (ntiles & 1) * C::BUF;
+  store_m(Mts);
+  __syncthreads();
 
-  // ---- retrieval from M_{s-1}, z_{s-1} (staged in the K buffers) and the gate
+  // ---- retrieval from M_{s-1}, z_{s-1} (staged in a tile buffer) and the gate
   const float l = pair_sum32(lpart);
 
   bf16x8_t sq[C::KS];
