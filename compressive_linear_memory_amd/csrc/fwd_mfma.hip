@@ -224,19 +224,32 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // unnormalised terms by 2^kRescaleSlack.
   constexpr float kRescaleSlack = 8.f;
   const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
-  auto tile_step = [&](const __bf16* Ks, const __bf16* Vt, int k0, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto tile_step = [&](const __bf16* Ks, const __bf16* Vt, int k0, bool masked) {
     f32x16_t sacc[2];
+    bf16x8_t ka[2][C::KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        ka[kb][ks] = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 32 + lq) * C::KSTR + ks * 16 + hh * 8);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x16_t{};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 32 + lq) * C::KSTR + ks * 16 + hh * 8);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[kb], 0, 0, 0);
-      }
+      for (int ks = 0; ks < C::KS; ++ks)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], qreg[ks], sacc[kb], 0, 0, 0);
     }
-    if constexpr (MASK) {
+    // Issue order: the first block's K reads, then each of its products
+    // beside one read of the second block, then the second block's products;
+    // at most 15 reads are outstanding when a product waits for its operand.
+    __builtin_amdgcn_sched_group_barrier(0x100, C::KS, 0);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, C::KS, 0);
+    if (masked) {
       // element (kb, r) holds key k0 + 4hh + kb*32 + 8(r/4) + r%4
       const int lim = min(qrow, Ls - 1) - (k0 + 4 * hh);
 #pragma unroll
@@ -290,6 +303,10 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   };
 
+  // The kernel arguments only the epilogue reads are brought into registers
+  // here: a scalar load still in flight when the key loop starts would make
+  // every tile's first LDS wait a full wait.
+  asm volatile("" ::"s"(beta), "s"(O), "s"(lse), "s"(msrc0));
   load_tile(0);
   // z_{s-1} has an LDS array of its own, written once before the first barrier
   if (wave < D / 64) zs[wave * 64 + lane] = zsrc[wave * 64 + lane];
@@ -305,8 +322,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const bool active = k0 <= q0 + C::WM - 1 && q0 < Ls;
     const bool masked = (k0 + C::BN - 1 > q0) || (k0 + C::BN > Ls);
     if (active) {
-      if (masked) tile_step(Ks, Vt, k0, std::true_type{});
-      else tile_step(Ks, Vt, k0, std::false_type{});
+      tile_step(Ks, Vt, k0, masked);
     }
     if (j + 1 < ntiles) store_tile((j + 1) & 1);
     __syncthreads();
