@@ -37,8 +37,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = 128;          // query rows per workgroup
+  static constexpr int BM = D == 128 ? 256 : 128;   // query rows per workgroup
   static constexpr int WM = 32;           // query rows per wave
+  static constexpr int NW = BM / WM;      // waves per workgroup
+  static constexpr int NT = NW * 64;      // threads per workgroup
   static constexpr int BN = 64;           // keys per tile
   static constexpr int KS = D / 16;       // MFMA k-steps over head_dim
   static constexpr int DB = D / 32;       // 32-row blocks of head_dim
@@ -46,8 +48,8 @@ struct FwdCfg {
   static constexpr int VSTR = BN + 4;     // V^T tile row stride; 8-byte aligned rows
   static constexpr int KTILE = BN * KSTR;
   static constexpr int VTILE = D * VSTR;
-  static constexpr int KPT = D / 32;      // keys per thread when staging V^T
-  static constexpr int CPT = D / 32;      // 16-byte chunks per thread per tile
+  static constexpr int KPT = BN * D / 8 / NT;   // keys per thread when staging V^T
+  static constexpr int CPT = BN * D / 8 / NT;   // 16-byte K chunks per thread per tile
   static constexpr int MSTR = D + 8;      // M^T stage row stride
   static constexpr int BUF = KTILE + VTILE;
   static constexpr int LDS_ELEMS = (2 * BUF > D * MSTR) ? 2 * BUF : D * MSTR;
@@ -65,7 +67,7 @@ __device__ __forceinline__ float pair_sum32(float x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(FwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const float* __restrict__ beta,
                      const __bf16* __restrict__ MsnapT, const float* __restrict__ zsnap,
@@ -126,7 +128,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   bf16x8_t kst[C::CPT], vst[C::KPT];
   // V^T staging: consecutive lanes take consecutive key groups so that the
   // transposed LDS stores of a 16-lane group hit distinct banks.
-  constexpr int NKG = 64 / C::KPT;
+  constexpr int NKG = C::BN / C::KPT;
   const int vkg = tid % NKG, vdc = tid / NKG;
   // Per-lane element offsets inside a tile are fixed; each tile adds a
   // workgroup-uniform row offset.  Keys past the segment end (only in the last
@@ -135,7 +137,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const __bf16* Kseg = K + kvbase;
   const __bf16* Vseg = V + kvbase;
   // K chunk i of this thread: row krow0 + i * KRS, columns kcol .. kcol + 7
-  constexpr int KRS = 256 / (D / 8);
+  constexpr int KRS = C::NT / (D / 8);
   const int krow0 = tid / (D / 8), kcol = (tid % (D / 8)) * 8;
   auto load_tile = [&](int k0) {
     const __bf16* kt = Kseg + (size_t)k0 * D + krow0 * D + kcol;
@@ -185,12 +187,12 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // chunk c ^ (r & 7), which keeps the epilogue's row reads conflict-free.
   // (Loads straight into LDS would make the compiler wait for every
   // outstanding global load before each tile's LDS reads.)
-  constexpr int MPT = D * D / 8 / 256;    // 16-byte chunks of M^T per thread
+  constexpr int MPT = D * D / 8 / C::NT;  // 16-byte chunks of M^T per thread
   static_assert(D * D <= C::BUF, "M^T stage must fit one tile buffer");
   const __bf16* msrc = MsnapT + ((size_t)bk * nseg + sl) * D * D;
   const float* zsrc = zsnap + ((size_t)bk * nseg + sl) * D;
-  // Chunk i of a thread in wave w covers 1 KB block i*4 + w, i.e. rows
-  // (i*4 + w) * RPB + lane / (D/8); (row & 7) does not depend on i, so every
+  // Chunk i of a thread in wave w covers 1 KB block i*NW + w, i.e. rows
+  // (i*NW + w) * RPB + lane / (D/8); (row & 7) does not depend on i, so every
   // load of a lane is one base address plus a constant.
   constexpr int RPB = 64 / (D / 8);               // M^T rows per 1 KB block
   const int mrow0 = wave * RPB + lane / (D / 8);
@@ -200,7 +202,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   auto load_m = [&]() {
 #pragma unroll
     for (int i = 0; i < MPT; ++i) {
-      const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(msrc0 + (size_t)i * 4 * RPB * D);
+      const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(msrc0 + (size_t)i * C::NW * RPB * D);
       if (i < C::CPT) kst[i] = v;
       else vst[i - C::CPT] = v;
     }
@@ -208,7 +210,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   auto store_m = [&](__bf16* dst) {
 #pragma unroll
     for (int i = 0; i < MPT; ++i)
-      *reinterpret_cast<bf16x8_t*>(dst + (i * 4 + wave) * 512 + lane * 8) = i < C::CPT ? kst[i] : vst[i - C::CPT];
+      *reinterpret_cast<bf16x8_t*>(dst + (i * C::NW + wave) * 512 + lane * 8) = i < C::CPT ? kst[i] : vst[i - C::CPT];
   };
 
   f32x16_t oacc[C::DB];
@@ -390,7 +392,7 @@ static hipError_t fwd_mfma_t(const Geometry& g, const void* Q, const void* K, co
   const long long nwg = (long long)g.B * g.Hq * nseg * nqt;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3((unsigned)nwg), dim3(256), 0, st,
+  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3((unsigned)nwg), dim3(FwdCfg<D>::NT), 0, st,
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
                      static_cast<const __bf16*>(V), beta, static_cast<const __bf16*>(MsnapT), zsnap,
                      static_cast<__bf16*>(O), lse, g.Hq, g.Hkv, g.N, g.L, s_begin, nseg, nqt, sl2);
