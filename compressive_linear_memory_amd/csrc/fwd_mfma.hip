@@ -45,7 +45,7 @@ struct FwdCfg {
   static constexpr int KS = D / 16;       // MFMA k-steps over head_dim
   static constexpr int DB = D / 32;       // 32-row blocks of head_dim
   static constexpr int KSTR = D + 8;      // K tile row stride (elements); 16-byte aligned rows
-  static constexpr int VSTR = BN + 4;     // V^T tile row stride; 8-byte aligned rows
+  static constexpr int VSTR = BN + 8;     // V^T tile row stride; 16-byte aligned rows
   static constexpr int KTILE = BN * KSTR;
   static constexpr int VTILE = D * VSTR;
   static constexpr int KPT = BN * D / 8 / NT;   // keys per thread when staging V^T
@@ -161,6 +161,10 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       }
     }
   };
+  // V^T columns hold the keys of each 16-key group with index bits 2 and 3
+  // swapped, so that the 8 keys one lane's PV operand needs (see below) are
+  // contiguous: one 16-byte LDS read per MFMA.
+  auto vcol = [](int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); };
   auto store_tile = [&](int buf) {
     __bf16* Ks = smem + buf * C::BUF;
     __bf16* Vt = Ks + C::KTILE;
@@ -169,7 +173,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       *reinterpret_cast<bf16x8_t*>(Ks + (krow0 + i * KRS) * C::KSTR + kcol) = kst[i];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      __bf16* dst = Vt + (vdc * 8 + e) * C::VSTR + vkg * C::KPT;
+      __bf16* dst = Vt + (vdc * 8 + e) * C::VSTR + vcol(vkg * C::KPT);
       if constexpr (C::KPT == 4) {
         bf16x4_t w = {vst[0][e], vst[1][e], vst[2][e], vst[3][e]};
         *reinterpret_cast<bf16x4_t*>(dst) = w;
@@ -288,17 +292,15 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int x = 0; x < 4; ++x)
           lpart = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pb[kb][t][2 * x], pb[kb][t][2 * x + 1]}, ones, lpart, false);
-    // O^T += V^T P^T: k-slot q of half hh <-> key 16t + 8(q/4) + 4hh + q%4
+    // O^T += V^T P^T: k-slot q of half hh <-> key 16t + 8(q/4) + 4hh + q%4,
+    // which is V^T column 16t + 8hh + q
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const __bf16* vp = Vt + (db * 32 + lq) * C::VSTR + kb * 32 + 16 * t + 4 * hh;
-          const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vp);
-          const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vp + 8);
-          const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Vt + (db * 32 + lq) * C::VSTR + kb * 32 + 16 * t + 8 * hh);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], oacc[db], 0, 0, 0);
         }
       }
