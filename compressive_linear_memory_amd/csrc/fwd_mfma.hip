@@ -98,7 +98,10 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 31, hh = lane >> 5;
-  const int q0 = qt * C::BM + wave * C::WM;   // wave's first row (segment-relative)
+  // waves w and w + 4 share a SIMD: they take row blocks w and 7 - w, so
+  // that each SIMD's pair attends to the same number of diagonal tiles
+  const int rblk = (C::NW == 8 && wave >= 4) ? 11 - wave : wave;
+  const int q0 = qt * C::BM + rblk * C::WM;   // wave's first row (segment-relative)
   const int qrow = q0 + lq;                   // this lane's query row
   const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
   const size_t kvbase = (((size_t)b * Hkv + kvh) * N + (size_t)s * L) * D;
