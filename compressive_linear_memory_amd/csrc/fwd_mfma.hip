@@ -313,7 +313,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // The kernel arguments only the epilogue reads are brought into registers
   // here: a scalar load still in flight when the key loop starts would make
   // every tile's first LDS wait a full wait.
-  asm volatile("" ::"s"(beta), "s"(O), "s"(lse), "s"(msrc0));
+  asm volatile("" ::"s"(beta), "s"(O), "s"(lse), "s"(msrc));
   load_tile(0);
   // z_{s-1} has an LDS array of its own, written once before the first barrier
   if (wave < D / 64) zs[wave * 64 + lane] = zsrc[wave * 64 + lane];
