@@ -329,12 +329,12 @@ def bench_stream(args):
     traffic as distinct inputs; the state still chains through every launch).
 
     Two schedules are timed.  Serial: one infini_attn_fwd per launch on one
-    stream.  Pipelined (the reported value): the memory phase of every launch
-    runs in order on one stream (it carries the state), and the attention
-    phase of launch i, which needs only the state launch i retrieves from,
-    runs on one of NPIPE streams as soon as its memory phase is done, so one
-    launch's attention fills the compute units the previous launch's longest
-    query tiles leave idle."""
+    stream.  Pipelined (the reported value): one infini_fwd_stream call per
+    step; the memory phase of every launch runs in order on one stream (it
+    carries the state), and the attention phase of launch i, which needs only
+    the state launch i retrieves from, runs on one of NPIPE streams as soon
+    as its memory phase is done, so one launch's attention fills the compute
+    units the previous launch's longest query tiles leave idle."""
     import torch
     from compressive_linear_memory_amd import binding as Bi
     Bi.lib()
@@ -360,32 +360,67 @@ def bench_stream(args):
             src, dst = st[i & 1], st[(i + 1) & 1]
             Bi.attn_fwd(q, k, v, b, w.seg_len, M0=src[0], z0=src[1], out=(O_, dst[0], dst[1], None), ws=ws)
 
-    NPIPE = 3                                   # workspaces and attention streams in rotation
-    wss = [torch.empty(Bi.workspace_bytes(p), dtype=torch.uint8, device=dev) for _ in range(NPIPE)]
+    NPIPE = 3                                   # workspace slots and attention streams in rotation
+    # Pipelined: one infini_fwd_stream call per step issues all nl calls (the
+    # memory phases in order on sm, each attention phase on sa[i % NPIPE]).
+    wsp = torch.empty(NPIPE * Bi.workspace_bytes(p), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(ins[0][0]) for _ in range(NPIPE)]
+    Mp, zp = torch.zeros_like(st[0][0]), torch.zeros_like(st[0][1])
     sm = torch.cuda.Stream()
     sa = [torch.cuda.Stream() for _ in range(NPIPE)]
-    ev_mem = [torch.cuda.Event() for _ in range(NPIPE)]
-    ev_att = [torch.cuda.Event() for _ in range(NPIPE)]
+    evs = [torch.cuda.Event() for _ in range(2 * NPIPE)]
+    calls = Bi.StreamCalls(p, [ins[i % nd][0] for i in range(nl)], [ins[i % nd][1] for i in range(nl)],
+                           [ins[i % nd][2] for i in range(nl)], b, Mp, zp, [outs[i % NPIPE] for i in range(nl)],
+                           wsp, NPIPE, sm, sa, evs)
 
     def run_pipelined():
         cur = torch.cuda.current_stream()
         sm.wait_stream(cur)
         for s_ in sa:
             s_.wait_stream(cur)
-        for i in range(nl):
-            r = i % NPIPE
-            q, k, v = ins[i % nd]
-            src, dst = st[i & 1], st[(i + 1) & 1]
-            with torch.cuda.stream(sm):
-                if i >= NPIPE:                  # workspace r is reused once attention i - NPIPE is done
-                    sm.wait_event(ev_att[r])
-                Bi.fwd_memory(p, k, v, src[0], src[1], dst[0], dst[1], wss[r])
-                ev_mem[r].record(sm)
-            with torch.cuda.stream(sa[r]):
-                sa[r].wait_event(ev_mem[r])
-                Bi.fwd_attend(p, q, k, v, b, outs[r], None, wss[r])
-                ev_att[r].record(sa[r])
+        calls()
+        cur.wait_stream(sm)
+        for s_ in sa:
+            cur.wait_stream(s_)
+
+    # The same schedule issued call by call from Python through the phased
+    # entry points (infini_fwd_memory / infini_fwd_attend) with torch events;
+    # arguments marshalled once.
+    L_ = Bi.lib()
+    fm, fa = L_.infini_fwd_memory, L_.infini_fwd_attend
+    P_ = lambda t: ctypes.c_void_p(t.data_ptr())
+    pp = ctypes.byref(p)
+    hm = ctypes.c_void_p(sm.cuda_stream)
+    ha = [ctypes.c_void_p(x.cuda_stream) for x in sa]
+    wsz = Bi.workspace_bytes(p)
+    wsl = [wsp[r * wsz:(r + 1) * wsz] for r in range(NPIPE)]
+    nws = ctypes.c_size_t(wsz)
+    ev_mem, ev_att = evs[:NPIPE], evs[NPIPE:]
+    percall = []
+    for i in range(nl):
+        r = i % NPIPE
+        q, k, v = ins[i % nd]
+        percall.append((r, (pp, P_(k), P_(v), P_(Mp), P_(zp), P_(st[1][0]), P_(st[1][1]), P_(wsl[r]), nws, hm),
+                        (pp, P_(q), P_(k), P_(v), P_(b), P_(outs[r]), None, P_(wsl[r]), nws, ha[r]),
+                        (pp, P_(k), P_(v), P_(st[1][0]), P_(st[1][1]), P_(Mp), P_(zp), P_(wsl[r]), nws, hm)))
+
+    def run_pipelined_calls():
+        cur = torch.cuda.current_stream()
+        sm.wait_stream(cur)
+        for s_ in sa:
+            s_.wait_stream(cur)
+        for i, (r, m_even, aargs, m_odd) in enumerate(percall):
+            if i >= NPIPE:                      # slot r is reused once attention i - NPIPE is done
+                sm.wait_event(ev_att[r])
+            rc = fm(*(m_even if i % 2 == 0 else m_odd))   # state alternates between two buffers
+            if rc:
+                raise Bi.InfiniError(rc, "infini_fwd_memory")
+            ev_mem[r].record(sm)
+            sa[r].wait_event(ev_mem[r])
+            rc = fa(*aargs)
+            if rc:
+                raise Bi.InfiniError(rc, "infini_fwd_attend")
+            ev_att[r].record(sa[r])
         cur.wait_stream(sm)
         for s_ in sa:
             cur.wait_stream(s_)
@@ -402,9 +437,21 @@ def bench_stream(args):
     for _ in range(max(1, args.warmup // 3)):
         run()
         run_pipelined()
+        run_pipelined_calls()
     torch.cuda.synchronize()
     ms_serial = timed(run)
-    step = run_pipelined
+
+    def host_issue_us(fn):
+        # host time to issue one step (no synchronisation inside)
+        torch.cuda.synchronize()
+        th0 = time.perf_counter()
+        fn()
+        us = (time.perf_counter() - th0) * 1e6 / nl
+        torch.cuda.synchronize()
+        return us
+
+    host_lib, host_calls = host_issue_us(run_pipelined), host_issue_us(run_pipelined_calls)
+    ms_lib, ms_calls = timed(run_pipelined), timed(run_pipelined_calls)
     if args.graph:
         # One step's launches recorded once and replayed: the host issues one
         # graph launch per step instead of two kernel launches per segment.
@@ -412,12 +459,16 @@ def bench_stream(args):
         with torch.cuda.graph(graph):
             run()
         torch.cuda.synchronize()
-        step = graph.replay
-        step()
+        graph.replay()
         torch.cuda.synchronize()
-    ms = timed(step)
-    say(f"[bench] stream: {1e3 * ms_serial / nl:.2f} us/launch serial, {1e3 * ms / nl:.2f} us/launch "
-        f"{'graph-replayed serial' if args.graph else 'pipelined'}")
+        ms, schedule = timed(graph.replay), "serial, graph-replayed"
+    elif ms_lib <= ms_calls:
+        ms, schedule = ms_lib, "pipelined, one infini_fwd_stream call per step"
+    else:
+        ms, schedule = ms_calls, "pipelined, issued per call (infini_fwd_memory / infini_fwd_attend)"
+    say(f"[bench] stream: {1e3 * ms_serial / nl:.2f} us/launch serial, {1e3 * ms_lib / nl:.2f} pipelined by "
+        f"infini_fwd_stream (host {host_lib:.1f}), {1e3 * ms_calls / nl:.2f} pipelined per call (host "
+        f"{host_calls:.1f}); reported: {schedule}")
     tok = w.seq_len * nl
     # Each launch is one 2048-token segment per head: matrix-core bound in
     # principle (arithmetic intensity ~545 flop/byte).
@@ -429,11 +480,15 @@ def bench_stream(args):
     print(json.dumps({"metric": "Infini-attention streaming fwd tokens/s (stream_1m)", "value": round(tok / (ms / 1e3), 1),
                       "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "ms_per_step": round(ms, 4), "us_per_launch": round(1e3 * ms / nl, 2),
-                      "us_per_launch_serial": round(1e3 * ms_serial / nl, 2), "higher_is_better": True,
+                      "us_per_launch_serial": round(1e3 * ms_serial / nl, 2),
+                      "us_per_launch_pipelined_stream_call": round(1e3 * ms_lib / nl, 2),
+                      "us_per_launch_pipelined_per_call": round(1e3 * ms_calls / nl, 2),
+                      "host_issue_us_per_launch": {"stream_call": round(host_lib, 2), "per_call": round(host_calls, 2)},
+                      "higher_is_better": True,
                       "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                       "config": {"workload": "stream_1m", "mode": "stream", "launches": nl,
-                                 "schedule": "serial, graph-replayed" if args.graph else "pipelined",
-                                 "graph": bool(args.graph), "kernel_path": Bi.fwd_path(p)}, "roofline": roof}), flush=True)
+                                 "schedule": schedule, "graph": bool(args.graph), "kernel_path": Bi.fwd_path(p)},
+                      "roofline": roof}), flush=True)
 
 
 def bench_decode(args):

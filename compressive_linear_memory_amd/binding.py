@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.infini_fwd_memory.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_size_t, _P]
         L.infini_fwd_attend.restype = ctypes.c_int
         L.infini_fwd_attend.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_size_t, _P]
+        L.infini_fwd_stream.restype = ctypes.c_int
+        L.infini_fwd_stream.argtypes = ([ctypes.POINTER(Problem), ctypes.c_int] + [_P] * 8 +
+                                        [ctypes.c_size_t, ctypes.c_int, _P, _P, _P])
         L.infini_decode.restype = ctypes.c_int
         L.infini_decode.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32] + [_P] * 12 + [ctypes.c_size_t, _P]
         _lib = L
@@ -173,6 +176,47 @@ def fwd_attend(p: Problem, q, k, v, beta, O, lse, ws):
                                  _ptr(ws), ws.numel(), _stream())
     if rc != 0:
         raise InfiniError(rc, "infini_fwd_attend")
+
+
+def _event_handle(ev):
+    """Raw HIP event of a torch.cuda.Event (created lazily by torch: recorded
+    once here if it does not exist yet)."""
+    if not ev.cuda_event:
+        ev.record()
+    return ev.cuda_event
+
+
+class StreamCalls:
+    """Marshalled arguments of one infini_fwd_stream call: a batch of calls of
+    shape `p` over the given per-call tensors, so that a loop that repeats the
+    batch pays the marshalling once.  The tensors must stay alive."""
+
+    def __init__(self, p: Problem, qs, ks, vs, beta, M, z, outs, ws, n_pipe, mem_stream, att_streams, events):
+        n = len(qs)
+        if not (len(ks) == len(vs) == len(outs) == n) or n < 1:
+            raise ValueError("qs, ks, vs, outs: one tensor per call")
+        if len(att_streams) != n_pipe or len(events) != 2 * n_pipe:
+            raise ValueError("need n_pipe attention streams and 2 * n_pipe events")
+        arr = lambda ts: (_P * n)(*[t.data_ptr() for t in ts])
+        self._keep = (arr(qs), arr(ks), arr(vs), arr(outs),
+                      (_P * n_pipe)(*[s.cuda_stream for s in att_streams]),
+                      (_P * (2 * n_pipe))(*[_event_handle(e) for e in events]))
+        self.args = (ctypes.byref(p), n, self._keep[0], self._keep[1], self._keep[2], _ptr(beta), _ptr(M), _ptr(z),
+                     self._keep[3], _ptr(ws), ws.numel(), n_pipe, _P(mem_stream.cuda_stream), self._keep[4],
+                     self._keep[5])
+        self._p = p
+
+    def __call__(self):
+        rc = lib().infini_fwd_stream(*self.args)
+        if rc != 0:
+            raise InfiniError(rc, "infini_fwd_stream")
+
+
+def fwd_stream(p: Problem, qs, ks, vs, beta, M, z, outs, ws, n_pipe, mem_stream, att_streams, events):
+    """infini_fwd_stream (see include/infini.h): len(qs) chained calls of shape
+    p, the memory phases on mem_stream and the attention phases overlapped on
+    att_streams; M, z hold the state and are updated in place."""
+    StreamCalls(p, qs, ks, vs, beta, M, z, outs, ws, n_pipe, mem_stream, att_streams, events)()
 
 
 def decode(q, k, v, beta, seg_len, pos, kcache, vcache, M=None, z=None, out=None, state_out=None, ws=None):

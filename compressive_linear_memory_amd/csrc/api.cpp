@@ -264,6 +264,52 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
   return INFINI_OK;
 }
 
+infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, const void* const* Q,
+                                  const void* const* K, const void* const* V, const float* beta,
+                                  float* M, float* z, void* const* O, void* ws, size_t ws_bytes,
+                                  int n_pipe, void* mem_stream, void* const* att_streams,
+                                  void* const* events) {
+  infini_status_t why;
+  if (!valid_problem(p, &why)) return why;
+  if (n_launches < 1 || n_pipe < 1) return INFINI_ERR_SHAPE;
+  if (!Q || !K || !V || !O || !beta || !M || !z || !ws || !att_streams || !events) return INFINI_ERR_NULL;
+  const Geometry g = geometry(p);
+  if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
+  const FwdWs lay = fwd_layout(g);
+  if (ws_bytes / (size_t)n_pipe < lay.total) return INFINI_ERR_WORKSPACE;
+  for (int r = 0; r < 2 * n_pipe; ++r)
+    if (!events[r]) return INFINI_ERR_NULL;
+  const size_t eb = elem_bytes(g);
+  const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
+  const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
+  const size_t wsz = (size_t)n_pipe * lay.total;
+  for (int i = 0; i < n_launches; ++i) {
+    if (!Q[i] || !K[i] || !V[i] || !O[i]) return INFINI_ERR_NULL;
+    const Span outs[] = {{O[i], nq * eb}, {M, nM}, {z, nz}, {ws, wsz}};
+    const Span ins[] = {{Q[i], nq * eb}, {K[i], nkv * eb}, {V[i], nkv * eb}, {beta, (size_t)g.Hq * 4}};
+    if (any_overlap(outs, 4, ins, 4)) return INFINI_ERR_ALIAS;
+  }
+  hipStream_t sm = static_cast<hipStream_t>(mem_stream);
+  char* base = static_cast<char*>(ws);
+  for (int i = 0; i < n_launches; ++i) {
+    const int r = i % n_pipe;
+    hipStream_t sa = static_cast<hipStream_t>(att_streams[r]);
+    hipEvent_t ev_mem = static_cast<hipEvent_t>(events[r]);
+    hipEvent_t ev_att = static_cast<hipEvent_t>(events[n_pipe + r]);
+    char* w = base + (size_t)r * lay.total;
+    // slot r is reused once the attention phase of call i - n_pipe is done
+    if (i >= n_pipe) TRY(hipStreamWaitEvent(sm, ev_att, 0));
+    TRY(run_fwd_chunk(g, lay, w, nullptr, K[i], V[i], nullptr, M, z, nullptr, M, z, nullptr, 0, g.S, sm,
+                      true, false));
+    TRY(hipEventRecord(ev_mem, sm));
+    TRY(hipStreamWaitEvent(sa, ev_mem, 0));
+    TRY(run_fwd_chunk(g, lay, w, Q[i], K[i], V[i], beta, nullptr, nullptr, O[i], nullptr, nullptr, nullptr, 0,
+                      g.S, sa, false, true));
+    TRY(hipEventRecord(ev_att, sa));
+  }
+  return INFINI_OK;
+}
+
 infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const void* K,
                                 const void* V, const float* beta, const float* M0, const float* z0,
                                 const float* lse, const void* dO, const float* dM_S,

@@ -161,6 +161,39 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
                                   const void* V, const float* beta, void* O, float* lse,
                                   const void* ws, size_t ws_bytes, void* stream);
 
+/* Streaming forward: n_launches consecutive calls of shape *p (each a whole
+ * number of segments, at most INFINI_CHUNK_SEGMENTS), the state carried from
+ * one call to the next (page "Hugging Face Infini-Attention 재현 분석",
+ * section "Infini-Attention 메커니즘", step State Transfer), issued so that
+ * they overlap: the memory phases (infini_fwd_memory) run in order on
+ * mem_stream, and the attention phase of call i (infini_fwd_attend) runs on
+ * att_streams[i % n_pipe] as soon as the memory phase of call i is done, in
+ * workspace slot i % n_pipe.  Outputs and final state are bit-identical to
+ * n_launches chained infini_attn_fwd calls.
+ *   Q, K, V, O   host arrays of n_launches device pointers; call i uses Q[i],
+ *                K[i], V[i] and writes O[i], with the layouts of infini_attn_fwd
+ *   beta         [q_heads] float32
+ *   M, z         [batch][kv_heads][head_dim][head_dim] and [batch][kv_heads]
+ *                [head_dim] float32: the state before call 0 on entry, updated
+ *                in place by the memory phases on mem_stream
+ *   ws           n_pipe * infini_fwd_workspace_bytes(p) bytes, one slot per
+ *                pipeline stage (ws_bytes: its size)
+ *   mem_stream   stream of the memory phases; att_streams: n_pipe streams for
+ *                the attention phases; events: 2 * n_pipe events of the
+ *                caller's (timing may be disabled), used to order the phases
+ * Inputs must be ready on every stream passed; the call returns once all work
+ * is issued, and the caller orders later work after mem_stream and all
+ * att_streams.  Errors are those of infini_attn_fwd, plus INFINI_ERR_SHAPE
+ * for n_launches < 1, n_pipe < 1 or more than INFINI_CHUNK_SEGMENTS segments
+ * per call; arguments are all checked before anything is issued.  Callers
+ * that cannot allocate, or that issue from a tight loop, get one library
+ * call per batch of calls instead of two per call. */
+infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, const void* const* Q,
+                                  const void* const* K, const void* const* V, const float* beta,
+                                  float* M, float* z, void* const* O, void* ws, size_t ws_bytes,
+                                  int n_pipe, void* mem_stream, void* const* att_streams,
+                                  void* const* events);
+
 /* Streaming decode: a few new tokens of the segment that is being filled.
  *
  * The same computation as infini_attn_fwd, evaluated for the tokens a

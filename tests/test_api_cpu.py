@@ -165,3 +165,33 @@ def test_decode_validation(L):
     assert dec(P1, 0, a, ws=None) == 5
     b = list(a); b[8] = FAKE[0]
     assert dec(P1, 0, b) == 4                                # O overlaps Q
+
+
+def test_fwd_stream_validation(L):
+    """Pipelined streaming forward: every argument is checked before any
+    work is issued, so these calls touch no device (codes: 1 null, 2 shape,
+    4 alias, 5 workspace)."""
+    p = P(N=16)                                   # one 16-token segment per call
+    n, npipe = 3, 2
+    arr = lambda vals: (ctypes.c_void_p * len(vals))(*[v.value if v else None for v in vals])
+    Q = arr(FAKE[0:3]); K = arr(FAKE[3:6]); V = arr(FAKE[6:9]); O = arr(FAKE[9:12])
+    streams = arr([FAKE[15], FAKE[16]])
+    events = arr([FAKE[17], FAKE[18], FAKE[19], FAKE[18]])
+    need = L.infini_fwd_workspace_bytes(ctypes.byref(p))
+
+    def call(p=p, n=n, Q=Q, K=K, V=V, O=O, beta=FAKE[12], M=FAKE[13], z=FAKE[14], ws=ctypes.c_void_p(1 << 36),
+             ws_bytes=npipe * need, npipe=npipe, streams=streams, events=events):
+        return L.infini_fwd_stream(ctypes.byref(p), n, Q, K, V, beta, M, z, O, ws, ws_bytes, npipe, None,
+                                   streams, events)
+
+    assert call(n=0) == 2
+    assert call(npipe=0) == 2
+    assert call(p=P(N=17 * 16)) == 2                            # more than 16 segments per call
+    assert call(Q=None) == 1
+    assert call(beta=None) == 1
+    assert call(M=None) == 1
+    assert call(events=arr([FAKE[17], None, FAKE[19], FAKE[18]])) == 1
+    assert call(V=arr([FAKE[6], None, FAKE[8]])) == 1
+    assert call(ws_bytes=npipe * need - 1) == 5
+    assert call(O=arr([FAKE[9], ctypes.c_void_p(FAKE[4].value + 64), FAKE[11]])) == 4   # O[1] inside K[1]
+    assert call(M=ctypes.c_void_p(FAKE[0].value + 64)) == 4                              # state inside Q[0]

@@ -415,6 +415,59 @@ def test_stream_1m_launch_shape_chained():
         assert eo < 2e-2 and eM < 2e-2 and ez < 2e-2
 
 
+STREAM_CASES = [
+    # B, Hq, Hkv, N per call, d, L, dtype, calls, n_pipe
+    (1, 4, 4, 256, 64, 128, "bf16", 5, 3),
+    (2, 4, 2, 300, 128, 128, "bf16", 4, 2),    # GQA, ragged last segment of each call
+    (1, 2, 2, 48, 32, 16, "fp32", 3, 2),       # generic fp32 path
+    (1, 32, 32, 2048, 64, 2048, "bf16", 4, 3),  # the streaming workload's call shape
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES, ids=lambda c: "-".join(map(str, c[:9])))
+def test_fwd_stream_equals_chained_calls(case):
+    """infini_fwd_stream (memory phases chained on one stream, attention
+    phases overlapped on n_pipe others) gives the outputs and the final state
+    of the same calls made one after another with infini_attn_fwd, bit for
+    bit; the chained calls also match the oracle on the first call (small
+    cases; the streaming-shape case relies on the chained test above)."""
+    Bn, Hq, Hkv, N, d, L, dtype, n, npipe = case
+    log(f"fwd_stream {case}")
+    ins = [make(Bn, Hq, Hkv, N, d, dtype, 700 + 10 * t, with_state=(t == 0)) for t in range(n)]
+    beta = dev(ins[0][3])
+    qs = [dev(x[0], dtype) for x in ins]
+    ks = [dev(x[1], dtype) for x in ins]
+    vs = [dev(x[2], dtype) for x in ins]
+    M0, z0 = ins[0][4], ins[0][5]
+    # chained reference calls
+    Mr, zr = dev(M0), dev(z0)
+    refs = []
+    for t in range(n):
+        o, Mr, zr = B().attn_fwd(qs[t], ks[t], vs[t], beta, L, Mr, zr)
+        refs.append(o)
+    if Hq * N <= 4096:                    # the oracle in seconds
+        ro, rM, rz = O.forward(ins[0][0], ins[0][1], ins[0][2], ins[0][3], L, M0, z0)
+        assert rel(host(refs[0]), ro) < TOL[dtype]
+    # one pipelined call
+    p = B().problem(qs[0], ks[0], L)
+    ws = torch.empty(npipe * B().workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(q) for q in qs]
+    M, z = dev(M0).clone(), dev(z0).clone()
+    sm = torch.cuda.Stream()
+    sa = [torch.cuda.Stream() for _ in range(npipe)]
+    evs = [torch.cuda.Event() for _ in range(2 * npipe)]
+    cur = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    B().fwd_stream(p, qs, ks, vs, beta, M, z, outs, ws, npipe, sm, sa, evs)
+    cur.wait_stream(sm)
+    for s_ in sa:
+        cur.wait_stream(s_)
+    torch.cuda.synchronize()
+    for t in range(n):
+        assert torch.equal(outs[t], refs[t]), t
+    assert torch.equal(M, Mr) and torch.equal(z, zr)
+
+
 # ------------------------------------------------------------------ streaming decode
 
 DECODE_CASES = [
