@@ -360,18 +360,20 @@ def bench_stream(args):
             src, dst = st[i & 1], st[(i + 1) & 1]
             Bi.attn_fwd(q, k, v, b, w.seg_len, M0=src[0], z0=src[1], out=(O_, dst[0], dst[1], None), ws=ws)
 
-    NPIPE = 3                                   # workspace slots and attention streams in rotation
+    NPIPE = 3                                   # groups in flight / attention streams
+    GROUP = 4                                   # calls per attention launch
     # Pipelined: one infini_fwd_stream call per step issues all nl calls (the
-    # memory phases in order on sm, each attention phase on sa[i % NPIPE]).
-    wsp = torch.empty(NPIPE * Bi.workspace_bytes(p), dtype=torch.uint8, device=dev)
-    outs = [torch.empty_like(ins[0][0]) for _ in range(NPIPE)]
+    # memory phases in order on sm, the attention phases of each group of
+    # GROUP calls in one launch on sa[group % NPIPE]).
+    wsp = torch.empty(NPIPE * GROUP * Bi.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(ins[0][0]) for _ in range(NPIPE * GROUP)]
     Mp, zp = torch.zeros_like(st[0][0]), torch.zeros_like(st[0][1])
     sm = torch.cuda.Stream()
     sa = [torch.cuda.Stream() for _ in range(NPIPE)]
     evs = [torch.cuda.Event() for _ in range(2 * NPIPE)]
     calls = Bi.StreamCalls(p, [ins[i % nd][0] for i in range(nl)], [ins[i % nd][1] for i in range(nl)],
-                           [ins[i % nd][2] for i in range(nl)], b, Mp, zp, [outs[i % NPIPE] for i in range(nl)],
-                           wsp, NPIPE, sm, sa, evs)
+                           [ins[i % nd][2] for i in range(nl)], b, Mp, zp,
+                           [outs[i % (NPIPE * GROUP)] for i in range(nl)], wsp, NPIPE, GROUP, sm, sa, evs)
 
     def run_pipelined():
         cur = torch.cuda.current_stream()

@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
         L.infini_fwd_attend.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_size_t, _P]
         L.infini_fwd_stream.restype = ctypes.c_int
         L.infini_fwd_stream.argtypes = ([ctypes.POINTER(Problem), ctypes.c_int] + [_P] * 8 +
-                                        [ctypes.c_size_t, ctypes.c_int, _P, _P, _P])
+                                        [ctypes.c_size_t, ctypes.c_int, ctypes.c_int, _P, _P, _P])
         L.infini_decode.restype = ctypes.c_int
         L.infini_decode.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32] + [_P] * 12 + [ctypes.c_size_t, _P]
         _lib = L
@@ -191,7 +191,8 @@ class StreamCalls:
     shape `p` over the given per-call tensors, so that a loop that repeats the
     batch pays the marshalling once.  The tensors must stay alive."""
 
-    def __init__(self, p: Problem, qs, ks, vs, beta, M, z, outs, ws, n_pipe, mem_stream, att_streams, events):
+    def __init__(self, p: Problem, qs, ks, vs, beta, M, z, outs, ws, n_pipe, group, mem_stream, att_streams,
+                 events):
         n = len(qs)
         if not (len(ks) == len(vs) == len(outs) == n) or n < 1:
             raise ValueError("qs, ks, vs, outs: one tensor per call")
@@ -202,8 +203,8 @@ class StreamCalls:
                       (_P * n_pipe)(*[s.cuda_stream for s in att_streams]),
                       (_P * (2 * n_pipe))(*[_event_handle(e) for e in events]))
         self.args = (ctypes.byref(p), n, self._keep[0], self._keep[1], self._keep[2], _ptr(beta), _ptr(M), _ptr(z),
-                     self._keep[3], _ptr(ws), ws.numel(), n_pipe, _P(mem_stream.cuda_stream), self._keep[4],
-                     self._keep[5])
+                     self._keep[3], _ptr(ws), ws.numel(), n_pipe, group, _P(mem_stream.cuda_stream),
+                     self._keep[4], self._keep[5])
         self._p = p
 
     def __call__(self):
@@ -212,11 +213,12 @@ class StreamCalls:
             raise InfiniError(rc, "infini_fwd_stream")
 
 
-def fwd_stream(p: Problem, qs, ks, vs, beta, M, z, outs, ws, n_pipe, mem_stream, att_streams, events):
+def fwd_stream(p: Problem, qs, ks, vs, beta, M, z, outs, ws, n_pipe, group, mem_stream, att_streams, events):
     """infini_fwd_stream (see include/infini.h): len(qs) chained calls of shape
-    p, the memory phases on mem_stream and the attention phases overlapped on
-    att_streams; M, z hold the state and are updated in place."""
-    StreamCalls(p, qs, ks, vs, beta, M, z, outs, ws, n_pipe, mem_stream, att_streams, events)()
+    p in groups of `group`, the memory phases on mem_stream and each group's
+    attention phases on att_streams; M, z hold the state and are updated in
+    place."""
+    StreamCalls(p, qs, ks, vs, beta, M, z, outs, ws, n_pipe, group, mem_stream, att_streams, events)()
 
 
 def decode(q, k, v, beta, seg_len, pos, kcache, vcache, M=None, z=None, out=None, state_out=None, ws=None):

@@ -264,47 +264,71 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
   return INFINI_OK;
 }
 
+static_assert(INFINI_STREAM_MAX_GROUP <= infini::kFwdMaxGroup, "a group's calls fit one call table");
+
 infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, const void* const* Q,
                                   const void* const* K, const void* const* V, const float* beta,
                                   float* M, float* z, void* const* O, void* ws, size_t ws_bytes,
-                                  int n_pipe, void* mem_stream, void* const* att_streams,
+                                  int n_pipe, int group, void* mem_stream, void* const* att_streams,
                                   void* const* events) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
-  if (n_launches < 1 || n_pipe < 1) return INFINI_ERR_SHAPE;
+  if (n_launches < 1 || n_pipe < 1 || group < 1 || group > INFINI_STREAM_MAX_GROUP) return INFINI_ERR_SHAPE;
   if (!Q || !K || !V || !O || !beta || !M || !z || !ws || !att_streams || !events) return INFINI_ERR_NULL;
   const Geometry g = geometry(p);
   if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
   const FwdWs lay = fwd_layout(g);
-  if (ws_bytes / (size_t)n_pipe < lay.total) return INFINI_ERR_WORKSPACE;
+  if (ws_bytes / ((size_t)n_pipe * group) < lay.total) return INFINI_ERR_WORKSPACE;
+  for (int r = 0; r < n_pipe; ++r)
+    if (!att_streams[r]) return INFINI_ERR_NULL;
   for (int r = 0; r < 2 * n_pipe; ++r)
     if (!events[r]) return INFINI_ERR_NULL;
   const size_t eb = elem_bytes(g);
   const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
   const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
-  const size_t wsz = (size_t)n_pipe * lay.total;
+  const size_t wsz = (size_t)n_pipe * group * lay.total;
   for (int i = 0; i < n_launches; ++i) {
     if (!Q[i] || !K[i] || !V[i] || !O[i]) return INFINI_ERR_NULL;
     const Span outs[] = {{O[i], nq * eb}, {M, nM}, {z, nz}, {ws, wsz}};
     const Span ins[] = {{Q[i], nq * eb}, {K[i], nkv * eb}, {V[i], nkv * eb}, {beta, (size_t)g.Hq * 4}};
     if (any_overlap(outs, 4, ins, 4)) return INFINI_ERR_ALIAS;
   }
+  const bool mfma = infini::fwd_mfma_supported(g);
   hipStream_t sm = static_cast<hipStream_t>(mem_stream);
   char* base = static_cast<char*>(ws);
-  for (int i = 0; i < n_launches; ++i) {
-    const int r = i % n_pipe;
+  // Group k (calls k*group ..) uses pipeline stage r = k % n_pipe: workspace
+  // slots r*group .., attention stream r, events r and n_pipe + r.
+  for (int k = 0; k * group < n_launches; ++k) {
+    const int r = k % n_pipe;
+    const int i0 = k * group, nc = std::min(group, n_launches - i0);
     hipStream_t sa = static_cast<hipStream_t>(att_streams[r]);
     hipEvent_t ev_mem = static_cast<hipEvent_t>(events[r]);
     hipEvent_t ev_att = static_cast<hipEvent_t>(events[n_pipe + r]);
-    char* w = base + (size_t)r * lay.total;
-    // slot r is reused once the attention phase of call i - n_pipe is done
-    if (i >= n_pipe) TRY(hipStreamWaitEvent(sm, ev_att, 0));
-    TRY(run_fwd_chunk(g, lay, w, nullptr, K[i], V[i], nullptr, M, z, nullptr, M, z, nullptr, 0, g.S, sm,
-                      true, false));
+    char* slots = base + (size_t)r * group * lay.total;
+    // the stage's slots are reused once the attention of group k - n_pipe is done
+    if (k >= n_pipe) TRY(hipStreamWaitEvent(sm, ev_att, 0));
+    for (int j = 0; j < nc; ++j)
+      TRY(run_fwd_chunk(g, lay, slots + (size_t)j * lay.total, nullptr, K[i0 + j], V[i0 + j], nullptr, M, z,
+                        nullptr, M, z, nullptr, 0, g.S, sm, true, false));
     TRY(hipEventRecord(ev_mem, sm));
     TRY(hipStreamWaitEvent(sa, ev_mem, 0));
-    TRY(run_fwd_chunk(g, lay, w, Q[i], K[i], V[i], beta, nullptr, nullptr, O[i], nullptr, nullptr, nullptr, 0,
-                      g.S, sa, false, true));
+    if (mfma && nc > 1) {
+      infini::FwdCallTable tab{};
+      for (int j = 0; j < nc; ++j) {
+        char* w = slots + (size_t)j * lay.total;
+        tab.Q[j] = static_cast<const __bf16*>(Q[i0 + j]);
+        tab.K[j] = static_cast<const __bf16*>(K[i0 + j]);
+        tab.V[j] = static_cast<const __bf16*>(V[i0 + j]);
+        tab.O[j] = static_cast<__bf16*>(O[i0 + j]);
+        tab.MsnapT[j] = reinterpret_cast<const __bf16*>(w + lay.MsnapT);
+        tab.zsnap[j] = reinterpret_cast<const float*>(w + lay.zsnap);
+      }
+      TRY(infini::launch_fwd_mfma_group(g, tab, nc, beta, sa));
+    } else {
+      for (int j = 0; j < nc; ++j)
+        TRY(run_fwd_chunk(g, lay, slots + (size_t)j * lay.total, Q[i0 + j], K[i0 + j], V[i0 + j], beta, nullptr,
+                          nullptr, O[i0 + j], nullptr, nullptr, nullptr, 0, g.S, sa, false, true));
+    }
     TRY(hipEventRecord(ev_att, sa));
   }
   return INFINI_OK;

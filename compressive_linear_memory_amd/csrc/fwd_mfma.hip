@@ -66,13 +66,17 @@ __device__ __forceinline__ float pair_sum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+// GROUPED: one launch for the segments of several calls of the same shape
+// (spc segments each); segment sl of the launch is segment sl % spc of call
+// sl / spc, whose tensors and published state `tab` holds.
+template <int D, bool GROUPED>
 __global__ __launch_bounds__(FwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const float* __restrict__ beta,
                      const __bf16* __restrict__ MsnapT, const float* __restrict__ zsnap,
                      __bf16* __restrict__ O, float* __restrict__ lse,
-                     int Hq, int Hkv, int N, int L, int s_begin, int nseg, int nqt, float sl2) {
+                     int Hq, int Hkv, int N, int L, int s_begin, int nseg, int nqt, float sl2,
+                     FwdCallTable tab, int spc) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[C::LDS_ELEMS];
   __shared__ __attribute__((aligned(16))) float zs[D];
@@ -93,7 +97,15 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int bk = grp / nseg;                  // b * Hkv + kvh
   const int b = bk / Hkv, kvh = bk % Hkv;
   const int h = kvh * G + h_in;
-  const int s = s_begin + sl;
+  int s = s_begin + sl;                       // segment within its call
+  int sc = sl, nsc = nseg;                    // its index among the call's published states
+  if constexpr (GROUPED) {
+    const int c = sl / spc;
+    s = sc = sl % spc;
+    nsc = spc;
+    Q = tab.Q[c]; K = tab.K[c]; V = tab.V[c]; O = tab.O[c];
+    MsnapT = tab.MsnapT[c]; zsnap = tab.zsnap[c];
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -196,8 +208,8 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // outstanding global load before each tile's LDS reads.)
   constexpr int MPT = D * D / 8 / C::NT;  // 16-byte chunks of M^T per thread
   static_assert(D * D <= C::BUF, "M^T stage must fit one tile buffer");
-  const __bf16* msrc = MsnapT + ((size_t)bk * nseg + sl) * D * D;
-  const float* zsrc = zsnap + ((size_t)bk * nseg + sl) * D;
+  const __bf16* msrc = MsnapT + ((size_t)bk * nsc + sc) * D * D;
+  const float* zsrc = zsnap + ((size_t)bk * nsc + sc) * D;
   // Chunk i of a thread in wave w covers 1 KB block i*NW + w, i.e. rows
   // (i*NW + w) * RPB + lane / (D/8); (row & 7) does not depend on i, so every
   // load of a lane is one base address plus a constant.
@@ -397,11 +409,34 @@ static hipError_t fwd_mfma_t(const Geometry& g, const void* Q, const void* K, co
   const long long nwg = (long long)g.B * g.Hq * nseg * nqt;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D>), dim3((unsigned)nwg), dim3(FwdCfg<D>::NT), 0, st,
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, false>), dim3((unsigned)nwg), dim3(FwdCfg<D>::NT), 0, st,
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
                      static_cast<const __bf16*>(V), beta, static_cast<const __bf16*>(MsnapT), zsnap,
-                     static_cast<__bf16*>(O), lse, g.Hq, g.Hkv, g.N, g.L, s_begin, nseg, nqt, sl2);
+                     static_cast<__bf16*>(O), lse, g.Hq, g.Hkv, g.N, g.L, s_begin, nseg, nqt, sl2,
+                     FwdCallTable{}, 1);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t fwd_mfma_group_t(const Geometry& g, const FwdCallTable& tab, int ncalls, const float* beta,
+                                   hipStream_t st) {
+  const int nseg = ncalls * g.S;
+  const int nqt = (g.L + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
+  const long long nwg = (long long)g.B * g.Hq * nseg * nqt;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, true>), dim3((unsigned)nwg), dim3(FwdCfg<D>::NT), 0, st,
+                     nullptr, nullptr, nullptr, beta, nullptr, nullptr, nullptr, nullptr, g.Hq, g.Hkv, g.N,
+                     g.L, 0, nseg, nqt, sl2, tab, g.S);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_mfma_group(const Geometry& g, const FwdCallTable& tab, int ncalls, const float* beta,
+                                 hipStream_t st) {
+  if (g.dtype != 1 || ncalls < 1 || ncalls > kFwdMaxGroup) return hipErrorInvalidValue;
+  if (g.D == 128) return fwd_mfma_group_t<128>(g, tab, ncalls, beta, st);
+  if (g.D == 64) return fwd_mfma_group_t<64>(g, tab, ncalls, beta, st);
+  return hipErrorInvalidValue;
 }
 
 bool fwd_mfma_supported(const Geometry& g) { return g.dtype == 1 && (g.D == 64 || g.D == 128); }

@@ -43,6 +43,21 @@ hipError_t launch_fwd_mfma(const Geometry& g, const void* Q, const void* K, cons
                            const float* beta, const void* MsnapT, const float* zsnap, void* O,
                            float* lse, int s_begin, int s_end, hipStream_t st);
 
+// The attention phase of several calls of the same shape in one launch:
+// call c's tensors, and the state its memory phase published (MsnapT, zsnap
+// as launch_fwd_mfma reads them), in entry c.
+constexpr int kFwdMaxGroup = 8;
+struct FwdCallTable {
+  const __bf16* Q[kFwdMaxGroup];
+  const __bf16* K[kFwdMaxGroup];
+  const __bf16* V[kFwdMaxGroup];
+  __bf16* O[kFwdMaxGroup];
+  const __bf16* MsnapT[kFwdMaxGroup];
+  const float* zsnap[kFwdMaxGroup];
+};
+hipError_t launch_fwd_mfma_group(const Geometry& g, const FwdCallTable& tab, int ncalls, const float* beta,
+                                 hipStream_t st);
+
 // Fused short-segment forward (bf16, head_dim 64 or 128, seg_len <= 64): one
 // workgroup per (batch, K/V head) walks all segments with (M, z) on chip.
 bool fwd_short_supported(const Geometry& g);

@@ -165,33 +165,38 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
  * number of segments, at most INFINI_CHUNK_SEGMENTS), the state carried from
  * one call to the next (page "Hugging Face Infini-Attention 재현 분석",
  * section "Infini-Attention 메커니즘", step State Transfer), issued so that
- * they overlap: the memory phases (infini_fwd_memory) run in order on
- * mem_stream, and the attention phase of call i (infini_fwd_attend) runs on
- * att_streams[i % n_pipe] as soon as the memory phase of call i is done, in
- * workspace slot i % n_pipe.  Outputs and final state are bit-identical to
- * n_launches chained infini_attn_fwd calls.
+ * they overlap.  The calls go in groups of `group`: the memory phases
+ * (infini_fwd_memory) of every call run in order on mem_stream, and once a
+ * group's memory phases are done its attention phases (infini_fwd_attend)
+ * run on att_streams[k % n_pipe] for group k, in one launch for the whole
+ * group where the problem takes the matrix-core path.  Outputs and final
+ * state are bit-identical to n_launches chained infini_attn_fwd calls.
  *   Q, K, V, O   host arrays of n_launches device pointers; call i uses Q[i],
  *                K[i], V[i] and writes O[i], with the layouts of infini_attn_fwd
  *   beta         [q_heads] float32
  *   M, z         [batch][kv_heads][head_dim][head_dim] and [batch][kv_heads]
  *                [head_dim] float32: the state before call 0 on entry, updated
  *                in place by the memory phases on mem_stream
- *   ws           n_pipe * infini_fwd_workspace_bytes(p) bytes, one slot per
- *                pipeline stage (ws_bytes: its size)
+ *   ws           n_pipe * group * infini_fwd_workspace_bytes(p) bytes, one
+ *                slot per call of the groups in flight (ws_bytes: its size)
+ *   n_pipe       groups in flight (>= 1); group: calls per group, 1 to
+ *                INFINI_STREAM_MAX_GROUP
  *   mem_stream   stream of the memory phases; att_streams: n_pipe streams for
  *                the attention phases; events: 2 * n_pipe events of the
  *                caller's (timing may be disabled), used to order the phases
  * Inputs must be ready on every stream passed; the call returns once all work
  * is issued, and the caller orders later work after mem_stream and all
  * att_streams.  Errors are those of infini_attn_fwd, plus INFINI_ERR_SHAPE
- * for n_launches < 1, n_pipe < 1 or more than INFINI_CHUNK_SEGMENTS segments
- * per call; arguments are all checked before anything is issued.  Callers
- * that cannot allocate, or that issue from a tight loop, get one library
- * call per batch of calls instead of two per call. */
+ * for n_launches < 1, n_pipe < 1, group outside [1, INFINI_STREAM_MAX_GROUP]
+ * or more than INFINI_CHUNK_SEGMENTS segments per call; arguments are all
+ * checked before anything is issued.  One library call per batch of calls,
+ * and two events per group rather than per call, keep the host's issue cost
+ * per call low. */
+#define INFINI_STREAM_MAX_GROUP 8
 infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, const void* const* Q,
                                   const void* const* K, const void* const* V, const float* beta,
                                   float* M, float* z, void* const* O, void* ws, size_t ws_bytes,
-                                  int n_pipe, void* mem_stream, void* const* att_streams,
+                                  int n_pipe, int group, void* mem_stream, void* const* att_streams,
                                   void* const* events);
 
 /* Streaming decode: a few new tokens of the segment that is being filled.

@@ -180,18 +180,21 @@ def test_fwd_stream_validation(L):
     need = L.infini_fwd_workspace_bytes(ctypes.byref(p))
 
     def call(p=p, n=n, Q=Q, K=K, V=V, O=O, beta=FAKE[12], M=FAKE[13], z=FAKE[14], ws=ctypes.c_void_p(1 << 36),
-             ws_bytes=npipe * need, npipe=npipe, streams=streams, events=events):
-        return L.infini_fwd_stream(ctypes.byref(p), n, Q, K, V, beta, M, z, O, ws, ws_bytes, npipe, None,
+             ws_bytes=2 * npipe * need, npipe=npipe, group=2, streams=streams, events=events):
+        return L.infini_fwd_stream(ctypes.byref(p), n, Q, K, V, beta, M, z, O, ws, ws_bytes, npipe, group, None,
                                    streams, events)
 
     assert call(n=0) == 2
     assert call(npipe=0) == 2
+    assert call(group=0) == 2
+    assert call(group=9) == 2
+    assert call(streams=arr([FAKE[15], None])) == 1
     assert call(p=P(N=17 * 16)) == 2                            # more than 16 segments per call
     assert call(Q=None) == 1
     assert call(beta=None) == 1
     assert call(M=None) == 1
     assert call(events=arr([FAKE[17], None, FAKE[19], FAKE[18]])) == 1
     assert call(V=arr([FAKE[6], None, FAKE[8]])) == 1
-    assert call(ws_bytes=npipe * need - 1) == 5
+    assert call(ws_bytes=2 * npipe * need - 1) == 5
     assert call(O=arr([FAKE[9], ctypes.c_void_p(FAKE[4].value + 64), FAKE[11]])) == 4   # O[1] inside K[1]
     assert call(M=ctypes.c_void_p(FAKE[0].value + 64)) == 4                              # state inside Q[0]

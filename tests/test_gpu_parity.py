@@ -416,22 +416,24 @@ def test_stream_1m_launch_shape_chained():
 
 
 STREAM_CASES = [
-    # B, Hq, Hkv, N per call, d, L, dtype, calls, n_pipe
-    (1, 4, 4, 256, 64, 128, "bf16", 5, 3),
-    (2, 4, 2, 300, 128, 128, "bf16", 4, 2),    # GQA, ragged last segment of each call
-    (1, 2, 2, 48, 32, 16, "fp32", 3, 2),       # generic fp32 path
-    (1, 32, 32, 2048, 64, 2048, "bf16", 4, 3),  # the streaming workload's call shape
+    # B, Hq, Hkv, N per call, d, L, dtype, calls, n_pipe, group
+    (1, 4, 4, 256, 64, 128, "bf16", 5, 3, 1),
+    (1, 4, 4, 256, 64, 128, "bf16", 7, 2, 3),   # groups of 3, the last one short
+    (2, 4, 2, 300, 128, 128, "bf16", 5, 2, 2),  # GQA, ragged last segment of each call
+    (1, 2, 2, 48, 32, 16, "fp32", 5, 2, 2),     # generic fp32 path (attention per call)
+    (1, 32, 32, 2048, 64, 2048, "bf16", 9, 2, 4),  # the streaming workload's call shape
 ]
 
 
-@pytest.mark.parametrize("case", STREAM_CASES, ids=lambda c: "-".join(map(str, c[:9])))
+@pytest.mark.parametrize("case", STREAM_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_fwd_stream_equals_chained_calls(case):
-    """infini_fwd_stream (memory phases chained on one stream, attention
-    phases overlapped on n_pipe others) gives the outputs and the final state
+    """infini_fwd_stream (memory phases chained on one stream, the attention
+    phases of each group of calls in one launch, overlapped on n_pipe other
+    streams) gives the outputs and the final state
     of the same calls made one after another with infini_attn_fwd, bit for
     bit; the chained calls also match the oracle on the first call (small
     cases; the streaming-shape case relies on the chained test above)."""
-    Bn, Hq, Hkv, N, d, L, dtype, n, npipe = case
+    Bn, Hq, Hkv, N, d, L, dtype, n, npipe, group = case
     log(f"fwd_stream {case}")
     ins = [make(Bn, Hq, Hkv, N, d, dtype, 700 + 10 * t, with_state=(t == 0)) for t in range(n)]
     beta = dev(ins[0][3])
@@ -450,7 +452,7 @@ def test_fwd_stream_equals_chained_calls(case):
         assert rel(host(refs[0]), ro) < TOL[dtype]
     # one pipelined call
     p = B().problem(qs[0], ks[0], L)
-    ws = torch.empty(npipe * B().workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(npipe * group * B().workspace_bytes(p), dtype=torch.uint8, device="cuda")
     outs = [torch.empty_like(q) for q in qs]
     M, z = dev(M0).clone(), dev(z0).clone()
     sm = torch.cuda.Stream()
@@ -458,7 +460,7 @@ def test_fwd_stream_equals_chained_calls(case):
     evs = [torch.cuda.Event() for _ in range(2 * npipe)]
     cur = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    B().fwd_stream(p, qs, ks, vs, beta, M, z, outs, ws, npipe, sm, sa, evs)
+    B().fwd_stream(p, qs, ks, vs, beta, M, z, outs, ws, npipe, group, sm, sa, evs)
     cur.wait_stream(sm)
     for s_ in sa:
         cur.wait_stream(s_)
