@@ -363,9 +363,10 @@ def bench_stream(args):
     NPIPE = 3                                   # groups in flight / attention streams
     GROUP = 4                                   # calls per attention launch
     # Pipelined: one infini_fwd_stream call per step issues all nl calls (the
-    # memory phases in order on sm, the attention phases of each group of
-    # GROUP calls in one launch on sa[group % NPIPE]).
-    wsp = torch.empty(NPIPE * GROUP * Bi.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    # memory phases of each group of GROUP calls as one run on sm, their
+    # attention phases as one launch on sa[group % NPIPE]).
+    wsp = torch.empty(max(Bi.stream_workspace_bytes(p, NPIPE, GROUP), NPIPE * Bi.workspace_bytes(p)),
+                      dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(ins[0][0]) for _ in range(NPIPE * GROUP)]
     Mp, zp = torch.zeros_like(st[0][0]), torch.zeros_like(st[0][1])
     sm = torch.cuda.Stream()

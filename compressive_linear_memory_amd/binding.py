@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.infini_fwd_memory.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_size_t, _P]
         L.infini_fwd_attend.restype = ctypes.c_int
         L.infini_fwd_attend.argtypes = [ctypes.POINTER(Problem)] + [_P] * 7 + [ctypes.c_size_t, _P]
+        L.infini_fwd_stream_workspace_bytes.restype = ctypes.c_size_t
+        L.infini_fwd_stream_workspace_bytes.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, ctypes.c_int]
         L.infini_fwd_stream.restype = ctypes.c_int
         L.infini_fwd_stream.argtypes = ([ctypes.POINTER(Problem), ctypes.c_int] + [_P] * 8 +
                                         [ctypes.c_size_t, ctypes.c_int, ctypes.c_int, _P, _P, _P])
@@ -211,6 +213,10 @@ class StreamCalls:
         rc = lib().infini_fwd_stream(*self.args)
         if rc != 0:
             raise InfiniError(rc, "infini_fwd_stream")
+
+
+def stream_workspace_bytes(p: Problem, n_pipe: int, group: int) -> int:
+    return int(lib().infini_fwd_stream_workspace_bytes(ctypes.byref(p), n_pipe, group))
 
 
 def fwd_stream(p: Problem, qs, ks, vs, beta, M, z, outs, ws, n_pipe, group, mem_stream, att_streams, events):

@@ -53,7 +53,9 @@ size_t elem_bytes(const Geometry& g) { return g.dtype == INFINI_FP32 ? 4 : 2; }
 // ---- workspace layouts (byte offsets, 256-aligned)
 
 struct FwdWs { size_t Msnap, zsnap, MsnapT, dz, total; };
-FwdWs fwd_layout(const Geometry& g) {
+// parts: key splits per segment of the matrix-core memory phase (0: the
+// library's choice for g)
+FwdWs fwd_layout(const Geometry& g, int parts_of = 0) {
   const size_t C = (size_t)(g.S < kMaxChunkSegments ? g.S : kMaxChunkSegments);
   const size_t bk = (size_t)g.B * g.Hkv;
   FwdWs w;
@@ -61,7 +63,7 @@ FwdWs fwd_layout(const Geometry& g) {
   // The matrix-core path keeps its per-segment dM parts (one per key split)
   // where the generic path keeps fp32 snapshots.
   const bool mfma = infini::fwd_mfma_supported(g);
-  const size_t parts = mfma ? (size_t)infini::delta_splits(g) : 1;
+  const size_t parts = mfma ? (size_t)(parts_of > 0 ? parts_of : infini::delta_splits(g)) : 1;
   w.Msnap = off; off = align_up(off + bk * C * parts * g.D * g.D * 4);
   w.zsnap = off; off = align_up(off + bk * C * g.D * 4);
   w.MsnapT = off; off = align_up(off + (mfma ? bk * C * g.D * g.D * 2 : 0));
@@ -266,6 +268,31 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
 
 static_assert(INFINI_STREAM_MAX_GROUP <= infini::kFwdMaxGroup, "a group's calls fit one call table");
 
+namespace {
+// Workspace of one pipeline stage of infini_fwd_stream: on the matrix-core
+// path one forward workspace for a run of nc * S segments (nc <= group calls),
+// else one per call.
+size_t stream_stage_bytes(const Geometry& g, int group) {
+  size_t b = (size_t)group * fwd_layout(g).total;
+  if (infini::fwd_mfma_supported(g))
+    for (int nc = 1; nc <= group; ++nc) {
+      Geometry gg = g;
+      gg.S = nc * g.S;
+      b = std::max(b, fwd_layout(gg, infini::delta_splits(g)).total);
+    }
+  return b;
+}
+}  // namespace
+
+size_t infini_fwd_stream_workspace_bytes(const infini_problem_t* p, int n_pipe, int group) {
+  infini_status_t why;
+  if (!valid_problem(p, &why) || n_pipe < 1 || group < 1 || group > INFINI_STREAM_MAX_GROUP) return 0;
+  const Geometry g = geometry(p);
+  if (g.S > kMaxChunkSegments) return 0;
+  if (infini::fwd_mfma_supported(g) && group * g.S > kMaxChunkSegments) return 0;
+  return (size_t)n_pipe * stream_stage_bytes(g, group);
+}
+
 infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, const void* const* Q,
                                   const void* const* K, const void* const* V, const float* beta,
                                   float* M, float* z, void* const* O, void* ws, size_t ws_bytes,
@@ -276,9 +303,10 @@ infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, con
   if (n_launches < 1 || n_pipe < 1 || group < 1 || group > INFINI_STREAM_MAX_GROUP) return INFINI_ERR_SHAPE;
   if (!Q || !K || !V || !O || !beta || !M || !z || !ws || !att_streams || !events) return INFINI_ERR_NULL;
   const Geometry g = geometry(p);
-  if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
-  const FwdWs lay = fwd_layout(g);
-  if (ws_bytes / ((size_t)n_pipe * group) < lay.total) return INFINI_ERR_WORKSPACE;
+  const bool mfma = infini::fwd_mfma_supported(g);
+  if (g.S > kMaxChunkSegments || (mfma && group * g.S > kMaxChunkSegments)) return INFINI_ERR_SHAPE;
+  const size_t stage = stream_stage_bytes(g, group);
+  if (ws_bytes / (size_t)n_pipe < stage) return INFINI_ERR_WORKSPACE;
   for (int r = 0; r < n_pipe; ++r)
     if (!att_streams[r]) return INFINI_ERR_NULL;
   for (int r = 0; r < 2 * n_pipe; ++r)
@@ -286,47 +314,55 @@ infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, con
   const size_t eb = elem_bytes(g);
   const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
   const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
-  const size_t wsz = (size_t)n_pipe * group * lay.total;
+  const size_t wsz = (size_t)n_pipe * stage;
   for (int i = 0; i < n_launches; ++i) {
     if (!Q[i] || !K[i] || !V[i] || !O[i]) return INFINI_ERR_NULL;
     const Span outs[] = {{O[i], nq * eb}, {M, nM}, {z, nz}, {ws, wsz}};
     const Span ins[] = {{Q[i], nq * eb}, {K[i], nkv * eb}, {V[i], nkv * eb}, {beta, (size_t)g.Hq * 4}};
     if (any_overlap(outs, 4, ins, 4)) return INFINI_ERR_ALIAS;
   }
-  const bool mfma = infini::fwd_mfma_supported(g);
+  const FwdWs lay = fwd_layout(g);
   hipStream_t sm = static_cast<hipStream_t>(mem_stream);
   char* base = static_cast<char*>(ws);
   // Group k (calls k*group ..) uses pipeline stage r = k % n_pipe: workspace
-  // slots r*group .., attention stream r, events r and n_pipe + r.
+  // stage r, attention stream r, events r and n_pipe + r.
   for (int k = 0; k * group < n_launches; ++k) {
     const int r = k % n_pipe;
     const int i0 = k * group, nc = std::min(group, n_launches - i0);
     hipStream_t sa = static_cast<hipStream_t>(att_streams[r]);
     hipEvent_t ev_mem = static_cast<hipEvent_t>(events[r]);
     hipEvent_t ev_att = static_cast<hipEvent_t>(events[n_pipe + r]);
-    char* slots = base + (size_t)r * group * lay.total;
-    // the stage's slots are reused once the attention of group k - n_pipe is done
+    char* w = base + (size_t)r * stage;
+    // the stage's workspace is reused once the attention of group k - n_pipe is done
     if (k >= n_pipe) TRY(hipStreamWaitEvent(sm, ev_att, 0));
-    for (int j = 0; j < nc; ++j)
-      TRY(run_fwd_chunk(g, lay, slots + (size_t)j * lay.total, nullptr, K[i0 + j], V[i0 + j], nullptr, M, z,
-                        nullptr, M, z, nullptr, 0, g.S, sm, true, false));
-    TRY(hipEventRecord(ev_mem, sm));
-    TRY(hipStreamWaitEvent(sa, ev_mem, 0));
-    if (mfma && nc > 1) {
+    if (mfma) {
+      // one memory phase over the group's calls as one run of segments, then
+      // one attention launch for all of them
       infini::FwdCallTable tab{};
       for (int j = 0; j < nc; ++j) {
-        char* w = slots + (size_t)j * lay.total;
         tab.Q[j] = static_cast<const __bf16*>(Q[i0 + j]);
         tab.K[j] = static_cast<const __bf16*>(K[i0 + j]);
         tab.V[j] = static_cast<const __bf16*>(V[i0 + j]);
         tab.O[j] = static_cast<__bf16*>(O[i0 + j]);
-        tab.MsnapT[j] = reinterpret_cast<const __bf16*>(w + lay.MsnapT);
-        tab.zsnap[j] = reinterpret_cast<const float*>(w + lay.zsnap);
       }
-      TRY(infini::launch_fwd_mfma_group(g, tab, nc, beta, sa));
+      Geometry gg = g;
+      gg.S = nc * g.S;
+      const FwdWs lg = fwd_layout(gg, infini::delta_splits(g));
+      TRY(infini::launch_sweep_mfma_group(g, tab, nc, M, z, M, z, reinterpret_cast<float*>(w + lg.Msnap),
+                                          reinterpret_cast<float*>(w + lg.dz), w + lg.MsnapT,
+                                          reinterpret_cast<float*>(w + lg.zsnap), sm));
+      TRY(hipEventRecord(ev_mem, sm));
+      TRY(hipStreamWaitEvent(sa, ev_mem, 0));
+      TRY(infini::launch_fwd_mfma_group(g, tab, nc, beta, w + lg.MsnapT, reinterpret_cast<float*>(w + lg.zsnap),
+                                        sa));
     } else {
       for (int j = 0; j < nc; ++j)
-        TRY(run_fwd_chunk(g, lay, slots + (size_t)j * lay.total, Q[i0 + j], K[i0 + j], V[i0 + j], beta, nullptr,
+        TRY(run_fwd_chunk(g, lay, w + (size_t)j * lay.total, nullptr, K[i0 + j], V[i0 + j], nullptr, M, z,
+                          nullptr, M, z, nullptr, 0, g.S, sm, true, false));
+      TRY(hipEventRecord(ev_mem, sm));
+      TRY(hipStreamWaitEvent(sa, ev_mem, 0));
+      for (int j = 0; j < nc; ++j)
+        TRY(run_fwd_chunk(g, lay, w + (size_t)j * lay.total, Q[i0 + j], K[i0 + j], V[i0 + j], beta, nullptr,
                           nullptr, O[i0 + j], nullptr, nullptr, nullptr, 0, g.S, sa, false, true));
     }
     TRY(hipEventRecord(ev_att, sa));

@@ -68,7 +68,8 @@ __device__ __forceinline__ float pair_sum32(float x) {
 
 // GROUPED: one launch for the segments of several calls of the same shape
 // (spc segments each); segment sl of the launch is segment sl % spc of call
-// sl / spc, whose tensors and published state `tab` holds.
+// sl / spc, whose tensors `tab` holds.  The published states (MsnapT, zsnap)
+// are those of one memory phase over all the launch's segments.
 template <int D, bool GROUPED>
 __global__ __launch_bounds__(FwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -98,13 +99,10 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int b = bk / Hkv, kvh = bk % Hkv;
   const int h = kvh * G + h_in;
   int s = s_begin + sl;                       // segment within its call
-  int sc = sl, nsc = nseg;                    // its index among the call's published states
   if constexpr (GROUPED) {
     const int c = sl / spc;
-    s = sc = sl % spc;
-    nsc = spc;
+    s = sl % spc;
     Q = tab.Q[c]; K = tab.K[c]; V = tab.V[c]; O = tab.O[c];
-    MsnapT = tab.MsnapT[c]; zsnap = tab.zsnap[c];
   }
 
   const int tid = threadIdx.x;
@@ -208,8 +206,8 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // outstanding global load before each tile's LDS reads.)
   constexpr int MPT = D * D / 8 / C::NT;  // 16-byte chunks of M^T per thread
   static_assert(D * D <= C::BUF, "M^T stage must fit one tile buffer");
-  const __bf16* msrc = MsnapT + ((size_t)bk * nsc + sc) * D * D;
-  const float* zsrc = zsnap + ((size_t)bk * nsc + sc) * D;
+  const __bf16* msrc = MsnapT + ((size_t)bk * nseg + sl) * D * D;
+  const float* zsrc = zsnap + ((size_t)bk * nseg + sl) * D;
   // Chunk i of a thread in wave w covers 1 KB block i*NW + w, i.e. rows
   // (i*NW + w) * RPB + lane / (D/8); (row & 7) does not depend on i, so every
   // load of a lane is one base address plus a constant.
@@ -419,23 +417,23 @@ static hipError_t fwd_mfma_t(const Geometry& g, const void* Q, const void* K, co
 
 template <int D>
 static hipError_t fwd_mfma_group_t(const Geometry& g, const FwdCallTable& tab, int ncalls, const float* beta,
-                                   hipStream_t st) {
+                                   const void* MsnapT, const float* zsnap, hipStream_t st) {
   const int nseg = ncalls * g.S;
   const int nqt = (g.L + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
   const long long nwg = (long long)g.B * g.Hq * nseg * nqt;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL((fwd_mfma_kernel<D, true>), dim3((unsigned)nwg), dim3(FwdCfg<D>::NT), 0, st,
-                     nullptr, nullptr, nullptr, beta, nullptr, nullptr, nullptr, nullptr, g.Hq, g.Hkv, g.N,
-                     g.L, 0, nseg, nqt, sl2, tab, g.S);
+                     nullptr, nullptr, nullptr, beta, static_cast<const __bf16*>(MsnapT), zsnap, nullptr,
+                     nullptr, g.Hq, g.Hkv, g.N, g.L, 0, nseg, nqt, sl2, tab, g.S);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_mfma_group(const Geometry& g, const FwdCallTable& tab, int ncalls, const float* beta,
-                                 hipStream_t st) {
+                                 const void* MsnapT, const float* zsnap, hipStream_t st) {
   if (g.dtype != 1 || ncalls < 1 || ncalls > kFwdMaxGroup) return hipErrorInvalidValue;
-  if (g.D == 128) return fwd_mfma_group_t<128>(g, tab, ncalls, beta, st);
-  if (g.D == 64) return fwd_mfma_group_t<64>(g, tab, ncalls, beta, st);
+  if (g.D == 128) return fwd_mfma_group_t<128>(g, tab, ncalls, beta, MsnapT, zsnap, st);
+  if (g.D == 64) return fwd_mfma_group_t<64>(g, tab, ncalls, beta, MsnapT, zsnap, st);
   return hipErrorInvalidValue;
 }
 

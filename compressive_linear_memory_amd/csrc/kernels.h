@@ -43,20 +43,25 @@ hipError_t launch_fwd_mfma(const Geometry& g, const void* Q, const void* K, cons
                            const float* beta, const void* MsnapT, const float* zsnap, void* O,
                            float* lse, int s_begin, int s_end, hipStream_t st);
 
-// The attention phase of several calls of the same shape in one launch:
-// call c's tensors, and the state its memory phase published (MsnapT, zsnap
-// as launch_fwd_mfma reads them), in entry c.
+// Several calls of the same shape (g: one call) in one memory-phase launch
+// pair and one attention launch: call c's tensors in entry c.  The memory
+// phase treats the calls' segments as one run of ncalls * g.S segments (the
+// state carried through them in order), with delta_splits(g) parts per
+// segment as each call alone would have, and publishes its states as
+// launch_sweep_mfma does for that many segments; the attention launch reads
+// them from there.
 constexpr int kFwdMaxGroup = 8;
 struct FwdCallTable {
   const __bf16* Q[kFwdMaxGroup];
   const __bf16* K[kFwdMaxGroup];
   const __bf16* V[kFwdMaxGroup];
   __bf16* O[kFwdMaxGroup];
-  const __bf16* MsnapT[kFwdMaxGroup];
-  const float* zsnap[kFwdMaxGroup];
 };
+hipError_t launch_sweep_mfma_group(const Geometry& g, const FwdCallTable& tab, int ncalls, const float* M_in,
+                                   const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
+                                   void* MsnapT, float* zsnap, hipStream_t st);
 hipError_t launch_fwd_mfma_group(const Geometry& g, const FwdCallTable& tab, int ncalls, const float* beta,
-                                 hipStream_t st);
+                                 const void* MsnapT, const float* zsnap, hipStream_t st);
 
 // Fused short-segment forward (bf16, head_dim 64 or 128, seg_len <= 64): one
 // workgroup per (batch, K/V head) walks all segments with (M, z) on chip.

@@ -43,11 +43,14 @@ struct DeltaCfg {
   static constexpr int NKG = 256 / (D / 8);   // key groups
 };
 
-template <int D>
+// GROUPED: segment sl of the launch is segment sl % spc of call sl / spc,
+// whose K and V `tab` holds.
+template <int D, bool GROUPED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                        float* __restrict__ dM, float* __restrict__ dz,
-                       int N, int L, int s_begin, int nseg, int nsplit, int split_keys) {
+                       int N, int L, int s_begin, int nseg, int nsplit, int split_keys,
+                       FwdCallTable tab, int spc) {
   using C = DeltaCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[4 * C::TILE];   // 2 buffers x (K^T, V^T)
   static_assert(C::NKG * (D + 1) * 4 <= 4 * C::TILE * 2, "dz reduction must fit the tile buffers");
@@ -58,7 +61,12 @@ void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ 
   const int k_begin = (part % nsplit) * split_keys;
   const int sl = unit % nseg;
   const size_t bk = unit / nseg;
-  const int s = s_begin + sl;
+  int s = s_begin + sl;
+  if constexpr (GROUPED) {
+    const int c = sl / spc;
+    s = sl % spc;
+    K = tab.K[c]; V = tab.V[c];
+  }
   const size_t base = (bk * N + (size_t)s * L + k_begin) * D;
   // keys of this split (may be none); the last segment may be short
   L = max(0, min(min(L, N - s * L) - k_begin, split_keys));
@@ -259,9 +267,9 @@ static hipError_t sweep_mfma_t(const Geometry& g, const void* K, const void* V, 
   const int split_keys = (((g.L + nsplit - 1) / nsplit + 63) / 64) * 64;
   const long long parts = (long long)g.B * g.Hkv * nseg * nsplit;
   if (parts > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((delta_mfma_kernel<D>), dim3((unsigned)parts), dim3(256), 0, st,
+  hipLaunchKernelGGL((delta_mfma_kernel<D, false>), dim3((unsigned)parts), dim3(256), 0, st,
                      static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), dM, dz, g.N, g.L,
-                     s_begin, nseg, nsplit, split_keys);
+                     s_begin, nseg, nsplit, split_keys, FwdCallTable{}, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((D / SC_T) * (D / SC_T), g.B * g.Hkv);
@@ -280,6 +288,36 @@ int delta_splits(const Geometry& g) {
   const long long most = g.L / 128 > 1 ? g.L / 128 : 1;
   const long long n = want < most ? want : most;
   return (int)(n < 16 ? n : 16);
+}
+
+template <int D>
+static hipError_t sweep_mfma_group_t(const Geometry& g, const FwdCallTable& tab, int ncalls, const float* M_in,
+                                     const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
+                                     void* MsnapT, float* zsnap, hipStream_t st) {
+  // the calls' segments as one run, each split as a single call's memory
+  // phase splits it (same parts, same summation order)
+  const int nseg = ncalls * g.S;
+  const int nsplit = delta_splits(g);
+  const int split_keys = (((g.L + nsplit - 1) / nsplit + 63) / 64) * 64;
+  const long long parts = (long long)g.B * g.Hkv * nseg * nsplit;
+  if (parts > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((delta_mfma_kernel<D, true>), dim3((unsigned)parts), dim3(256), 0, st, nullptr, nullptr, dM,
+                     dz, g.N, g.L, 0, nseg, nsplit, split_keys, tab, g.S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((D / SC_T) * (D / SC_T), g.B * g.Hkv);
+  hipLaunchKernelGGL((scan_kernel<D>), grid, dim3(256), 0, st, dM, dz, M_in, z_in, M_out, z_out,
+                     static_cast<__bf16*>(MsnapT), zsnap, nseg, nsplit);
+  return hipGetLastError();
+}
+
+hipError_t launch_sweep_mfma_group(const Geometry& g, const FwdCallTable& tab, int ncalls, const float* M_in,
+                                   const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
+                                   void* MsnapT, float* zsnap, hipStream_t st) {
+  if (g.dtype != 1 || ncalls < 1 || ncalls > kFwdMaxGroup) return hipErrorInvalidValue;
+  if (g.D == 128) return sweep_mfma_group_t<128>(g, tab, ncalls, M_in, z_in, M_out, z_out, dM, dz, MsnapT, zsnap, st);
+  if (g.D == 64) return sweep_mfma_group_t<64>(g, tab, ncalls, M_in, z_in, M_out, z_out, dM, dz, MsnapT, zsnap, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_sweep_mfma(const Geometry& g, const void* K, const void* V, const float* M_in,

@@ -166,10 +166,12 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
  * one call to the next (page "Hugging Face Infini-Attention 재현 분석",
  * section "Infini-Attention 메커니즘", step State Transfer), issued so that
  * they overlap.  The calls go in groups of `group`: the memory phases
- * (infini_fwd_memory) of every call run in order on mem_stream, and once a
- * group's memory phases are done its attention phases (infini_fwd_attend)
- * run on att_streams[k % n_pipe] for group k, in one launch for the whole
- * group where the problem takes the matrix-core path.  Outputs and final
+ * (infini_fwd_memory) run in order on mem_stream, and once a group's memory
+ * phases are done its attention phases (infini_fwd_attend) run on
+ * att_streams[k % n_pipe] for group k.  Where the problem takes the
+ * matrix-core path a group's memory phases are one run over the group's
+ * segments and its attention phases one launch (then group * segments per
+ * call may not exceed INFINI_CHUNK_SEGMENTS).  Outputs and final
  * state are bit-identical to n_launches chained infini_attn_fwd calls.
  *   Q, K, V, O   host arrays of n_launches device pointers; call i uses Q[i],
  *                K[i], V[i] and writes O[i], with the layouts of infini_attn_fwd
@@ -177,8 +179,8 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
  *   M, z         [batch][kv_heads][head_dim][head_dim] and [batch][kv_heads]
  *                [head_dim] float32: the state before call 0 on entry, updated
  *                in place by the memory phases on mem_stream
- *   ws           n_pipe * group * infini_fwd_workspace_bytes(p) bytes, one
- *                slot per call of the groups in flight (ws_bytes: its size)
+ *   ws           infini_fwd_stream_workspace_bytes(p, n_pipe, group) bytes
+ *                (ws_bytes: its size)
  *   n_pipe       groups in flight (>= 1); group: calls per group, 1 to
  *                INFINI_STREAM_MAX_GROUP
  *   mem_stream   stream of the memory phases; att_streams: n_pipe streams for
@@ -187,12 +189,16 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
  * Inputs must be ready on every stream passed; the call returns once all work
  * is issued, and the caller orders later work after mem_stream and all
  * att_streams.  Errors are those of infini_attn_fwd, plus INFINI_ERR_SHAPE
- * for n_launches < 1, n_pipe < 1, group outside [1, INFINI_STREAM_MAX_GROUP]
- * or more than INFINI_CHUNK_SEGMENTS segments per call; arguments are all
+ * for n_launches < 1, n_pipe < 1, group outside [1, INFINI_STREAM_MAX_GROUP],
+ * more than INFINI_CHUNK_SEGMENTS segments per call, or (matrix-core path)
+ * per group; arguments are all
  * checked before anything is issued.  One library call per batch of calls,
  * and two events per group rather than per call, keep the host's issue cost
  * per call low. */
 #define INFINI_STREAM_MAX_GROUP 8
+/* Workspace bytes for infini_fwd_stream; 0 for an invalid problem or
+ * arguments. */
+size_t infini_fwd_stream_workspace_bytes(const infini_problem_t* p, int n_pipe, int group);
 infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, const void* const* Q,
                                   const void* const* K, const void* const* V, const float* beta,
                                   float* M, float* z, void* const* O, void* ws, size_t ws_bytes,

@@ -177,10 +177,13 @@ def test_fwd_stream_validation(L):
     Q = arr(FAKE[0:3]); K = arr(FAKE[3:6]); V = arr(FAKE[6:9]); O = arr(FAKE[9:12])
     streams = arr([FAKE[15], FAKE[16]])
     events = arr([FAKE[17], FAKE[18], FAKE[19], FAKE[18]])
-    need = L.infini_fwd_workspace_bytes(ctypes.byref(p))
+    need = L.infini_fwd_stream_workspace_bytes(ctypes.byref(p), npipe, 2)
+    assert need >= 2 * npipe * L.infini_fwd_workspace_bytes(ctypes.byref(p)) > 0
+    assert L.infini_fwd_stream_workspace_bytes(ctypes.byref(p), 0, 2) == 0
+    assert L.infini_fwd_stream_workspace_bytes(ctypes.byref(p), npipe, 9) == 0
 
     def call(p=p, n=n, Q=Q, K=K, V=V, O=O, beta=FAKE[12], M=FAKE[13], z=FAKE[14], ws=ctypes.c_void_p(1 << 36),
-             ws_bytes=2 * npipe * need, npipe=npipe, group=2, streams=streams, events=events):
+             ws_bytes=need, npipe=npipe, group=2, streams=streams, events=events):
         return L.infini_fwd_stream(ctypes.byref(p), n, Q, K, V, beta, M, z, O, ws, ws_bytes, npipe, group, None,
                                    streams, events)
 
@@ -195,6 +198,6 @@ def test_fwd_stream_validation(L):
     assert call(M=None) == 1
     assert call(events=arr([FAKE[17], None, FAKE[19], FAKE[18]])) == 1
     assert call(V=arr([FAKE[6], None, FAKE[8]])) == 1
-    assert call(ws_bytes=2 * npipe * need - 1) == 5
+    assert call(ws_bytes=need - 1) == 5
     assert call(O=arr([FAKE[9], ctypes.c_void_p(FAKE[4].value + 64), FAKE[11]])) == 4   # O[1] inside K[1]
     assert call(M=ctypes.c_void_p(FAKE[0].value + 64)) == 4                              # state inside Q[0]

@@ -427,9 +427,10 @@ STREAM_CASES = [
 
 @pytest.mark.parametrize("case", STREAM_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_fwd_stream_equals_chained_calls(case):
-    """infini_fwd_stream (memory phases chained on one stream, the attention
-    phases of each group of calls in one launch, overlapped on n_pipe other
-    streams) gives the outputs and the final state
+    """infini_fwd_stream (memory phases in order on one stream, each group
+    of calls' memory phases as one run and its attention phases as one
+    launch, overlapped on n_pipe other streams) gives the outputs and the
+    final state
     of the same calls made one after another with infini_attn_fwd, bit for
     bit; the chained calls also match the oracle on the first call (small
     cases; the streaming-shape case relies on the chained test above)."""
@@ -452,7 +453,7 @@ def test_fwd_stream_equals_chained_calls(case):
         assert rel(host(refs[0]), ro) < TOL[dtype]
     # one pipelined call
     p = B().problem(qs[0], ks[0], L)
-    ws = torch.empty(npipe * group * B().workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(B().stream_workspace_bytes(p, npipe, group), dtype=torch.uint8, device="cuda")
     outs = [torch.empty_like(q) for q in qs]
     M, z = dev(M0).clone(), dev(z0).clone()
     sm = torch.cuda.Stream()
