@@ -360,7 +360,9 @@ def bench_stream(args):
             src, dst = st[i & 1], st[(i + 1) & 1]
             Bi.attn_fwd(q, k, v, b, w.seg_len, M0=src[0], z0=src[1], out=(O_, dst[0], dst[1], None), ws=ws)
 
-    NPIPE = 3                                   # groups in flight / attention streams
+    NPIPE = 2                                   # groups in flight / attention streams (with the
+                                                # memory stream and the current one, within the 4
+                                                # hardware queues a process gets)
     GROUP = 4                                   # calls per attention launch
     # Pipelined: one infini_fwd_stream call per step issues all nl calls (the
     # memory phases of each group of GROUP calls as one run on sm, their
