@@ -184,7 +184,10 @@ void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ 
 
 // ---------------------------------------------------------------- scan
 
-constexpr int SC_T = 64;   // tile edge
+constexpr int SC_T = 32;   // tile edge: (D/32)^2 workgroups per (b, K/V head)
+constexpr int SC_E = SC_T * SC_T / 256;   // state elements per thread
+constexpr int SC_W = SC_T / SC_E;         // threads per tile row
+static_assert(SC_E == 4, "one float4 of state and one bf16x4 of the transposed snapshot per thread");
 
 template <int D>
 __global__ __launch_bounds__(256) void scan_kernel(
@@ -197,12 +200,12 @@ __global__ __launch_bounds__(256) void scan_kernel(
   const bool do_z = (blockIdx.x % TPR) == 0;
   const size_t bk = blockIdx.y;
   const int tid = threadIdx.x;
-  const int ra = tid >> 2, rc = (tid & 3) * 16;       // row a0+ra, columns c0+rc..+15
+  const int ra = tid / SC_W, rc = (tid % SC_W) * SC_E;   // row a0+ra, columns c0+rc..+SC_E-1
   const size_t eoff = (size_t)(a0 + ra) * D + c0 + rc;
 
-  float run[16];
+  float run[SC_E];
 #pragma unroll
-  for (int x = 0; x < 16; ++x) run[x] = M_in ? M_in[bk * D * D + eoff + x] : 0.f;
+  for (int x = 0; x < SC_E; ++x) run[x] = M_in ? M_in[bk * D * D + eoff + x] : 0.f;
   float zr = 0.f;
   if (do_z && tid < SC_T) zr = z_in ? z_in[bk * D + a0 + tid] : 0.f;
 
@@ -210,12 +213,12 @@ __global__ __launch_bounds__(256) void scan_kernel(
     const size_t unit = bk * nseg + sl;
     // dM_s = sum of its key-split parts, added in split order.  The loads are
     // issued before M_{s-1} is published so that they overlap the transpose.
-    float part[16];
+    float part[SC_E];
 #pragma unroll 4
     for (int sp = 0; sp < nsplit; ++sp) {
       const float* src = dM + (unit * nsplit + sp) * D * D + eoff;
 #pragma unroll
-      for (int x = 0; x < 16; x += 4) {
+      for (int x = 0; x < SC_E; x += 4) {
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + x);
         if (sp == 0) {
           part[x] = v[0]; part[x + 1] = v[1]; part[x + 2] = v[2]; part[x + 3] = v[3];
@@ -232,28 +235,25 @@ __global__ __launch_bounds__(256) void scan_kernel(
     }
     // publish M_{s-1} transposed in bf16: stage the fp32 tile, read columns
 #pragma unroll
-    for (int x = 0; x < 16; ++x) tr[ra][rc + x] = run[x];
+    for (int x = 0; x < SC_E; ++x) tr[ra][rc + x] = run[x];
     if (do_z && tid < SC_T) zsnap[unit * D + a0 + tid] = zr;
     __syncthreads();
     {
-      const int cc = tid >> 2, aa = (tid & 3) * 16;    // output row c0+cc, columns a0+aa..+15
+      const int cc = tid / SC_W, aa = (tid % SC_W) * SC_E;   // output row c0+cc, columns a0+aa..
       __bf16* dst = MsnapT + unit * D * D + (size_t)(c0 + cc) * D + a0 + aa;
+      bf16x4_t w;
 #pragma unroll
-      for (int x = 0; x < 16; x += 8) {
-        bf16x8_t w;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = (__bf16)tr[aa + x + e][cc];
-        *reinterpret_cast<bf16x8_t*>(dst + x) = w;
-      }
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)tr[aa + e][cc];
+      *reinterpret_cast<bf16x4_t*>(dst) = w;
     }
     __syncthreads();
 #pragma unroll
-    for (int x = 0; x < 16; ++x) run[x] += part[x];
+    for (int x = 0; x < SC_E; ++x) run[x] += part[x];
     if (do_z && tid < SC_T) zr += zpart;
   }
   if (M_out) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) M_out[bk * D * D + eoff + x] = run[x];
+    for (int x = 0; x < SC_E; ++x) M_out[bk * D * D + eoff + x] = run[x];
     if (do_z && tid < SC_T) z_out[bk * D + a0 + tid] = zr;
   }
 }
