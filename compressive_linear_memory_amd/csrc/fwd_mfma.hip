@@ -1,20 +1,23 @@
 // bf16 matrix-core forward of the Infini-attention segment kernel (gfx950).
 //
-// One workgroup = 4 waves = 128 query rows of one (batch, query head,
-// segment); each wave owns 32 query rows.  Per 64-key tile:
+// One workgroup = 8 waves = 256 query rows (head_dim 128; 4 waves = 128 rows
+// for head_dim 64) of one (batch, query head, segment); each wave owns 32
+// query rows, and all waves share each staged K/V tile.  Per 64-key tile:
 //   S^T = K Q^T          v_mfma_f32_32x32x16_bf16, K from LDS, Q^T in registers
 //   online softmax       base-2, row max/sum inside the lane plus one swap with
 //                        the lane 32 apart (page "Context Memorization for
 //                        Efficient Long Context Generation", section "방법론":
 //                        attention states over key sub-blocks merge exactly)
 //   O^T += V^T P^T       P^T straight from the S^T accumulators (no LDS trip);
-//                        V^T staged transposed in LDS
+//                        V^T staged transposed in LDS, its columns permuted so
+//                        that each operand is one 16-byte read
 // Working on the transposed products makes every lane own one query row, so
 // the softmax statistics need no cross-lane reduction beyond one exchange.
 //
 // Epilogue (page "Hugging Face Infini-Attention 재현 분석", section
 // "Infini-Attention 메커니즘", steps Memory Retrieval and Integration):
-//   A_mem^T = M_{s-1}^T sigma(Q)^T   on the matrix cores, M^T staged in LDS (bf16)
+//   A_mem^T = M_{s-1}^T sigma(Q)^T   on the matrix cores, M^T (bf16) staged in
+//                                    LDS through the free K/V staging registers
 //   den     = sigma(Q) z_{s-1} + eps  fp32 dot per lane
 //   O       = g A_mem + (1 - g) A_dot, rounded once to bf16
 //
