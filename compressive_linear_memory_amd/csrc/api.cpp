@@ -15,7 +15,9 @@ constexpr int kMaxChunkSegments = INFINI_CHUNK_SEGMENTS;   // segments whose sna
 
 bool valid_problem(const infini_problem_t* p, infini_status_t* why) {
   if (!p) { *why = INFINI_ERR_NULL; return false; }
-  if (p->batch <= 0 || p->q_heads <= 0 || p->kv_heads <= 0 || p->seq_len <= 0 ||
+  // batch = 0 or seq_len = 0 is an empty problem: nothing to compute, the
+  // state passes through
+  if (p->batch < 0 || p->q_heads <= 0 || p->kv_heads <= 0 || p->seq_len < 0 ||
       p->head_dim <= 0 || p->seg_len <= 0) { *why = INFINI_ERR_SHAPE; return false; }
   if (p->q_heads % p->kv_heads != 0) { *why = INFINI_ERR_SHAPE; return false; }
   if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) {
@@ -193,14 +195,15 @@ infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const 
                                 size_t ws_bytes, void* stream) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
-  if (!Q || !K || !V || !beta || !O || !M_S || !z_S) return INFINI_ERR_NULL;
-  if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
   const Geometry g = geometry(p);
-  const FwdWs lay = fwd_layout(g);
-  if (!ws || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   const size_t eb = elem_bytes(g);
   const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
   const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
+  // tensors of no elements may be null (torch gives them no storage)
+  if ((nq && (!Q || !O)) || (nkv && (!K || !V)) || !beta || (nM && (!M_S || !z_S))) return INFINI_ERR_NULL;
+  if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
+  const FwdWs lay = fwd_layout(g);
+  if ((lay.total && !ws) || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   const Span outs[] = {{O, nq * eb}, {M_S, nM}, {z_S, nz}, {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0},
                        {ws, lay.total}};
   const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
@@ -208,6 +211,12 @@ infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const 
   if (any_overlap(outs, 5, ins, 6)) return INFINI_ERR_ALIAS;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (g.N == 0) {                         // no tokens: the state passes through
+    TRY(infini::launch_state_copy(M_S, M0, nM / 4, st));
+    TRY(infini::launch_state_copy(z_S, z0, nz / 4, st));
+    return INFINI_OK;
+  }
+  if (g.B == 0) return INFINI_OK;
   if (infini::fwd_short_supported(g)) {   // state stays on chip for the whole call
     TRY(infini::launch_fwd_short(g, Q, K, V, beta, M0, z0, O, M_S, z_S, lse, st));
     return INFINI_OK;
@@ -228,18 +237,23 @@ infini_status_t infini_fwd_memory(const infini_problem_t* p, const void* K, cons
                                   void* ws, size_t ws_bytes, void* stream) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
-  if (!K || !V || !M_S || !z_S) return INFINI_ERR_NULL;
-  if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
   const Geometry g = geometry(p);
-  if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
-  const FwdWs lay = fwd_layout(g);
-  if (!ws || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   const size_t eb = elem_bytes(g);
   const size_t nkv = (size_t)g.B * g.Hkv * g.N * g.D;
   const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
+  if ((nkv && (!K || !V)) || (nM && (!M_S || !z_S))) return INFINI_ERR_NULL;
+  if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
+  if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
+  const FwdWs lay = fwd_layout(g);
+  if ((lay.total && !ws) || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   const Span outs[] = {{M_S, nM}, {z_S, nz}, {ws, lay.total}};
   const Span ins[] = {{K, nkv * eb}, {V, nkv * eb}, {M0, M0 ? nM : 0}, {z0, z0 ? nz : 0}};
   if (any_overlap(outs, 3, ins, 4)) return INFINI_ERR_ALIAS;
+  if (g.N == 0 || g.B == 0) {  // no tokens: the state passes through
+    TRY(infini::launch_state_copy(M_S, M0, nM / 4, static_cast<hipStream_t>(stream)));
+    TRY(infini::launch_state_copy(z_S, z0, nz / 4, static_cast<hipStream_t>(stream)));
+    return INFINI_OK;
+  }
   TRY(run_fwd_chunk(g, lay, static_cast<char*>(ws), nullptr, K, V, nullptr, M0, z0, nullptr, M_S, z_S,
                     nullptr, 0, g.S, static_cast<hipStream_t>(stream), true, false));
   return INFINI_OK;
@@ -250,17 +264,18 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
                                   const void* ws, size_t ws_bytes, void* stream) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
-  if (!Q || !K || !V || !beta || !O) return INFINI_ERR_NULL;
   const Geometry g = geometry(p);
-  if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
-  const FwdWs lay = fwd_layout(g);
-  if (!ws || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   const size_t eb = elem_bytes(g);
   const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
+  if ((nq && (!Q || !O)) || (nkv && (!K || !V)) || !beta) return INFINI_ERR_NULL;
+  if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
+  const FwdWs lay = fwd_layout(g);
+  if ((lay.total && !ws) || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   const Span outs[] = {{O, nq * eb}, {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0}};
   const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
                       {ws, lay.total}};
   if (any_overlap(outs, 2, ins, 5)) return INFINI_ERR_ALIAS;
+  if (g.N == 0 || g.B == 0) return INFINI_OK;
   TRY(run_fwd_chunk(g, lay, static_cast<char*>(const_cast<void*>(ws)), Q, K, V, beta, nullptr, nullptr, O,
                     nullptr, nullptr, lse, 0, g.S, static_cast<hipStream_t>(stream), false, true));
   return INFINI_OK;
@@ -301,6 +316,7 @@ infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, con
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
   if (n_launches < 1 || n_pipe < 1 || group < 1 || group > INFINI_STREAM_MAX_GROUP) return INFINI_ERR_SHAPE;
+  if (p->seq_len == 0 || p->batch == 0) return INFINI_OK;  // no tokens: M and z stay as they are
   if (!Q || !K || !V || !O || !beta || !M || !z || !ws || !att_streams || !events) return INFINI_ERR_NULL;
   const Geometry g = geometry(p);
   const bool mfma = infini::fwd_mfma_supported(g);
@@ -378,16 +394,17 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
   (void)lse;  // the generic backward recomputes the row statistics
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
-  if (!Q || !K || !V || !beta || !dO || !dQ || !dK || !dV || !dbeta) return INFINI_ERR_NULL;
-  if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
-  if ((dM_S == nullptr) != (dz_S == nullptr)) return INFINI_ERR_NULL;
-  if ((dM0 == nullptr) != (dz0 == nullptr)) return INFINI_ERR_NULL;
   const Geometry g = geometry(p);
-  const BwdWs lay = bwd_layout(g);
-  if (!ws || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   const size_t eb = elem_bytes(g);
   const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
   const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
+  // tensors of no elements may be null (torch gives them no storage)
+  if ((nq && (!Q || !dO || !dQ)) || (nkv && (!K || !V || !dK || !dV)) || !beta || !dbeta) return INFINI_ERR_NULL;
+  if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
+  if ((dM_S == nullptr) != (dz_S == nullptr)) return INFINI_ERR_NULL;
+  if ((dM0 == nullptr) != (dz0 == nullptr)) return INFINI_ERR_NULL;
+  const BwdWs lay = bwd_layout(g);
+  if ((lay.total && !ws) || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   const Span outs[] = {{dQ, nq * eb}, {dK, nkv * eb}, {dV, nkv * eb}, {dbeta, (size_t)g.Hq * 4},
                        {dM0, dM0 ? nM : 0}, {dz0, dz0 ? nz : 0}, {ws, lay.total}};
   const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
@@ -397,6 +414,14 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
   if (any_overlap(outs, 7, ins, 10)) return INFINI_ERR_ALIAS;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (g.N == 0 || g.B == 0) {             // no tokens: the state's gradient passes through
+    TRY(infini::launch_state_copy(dbeta, nullptr, (size_t)g.Hq, st));
+    if (dM0) {
+      TRY(infini::launch_state_copy(dM0, dM_S, nM / 4, st));
+      TRY(infini::launch_state_copy(dz0, dz_S, nz / 4, st));
+    }
+    return INFINI_OK;
+  }
   char* base = static_cast<char*>(ws);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   if (infini::bwd_short_supported(g)) {   // state and its gradient stay on chip
@@ -443,7 +468,11 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
 // caches and of the memory update that closes the segment).
 static bool decode_problem(const infini_problem_t* p, int32_t pos, Geometry* seg, infini_status_t* why) {
   if (!valid_problem(p, why)) return false;
-  if (pos < 0 || (int64_t)pos + p->seq_len > p->seg_len) { *why = INFINI_ERR_SHAPE; return false; }
+  // a decode step carries at least one token of at least one sequence
+  if (p->seq_len < 1 || p->batch < 1 || pos < 0 || (int64_t)pos + p->seq_len > p->seg_len) {
+    *why = INFINI_ERR_SHAPE;
+    return false;
+  }
   infini_problem_t q = *p;
   q.seq_len = p->seg_len;
   *seg = geometry(&q);

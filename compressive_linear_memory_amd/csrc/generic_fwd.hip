@@ -15,6 +15,8 @@
 // Efficient Long Context Generation", section "방법론": attention states over
 // key sub-blocks merge exactly), then retrieval and the gate fused in the
 // epilogue.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -274,6 +276,21 @@ hipError_t launch_fwd_generic(const Geometry& g, const void* Q, const void* K, c
   }
 #undef GF_CASE
   return hipErrorInvalidValue;
+}
+
+// dst[i] = src ? src[i] : 0 for i < n (the state an empty sequence passes
+// through unchanged, or its gradient).
+__global__ __launch_bounds__(256) void state_copy_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                                                         size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    dst[i] = src ? src[i] : 0.f;
+}
+
+hipError_t launch_state_copy(float* dst, const float* src, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dst, src, n);
+  return hipGetLastError();
 }
 
 }  // namespace infini

@@ -80,6 +80,9 @@ hipError_t launch_bwd_short(const Geometry& g, const void* Q, const void* K, con
 
 // Generic forward (fp32 vector arithmetic) over segments [s_begin, s_end),
 // reading the per-segment snapshots written by launch_sweep.
+// dst[i] = src ? src[i] : 0 for i < n.
+hipError_t launch_state_copy(float* dst, const float* src, size_t n, hipStream_t st);
+
 hipError_t launch_fwd_generic(const Geometry& g, const void* Q, const void* K, const void* V,
                               const float* beta, const float* Msnap, const float* zsnap,
                               void* O, float* lse, int s_begin, int s_end, hipStream_t st);

@@ -283,7 +283,7 @@ static hipError_t sweep_mfma_t(const Geometry& g, const void* K, const void* V, 
 // keys to reach about 512 workgroups.
 int delta_splits(const Geometry& g) {
   const long long units = (long long)g.B * g.Hkv * (g.S < INFINI_CHUNK_SEGMENTS ? g.S : INFINI_CHUNK_SEGMENTS);
-  if (units >= 256) return 1;
+  if (units == 0 || units >= 256) return 1;   // units = 0: an empty problem
   const long long want = (512 + units - 1) / units;
   const long long most = g.L / 128 > 1 ? g.L / 128 : 1;
   const long long n = want < most ? want : most;

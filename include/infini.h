@@ -65,7 +65,8 @@ extern "C" {
 typedef enum {
   INFINI_OK = 0,
   INFINI_ERR_NULL = 1,        /* a required pointer is NULL                                   */
-  INFINI_ERR_SHAPE = 2,       /* a dim <= 0 or q_heads % kv_heads != 0                      */
+  INFINI_ERR_SHAPE = 2,       /* a negative batch or seq_len, another dim <= 0, or
+                                 q_heads % kv_heads != 0                                       */
   INFINI_ERR_UNSUPPORTED = 3, /* head_dim not 32, 64 or 128, or unknown dtype                   */
   INFINI_ERR_ALIAS = 4,       /* an output buffer overlaps an input or another output          */
   INFINI_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns          */
@@ -74,7 +75,14 @@ typedef enum {
 
 typedef enum { INFINI_FP32 = 0, INFINI_BF16 = 1 } infini_dtype_t;
 
-/* One call's problem.  The carried state is always float32. */
+/* One call's problem.  The carried state is always float32.
+ *
+ * Empty problems: batch = 0 or seq_len = 0 is valid for every entry point
+ * except infini_decode.  Nothing is computed: a forward hands the state through
+ * (M_S = M0, z_S = z0, zeros when they are NULL; infini_fwd_stream leaves M and
+ * z as they are), a backward writes dbeta = 0 and dM0 = dM_S, dz0 = dz_S
+ * (zeros when NULL).  Pointers to tensors of no elements may be NULL, and a
+ * workspace of 0 bytes may be NULL. */
 typedef struct {
   int32_t batch;
   int32_t q_heads;

@@ -93,11 +93,43 @@ def test_fwd_half_state_is_null_error(L):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(Hkv=0), 2), (dict(Hq=3, Hkv=2), 2), (dict(B=0), 2), (dict(L=0), 2), (dict(N=-16), 2),
+    (dict(Hkv=0), 2), (dict(Hq=3, Hkv=2), 2), (dict(B=-1), 2), (dict(L=0), 2), (dict(N=-16), 2),
     (dict(d=48), 3), (dict(d=256), 3), (dict(dtype=7), 3),
 ])
 def test_fwd_shape_errors(L, kw, code):
     assert fwd(L, P(**kw)) == code
+
+
+def test_empty_batch_is_a_no_op(L):
+    """batch = 0: every forward entry point validates and returns ok without
+    issuing work (tensors of no elements may be NULL); decode needs a token."""
+    p = P(B=0)
+    assert L.infini_fwd_workspace_bytes(ctypes.byref(p)) == 0
+    # Q K V beta M0 z0 O M_S z_S lse ws: only beta is non-empty
+    assert fwd(L, p, [None, None, None, FAKE[3]] + [None] * 7, ws_bytes=0) == 0
+    assert fwd(L, p, [None, None, None, None] + [None] * 7, ws_bytes=0) == 1   # beta is [q_heads]
+    assert L.infini_fwd_memory(ctypes.byref(p), None, None, None, None, None, None, None, 0, None) == 0
+    assert L.infini_fwd_attend(ctypes.byref(p), None, None, None, FAKE[3], None, None, None, 0, None) == 0
+    one = (ctypes.c_void_p * 1)(None)
+    assert L.infini_fwd_stream(ctypes.byref(p), 1, one, one, one, None, None, None, one, None, 0, 1, 1,
+                               None, one, one) == 0
+    a = [FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], FAKE[5], None, None, FAKE[6], FAKE[7], FAKE[8]]
+    for q in (P(B=0, N=1), P(N=0)):
+        assert L.infini_decode(ctypes.byref(q), 0, *a, FAKE[10], 1 << 30, None) == 2
+        assert L.infini_decode_workspace_bytes(ctypes.byref(q)) == 0
+
+
+@pytest.mark.parametrize("dtype,d", [(0, 32), (0, 128), (1, 64), (1, 128)])
+def test_empty_problem_size_queries(L, dtype, d):
+    """Size queries of empty problems on every kernel path are well defined
+    (no division by the zero segment or batch count)."""
+    for kw in (dict(N=0), dict(B=0), dict(B=0, N=0), dict(N=0, L=2048)):
+        p = P(Hq=32, Hkv=8, d=d, dtype=dtype, **kw)
+        for f in (L.infini_fwd_workspace_bytes, L.infini_bwd_workspace_bytes):
+            f(ctypes.byref(p))
+        for g in (1, 4, 8):
+            L.infini_fwd_stream_workspace_bytes(ctypes.byref(p), 2, g)
+        assert L.infini_fwd_path(ctypes.byref(p)) is not None
 
 
 def test_fwd_workspace_too_small(L):

@@ -339,6 +339,34 @@ def test_errors_raise_with_real_tensors():
     del o
 
 
+@pytest.mark.parametrize("dtype,d", [("fp32", 32), ("bf16", 128)])
+def test_empty_sequence_passes_state_through(dtype, d):
+    """seq_len = 0: no tokens, so the forward hands the state on unchanged
+    (zeros for an empty memory) and the backward hands its gradient back
+    (dbeta = 0); batch = 0 gives empty outputs."""
+    log(f"empty sequence {dtype} d={d}")
+    Q, K, V, beta, _, _ = make(2, 4, 2, 0, d, dtype, seed=41)
+    M0, z0 = make(2, 4, 2, 48, d, dtype, seed=42, with_state=True)[4:]
+    o, M, z = run_fwd(Q, K, V, beta, 16, M0, z0, dtype)
+    assert o.shape == (2, 4, 0, d)
+    assert np.array_equal(host(M), M0) and np.array_equal(host(z), z0)
+    o, M, z = run_fwd(Q, K, V, beta, 16, None, None, dtype)
+    assert not host(M).any() and not host(z).any()
+    dMS = rnd((2, 2, d, d), 43, 1.0, "fp32")
+    dzS = rnd((2, 2, d), 44, 1.0, "fp32")
+    g = B().attn_bwd(dev(Q, dtype), dev(K, dtype), dev(V, dtype), dev(beta), 16, dev(Q, dtype),
+                     dev(M0), dev(z0), dM_S=dev(dMS), dz_S=dev(dzS), want_state_grads=True)
+    assert not host(g[3]).any()
+    assert np.array_equal(host(g[4]), dMS) and np.array_equal(host(g[5]), dzS)
+    g = B().attn_bwd(dev(Q, dtype), dev(K, dtype), dev(V, dtype), dev(beta), 16, dev(Q, dtype),
+                     want_state_grads=True)
+    assert not host(g[4]).any() and not host(g[5]).any()
+    Q, K, V, beta, _, _ = make(0, 4, 2, 64, d, dtype, seed=45)
+    o, M, z = run_fwd(Q, K, V, beta, 16, None, None, dtype)
+    assert o.shape == (0, 4, 64, d) and M.numel() == 0 and z.numel() == 0
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ the five workloads at full size
 
 def test_fwd_200m_full():
