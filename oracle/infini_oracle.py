@@ -103,8 +103,9 @@ def _dims(Q, K, seg_len):
 
 
 def num_segments(N, seg_len):
-    """Segments of a call: ceil(N / seg_len), the last one possibly shorter (R10)."""
-    assert N > 0 and seg_len > 0
+    """Segments of a call: ceil(N / seg_len), the last one possibly shorter
+    (R10); an empty call (N = 0) has none, so the state passes through (R13)."""
+    assert N >= 0 and seg_len > 0
     return -(-N // seg_len)
 
 

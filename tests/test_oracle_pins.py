@@ -196,6 +196,28 @@ def test_I6_chaining_single_segment_calls_equals_one_call():
     assert np.array_equal(M, M_all) and np.array_equal(z, z_all)
 
 
+def test_R13_empty_call_in_a_chain_changes_nothing():
+    """A call of no tokens between two calls: the chain's outputs, final state
+    and gradients equal those of the two calls alone (the recurrence takes no
+    step, so the empty call is the identity on the state and its gradient)."""
+    Q, K, V, beta = _problem(Hq=4, Hkv=2, N=10, seed=72)
+    L = 5
+    a, b, e = slice(0, 5), slice(5, 10), slice(5, 5)
+    _, M1, z1 = O.forward(Q[:, :, a], K[:, :, a], V[:, :, a], beta, L)
+    o_e, M_e, z_e = O.forward(Q[:, :, e], K[:, :, e], V[:, :, e], beta, L, M1, z1)
+    assert o_e.shape == (1, 4, 0, 4) and np.array_equal(M_e, M1) and np.array_equal(z_e, z1)
+    rng = np.random.default_rng(73)
+    dO = rng.standard_normal(Q[:, :, b].shape)
+    direct = O.backward(Q[:, :, b], K[:, :, b], V[:, :, b], beta, L, dO, M1, z1)
+    g_e = O.backward(Q[:, :, e], K[:, :, e], V[:, :, e], beta, L, Q[:, :, e], M1, z1,
+                     dM_S=direct["dM0"], dz_S=direct["dz0"])
+    assert np.array_equal(g_e["dM0"], direct["dM0"]) and np.array_equal(g_e["dz0"], direct["dz0"])
+    assert not g_e["dbeta"].any()
+    # the empty batch: outputs of no elements
+    o0, M0, z0 = O.forward(Q[:0], K[:0], V[:0], beta, L)
+    assert o0.shape == (0, 4, 10, 4) and M0.shape == (0, 2, 4, 4) and z0.shape == (0, 2, 4)
+
+
 # ----------------------------------------------------------- I7: direct form
 
 @pytest.mark.parametrize("with_state", [False, True])
