@@ -288,11 +288,26 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
     for (int h = kvh * G; h < (kvh + 1) * G; ++h) {
       const size_t qb = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
-      // stage Q rows of this head
-      for (int c = tid; c < C::BL * D / 8; c += 256) {
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *reinterpret_cast<bbf16x8*>(Qs + row * RS + col) =
-            *reinterpret_cast<const bbf16x8*>(Q + qb + (size_t)min(row, Ls - 1) * D + col);
+      // this lane's dO pieces (row q, columns cb*16 + 4g ..) are read now and
+      // used after the score and retrieval products
+      const __bf16* dop = dO + qb + (size_t)min(q, Ls - 1) * D;
+      bbf16x4 dov[C::DB];
+#pragma unroll
+      for (int cb = 0; cb < C::DB; ++cb) dov[cb] = *reinterpret_cast<const bbf16x4*>(dop + cb * 16 + 4 * g);
+      // stage Q rows of this head: every load issued before the first store
+      {
+        constexpr int QPT = C::BL * D / 8 / 256;
+        bbf16x8 qv[QPT];
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+          const int c = tid + i * 256, row = c / (D / 8), col = (c % (D / 8)) * 8;
+          qv[i] = *reinterpret_cast<const bbf16x8*>(Q + qb + (size_t)min(row, Ls - 1) * D + col);
+        }
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+          const int c = tid + i * 256, row = c / (D / 8), col = (c % (D / 8)) * 8;
+          *reinterpret_cast<bbf16x8*>(Qs + row * RS + col) = qv[i];
+        }
       }
       __syncthreads();
 
@@ -365,7 +380,6 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       // gate and retrieval gradients per (q, c = cb*16 + 4g + i)
       float bsum = 0.f, ddot = 0.f, dmem = 0.f;
       bbf16x8 dnp[C::KS], dap[C::KS];     // dnum, dA_dot packed like pb (c in place of keys)
-      const __bf16* dop = dO + qb + (size_t)min(q, Ls - 1) * D;
 #pragma unroll
       for (int cb = 0; cb < C::DB; ++cb) {
         bf32x4 nacc = {};
@@ -376,10 +390,9 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           nacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, sq[ks], nacc, 0, 0, 0);
           nacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, sq[ks], nacc, 0, 0, 0);
         }
-        const bbf16x4 dov = *reinterpret_cast<const bbf16x4*>(dop + cb * 16 + 4 * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float go = qok ? (float)dov[i] : 0.f;
+          const float go = qok ? (float)dov[cb][i] : 0.f;
           const float am = nacc[i] * inv_den;
           const float ad = oacc[cb][i] * inv_l;
           // the row sums pair with the rounded operands the products use, so
@@ -505,9 +518,11 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         }
       }
       if (tid < D) {
-        float t = 0.f;
-        for (int r = 0; r < C::BL; ++r) t += elu1((float)Qs[r * RS + tid]) * dds[r];
-        dzs[tid] += t;
+        // four independent partial sums so that the LDS reads overlap
+        float t4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < C::BL; ++r) t4[r & 3] += elu1((float)Qs[r * RS + tid]) * dds[r];
+        dzs[tid] += (t4[0] + t4[1]) + (t4[2] + t4[3]);
       }
       __syncthreads();
     }
