@@ -44,7 +44,9 @@
  * ordered by the caller.
  *
  * Errors: arguments are validated on the host before anything is launched;
- * on any error nothing is written.  INFINI_ERR_HIP reports a failed launch.
+ * on a validation error nothing is written.  INFINI_ERR_HIP reports a failed
+ * launch; launches of the same call issued before it may have run, so the
+ * outputs are then unspecified.
  */
 #ifndef INFINI_H
 #define INFINI_H
@@ -169,8 +171,9 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
                                   const void* V, const float* beta, void* O, float* lse,
                                   const void* ws, size_t ws_bytes, void* stream);
 
-/* Streaming forward: n_launches consecutive calls of shape *p (each a whole
- * number of segments, at most INFINI_CHUNK_SEGMENTS), the state carried from
+/* Streaming forward: n_launches consecutive calls of shape *p (each at most
+ * INFINI_CHUNK_SEGMENTS segments; a call whose seq_len is not a multiple of
+ * seg_len ends in a shorter segment, as in infini_attn_fwd), the state carried from
  * one call to the next (page "Hugging Face Infini-Attention 재현 분석",
  * section "Infini-Attention 메커니즘", step State Transfer), issued so that
  * they overlap.  The calls go in groups of `group`: the memory phases
@@ -242,8 +245,8 @@ infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, con
  *                update when the call completes the segment); it depends on
  *                T and the shape, not on pos
  *
- * Errors: INFINI_ERR_SHAPE for pos < 0 or pos + T > L (and the shape checks
- * of infini_attn_fwd); INFINI_ERR_NULL for a missing pointer, a half-given
+ * Errors: INFINI_ERR_SHAPE for T < 1, batch < 1, pos < 0 or pos + T > L (and
+ * the shape checks of infini_attn_fwd); INFINI_ERR_NULL for a missing pointer, a half-given
  * state, or a missing M_next/z_next on the completing call;
  * INFINI_ERR_WORKSPACE; INFINI_ERR_ALIAS when O, the caches, M_next, z_next
  * or ws overlap an input or each other.  Calls are asynchronous on stream. */
