@@ -136,6 +136,10 @@ FWD_CASES = [
     (2, 4, 2, 100, 64, 64, "bf16", True),      # fused short path, 36-token tail
     (1, 4, 4, 70, 128, 16, "bf16", True),      # fused short path, 6-token tail
     (1, 2, 2, 9, 64, 8, "bf16", False),        # fused short path, 1-token tail
+    # wide query groups (query heads per K/V head)
+    (1, 16, 2, 128, 128, 64, "bf16", True),    # fused short path, 8 heads per K/V head
+    (1, 32, 2, 96, 64, 32, "bf16", True),      # fused short path, 16 heads per K/V head
+    (1, 16, 1, 300, 128, 128, "bf16", True),   # long path, 16 heads per K/V head
 ]
 
 
@@ -164,6 +168,10 @@ BWD_CASES = [
     (2, 4, 2, 100, 64, 64, "bf16", True),      # fused short backward, 36-token tail
     (1, 4, 4, 70, 128, 16, "bf16", True),      # fused short backward, 6-token tail
     (1, 2, 1, 41, 128, 8, "bf16", False),      # fused short backward, 1-token tail
+    # wide query groups: 16 heads per K/V head is the fused backward's limit,
+    # 17 takes the generic backward
+    (1, 16, 1, 128, 128, 64, "bf16", True),
+    (1, 34, 2, 64, 64, 32, "bf16", False),
 ]
 
 
@@ -361,6 +369,15 @@ def test_empty_sequence_passes_state_through(dtype, d):
     g = B().attn_bwd(dev(Q, dtype), dev(K, dtype), dev(V, dtype), dev(beta), 16, dev(Q, dtype),
                      want_state_grads=True)
     assert not host(g[4]).any() and not host(g[5]).any()
+    # the phased forward: the memory phase hands the state on, attend writes nothing
+    q, k, v = dev(Q, dtype), dev(K, dtype), dev(V, dtype)
+    p = B().problem(q, k, 16)
+    ws = torch.empty(max(B().workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
+    Ms = torch.full((2, 2, d, d), 7.0, device="cuda")
+    zs = torch.full((2, 2, d), 7.0, device="cuda")
+    B().fwd_memory(p, k, v, dev(M0), dev(z0), Ms, zs, ws)
+    B().fwd_attend(p, q, k, v, dev(beta), torch.empty_like(q), None, ws)
+    assert np.array_equal(host(Ms), M0) and np.array_equal(host(zs), z0)
     Q, K, V, beta, _, _ = make(0, 4, 2, 64, d, dtype, seed=45)
     o, M, z = run_fwd(Q, K, V, beta, 16, None, None, dtype)
     assert o.shape == (0, 4, 64, d) and M.numel() == 0 and z.numel() == 0
