@@ -95,6 +95,8 @@ def test_fwd_half_state_is_null_error(L):
 @pytest.mark.parametrize("kw,code", [
     (dict(Hkv=0), 2), (dict(Hq=3, Hkv=2), 2), (dict(B=-1), 2), (dict(L=0), 2), (dict(N=-16), 2),
     (dict(d=48), 3), (dict(d=256), 3), (dict(dtype=7), 3),
+    # per-call counts past 32 bits and element counts past the 64-bit index budget
+    (dict(B=1 << 20, Hq=4096, Hkv=4096), 2), (dict(B=1 << 16, Hq=1 << 10, Hkv=1 << 10, N=1 << 20, d=128), 2),
 ])
 def test_fwd_shape_errors(L, kw, code):
     assert fwd(L, P(**kw)) == code
