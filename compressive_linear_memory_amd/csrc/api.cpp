@@ -101,6 +101,12 @@ hipError_t run_fwd_chunk(const Geometry& g, const FwdWs& lay, char* base, const 
 
 struct BwdWs { size_t Mst, zst, Msnap, zsnap, dMc, dzc, dMsnap, dzsnap, lse, Dd, dden, dnum, dbp, dbacc, dbs, total; };
 BwdWs bwd_layout(const Geometry& g) {
+  if (infini::bwd_short_supported(g)) {   // the fused backward needs only its dbeta partials
+    BwdWs w{};
+    w.dbs = 0;
+    w.total = align_up((size_t)g.B * g.Hq * 4);
+    return w;
+  }
   const size_t C = (size_t)(g.S < kMaxChunkSegments ? g.S : kMaxChunkSegments);
   const size_t bk = (size_t)g.B * g.Hkv;
   const size_t rows = (size_t)g.B * g.Hq * C * g.L;
@@ -158,7 +164,7 @@ const char* infini_status_string(infini_status_t s) {
   switch (s) {
     case INFINI_OK: return "ok";
     case INFINI_ERR_NULL: return "a required pointer is NULL";
-    case INFINI_ERR_SHAPE: return "invalid shape (dims must be > 0, q_heads % kv_heads == 0)";
+    case INFINI_ERR_SHAPE: return "invalid shape (batch, seq_len >= 0, other dims > 0, q_heads % kv_heads == 0, sizes within limits)";
     case INFINI_ERR_UNSUPPORTED: return "unsupported head_dim (32, 64, 128) or dtype";
     case INFINI_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case INFINI_ERR_WORKSPACE: return "workspace is NULL or too small";

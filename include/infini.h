@@ -101,7 +101,8 @@ typedef struct {
  * problem. */
 size_t infini_fwd_workspace_bytes(const infini_problem_t* p);
 
-/* Workspace bytes for infini_attn_bwd (does not grow with seq_len either). */
+/* Workspace bytes for infini_attn_bwd (does not grow with seq_len either;
+ * on the fused short-segment path only batch * q_heads floats). */
 size_t infini_bwd_workspace_bytes(const infini_problem_t* p);
 
 /* Forward.
