@@ -209,9 +209,11 @@ infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const 
   if ((nq && (!Q || !O)) || (nkv && (!K || !V)) || !beta || (nM && (!M_S || !z_S))) return INFINI_ERR_NULL;
   if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
   const FwdWs lay = fwd_layout(g);
-  if ((lay.total && !ws) || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
+  // the fused short-segment kernel keeps its state on chip and needs none
+  const size_t need = infini::fwd_short_supported(g) ? 0 : lay.total;
+  if ((need && !ws) || ws_bytes < need) return INFINI_ERR_WORKSPACE;
   const Span outs[] = {{O, nq * eb}, {M_S, nM}, {z_S, nz}, {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0},
-                       {ws, lay.total}};
+                       {ws, need}};
   const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
                       {M0, M0 ? nM : 0}, {z0, z0 ? nz : 0}};
   if (any_overlap(outs, 5, ins, 6)) return INFINI_ERR_ALIAS;

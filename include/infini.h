@@ -117,7 +117,11 @@ size_t infini_bwd_workspace_bytes(const infini_problem_t* p);
  *             calls ping-pong between two state buffers)
  *   lse       optional [batch][q_heads][seq_len] float32 output, for the
  *             backward; NULL to skip
- *   ws        device workspace of at least infini_fwd_workspace_bytes(p)
+ *   ws        device workspace of at least infini_fwd_workspace_bytes(p); on
+ *             the fused short-segment path (infini_fwd_path(p) returns
+ *             "mfma_bf16_short") the call uses none and ws may be NULL with
+ *             ws_bytes 0 (the size query still returns what the phased entry
+ *             points below need for the same problem)
  */
 infini_status_t infini_attn_fwd(const infini_problem_t* p,
                                 const void* Q, const void* K, const void* V,

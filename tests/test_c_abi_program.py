@@ -43,9 +43,15 @@ int main(void) {
   bad = p;
   bad.head_dim = 48;
   CHECK(infini_attn_fwd(&bad, a, a, a, fa, NULL, NULL, a, fo, fo, NULL, a, 0, NULL) == INFINI_ERR_UNSUPPORTED);
-  /* a workspace smaller than the query returns */
-  CHECK(infini_attn_fwd(&p, a, a, a, fa, NULL, NULL, a, fo, fo, NULL, a,
-                        infini_fwd_workspace_bytes(&p) - 1, NULL) == INFINI_ERR_WORKSPACE);
+  /* a workspace smaller than the query returns (long segments: memory phase
+     then attention phase) */
+  infini_problem_t lp = {1, 4, 2, 256, 64, 128, INFINI_BF16};
+  CHECK(infini_attn_fwd(&lp, a, a, a, fa, NULL, NULL, a, fo, fo, NULL, a,
+                        infini_fwd_workspace_bytes(&lp) - 1, NULL) == INFINI_ERR_WORKSPACE);
+  /* the fused short-segment forward needs none: with no workspace the call
+     gets as far as the aliasing check (every pointer here is the same) */
+  CHECK(strcmp(infini_fwd_path(&p), "mfma_bf16_short") == 0);
+  CHECK(infini_attn_fwd(&p, a, a, a, fa, NULL, NULL, a, fo, fo, NULL, NULL, 0, NULL) == INFINI_ERR_ALIAS);
   CHECK(infini_attn_bwd(&p, a, a, a, fa, NULL, NULL, NULL, NULL, NULL, NULL, a, a, a, fo, NULL, NULL,
                         a, 1u << 30, NULL) == INFINI_ERR_NULL);
   CHECK(infini_decode_workspace_bytes(&p) == 0); /* 64 new tokens do not fit a 16-token segment */

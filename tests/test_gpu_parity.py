@@ -331,6 +331,19 @@ def test_run_twice_bitwise_identical():
         assert torch.equal(x, y)
 
 
+def test_short_forward_needs_no_workspace():
+    """The fused short-segment forward keeps its state on chip: with no
+    workspace at all it gives the same bits as with one."""
+    Q, K, V, beta, M0, z0 = make(2, 8, 2, 256, 128, "bf16", seed=29, with_state=True)
+    q, k, v = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    assert B().fwd_path(B().problem(q, k, 64)) == "mfma_bf16_short"
+    a = B().attn_fwd(q, k, v, dev(beta), 64, dev(M0), dev(z0))
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
+    b = B().attn_fwd(q, k, v, dev(beta), 64, dev(M0), dev(z0), ws=none)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 def test_errors_raise_with_real_tensors():
     Q, K, V, beta, _, _ = make(1, 2, 2, 64, 32, "fp32", seed=31)
     q = dev(Q)
