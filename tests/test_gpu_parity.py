@@ -188,6 +188,36 @@ def test_backward_shapes(case):
 
 
 
+def _random_cases(n, seed):
+    """Seeded shapes across every kernel path: head dims 32/64/128, fp32 and
+    bf16, seg_len from 1 past the sequence length, ragged tails, GQA."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([32, 64, 128]))
+        dtype = "fp32" if d == 32 or rng.random() < 0.25 else "bf16"
+        Hkv = int(rng.integers(1, 4))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        N = int(rng.integers(1, 400))
+        L = int(rng.choice([1, 7, 16, 48, 64, 65, 128, 300, 512]))
+        out.append((int(rng.integers(1, 3)), Hq, Hkv, N, d, L, dtype, bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(16, 2026), ids=lambda c: "-".join(map(str, c)))
+def test_random_shapes_forward_and_backward(case):
+    """Forward and backward of seeded random shapes against the oracle."""
+    Bn, Hq, Hkv, N, d, L, dtype, st = case
+    Q, K, V, beta, M0, z0 = make(Bn, Hq, Hkv, N, d, dtype, seed=N * 7 + d, with_state=st)
+    check_fwd(Q, K, V, beta, L, M0, z0, dtype, "random")
+    dO = rnd(Q.shape, N + 5, 1.0, dtype)
+    dMS = dzS = None
+    if st:
+        dMS = np.random.default_rng(N).standard_normal(M0.shape).astype(np.float32) * 1e-2
+        dzS = np.random.default_rng(N + 1).standard_normal(z0.shape).astype(np.float32) * 1e-2
+    _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, "random")
+
+
 @pytest.mark.parametrize("case", [
     (1, 2, 2, 64, 32, 16, "fp32"),           # generic path
     (1, 4, 2, 600, 64, 256, "bf16"),         # long path, ragged tail
