@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <initializer_list>
+
 #include "../../include/infini.h"
 #include "kernels.h"
 
@@ -148,6 +150,14 @@ bool any_overlap(const Span* outs, int no, const Span* ins, int ni) {
   return false;
 }
 
+// The kernels move tensors in 16-byte vectors: every tensor pointer but
+// beta, dbeta and lse must be 16-byte aligned (NULL counts as aligned).
+bool misaligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return true;
+  return false;
+}
+
 infini_status_t hip_status(hipError_t e) { return e == hipSuccess ? INFINI_OK : INFINI_ERR_HIP; }
 
 #define TRY(expr)                                       \
@@ -165,7 +175,7 @@ const char* infini_status_string(infini_status_t s) {
     case INFINI_OK: return "ok";
     case INFINI_ERR_NULL: return "a required pointer is NULL";
     case INFINI_ERR_SHAPE: return "invalid shape (batch, seq_len >= 0, other dims > 0, q_heads % kv_heads == 0, sizes within limits)";
-    case INFINI_ERR_UNSUPPORTED: return "unsupported head_dim (32, 64, 128) or dtype";
+    case INFINI_ERR_UNSUPPORTED: return "unsupported head_dim (32, 64, 128), dtype, or a tensor pointer not 16-byte aligned";
     case INFINI_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case INFINI_ERR_WORKSPACE: return "workspace is NULL or too small";
     case INFINI_ERR_HIP: return "HIP launch or runtime error";
@@ -208,6 +218,7 @@ infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const 
   // tensors of no elements may be null (torch gives them no storage)
   if ((nq && (!Q || !O)) || (nkv && (!K || !V)) || !beta || (nM && (!M_S || !z_S))) return INFINI_ERR_NULL;
   if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
+  if (misaligned({Q, K, V, M0, z0, O, M_S, z_S, ws})) return INFINI_ERR_UNSUPPORTED;
   const FwdWs lay = fwd_layout(g);
   // the fused short-segment kernel keeps its state on chip and needs none
   const size_t need = infini::fwd_short_supported(g) ? 0 : lay.total;
@@ -251,6 +262,7 @@ infini_status_t infini_fwd_memory(const infini_problem_t* p, const void* K, cons
   const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
   if ((nkv && (!K || !V)) || (nM && (!M_S || !z_S))) return INFINI_ERR_NULL;
   if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
+  if (misaligned({K, V, M0, z0, M_S, z_S, ws})) return INFINI_ERR_UNSUPPORTED;
   if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
   const FwdWs lay = fwd_layout(g);
   if ((lay.total && !ws) || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
@@ -276,6 +288,7 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
   const size_t eb = elem_bytes(g);
   const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
   if ((nq && (!Q || !O)) || (nkv && (!K || !V)) || !beta) return INFINI_ERR_NULL;
+  if (misaligned({Q, K, V, O, ws})) return INFINI_ERR_UNSUPPORTED;
   if (g.S > kMaxChunkSegments) return INFINI_ERR_SHAPE;
   const FwdWs lay = fwd_layout(g);
   if ((lay.total && !ws) || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
@@ -326,6 +339,7 @@ infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, con
   if (n_launches < 1 || n_pipe < 1 || group < 1 || group > INFINI_STREAM_MAX_GROUP) return INFINI_ERR_SHAPE;
   if (p->seq_len == 0 || p->batch == 0) return INFINI_OK;  // no tokens: M and z stay as they are
   if (!Q || !K || !V || !O || !beta || !M || !z || !ws || !att_streams || !events) return INFINI_ERR_NULL;
+  if (misaligned({M, z, ws})) return INFINI_ERR_UNSUPPORTED;
   const Geometry g = geometry(p);
   const bool mfma = infini::fwd_mfma_supported(g);
   if (g.S > kMaxChunkSegments || (mfma && group * g.S > kMaxChunkSegments)) return INFINI_ERR_SHAPE;
@@ -341,6 +355,7 @@ infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, con
   const size_t wsz = (size_t)n_pipe * stage;
   for (int i = 0; i < n_launches; ++i) {
     if (!Q[i] || !K[i] || !V[i] || !O[i]) return INFINI_ERR_NULL;
+    if (misaligned({Q[i], K[i], V[i], O[i]})) return INFINI_ERR_UNSUPPORTED;
     const Span outs[] = {{O[i], nq * eb}, {M, nM}, {z, nz}, {ws, wsz}};
     const Span ins[] = {{Q[i], nq * eb}, {K[i], nkv * eb}, {V[i], nkv * eb}, {beta, (size_t)g.Hq * 4}};
     if (any_overlap(outs, 4, ins, 4)) return INFINI_ERR_ALIAS;
@@ -411,6 +426,7 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
   if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
   if ((dM_S == nullptr) != (dz_S == nullptr)) return INFINI_ERR_NULL;
   if ((dM0 == nullptr) != (dz0 == nullptr)) return INFINI_ERR_NULL;
+  if (misaligned({Q, K, V, M0, z0, dO, dM_S, dz_S, dQ, dK, dV, dM0, dz0, ws})) return INFINI_ERR_UNSUPPORTED;
   const BwdWs lay = bwd_layout(g);
   if ((lay.total && !ws) || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   const Span outs[] = {{dQ, nq * eb}, {dK, nkv * eb}, {dV, nkv * eb}, {dbeta, (size_t)g.Hq * 4},
@@ -513,6 +529,7 @@ infini_status_t infini_decode(const infini_problem_t* p, int32_t pos, const void
   if ((M == nullptr) != (z == nullptr)) return INFINI_ERR_NULL;
   const bool closes = pos + p->seq_len == p->seg_len;
   if (closes && (!M_next || !z_next)) return INFINI_ERR_NULL;
+  if (misaligned({Q, K, V, Kcache, Vcache, M, z, O, M_next, z_next, ws})) return INFINI_ERR_UNSUPPORTED;
   const FwdWs lay = fwd_layout(seg);
   const size_t need = decode_ws_bytes(seg, p->seq_len);
   if (!ws || ws_bytes < need) return INFINI_ERR_WORKSPACE;

@@ -36,6 +36,10 @@
  *   lse          : [batch][q_heads][seq_len]                float32, natural-log
  *                  log-sum-exp of each row's scaled local scores
  *
+ * Alignment: every tensor pointer except beta, dbeta and lse, and every
+ * workspace, must be 16-byte aligned (the kernels move 16-byte vectors);
+ * a misaligned one is refused with INFINI_ERR_UNSUPPORTED.
+ *
  * Ownership: the caller allocates and frees every buffer (inputs, outputs,
  * workspace).  The library never allocates, frees or synchronises; calls are
  * asynchronous on `stream` (a hipStream_t, NULL = the default stream).  The
@@ -69,7 +73,8 @@ typedef enum {
   INFINI_ERR_NULL = 1,        /* a required pointer is NULL                                   */
   INFINI_ERR_SHAPE = 2,       /* a negative batch or seq_len, another dim <= 0, or
                                  q_heads % kv_heads != 0                                       */
-  INFINI_ERR_UNSUPPORTED = 3, /* head_dim not 32, 64 or 128, or unknown dtype                   */
+  INFINI_ERR_UNSUPPORTED = 3, /* head_dim not 32, 64 or 128, unknown dtype, or a tensor pointer
+                                 (any but beta, dbeta, lse) not 16-byte aligned                */
   INFINI_ERR_ALIAS = 4,       /* an output buffer overlaps an input or another output          */
   INFINI_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns          */
   INFINI_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed                      */

@@ -134,6 +134,36 @@ def test_empty_problem_size_queries(L, dtype, d):
         assert L.infini_fwd_path(ctypes.byref(p)) is not None
 
 
+def test_misaligned_tensor_pointers_are_refused(L):
+    """Tensors move in 16-byte vectors: a tensor pointer off a 16-byte boundary
+    is refused (3) before anything is issued; beta, dbeta and lse may sit
+    anywhere (here the call then fails later, on its workspace)."""
+    off = lambda i, k: ctypes.c_void_p(FAKE[i].value + k)
+    for i in (0, 1, 2, 4, 6, 7, 10):              # Q K V M0 O M_S ws
+        a = list(FAKE[:11])
+        a[i] = off(i, 2)
+        if i == 4:
+            a[5] = off(5, 2)                       # M0 and z0 come together
+        assert fwd(L, P(), a) == 3, i
+    a = list(FAKE[:11])
+    a[3] = off(3, 4)                               # beta
+    a[9] = off(9, 4)                               # lse
+    assert fwd(L, P(), a, ws_bytes=1) == 5
+    p = P()
+    b = list(FAKE[:17])
+    b[10] = off(10, 8)                             # dQ
+    assert L.infini_attn_bwd(ctypes.byref(p), *b[:16], b[16], 1 << 40, None) == 3
+    b = list(FAKE[:17])
+    b[13] = off(13, 4)                             # dbeta may sit anywhere: fails on the workspace
+    assert L.infini_attn_bwd(ctypes.byref(p), *b[:16], b[16], 1, None) == 5
+    assert L.infini_fwd_memory(ctypes.byref(p), FAKE[1], off(2, 6), None, None, FAKE[7], FAKE[8], FAKE[10],
+                               1 << 40, None) == 3
+    assert L.infini_fwd_attend(ctypes.byref(p), FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[6], None,
+                               off(10, 1), 1 << 40, None) == 3
+    d = [FAKE[0], FAKE[1], FAKE[2], FAKE[3], off(4, 2), FAKE[5], None, None, FAKE[6], FAKE[7], FAKE[8]]
+    assert L.infini_decode(ctypes.byref(P(N=3)), 0, *d, FAKE[10], 1 << 30, None) == 3   # Kcache
+
+
 def test_fwd_workspace_too_small(L):
     need = L.infini_fwd_workspace_bytes(ctypes.byref(P()))
     assert fwd(L, P(), ws_bytes=need - 1) == 5
@@ -235,3 +265,4 @@ def test_fwd_stream_validation(L):
     assert call(ws_bytes=need - 1) == 5
     assert call(O=arr([FAKE[9], ctypes.c_void_p(FAKE[4].value + 64), FAKE[11]])) == 4   # O[1] inside K[1]
     assert call(M=ctypes.c_void_p(FAKE[0].value + 64)) == 4                              # state inside Q[0]
+    assert call(K=arr([FAKE[3], ctypes.c_void_p(FAKE[4].value + 2), FAKE[5]])) == 3     # K[1] misaligned
