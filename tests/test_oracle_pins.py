@@ -218,6 +218,27 @@ def test_R13_empty_call_in_a_chain_changes_nothing():
     assert o0.shape == (0, 4, 10, 4) and M0.shape == (0, 2, 4, 4) and z0.shape == (0, 2, 4)
 
 
+@pytest.mark.parametrize("N,L", [(12, 4), (10, 4), (7, 16)])
+def test_row_logsumexp_bruteforce(N, L):
+    """The oracle's per-row log-sum-exp: for each row, the natural log of the
+    sum over the causal keys of its own segment of exp(q . k / sqrt d),
+    written out with Python loops and math.exp (ragged last segments
+    included); and the gate-closed output equals sum_j exp(s_ij - lse_i) v_j."""
+    Q, K, V, beta = _problem(Hq=2, Hkv=1, N=N, seed=91)
+    d = Q.shape[-1]
+    _, _, _, lse = O.forward(Q, K, V, np.full(2, -np.inf), L, want_lse=True)
+    o_closed, _, _ = O.forward(Q, K, V, np.full(2, -np.inf), L)
+    for h in range(2):
+        for i in range(N):
+            s0 = (i // L) * L
+            scores = [sum(Q[0, h, i, e] * K[0, 0, j, e] for e in range(d)) / math.sqrt(d)
+                      for j in range(s0, i + 1)]
+            ref = math.log(sum(math.exp(x) for x in scores))
+            assert abs(lse[0, h, i] - ref) < 1e-12 * max(1.0, abs(ref))
+            out = sum(math.exp(x - lse[0, h, i]) * V[0, 0, s0 + t] for t, x in enumerate(scores))
+            assert np.allclose(o_closed[0, h, i], out, rtol=1e-12, atol=1e-13)
+
+
 # ----------------------------------------------------------- I7: direct form
 
 @pytest.mark.parametrize("with_state", [False, True])
