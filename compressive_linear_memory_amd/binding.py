@@ -48,7 +48,8 @@ def lib() -> ctypes.CDLL:
         L.infini_status_string.argtypes = [ctypes.c_int]
         L.infini_version.restype = ctypes.c_int
         L.infini_version.argtypes = []
-        for fn in ("infini_fwd_workspace_bytes", "infini_bwd_workspace_bytes", "infini_decode_workspace_bytes"):
+        for fn in ("infini_fwd_workspace_bytes", "infini_bwd_workspace_bytes", "infini_decode_workspace_bytes",
+                   "infini_fwd_saved_bytes"):
             getattr(L, fn).restype = ctypes.c_size_t
             getattr(L, fn).argtypes = [ctypes.POINTER(Problem)]
         L.infini_attn_fwd.restype = ctypes.c_int
@@ -84,6 +85,11 @@ def problem(q: torch.Tensor, k: torch.Tensor, seg_len: int) -> Problem:
 def workspace_bytes(p: Problem, backward: bool = False) -> int:
     fn = lib().infini_bwd_workspace_bytes if backward else lib().infini_fwd_workspace_bytes
     return int(fn(ctypes.byref(p)))
+
+
+def saved_bytes(p: Problem) -> int:
+    """Bytes of the forward's saved row statistics (its lse output)."""
+    return int(lib().infini_fwd_saved_bytes(ctypes.byref(p)))
 
 
 def _ptr(t):
@@ -123,6 +129,9 @@ def attn_fwd(q, k, v, beta, seg_len, M0=None, z0=None, want_lse=False, out=None,
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if want_lse else None
     else:
         O, M_S, z_S, lse = out
+        for name, t, dt, shp in (("O", O, q.dtype, q.shape), ("M_S", M_S, torch.float32, (B, Hkv, d, d)),
+                                 ("z_S", z_S, torch.float32, (B, Hkv, d)), ("lse", lse, torch.float32, (B, Hq, N))):
+            _check(name, t, dt, shp, dev)
     if ws is None:
         ws = torch.empty(max(workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
     rc = lib().infini_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
@@ -133,8 +142,11 @@ def attn_fwd(q, k, v, beta, seg_len, M0=None, z0=None, want_lse=False, out=None,
 
 
 def attn_bwd(q, k, v, beta, seg_len, dO, M0=None, z0=None, lse=None, dM_S=None, dz_S=None,
-             want_state_grads=False, ws=None):
-    """dQ, dK, dV, dbeta (and dM0, dz0 if want_state_grads); see include/infini.h."""
+             want_state_grads=False, ws=None, out=None):
+    """dQ, dK, dV, dbeta (and dM0, dz0 if want_state_grads); see include/infini.h.
+
+    `out` may hold preallocated (dQ, dK, dV, dbeta, dM0, dz0) tensors (dM0 and
+    dz0 None unless want_state_grads)."""
     p = problem(q, k, seg_len)
     dev = q.device
     B, Hq, N, d = q.shape
@@ -146,12 +158,20 @@ def attn_bwd(q, k, v, beta, seg_len, dO, M0=None, z0=None, lse=None, dM_S=None, 
                              ("dM_S", dM_S, torch.float32, (B, Hkv, d, d)),
                              ("dz_S", dz_S, torch.float32, (B, Hkv, d))):
         _check(name, t, dt, shp, dev)
-    dQ = torch.empty_like(q)
-    dK = torch.empty_like(k)
-    dV = torch.empty_like(v)
-    dbeta = torch.empty((Hq,), dtype=torch.float32, device=dev)
-    dM0 = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=dev) if want_state_grads else None
-    dz0 = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev) if want_state_grads else None
+    if out is None:
+        dQ = torch.empty_like(q)
+        dK = torch.empty_like(k)
+        dV = torch.empty_like(v)
+        dbeta = torch.empty((Hq,), dtype=torch.float32, device=dev)
+        dM0 = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=dev) if want_state_grads else None
+        dz0 = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev) if want_state_grads else None
+    else:
+        dQ, dK, dV, dbeta, dM0, dz0 = out
+        for name, t, dt, shp in (("dQ", dQ, q.dtype, q.shape), ("dK", dK, q.dtype, k.shape),
+                                 ("dV", dV, q.dtype, v.shape), ("dbeta", dbeta, torch.float32, (Hq,)),
+                                 ("dM0", dM0, torch.float32, (B, Hkv, d, d)),
+                                 ("dz0", dz0, torch.float32, (B, Hkv, d))):
+            _check(name, t, dt, shp, dev)
     if ws is None:
         ws = torch.empty(max(workspace_bytes(p, backward=True), 1), dtype=torch.uint8, device=dev)
     rc = lib().infini_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),

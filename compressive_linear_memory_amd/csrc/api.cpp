@@ -37,7 +37,9 @@ Geometry geometry(const infini_problem_t* p) {
   Geometry g;
   g.B = p->batch; g.Hq = p->q_heads; g.Hkv = p->kv_heads; g.N = p->seq_len;
   g.D = p->head_dim; g.L = p->seg_len; g.dtype = p->dtype;
-  g.S = (p->seq_len + p->seg_len - 1) / p->seg_len;   // the last segment may be shorter
+  // the last segment may be shorter; formed in 64 bits (seq_len + seg_len
+  // can exceed the 32-bit range)
+  g.S = (int)(((int64_t)p->seq_len + p->seg_len - 1) / p->seg_len);
   return g;
 }
 
@@ -171,7 +173,10 @@ infini_status_t hip_status(hipError_t e) { return e == hipSuccess ? INFINI_OK : 
 extern "C" {
 
 const char* infini_status_string(infini_status_t s) {
-  switch (s) {
+  // a C caller may pass any int; read the bits rather than the enum value
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case INFINI_OK: return "ok";
     case INFINI_ERR_NULL: return "a required pointer is NULL";
     case INFINI_ERR_SHAPE: return "invalid shape (batch, seq_len >= 0, other dims > 0, q_heads % kv_heads == 0, sizes within limits)";
@@ -197,6 +202,12 @@ size_t infini_fwd_workspace_bytes(const infini_problem_t* p) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return 0;
   return fwd_layout(geometry(p)).total;
+}
+
+size_t infini_fwd_saved_bytes(const infini_problem_t* p) {
+  infini_status_t why;
+  if (!valid_problem(p, &why)) return 0;
+  return (size_t)p->batch * p->q_heads * p->seq_len * 4;
 }
 
 size_t infini_bwd_workspace_bytes(const infini_problem_t* p) {
@@ -360,6 +371,14 @@ infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, con
     const Span ins[] = {{Q[i], nq * eb}, {K[i], nkv * eb}, {V[i], nkv * eb}, {beta, (size_t)g.Hq * 4}};
     if (any_overlap(outs, 4, ins, 4)) return INFINI_ERR_ALIAS;
   }
+  // Graph capture of this schedule is not supported: the streams are joined
+  // by events that each group records again, and a capture of that pattern
+  // has ended a process.  Refused before anything is issued.
+  for (int r = -1; r < n_pipe; ++r) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    TRY(hipStreamIsCapturing(static_cast<hipStream_t>(r < 0 ? mem_stream : att_streams[r]), &cs));
+    if (cs != hipStreamCaptureStatusNone) return INFINI_ERR_UNSUPPORTED;
+  }
   const FwdWs lay = fwd_layout(g);
   hipStream_t sm = static_cast<hipStream_t>(mem_stream);
   char* base = static_cast<char*>(ws);
@@ -414,7 +433,6 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
                                 const float* lse, const void* dO, const float* dM_S,
                                 const float* dz_S, void* dQ, void* dK, void* dV, float* dbeta,
                                 float* dM0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
-  (void)lse;  // the generic backward recomputes the row statistics
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
   const Geometry g = geometry(p);
@@ -450,7 +468,7 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
   auto F = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   if (infini::bwd_short_supported(g)) {   // state and its gradient stay on chip
     TRY(infini::launch_bwd_short(g, Q, K, V, beta, M0, z0, dO, dM_S, dz_S, dQ, dK, dV, dbeta, dM0, dz0,
-                                 F(lay.dbs), st));
+                                 F(lay.dbs), lse, st));
     return INFINI_OK;
   }
   infini::BwdChunkWs w;
@@ -473,7 +491,7 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
       Mstart = Mst; zstart = zst;
     }
     TRY(infini::launch_sweep(g, K, V, Mstart, zstart, nullptr, nullptr, Msnap, zsnap, s0, s1, st));
-    TRY(infini::launch_bwd_q(g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, s0, s1, st));
+    TRY(infini::launch_bwd_q(g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, lse, s0, s1, st));
     const bool first = ci == nchunks - 1, last = ci == 0;
     TRY(infini::launch_dbeta_reduce(g, beta, w, dbacc, dbeta, s1 - s0, first, last, st));
     const float* dMin = first ? dM_S : dMc;

@@ -99,8 +99,8 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       const float* __restrict__ dz_S, __bf16* __restrict__ dQ,
                       __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                       float* __restrict__ dM0, float* __restrict__ dz0,
-                      float* __restrict__ dbeta_part, int Hq, int Hkv, int N, int L, float scale,
-                      float sl2) {
+                      float* __restrict__ dbeta_part, const float* __restrict__ lse, int Hq, int Hkv,
+                      int N, int L, float scale, float sl2) {
   using C = BwdCfg<D>;
   constexpr int RS = C::RS, PS = C::PS;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[C::BL * RS];
@@ -328,17 +328,27 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         }
       }
       const int lim = min(q, Ls - 1);
-      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
           if (kb * 16 + 4 * g + i > lim) pacc[kb][i] = -INFINITY;
-          mx = fmaxf(mx, pacc[kb][i]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mref = mx * sl2;
+      // With the forward's row log-sum-exp the probabilities come out
+      // normalised (1/l = 1); otherwise they are formed against the row max
+      // and normalised by their own sum.
+      float mref;
+      if (lse) {
+        mref = lse[((size_t)b * Hq + h) * N + (size_t)s * L + lim] * 1.4426950408889634f;
+      } else {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pacc[kb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mref = mx * sl2;
+      }
       float lsum = 0.f;
       bbf16x8 pb[2];     // P^T operand, slot 8g + x <-> key 32t + 16(x/4) + 4g + x%4
 #pragma unroll
@@ -349,8 +359,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           lsum += (float)pr;
           pb[kb >> 1][(kb & 1) * 4 + i] = pr;
         }
-      lsum = red16x4(lsum);
-      const float inv_l = 1.f / lsum;
+      const float inv_l = lse ? 1.f : 1.f / red16x4(lsum);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -571,13 +580,14 @@ bool bwd_short_supported(const Geometry& g) {
 hipError_t launch_bwd_short(const Geometry& g, const void* Q, const void* K, const void* V,
                             const float* beta, const float* M0, const float* z0, const void* dO,
                             const float* dM_S, const float* dz_S, void* dQ, void* dK, void* dV,
-                            float* dbeta, float* dM0, float* dz0, float* dbeta_part, hipStream_t st) {
+                            float* dbeta, float* dM0, float* dz0, float* dbeta_part, const float* lse,
+                            hipStream_t st) {
   if (!bwd_short_supported(g)) return hipErrorInvalidValue;
   const float scale = 1.f / sqrtf((float)g.D);
   const float sl2 = 1.4426950408889634f * scale;
 #define BS_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), beta, \
                 M0, z0, static_cast<const __bf16*>(dO), dM_S, dz_S, static_cast<__bf16*>(dQ), static_cast<__bf16*>(dK), \
-                static_cast<__bf16*>(dV), dM0, dz0, dbeta_part, g.Hq, g.Hkv, g.N, g.L, scale, sl2
+                static_cast<__bf16*>(dV), dM0, dz0, dbeta_part, lse, g.Hq, g.Hkv, g.N, g.L, scale, sl2
   if (g.D == 128) hipLaunchKernelGGL(bwd_short_kernel<128>, dim3(g.B * g.Hkv), dim3(256), 0, st, BS_ARGS);
   else hipLaunchKernelGGL(bwd_short_kernel<64>, dim3(g.B * g.Hkv), dim3(256), 0, st, BS_ARGS);
 #undef BS_ARGS

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_q_kernel(
     const float* __restrict__ beta, const float* __restrict__ Msnap, const float* __restrict__ zsnap,
     const T* __restrict__ dO, T* __restrict__ dQ,
     float* __restrict__ ws_lse, float* __restrict__ ws_Dd, float* __restrict__ ws_dden,
-    float* __restrict__ ws_dnum, float* __restrict__ dbeta_part,
+    float* __restrict__ ws_dnum, float* __restrict__ dbeta_part, const float* __restrict__ lse_in,
     int Hq, int Hkv, int N, int L, int s_begin, int nseg, float scale) {
   using RS = QSplit<D>;
   constexpr int LPR = RS::LPR, DL = RS::DL, ROWS = RS::ROWS;
@@ -87,7 +87,11 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_q_kernel(
   float q[DL], o[DL];
 #pragma unroll
   for (int c = 0; c < DL; ++c) { q[c] = io<T>::load(Q, qrow + c); o[c] = 0.f; }
-  float m = -INFINITY, l = 0.f;
+  // With the forward's row log-sum-exp the probabilities are final as they
+  // are formed (m = lse, l = 1, no rescale); otherwise the running max and
+  // sum are kept as usual.
+  const float lse_row = lse_in ? lse_in[((size_t)b * Hq + h) * N + (size_t)s * L + i] : 0.f;
+  float m = lse_in ? lse_row : -INFINITY, l = lse_in ? 1.f : 0.f;
   const int kend = min(Ls, (int)(blockIdx.x + 1) * ROWS);
 
   // Pass 1: recompute A_dot and the row log-sum-exp.
@@ -110,15 +114,17 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_q_kernel(
       sc[jj] = (j0 + jj <= i) ? acc : -INFINITY;
       mt = fmaxf(mt, sc[jj]);
     }
-    const float mn = fmaxf(m, mt);
-    const float corr = __expf(m - mn);
-    l *= corr;
+    const float mn = lse_in ? m : fmaxf(m, mt);
+    if (!lse_in) {
+      const float corr = __expf(m - mn);
+      l *= corr;
 #pragma unroll
-    for (int c = 0; c < DL; ++c) o[c] *= corr;
+      for (int c = 0; c < DL; ++c) o[c] *= corr;
+    }
 #pragma unroll
     for (int jj = 0; jj < GB_KT; ++jj) {
       const float p = __expf(sc[jj] - mn);
-      l += p;
+      if (!lse_in) l += p;
       const float* vr = sV + jj * D + part * DL;
 #pragma unroll
       for (int c = 0; c < DL; ++c) o[c] += p * vr[c];
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_q_kernel(
     m = mn;
     __syncthreads();
   }
-  const float lse = m + __logf(l);
+  const float lse = lse_in ? lse_row : m + __logf(l);
   const float inv_l = 1.f / l;
   const float gt = sigmoid(beta[h]);
   const float og = 1.f - gt;
@@ -234,14 +240,15 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_q_kernel(
 template <typename T, int D>
 static hipError_t bwd_q_t(const Geometry& g, const void* Q, const void* K, const void* V,
                           const float* beta, const float* Msnap, const float* zsnap, const void* dO,
-                          void* dQ, const BwdChunkWs& w, int s_begin, int s_end, hipStream_t st) {
+                          void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin, int s_end,
+                          hipStream_t st) {
   using RS = QSplit<D>;
   const int nseg = s_end - s_begin;
   dim3 grid((g.L + RS::ROWS - 1) / RS::ROWS, g.Hq, g.B * nseg);
   hipLaunchKernelGGL((bwd_q_kernel<T, D>), grid, dim3(GB_THREADS), 0, st,
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
                      beta, Msnap, zsnap, static_cast<const T*>(dO), static_cast<T*>(dQ), w.lse, w.Dd,
-                     w.dden, w.dnum, w.dbeta_part, g.Hq, g.Hkv, g.N, g.L, s_begin, nseg,
+                     w.dden, w.dnum, w.dbeta_part, lse_in, g.Hq, g.Hkv, g.N, g.L, s_begin, nseg,
                      1.f / sqrtf((float)D));
   return hipGetLastError();
 }
@@ -510,8 +517,9 @@ hipError_t launch_dbeta_reduce(const Geometry& g, const float* beta, const BwdCh
 
 hipError_t launch_bwd_q(const Geometry& g, const void* Q, const void* K, const void* V,
                         const float* beta, const float* Msnap, const float* zsnap, const void* dO,
-                        void* dQ, const BwdChunkWs& w, int s_begin, int s_end, hipStream_t st) {
-  DISPATCH_TD(bwd_q_t, g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, s_begin, s_end, st);
+                        void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin, int s_end,
+                        hipStream_t st) {
+  DISPATCH_TD(bwd_q_t, g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, lse_in, s_begin, s_end, st);
 }
 
 hipError_t launch_rscan(const Geometry& g, const void* Q, const BwdChunkWs& w, const float* dM_in,

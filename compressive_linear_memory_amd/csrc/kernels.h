@@ -71,12 +71,15 @@ hipError_t launch_fwd_short(const Geometry& g, const void* Q, const void* K, con
                             float* M_S, float* z_S, float* lse, hipStream_t st);
 
 // Fused short-segment backward (bf16, head_dim 64 or 128, seg_len <= 64,
-// at most 16 query heads per K/V head).  dbeta_part: [B][Hq] scratch.
+// at most 16 query heads per K/V head).  dbeta_part: [B][Hq] scratch.  lse:
+// the forward's row log-sum-exp [B][Hq][N], or NULL to form the softmax
+// statistics again.
 bool bwd_short_supported(const Geometry& g);
 hipError_t launch_bwd_short(const Geometry& g, const void* Q, const void* K, const void* V,
                             const float* beta, const float* M0, const float* z0, const void* dO,
                             const float* dM_S, const float* dz_S, void* dQ, void* dK, void* dV,
-                            float* dbeta, float* dM0, float* dz0, float* dbeta_part, hipStream_t st);
+                            float* dbeta, float* dM0, float* dz0, float* dbeta_part, const float* lse,
+                            hipStream_t st);
 
 // Generic forward (fp32 vector arithmetic) over segments [s_begin, s_end),
 // reading the per-segment snapshots written by launch_sweep.
@@ -100,9 +103,11 @@ struct BwdChunkWs {
 
 int bwd_q_row_blocks(const Geometry& g);
 
+// lse_in: the forward's row log-sum-exp [B][Hq][N] (the probabilities are
+// then formed from it directly), or NULL to form it again.
 hipError_t launch_bwd_q(const Geometry& g, const void* Q, const void* K, const void* V,
                         const float* beta, const float* Msnap, const float* zsnap,
-                        const void* dO, void* dQ, const BwdChunkWs& w,
+                        const void* dO, void* dQ, const BwdChunkWs& w, const float* lse_in,
                         int s_begin, int s_end, hipStream_t st);
 
 hipError_t launch_rscan(const Geometry& g, const void* Q, const BwdChunkWs& w,

@@ -66,7 +66,7 @@ extern "C" {
  * (M0 = z0 = 0) it makes A_mem exactly 0 in the first segment instead of 0/0. */
 #define INFINI_MEM_EPS 1e-6f
 
-#define INFINI_VERSION 1
+#define INFINI_VERSION 2
 
 typedef enum {
   INFINI_OK = 0,
@@ -110,6 +110,14 @@ size_t infini_fwd_workspace_bytes(const infini_problem_t* p);
  * on the fused short-segment path only batch * q_heads floats). */
 size_t infini_bwd_workspace_bytes(const infini_problem_t* p);
 
+/* Bytes of what the forward saves for the backward: its optional lse output,
+ * batch * q_heads * seq_len floats (the natural-log log-sum-exp of every
+ * row's scaled causal scores inside its segment).  Nothing else needs to be
+ * kept: the backward recomputes the attention probabilities from Q, K and
+ * this row statistic, and the state from K, V, M0 and z0.  0 for an invalid
+ * problem. */
+size_t infini_fwd_saved_bytes(const infini_problem_t* p);
+
 /* Forward.
  *   Q, K, V   inputs (layouts above)
  *   beta      [q_heads] gate parameters
@@ -120,8 +128,9 @@ size_t infini_bwd_workspace_bytes(const infini_problem_t* p);
  *   O         [batch][q_heads][seq_len][head_dim] output
  *   M_S, z_S  state after the last segment (must not alias M0 / z0: chained
  *             calls ping-pong between two state buffers)
- *   lse       optional [batch][q_heads][seq_len] float32 output, for the
- *             backward; NULL to skip
+ *   lse       optional [batch][q_heads][seq_len] float32 output (the saved
+ *             buffer, infini_fwd_saved_bytes(p) bytes), for the backward;
+ *             NULL to skip
  *   ws        device workspace of at least infini_fwd_workspace_bytes(p); on
  *             the fused short-segment path (infini_fwd_path(p) returns
  *             "mfma_bf16_short") the call uses none and ws may be NULL with
@@ -137,7 +146,12 @@ infini_status_t infini_attn_fwd(const infini_problem_t* p,
 /* Backward: the exact gradient of infini_attn_fwd for
  *   loss = <dO, O> + <dM_S, M_S> + <dz_S, z_S>.
  *   Q, K, V, beta, M0, z0   the forward's inputs (M0, z0 both NULL = empty memory)
- *   lse        the forward's lse output, or NULL (then recomputed)
+ *   lse        the forward's lse output for the same inputs, or NULL.  When
+ *              given, the attention probabilities are formed from it directly
+ *              (exp(score - lse): no running row maximum, no row sum); when
+ *              NULL those statistics are formed again.  Either way the
+ *              gradients agree within rounding; an lse that does not belong
+ *              to these inputs gives unspecified gradients (no fault).
  *   dO         upstream gradient of O (dtype of the problem)
  *   dM_S, dz_S upstream gradients of the final state, or NULL for zero
  *   dQ, dK, dV gradients (dtype of the problem), overwritten
@@ -209,7 +223,10 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
  *                caller's (timing may be disabled), used to order the phases
  * Inputs must be ready on every stream passed; the call returns once all work
  * is issued, and the caller orders later work after mem_stream and all
- * att_streams.  Errors are those of infini_attn_fwd, plus INFINI_ERR_SHAPE
+ * att_streams.  The schedule cannot be recorded into a HIP graph: if
+ * mem_stream or an attention stream is being captured the call returns
+ * INFINI_ERR_UNSUPPORTED and issues nothing (chained infini_attn_fwd calls
+ * on one stream can be captured).  Errors are those of infini_attn_fwd, plus INFINI_ERR_SHAPE
  * for n_launches < 1, n_pipe < 1, group outside [1, INFINI_STREAM_MAX_GROUP],
  * more than INFINI_CHUNK_SEGMENTS segments per call, or (matrix-core path)
  * per group; arguments are all

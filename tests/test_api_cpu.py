@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.infini_version() == 1
+    assert L.infini_version() == 2
     for code in range(7):
         assert len(L.infini_status_string(code)) > 0
     assert L.infini_status_string(0) == b"ok"
