@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                         [ctypes.c_size_t, ctypes.c_int, ctypes.c_int, _P, _P, _P])
         L.infini_decode.restype = ctypes.c_int
         L.infini_decode.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32] + [_P] * 12 + [ctypes.c_size_t, _P]
+        L.infini_decode_noalloc.restype = ctypes.c_int
+        L.infini_decode_noalloc.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32] + [_P] * 12
         _lib = L
     return _lib
 
@@ -282,6 +284,41 @@ def decode(q, k, v, beta, seg_len, pos, kcache, vcache, M=None, z=None, out=None
                              ws.numel(), _stream())
     if rc != 0:
         raise InfiniError(rc, "infini_decode")
+    return (O, M_next, z_next) if closes else O
+
+
+def decode_noalloc(q, k, v, beta, seg_len, pos, kcache, vcache, M=None, z=None, out=None, state_out=None):
+    """infini_decode_noalloc (see include/infini.h): infini_decode with the
+    library's static per-device scratch instead of a workspace.  Outputs must
+    be preallocated (out, and state_out when the call completes the segment)
+    for the call to allocate nothing."""
+    p = problem(q, k, seg_len)
+    p.seq_len = q.shape[2]
+    dev = q.device
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    for name, t, dt, shp in (("k", k, q.dtype, (B, Hkv, T, d)), ("v", v, q.dtype, (B, Hkv, T, d)),
+                             ("beta", beta, torch.float32, (Hq,)),
+                             ("kcache", kcache, q.dtype, (B, Hkv, seg_len, d)),
+                             ("vcache", vcache, q.dtype, (B, Hkv, seg_len, d)),
+                             ("M", M, torch.float32, (B, Hkv, d, d)), ("z", z, torch.float32, (B, Hkv, d)),
+                             ("out", out, q.dtype, (B, Hq, T, d))):
+        _check(name, t, dt, shp, dev)
+    _check("q", q, q.dtype, q.shape, dev)
+    closes = pos + T == seg_len
+    O = torch.empty_like(q) if out is None else out
+    M_next = z_next = None
+    if closes:
+        if state_out is None:
+            M_next = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=dev)
+            z_next = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
+        else:
+            M_next, z_next = state_out
+    rc = lib().infini_decode_noalloc(ctypes.byref(p), int(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                     _ptr(kcache), _ptr(vcache), _ptr(M), _ptr(z), _ptr(O), _ptr(M_next),
+                                     _ptr(z_next), _stream())
+    if rc != 0:
+        raise InfiniError(rc, "infini_decode_noalloc")
     return (O, M_next, z_next) if closes else O
 
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/infini.h"
 #include "kernels.h"
@@ -168,6 +169,36 @@ infini_status_t hip_status(hipError_t e) { return e == hipSuccess ? INFINI_OK : 
     if (e_ != hipSuccess) return hip_status(e_);        \
   } while (0)
 
+// ---- static scratch of the allocation-free decode
+//
+// One array per device, in device memory, for the whole process.  In host
+// code its name stands for a host-side handle, not a device address: the
+// address is taken once per device with hipGetSymbolAddress and only that
+// pointer is passed to kernels.
+__device__ __align__(256) unsigned char scratch[INFINI_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (set up on its first use).
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,6 +215,7 @@ const char* infini_status_string(infini_status_t s) {
     case INFINI_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case INFINI_ERR_WORKSPACE: return "workspace is NULL or too small";
     case INFINI_ERR_HIP: return "HIP launch or runtime error";
+    case INFINI_ERR_SCRATCH: return "the problem needs more scratch than the allocation-free entry point's static maximum (INFINI_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -536,10 +568,11 @@ size_t infini_decode_workspace_bytes(const infini_problem_t* p) {
   return decode_ws_bytes(seg, p->seq_len);
 }
 
-infini_status_t infini_decode(const infini_problem_t* p, int32_t pos, const void* Q, const void* K,
-                              const void* V, const float* beta, void* Kcache, void* Vcache,
-                              const float* M, const float* z, void* O, float* M_next, float* z_next,
-                              void* ws, size_t ws_bytes, void* stream) {
+// ws NULL with noalloc: the workspace is this device's static scratch.
+static infini_status_t decode_impl(const infini_problem_t* p, int32_t pos, const void* Q, const void* K,
+                                   const void* V, const float* beta, void* Kcache, void* Vcache,
+                                   const float* M, const float* z, void* O, float* M_next, float* z_next,
+                                   void* ws, size_t ws_bytes, void* stream, bool noalloc) {
   infini_status_t why;
   Geometry seg;
   if (!decode_problem(p, pos, &seg, &why)) return why;
@@ -550,17 +583,22 @@ infini_status_t infini_decode(const infini_problem_t* p, int32_t pos, const void
   if (misaligned({Q, K, V, Kcache, Vcache, M, z, O, M_next, z_next, ws})) return INFINI_ERR_UNSUPPORTED;
   const FwdWs lay = fwd_layout(seg);
   const size_t need = decode_ws_bytes(seg, p->seq_len);
-  if (!ws || ws_bytes < need) return INFINI_ERR_WORKSPACE;
+  if (noalloc) {
+    if (need > (size_t)INFINI_NOALLOC_SCRATCH_BYTES) return INFINI_ERR_SCRATCH;
+  } else if (!ws || ws_bytes < need) {
+    return INFINI_ERR_WORKSPACE;
+  }
   const size_t eb = elem_bytes(seg);
   const size_t Tn = (size_t)p->seq_len;
   const size_t nq = (size_t)seg.B * seg.Hq * Tn * seg.D, nkv = (size_t)seg.B * seg.Hkv * Tn * seg.D;
   const size_t nc = (size_t)seg.B * seg.Hkv * seg.L * seg.D;
   const size_t nM = (size_t)seg.B * seg.Hkv * seg.D * seg.D * 4, nz = (size_t)seg.B * seg.Hkv * seg.D * 4;
   const Span outs[] = {{O, nq * eb}, {Kcache, nc * eb}, {Vcache, nc * eb},
-                       {M_next, closes ? nM : 0}, {z_next, closes ? nz : 0}, {ws, need}};
+                       {M_next, closes ? nM : 0}, {z_next, closes ? nz : 0}, {ws, noalloc ? 0 : need}};
   const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)seg.Hq * 4},
                       {M, M ? nM : 0}, {z, z ? nz : 0}};
   if (any_overlap(outs, 6, ins, 6)) return INFINI_ERR_ALIAS;
+  if (noalloc) TRY(scratch_of_current_device(&ws));
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   TRY(infini::launch_decode(seg, (int)Tn, pos, Q, K, V, beta, Kcache, Vcache, M, z, O,
@@ -569,6 +607,21 @@ infini_status_t infini_decode(const infini_problem_t* p, int32_t pos, const void
     TRY(run_fwd_chunk(seg, lay, static_cast<char*>(ws), nullptr, Kcache, Vcache, nullptr, M, z, nullptr,
                       M_next, z_next, nullptr, 0, 1, st, true, false));
   return INFINI_OK;
+}
+
+infini_status_t infini_decode(const infini_problem_t* p, int32_t pos, const void* Q, const void* K,
+                              const void* V, const float* beta, void* Kcache, void* Vcache,
+                              const float* M, const float* z, void* O, float* M_next, float* z_next,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(p, pos, Q, K, V, beta, Kcache, Vcache, M, z, O, M_next, z_next, ws, ws_bytes, stream,
+                     false);
+}
+
+infini_status_t infini_decode_noalloc(const infini_problem_t* p, int32_t pos, const void* Q, const void* K,
+                                      const void* V, const float* beta, void* Kcache, void* Vcache,
+                                      const float* M, const float* z, void* O, float* M_next, float* z_next,
+                                      void* stream) {
+  return decode_impl(p, pos, Q, K, V, beta, Kcache, Vcache, M, z, O, M_next, z_next, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

@@ -43,9 +43,10 @@
  * Ownership: the caller allocates and frees every buffer (inputs, outputs,
  * workspace).  The library never allocates, frees or synchronises; calls are
  * asynchronous on `stream` (a hipStream_t, NULL = the default stream).  The
- * library keeps no mutable global state, so concurrent calls on different
- * streams with disjoint buffers are safe; calls sharing a workspace must be
- * ordered by the caller.
+ * only global state is the static per-device scratch of
+ * infini_decode_noalloc (below); every other entry point keeps none, so
+ * concurrent calls on different streams with disjoint buffers are safe;
+ * calls sharing a workspace (or that scratch) must be ordered by the caller.
  *
  * Errors: arguments are validated on the host before anything is launched;
  * on a validation error nothing is written.  INFINI_ERR_HIP reports a failed
@@ -77,7 +78,9 @@ typedef enum {
                                  (any but beta, dbeta, lse) not 16-byte aligned                */
   INFINI_ERR_ALIAS = 4,       /* an output buffer overlaps an input or another output          */
   INFINI_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns          */
-  INFINI_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed                      */
+  INFINI_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed                      */
+  INFINI_ERR_SCRATCH = 7      /* infini_decode_noalloc: the problem needs more scratch than
+                                 INFINI_NOALLOC_SCRATCH_BYTES                                  */
 } infini_status_t;
 
 typedef enum { INFINI_FP32 = 0, INFINI_BF16 = 1 } infini_dtype_t;
@@ -282,6 +285,25 @@ infini_status_t infini_decode(const infini_problem_t* p, int32_t pos, const void
                               const void* V, const float* beta, void* Kcache, void* Vcache,
                               const float* M, const float* z, void* O, float* M_next, float* z_next,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* Allocation-free streaming decode, for callers that cannot allocate device
+ * memory: code recorded under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  Arguments, results and errors are those
+ * of infini_decode, without the workspace: the scratch comes from a static
+ * per-device array of INFINI_NOALLOC_SCRATCH_BYTES that the library holds
+ * for the life of the process (set up, without allocating, on the first call
+ * made with each device current; stream must belong to the current device).
+ * A problem whose infini_decode_workspace_bytes exceeds that size returns
+ * INFINI_ERR_SCRATCH before anything is issued.  Every call on a device
+ * shares that device's array, and no value in it survives from one call to
+ * the next that a later call reads; calls on one device whose executions
+ * overlap (different streams, not ordered by the caller) race on it and
+ * give unspecified results.  The call itself allocates and frees nothing. */
+#define INFINI_NOALLOC_SCRATCH_BYTES (32u << 20)
+infini_status_t infini_decode_noalloc(const infini_problem_t* p, int32_t pos, const void* Q, const void* K,
+                                      const void* V, const float* beta, void* Kcache, void* Vcache,
+                                      const float* M, const float* z, void* O, float* M_next, float* z_next,
+                                      void* stream);
 
 /* Name of the kernel family infini_attn_fwd runs for this problem
  * ("generic_fp32": fp32 vector-ALU path; "mfma_bf16": bf16 matrix-core

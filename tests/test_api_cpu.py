@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert L.infini_version() == 2
-    for code in range(7):
+    for code in range(8):
         assert len(L.infini_status_string(code)) > 0
     assert L.infini_status_string(0) == b"ok"
 
@@ -266,3 +266,20 @@ def test_fwd_stream_validation(L):
     assert call(O=arr([FAKE[9], ctypes.c_void_p(FAKE[4].value + 64), FAKE[11]])) == 4   # O[1] inside K[1]
     assert call(M=ctypes.c_void_p(FAKE[0].value + 64)) == 4                              # state inside Q[0]
     assert call(K=arr([FAKE[3], ctypes.c_void_p(FAKE[4].value + 2), FAKE[5]])) == 3     # K[1] misaligned
+
+
+def test_decode_noalloc_refuses_problems_beyond_its_scratch(L):
+    """The allocation-free decode checks its arguments like infini_decode and
+    refuses a problem whose workspace would exceed the static scratch
+    (INFINI_ERR_SCRATCH = 7) before touching any device."""
+    arr = [FAKE[i] for i in range(12)]
+    big = P(B=64, Hq=64, Hkv=64, N=64, d=128, L=4096, dtype=1)
+    need = L.infini_decode_workspace_bytes(ctypes.byref(big))
+    assert need > 32 << 20
+    assert L.infini_decode_noalloc(ctypes.byref(big), 0, *arr[:11], None) == 7
+    small = P(B=1, Hq=4, Hkv=2, N=3, d=64, L=16, dtype=1)
+    a = list(arr)
+    a[8] = a[0]                                   # O aliases Q
+    assert L.infini_decode_noalloc(ctypes.byref(small), 0, *a[:11], None) == 4
+    assert L.infini_decode_noalloc(ctypes.byref(small), 14, *arr[:11], None) == 2
+    assert L.infini_decode_noalloc(None, 0, *arr[:11], None) == 1
