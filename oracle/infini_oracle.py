@@ -56,6 +56,15 @@ Readings where the pages leave a step open (each is stated where it is used):
       it, and an update with its keys.  So segments are the slices
       [s L, min((s+1) L, N)) for s = 0 .. ceil(N / L) - 1.
 
+  R14 Variable-length batches: each sequence b of a batch has its own length
+      n_b <= N and is stored in the first n_b rows of its [N, d] slot; it is
+      cut into segments and processed exactly as if it were alone (its own
+      ragged last segment, R10), and its state M_S[b] is the state after its
+      own last segment.  Rows past n_b belong to no segment: they are never
+      read, and every per-row output there (O, lse, dQ, dK, dV) is zero.
+      [HF] Segmentation cuts each input sequence; nothing couples the
+      sequences of a batch.
+
 Parity pins: every public function is pinned by tests in tests/test_oracle_pins.py
 against brute force, closed forms, invariants, a library attention routine
 and finite differences.  No function here is "parity unpinned".
@@ -114,6 +123,15 @@ def seg_rows(s, seg_len, N):
     return slice(s * seg_len, min((s + 1) * seg_len, N))
 
 
+def seq_lengths(lens, B, N):
+    """Length of each sequence of the batch (R14); all N when lens is None."""
+    if lens is None:
+        return [N] * B
+    out = [int(x) for x in np.asarray(lens).reshape(-1)]
+    assert len(out) == B and all(0 <= x <= N for x in out), "lengths must lie in [0, N]"
+    return out
+
+
 def _state_or_zero(M0, z0, B, Hkv, d):
     M = np.zeros((B, Hkv, d, d)) if M0 is None else f64(M0).copy()
     z = np.zeros((B, Hkv, d)) if z0 is None else f64(z0).copy()
@@ -166,23 +184,28 @@ def memory_update(M, z, Ks, Vs):
 
 # ------------------------------------------------------------------ forward
 
-def state_sweep(K, V, seg_len, M0=None, z0=None):
+def state_sweep(K, V, seg_len, M0=None, z0=None, lens=None):
     """Run only the memory path ([HF] Memory Update, State Transfer).
 
     Returns (Msnap, zsnap, M_S, z_S) where Msnap[b, k, s] is M_{s-1}, the state
-    that segment s retrieves from (R6), and M_S the state after the last segment."""
+    that segment s retrieves from (R6), and M_S the state after the last segment.
+    With lens (R14) sequence b has ceil(lens[b] / seg_len) segments; its
+    snapshots past them repeat its final state."""
     K, V = f64(K), f64(V)
     B, Hkv, N, d = K.shape
     S = num_segments(N, seg_len)
+    nb = seq_lengths(lens, B, N)
     M, z = _state_or_zero(M0, z0, B, Hkv, d)
     Msnap = np.empty((B, Hkv, S, d, d))
     zsnap = np.empty((B, Hkv, S, d))
     for b in range(B):
         for k in range(Hkv):
             for s in range(S):
-                r = seg_rows(s, seg_len, N)
                 Msnap[b, k, s] = M[b, k]
                 zsnap[b, k, s] = z[b, k]
+                if s >= num_segments(nb[b], seg_len):
+                    continue
+                r = seg_rows(s, seg_len, nb[b])
                 M[b, k], z[b, k] = memory_update(M[b, k], z[b, k], K[b, k, r], V[b, k, r])
     return Msnap, zsnap, M, z
 
@@ -200,22 +223,25 @@ def segment_unit(Qs, Ks, Vs, Mprev, zprev, beta_h, rows=None, eps=EPS):
     return integrate(A_mem, A_dot, beta_h)
 
 
-def forward(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS, want_lse=False):
+def forward(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS, want_lse=False, lens=None):
     """Infini-attention forward over one call ([HF] all six steps, in order).
 
     Q: [B, Hq, N, d]; K, V: [B, Hkv, N, d]; beta: [Hq]; M0: [B, Hkv, d, d];
     z0: [B, Hkv, d] (None = empty memory).  Returns (O, M_S, z_S) and, with
-    want_lse, the per-row log-sum-exp of the local attention scores."""
+    want_lse, the per-row log-sum-exp of the local attention scores.
+    lens: optional per-sequence lengths (R14); rows past a sequence's length
+    come out zero."""
     Q, K, V = f64(Q), f64(K), f64(V)
-    B, Hq, Hkv, N, d, G, S = _dims(Q, K, seg_len)
+    B, Hq, Hkv, N, d, G, _ = _dims(Q, K, seg_len)
+    nb = seq_lengths(lens, B, N)
     M, z = _state_or_zero(M0, z0, B, Hkv, d)
-    O = np.empty((B, Hq, N, d))
-    lse = np.empty((B, Hq, N))
+    O = np.zeros((B, Hq, N, d))
+    lse = np.zeros((B, Hq, N))
     beta = f64(beta)
     for b in range(B):
         for k in range(Hkv):
-            for s in range(S):                                  # Segmentation
-                r = seg_rows(s, seg_len, N)
+            for s in range(num_segments(nb[b], seg_len)):       # Segmentation
+                r = seg_rows(s, seg_len, nb[b])
                 Ks, Vs = K[b, k, r], V[b, k, r]
                 for h in range(k * G, (k + 1) * G):             # R7
                     Qs = Q[b, h, r]
@@ -273,7 +299,7 @@ def forward_per_token(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS):
 
 # ------------------------------------------------------------------ backward
 
-def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None, eps=EPS):
+def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None, eps=EPS, lens=None):
     """Exact gradient of `forward` (R9) for loss = <dO, O> + <dM_S, M_S> + <dz_S, z_S>.
 
     Returns dict with dQ, dK, dV, dbeta, dM0, dz0.  Steps, per (batch, K/V head),
@@ -286,8 +312,9 @@ def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None,
       local:     dV += P^T dA_dot, dP = dA_dot V^T, dS = P * (dP - rowsum(P*dP)),
                  dQ += dS K / sqrt d, dK += dS^T Q / sqrt d."""
     Q, K, V, dO = f64(Q), f64(K), f64(V), f64(dO)
-    B, Hq, Hkv, N, d, G, S = _dims(Q, K, seg_len)
-    Msnap, zsnap, _, _ = state_sweep(K, V, seg_len, M0, z0)
+    B, Hq, Hkv, N, d, G, _ = _dims(Q, K, seg_len)
+    nb = seq_lengths(lens, B, N)
+    Msnap, zsnap, _, _ = state_sweep(K, V, seg_len, M0, z0, lens)
     dM = np.zeros((B, Hkv, d, d)) if dM_S is None else f64(dM_S).copy()
     dz = np.zeros((B, Hkv, d)) if dz_S is None else f64(dz_S).copy()
     dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
@@ -296,8 +323,8 @@ def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None,
     inv = 1.0 / math.sqrt(d)
     for b in range(B):
         for k in range(Hkv):
-            for s in reversed(range(S)):
-                r = seg_rows(s, seg_len, N)
+            for s in reversed(range(num_segments(nb[b], seg_len))):
+                r = seg_rows(s, seg_len, nb[b])
                 Ks, Vs = K[b, k, r], V[b, k, r]
                 sK = sigma(Ks)
                 # memory update of segment s: M_s = M_{s-1} + sK^T V_s

@@ -501,3 +501,101 @@ def test_R10_ragged_backward_matches_central_differences():
             minus[p][idx] -= h
             fd[idx] = (_loss(plus, dO, dMS, dzS, L) - _loss(minus, dO, dMS, dzS, L)) / (2 * h)
         assert max_rel_err(g[gname], fd) < 1e-6, p
+
+
+# ----------------------------------------------------------- R14 variable-length batches
+#
+# Each sequence of a batch, with its own length, equals that sequence run
+# alone through the single-sequence oracle (itself pinned above to brute
+# force, SDPA and finite differences); nothing couples the sequences.
+
+VARLEN = [
+    # B, Hq, Hkv, N, d, L, lengths
+    (4, 4, 2, 23, 4, 5, [23, 0, 11, 7]),
+    (3, 2, 1, 16, 3, 4, [16, 4, 1]),
+    (2, 3, 3, 9, 2, 9, [9, 2]),
+]
+
+
+def _varlen_problem(B, Hq, Hkv, N, d, seed):
+    Q, K, V, beta = _problem(B, Hq, Hkv, N, d, seed)
+    M0, z0 = _prefix_state(B, Hkv, d, seed=seed + 9)
+    return Q, K, V, beta, M0, z0
+
+
+@pytest.mark.parametrize("case", VARLEN)
+def test_R14_each_sequence_equals_that_sequence_alone(case):
+    B, Hq, Hkv, N, d, L, lens = case
+    Q, K, V, beta, M0, z0 = _varlen_problem(B, Hq, Hkv, N, d, 61)
+    o, M, z, lse = O.forward(Q, K, V, beta, L, M0, z0, want_lse=True, lens=lens)
+    for b, n in enumerate(lens):
+        ob, Mb, zb, lb = O.forward(Q[b:b + 1, :, :n], K[b:b + 1, :, :n], V[b:b + 1, :, :n], beta, L,
+                                   M0[b:b + 1], z0[b:b + 1], want_lse=True)
+        assert np.array_equal(o[b, :, :n], ob[0]) and np.array_equal(lse[b, :, :n], lb[0])
+        assert np.array_equal(M[b], Mb[0]) and np.array_equal(z[b], zb[0])
+        assert not o[b, :, n:].any() and not lse[b, :, n:].any()      # rows past the end are zero
+    # an empty sequence hands its state through
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.array_equal(M[b], M0[b]) and np.array_equal(z[b], z0[b])
+
+
+@pytest.mark.parametrize("case", VARLEN)
+def test_R14_rows_past_a_sequence_are_never_read(case):
+    B, Hq, Hkv, N, d, L, lens = case
+    Q, K, V, beta, M0, z0 = _varlen_problem(B, Hq, Hkv, N, d, 62)
+    Q2, K2, V2 = Q.copy(), K.copy(), V.copy()
+    for b, n in enumerate(lens):
+        for X in (Q2, K2, V2):
+            X[b, :, n:] = 1e3 * _rand(X[b, :, n:].shape, 70 + b)
+    a = O.forward(Q, K, V, beta, L, M0, z0, lens=lens)
+    c = O.forward(Q2, K2, V2, beta, L, M0, z0, lens=lens)
+    for x, y in zip(a, c):
+        assert np.array_equal(x, y)
+    dO = _rand(Q.shape, 71)
+    ga = O.backward(Q, K, V, beta, L, dO, M0, z0, lens=lens)
+    gc = O.backward(Q2, K2, V2, beta, L, dO, M0, z0, lens=lens)
+    for key in ga:
+        assert np.array_equal(ga[key], gc[key]), key
+
+
+def test_R14_full_lengths_equal_the_uniform_batch():
+    Q, K, V, beta, M0, z0 = _varlen_problem(3, 4, 2, 14, 4, 63)
+    a = O.forward(Q, K, V, beta, 5, M0, z0, want_lse=True)
+    b = O.forward(Q, K, V, beta, 5, M0, z0, want_lse=True, lens=[14, 14, 14])
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("case", VARLEN)
+def test_R14_backward_each_sequence_equals_that_sequence_alone(case):
+    B, Hq, Hkv, N, d, L, lens = case
+    Q, K, V, beta, M0, z0 = _varlen_problem(B, Hq, Hkv, N, d, 64)
+    dO = _rand(Q.shape, 72)
+    dMS = _rand(M0.shape, 73, 0.1)
+    dzS = _rand(z0.shape, 74, 0.1)
+    g = O.backward(Q, K, V, beta, L, dO, M0, z0, dMS, dzS, lens=lens)
+    dbeta = np.zeros_like(beta)
+    for b, n in enumerate(lens):
+        gb = O.backward(Q[b:b + 1, :, :n], K[b:b + 1, :, :n], V[b:b + 1, :, :n], beta, L, dO[b:b + 1, :, :n],
+                        M0[b:b + 1], z0[b:b + 1], dMS[b:b + 1], dzS[b:b + 1])
+        for key in ("dQ", "dK", "dV"):
+            assert np.array_equal(g[key][b, :, :n], gb[key][0]), key
+            assert not g[key][b, :, n:].any(), key
+        assert np.array_equal(g["dM0"][b], gb["dM0"][0]) and np.array_equal(g["dz0"][b], gb["dz0"][0])
+        dbeta += gb["dbeta"]
+    assert max_rel_err(g["dbeta"], dbeta) < 1e-13           # the sum over sequences, in another order
+
+
+def test_R14_state_sweep_matches_forward_state():
+    B, Hq, Hkv, N, d, L, lens = VARLEN[0]
+    Q, K, V, beta, M0, z0 = _varlen_problem(B, Hq, Hkv, N, d, 65)
+    _, M, z = O.forward(Q, K, V, beta, L, M0, z0, lens=lens)
+    Msnap, zsnap, M2, z2 = O.state_sweep(K, V, L, M0, z0, lens=lens)
+    assert np.array_equal(M, M2) and np.array_equal(z, z2)
+    for b, n in enumerate(lens):
+        S_b = O.num_segments(n, L)
+        if S_b:     # snapshot of the last segment + its update = final state
+            r = O.seg_rows(S_b - 1, L, n)
+            Mn, zn = O.memory_update(Msnap[b, 0, S_b - 1], zsnap[b, 0, S_b - 1], K[b, 0, r], V[b, 0, r])
+            assert np.array_equal(Mn, M[b, 0]) and np.array_equal(zn, z[b, 0])
