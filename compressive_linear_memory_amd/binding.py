@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.infini_attn_fwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 11 + [ctypes.c_size_t, _P]
         L.infini_attn_bwd.restype = ctypes.c_int
         L.infini_attn_bwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 17 + [ctypes.c_size_t, _P]
+        L.infini_attn_fwd_varlen.restype = ctypes.c_int
+        L.infini_attn_fwd_varlen.argtypes = [ctypes.POINTER(Problem)] + [_P] * 12 + [ctypes.c_size_t, _P]
+        L.infini_attn_bwd_varlen.restype = ctypes.c_int
+        L.infini_attn_bwd_varlen.argtypes = [ctypes.POINTER(Problem)] + [_P] * 18 + [ctypes.c_size_t, _P]
         L.infini_fwd_path.restype = ctypes.c_char_p
         L.infini_fwd_path.argtypes = [ctypes.POINTER(Problem)]
         L.infini_fwd_memory.restype = ctypes.c_int
@@ -110,11 +114,13 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def attn_fwd(q, k, v, beta, seg_len, M0=None, z0=None, want_lse=False, out=None, ws=None):
+def attn_fwd(q, k, v, beta, seg_len, M0=None, z0=None, want_lse=False, out=None, ws=None, seq_lens=None):
     """O, M_S, z_S (and lse if want_lse) of one call; see include/infini.h.
 
     `out` may hold preallocated (O, M_S, z_S, lse) tensors and `ws` a uint8
-    workspace tensor, so that a timed loop allocates nothing."""
+    workspace tensor, so that a timed loop allocates nothing.  `seq_lens`
+    (int32 [batch] on the device) makes it a variable-length batch
+    (infini_attn_fwd_varlen)."""
     p = problem(q, k, seg_len)
     dev = q.device
     B, Hq, N, d = q.shape
@@ -124,6 +130,7 @@ def attn_fwd(q, k, v, beta, seg_len, M0=None, z0=None, want_lse=False, out=None,
                              ("M0", M0, torch.float32, (B, Hkv, d, d)), ("z0", z0, torch.float32, (B, Hkv, d))):
         _check(name, t, dt, shp, dev)
     _check("q", q, q.dtype, q.shape, dev)
+    _check("seq_lens", seq_lens, torch.int32, (B,), dev)
     if out is None:
         O = torch.empty_like(q)
         M_S = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=dev)
@@ -136,19 +143,24 @@ def attn_fwd(q, k, v, beta, seg_len, M0=None, z0=None, want_lse=False, out=None,
             _check(name, t, dt, shp, dev)
     if ws is None:
         ws = torch.empty(max(workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
-    rc = lib().infini_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
-                               _ptr(O), _ptr(M_S), _ptr(z_S), _ptr(lse), _ptr(ws), ws.numel(), _stream())
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0), _ptr(O), _ptr(M_S), _ptr(z_S), _ptr(lse),
+            _ptr(ws), ws.numel(), _stream())
+    if seq_lens is None:
+        rc = lib().infini_attn_fwd(ctypes.byref(p), *args)
+    else:
+        rc = lib().infini_attn_fwd_varlen(ctypes.byref(p), _ptr(seq_lens), *args)
     if rc != 0:
-        raise InfiniError(rc, "infini_attn_fwd")
+        raise InfiniError(rc, "infini_attn_fwd" if seq_lens is None else "infini_attn_fwd_varlen")
     return (O, M_S, z_S, lse) if want_lse else (O, M_S, z_S)
 
 
 def attn_bwd(q, k, v, beta, seg_len, dO, M0=None, z0=None, lse=None, dM_S=None, dz_S=None,
-             want_state_grads=False, ws=None, out=None):
+             want_state_grads=False, ws=None, out=None, seq_lens=None):
     """dQ, dK, dV, dbeta (and dM0, dz0 if want_state_grads); see include/infini.h.
 
     `out` may hold preallocated (dQ, dK, dV, dbeta, dM0, dz0) tensors (dM0 and
-    dz0 None unless want_state_grads)."""
+    dz0 None unless want_state_grads).  `seq_lens` (int32 [batch] on the
+    device) makes it a variable-length batch (infini_attn_bwd_varlen)."""
     p = problem(q, k, seg_len)
     dev = q.device
     B, Hq, N, d = q.shape
@@ -158,7 +170,8 @@ def attn_bwd(q, k, v, beta, seg_len, dO, M0=None, z0=None, lse=None, dM_S=None, 
                              ("M0", M0, torch.float32, (B, Hkv, d, d)), ("z0", z0, torch.float32, (B, Hkv, d)),
                              ("lse", lse, torch.float32, (B, Hq, N)),
                              ("dM_S", dM_S, torch.float32, (B, Hkv, d, d)),
-                             ("dz_S", dz_S, torch.float32, (B, Hkv, d))):
+                             ("dz_S", dz_S, torch.float32, (B, Hkv, d)),
+                             ("seq_lens", seq_lens, torch.int32, (B,))):
         _check(name, t, dt, shp, dev)
     if out is None:
         dQ = torch.empty_like(q)
@@ -176,11 +189,15 @@ def attn_bwd(q, k, v, beta, seg_len, dO, M0=None, z0=None, lse=None, dM_S=None, 
             _check(name, t, dt, shp, dev)
     if ws is None:
         ws = torch.empty(max(workspace_bytes(p, backward=True), 1), dtype=torch.uint8, device=dev)
-    rc = lib().infini_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
-                               _ptr(lse), _ptr(dO), _ptr(dM_S), _ptr(dz_S), _ptr(dQ), _ptr(dK), _ptr(dV),
-                               _ptr(dbeta), _ptr(dM0), _ptr(dz0), _ptr(ws), ws.numel(), _stream())
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0), _ptr(lse), _ptr(dO), _ptr(dM_S),
+            _ptr(dz_S), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dbeta), _ptr(dM0), _ptr(dz0), _ptr(ws), ws.numel(),
+            _stream())
+    if seq_lens is None:
+        rc = lib().infini_attn_bwd(ctypes.byref(p), *args)
+    else:
+        rc = lib().infini_attn_bwd_varlen(ctypes.byref(p), _ptr(seq_lens), *args)
     if rc != 0:
-        raise InfiniError(rc, "infini_attn_bwd")
+        raise InfiniError(rc, "infini_attn_bwd" if seq_lens is None else "infini_attn_bwd_varlen")
     if want_state_grads:
         return dQ, dK, dV, dbeta, dM0, dz0
     return dQ, dK, dV, dbeta

@@ -248,13 +248,17 @@ size_t infini_bwd_workspace_bytes(const infini_problem_t* p) {
   return bwd_layout(geometry(p)).total;
 }
 
-infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const void* K,
-                                const void* V, const float* beta, const float* M0, const float* z0,
-                                void* O, float* M_S, float* z_S, float* lse, void* ws,
-                                size_t ws_bytes, void* stream) {
+// lens: device int32 [batch] of sequence lengths (variable-length batch), or
+// NULL when every sequence has p->seq_len tokens.
+static infini_status_t attn_fwd_impl(const infini_problem_t* p, const int32_t* lens, const void* Q,
+                                     const void* K, const void* V, const float* beta, const float* M0,
+                                     const float* z0, void* O, float* M_S, float* z_S, float* lse, void* ws,
+                                     size_t ws_bytes, void* stream) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
-  const Geometry g = geometry(p);
+  Geometry g = geometry(p);
+  g.lens = lens;
+  if (reinterpret_cast<uintptr_t>(lens) & 3) return INFINI_ERR_UNSUPPORTED;
   const size_t eb = elem_bytes(g);
   const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
   const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
@@ -269,8 +273,8 @@ infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const 
   const Span outs[] = {{O, nq * eb}, {M_S, nM}, {z_S, nz}, {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0},
                        {ws, need}};
   const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
-                      {M0, M0 ? nM : 0}, {z0, z0 ? nz : 0}};
-  if (any_overlap(outs, 5, ins, 6)) return INFINI_ERR_ALIAS;
+                      {M0, M0 ? nM : 0}, {z0, z0 ? nz : 0}, {lens, lens ? (size_t)g.B * 4 : 0}};
+  if (any_overlap(outs, 5, ins, 7)) return INFINI_ERR_ALIAS;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (g.N == 0) {                         // no tokens: the state passes through
@@ -279,6 +283,10 @@ infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const 
     return INFINI_OK;
   }
   if (g.B == 0) return INFINI_OK;
+  if (lens) {                             // rows past each sequence's end are zero
+    TRY(infini::launch_zero_tail(O, lens, g.B, g.Hq, g.N, g.D * eb / 4, st));
+    TRY(infini::launch_zero_tail(lse, lens, g.B, g.Hq, g.N, 1, st));
+  }
   if (infini::fwd_short_supported(g)) {   // state stays on chip for the whole call
     TRY(infini::launch_fwd_short(g, Q, K, V, beta, M0, z0, O, M_S, z_S, lse, st));
     return INFINI_OK;
@@ -292,6 +300,20 @@ infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const 
     TRY(run_fwd_chunk(g, lay, base, Q, K, V, beta, Min, zin, O, M_S, z_S, lse, s0, s1, st, true, true));
   }
   return INFINI_OK;
+}
+
+infini_status_t infini_attn_fwd(const infini_problem_t* p, const void* Q, const void* K,
+                                const void* V, const float* beta, const float* M0, const float* z0,
+                                void* O, float* M_S, float* z_S, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return attn_fwd_impl(p, nullptr, Q, K, V, beta, M0, z0, O, M_S, z_S, lse, ws, ws_bytes, stream);
+}
+
+infini_status_t infini_attn_fwd_varlen(const infini_problem_t* p, const int32_t* seq_lens, const void* Q,
+                                       const void* K, const void* V, const float* beta, const float* M0,
+                                       const float* z0, void* O, float* M_S, float* z_S, float* lse, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  return attn_fwd_impl(p, seq_lens, Q, K, V, beta, M0, z0, O, M_S, z_S, lse, ws, ws_bytes, stream);
 }
 
 infini_status_t infini_fwd_memory(const infini_problem_t* p, const void* K, const void* V,
@@ -460,14 +482,16 @@ infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, con
   return INFINI_OK;
 }
 
-infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const void* K,
-                                const void* V, const float* beta, const float* M0, const float* z0,
-                                const float* lse, const void* dO, const float* dM_S,
-                                const float* dz_S, void* dQ, void* dK, void* dV, float* dbeta,
-                                float* dM0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
+static infini_status_t attn_bwd_impl(const infini_problem_t* p, const int32_t* lens, const void* Q,
+                                     const void* K, const void* V, const float* beta, const float* M0,
+                                     const float* z0, const float* lse, const void* dO, const float* dM_S,
+                                     const float* dz_S, void* dQ, void* dK, void* dV, float* dbeta,
+                                     float* dM0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
-  const Geometry g = geometry(p);
+  Geometry g = geometry(p);
+  g.lens = lens;
+  if (reinterpret_cast<uintptr_t>(lens) & 3) return INFINI_ERR_UNSUPPORTED;
   const size_t eb = elem_bytes(g);
   const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
   const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
@@ -484,8 +508,8 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
   const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
                       {M0, M0 ? nM : 0}, {z0, z0 ? nz : 0}, {dO, nq * eb},
                       {dM_S, dM_S ? nM : 0}, {dz_S, dz_S ? nz : 0},
-                      {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0}};
-  if (any_overlap(outs, 7, ins, 10)) return INFINI_ERR_ALIAS;
+                      {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0}, {lens, lens ? (size_t)g.B * 4 : 0}};
+  if (any_overlap(outs, 7, ins, 11)) return INFINI_ERR_ALIAS;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (g.N == 0 || g.B == 0) {             // no tokens: the state's gradient passes through
@@ -495,6 +519,11 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
       TRY(infini::launch_state_copy(dz0, dz_S, nz / 4, st));
     }
     return INFINI_OK;
+  }
+  if (lens) {                             // rows past each sequence's end are zero
+    TRY(infini::launch_zero_tail(dQ, lens, g.B, g.Hq, g.N, g.D * eb / 4, st));
+    TRY(infini::launch_zero_tail(dK, lens, g.B, g.Hkv, g.N, g.D * eb / 4, st));
+    TRY(infini::launch_zero_tail(dV, lens, g.B, g.Hkv, g.N, g.D * eb / 4, st));
   }
   char* base = static_cast<char*>(ws);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
@@ -534,6 +563,24 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
     TRY(infini::launch_bwd_kv(g, Q, K, V, beta, dO, w, dK, dV, s0, s1, st));
   }
   return INFINI_OK;
+}
+
+infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const void* K,
+                                const void* V, const float* beta, const float* M0, const float* z0,
+                                const float* lse, const void* dO, const float* dM_S,
+                                const float* dz_S, void* dQ, void* dK, void* dV, float* dbeta,
+                                float* dM0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
+  return attn_bwd_impl(p, nullptr, Q, K, V, beta, M0, z0, lse, dO, dM_S, dz_S, dQ, dK, dV, dbeta, dM0, dz0, ws,
+                       ws_bytes, stream);
+}
+
+infini_status_t infini_attn_bwd_varlen(const infini_problem_t* p, const int32_t* seq_lens, const void* Q,
+                                       const void* K, const void* V, const float* beta, const float* M0,
+                                       const float* z0, const float* lse, const void* dO, const float* dM_S,
+                                       const float* dz_S, void* dQ, void* dK, void* dV, float* dbeta,
+                                       float* dM0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
+  return attn_bwd_impl(p, seq_lens, Q, K, V, beta, M0, z0, lse, dO, dM_S, dz_S, dQ, dK, dV, dbeta, dM0, dz0, ws,
+                       ws_bytes, stream);
 }
 
 // ---- streaming decode

@@ -99,8 +99,8 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       const float* __restrict__ dz_S, __bf16* __restrict__ dQ,
                       __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                       float* __restrict__ dM0, float* __restrict__ dz0,
-                      float* __restrict__ dbeta_part, const float* __restrict__ lse, int Hq, int Hkv,
-                      int N, int L, float scale, float sl2) {
+                      float* __restrict__ dbeta_part, const float* __restrict__ lse,
+                      const int* __restrict__ lens, int Hq, int Hkv, int N, int L, float scale, float sl2) {
   using C = BwdCfg<D>;
   constexpr int RS = C::RS, PS = C::PS;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[C::BL * RS];
@@ -119,7 +119,8 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int bk = blockIdx.x;
   const int b = bk / Hkv, kvh = bk % Hkv;
   const int G = Hq / Hkv;
-  const int S = (N + L - 1) / L;            // the last segment may be short
+  const int Nb = seq_len_of(lens, b, N);    // tokens of this sequence
+  const int S = (Nb + L - 1) / L;           // the last segment may be short
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lc = lane & 15, g = lane >> 4;
@@ -149,7 +150,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     float zp[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) zp[e] = 0.f;
-    const int Lk = min(L, N - s * L);      // keys of this segment
+    const int Lk = min(L, Nb - s * L);     // keys of this segment
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int key = kg * C::KPT + i;
@@ -218,7 +219,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
   // ---- 2. segments in reverse
   for (int s = S - 1; s >= 0; --s) {
-    const int Ls = min(L, N - s * L);      // rows and keys of this segment
+    const int Ls = min(L, Nb - s * L);     // rows and keys of this segment
     stage_kv(s);
     __syncthreads();
     if (s > 0) {
@@ -587,7 +588,7 @@ hipError_t launch_bwd_short(const Geometry& g, const void* Q, const void* K, con
   const float sl2 = 1.4426950408889634f * scale;
 #define BS_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), beta, \
                 M0, z0, static_cast<const __bf16*>(dO), dM_S, dz_S, static_cast<__bf16*>(dQ), static_cast<__bf16*>(dK), \
-                static_cast<__bf16*>(dV), dM0, dz0, dbeta_part, lse, g.Hq, g.Hkv, g.N, g.L, scale, sl2
+                static_cast<__bf16*>(dV), dM0, dz0, dbeta_part, lse, g.lens, g.Hq, g.Hkv, g.N, g.L, scale, sl2
   if (g.D == 128) hipLaunchKernelGGL(bwd_short_kernel<128>, dim3(g.B * g.Hkv), dim3(256), 0, st, BS_ARGS);
   else hipLaunchKernelGGL(bwd_short_kernel<64>, dim3(g.B * g.Hkv), dim3(256), 0, st, BS_ARGS);
 #undef BS_ARGS

@@ -30,6 +30,13 @@ template <> struct io<bf16_t> {
   __device__ __forceinline__ static void store(bf16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// Tokens of sequence b of the call: all N, or, in a variable-length batch,
+// lens[b] clamped to [0, N] (so no length can move an access outside the
+// padded [N] rows of its slot).
+__device__ __forceinline__ int seq_len_of(const int* lens, int b, int N) {
+  return lens ? min(max(lens[b], 0), N) : N;
+}
+
 // ELU(x) + 1 with alpha = 1.
 __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 // Its derivative: 1 for x > 0, exp(x) otherwise.

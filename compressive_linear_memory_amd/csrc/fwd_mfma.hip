@@ -80,7 +80,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ MsnapT, const float* __restrict__ zsnap,
                      __bf16* __restrict__ O, float* __restrict__ lse,
                      int Hq, int Hkv, int N, int L, int s_begin, int nseg, int nqt, float sl2,
-                     FwdCallTable tab, int spc) {
+                     FwdCallTable tab, int spc, const int* __restrict__ lens) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[C::LDS_ELEMS];
   __shared__ __attribute__((aligned(16))) float zs[D];
@@ -118,7 +118,9 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int qrow = q0 + lq;                   // this lane's query row
   const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
   const size_t kvbase = (((size_t)b * Hkv + kvh) * N + (size_t)s * L) * D;
-  const int Ls = min(L, N - s * L);           // rows and keys of this segment (the last may be short)
+  // rows and keys of this segment: the last may be short, and in a
+  // variable-length batch the segment may lie past its sequence's end
+  const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
   if (qt * C::BM >= Ls) return;               // a query tile past the end of a short segment
 
   // ---- Q^T operand in registers for the whole key loop
@@ -414,7 +416,7 @@ static hipError_t fwd_mfma_t(const Geometry& g, const void* Q, const void* K, co
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
                      static_cast<const __bf16*>(V), beta, static_cast<const __bf16*>(MsnapT), zsnap,
                      static_cast<__bf16*>(O), lse, g.Hq, g.Hkv, g.N, g.L, s_begin, nseg, nqt, sl2,
-                     FwdCallTable{}, 1);
+                     FwdCallTable{}, 1, g.lens);
   return hipGetLastError();
 }
 
@@ -428,7 +430,7 @@ static hipError_t fwd_mfma_group_t(const Geometry& g, const FwdCallTable& tab, i
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL((fwd_mfma_kernel<D, true>), dim3((unsigned)nwg), dim3(FwdCfg<D>::NT), 0, st,
                      nullptr, nullptr, nullptr, beta, static_cast<const __bf16*>(MsnapT), zsnap, nullptr,
-                     nullptr, g.Hq, g.Hkv, g.N, g.L, 0, nseg, nqt, sl2, tab, g.S);
+                     nullptr, g.Hq, g.Hkv, g.N, g.L, 0, nseg, nqt, sl2, tab, g.S, nullptr);
   return hipGetLastError();
 }
 

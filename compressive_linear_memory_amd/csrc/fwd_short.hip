@@ -64,7 +64,8 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       const __bf16* __restrict__ V, const float* __restrict__ beta,
                       const float* __restrict__ M0, const float* __restrict__ z0,
                       __bf16* __restrict__ O, float* __restrict__ M_S, float* __restrict__ z_S,
-                      float* __restrict__ lse, int Hq, int Hkv, int N, int L, int parts, float sl2) {
+                      float* __restrict__ lse, const int* __restrict__ lens, int Hq, int Hkv, int N, int L,
+                      int parts, float sl2) {
   using C = ShortCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[C::KTILE];
   __shared__ __attribute__((aligned(16))) __bf16 Vt[C::TTILE];
@@ -77,7 +78,8 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int part = blockIdx.x % parts;
   const int b = bk / Hkv, kvh = bk % Hkv;
   const int G = Hq / Hkv;
-  const int S = (N + L - 1) / L;            // the last segment may be short
+  const int Nb = seq_len_of(lens, b, N);    // tokens of this sequence
+  const int S = (Nb + L - 1) / L;           // the last segment may be short
   auto bound = [&](int p) {                // first segment of part p
     if (p >= parts) return S;
     const float q = 1.f - kReplayCost;
@@ -122,7 +124,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   sbf16x8 kst[C::KPT], vst[C::KPT];
   int Lst = L;                             // keys of the staged segment
   auto load_seg = [&](int s) {
-    Lst = min(L, N - s * L);
+    Lst = min(L, Nb - s * L);
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int key = min(kg * C::KPT + i, Lst - 1);
@@ -177,7 +179,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int qrow = q0 + lc;                // this lane's query row
 
   for (int s = 0; s < s_end; ++s) {
-    const int Ls = min(L, N - s * L);      // rows and keys of this segment
+    const int Ls = min(L, Nb - s * L);     // rows and keys of this segment
     if (s + 1 < s_end) load_seg(s + 1);    // in flight while this segment computes
 
     for (int h = kvh * G; s >= s_att && h < (kvh + 1) * G; ++h) {
@@ -335,7 +337,7 @@ hipError_t launch_fwd_short(const Geometry& g, const void* Q, const void* K, con
   while (parts < 4 && parts * 4 <= g.S && units * parts * 2 <= 256) parts *= 2;
   dim3 grid(units * parts);
 #define FS_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), \
-                beta, M0, z0, static_cast<__bf16*>(O), M_S, z_S, lse, g.Hq, g.Hkv, g.N, g.L, parts, sl2
+                beta, M0, z0, static_cast<__bf16*>(O), M_S, z_S, lse, g.lens, g.Hq, g.Hkv, g.N, g.L, parts, sl2
   if (g.D == 128) hipLaunchKernelGGL(fwd_short_kernel<128>, grid, dim3(256), 0, st, FS_ARGS);
   else hipLaunchKernelGGL(fwd_short_kernel<64>, grid, dim3(256), 0, st, FS_ARGS);
 #undef FS_ARGS

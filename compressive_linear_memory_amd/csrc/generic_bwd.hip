@@ -57,7 +57,7 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_q_kernel(
     const T* __restrict__ dO, T* __restrict__ dQ,
     float* __restrict__ ws_lse, float* __restrict__ ws_Dd, float* __restrict__ ws_dden,
     float* __restrict__ ws_dnum, float* __restrict__ dbeta_part, const float* __restrict__ lse_in,
-    int Hq, int Hkv, int N, int L, int s_begin, int nseg, float scale) {
+    int Hq, int Hkv, int N, int L, int s_begin, int nseg, float scale, const int* __restrict__ lens) {
   using RS = QSplit<D>;
   constexpr int LPR = RS::LPR, DL = RS::DL, ROWS = RS::ROWS;
   constexpr int REGION_A = (2 * GB_KT * D > D * D + D) ? 2 * GB_KT * D : D * D + D;
@@ -76,7 +76,13 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_q_kernel(
   const int b = blockIdx.z / nseg;
   const int s = s_begin + sl;
   const int kvh = h / (Hq / Hkv);
-  const int Ls = min(L, N - s * L);           // rows of this segment (the last may be short)
+  // rows of this segment: the last may be short; none past the end of a
+  // sequence of a variable-length batch (its dbeta part is then zero)
+  const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
+  if (Ls <= 0) {
+    if (t == 0) dbeta_part[(((size_t)b * Hq + h) * nseg + sl) * gridDim.x + blockIdx.x] = 0.f;
+    return;
+  }
   const int i_raw = blockIdx.x * ROWS + r;
   const bool valid = i_raw < Ls;
   const int i = valid ? i_raw : Ls - 1;
@@ -249,7 +255,7 @@ static hipError_t bwd_q_t(const Geometry& g, const void* Q, const void* K, const
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
                      beta, Msnap, zsnap, static_cast<const T*>(dO), static_cast<T*>(dQ), w.lse, w.Dd,
                      w.dden, w.dnum, w.dbeta_part, lse_in, g.Hq, g.Hkv, g.N, g.L, s_begin, nseg,
-                     1.f / sqrtf((float)D));
+                     1.f / sqrtf((float)D), g.lens);
   return hipGetLastError();
 }
 
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(256) void rscan_kernel(
     const T* __restrict__ Q, const float* __restrict__ dnum, const float* __restrict__ dden,
     const float* dM_in, const float* dz_in, float* dM_out, float* dz_out,
     float* __restrict__ dMsnap, float* __restrict__ dzsnap,
-    int Hq, int Hkv, int N, int L, int s_begin, int nseg) {
+    int Hq, int Hkv, int N, int L, int s_begin, int nseg, const int* __restrict__ lens) {
   constexpr int TPR = D / RS_TILE;
   const int tile = blockIdx.x;
   const int a0 = (tile / TPR) * RS_TILE;
@@ -292,7 +298,8 @@ __global__ __launch_bounds__(256) void rscan_kernel(
     const size_t sb = ((size_t)bk * nseg + sl) * D * D + (size_t)(a0 + ta) * D + c0 + tc;
     for (int c = 0; c < 4; ++c) dMsnap[sb + c] = acc[c];
     if (z_lane) dzsnap[((size_t)bk * nseg + sl) * D + a0 + t] = zacc;
-    const int Ls = min(L, N - s * L);         // rows of this segment (the last may be short)
+    // rows of this segment (the last may be short; none past a sequence's end)
+    const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
     for (int h = kvh * G; h < (kvh + 1) * G; ++h) {
       const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
       const size_t cbase = ((size_t)b * Hq + h) * ((size_t)nseg * L) + (size_t)sl * L;
@@ -328,7 +335,7 @@ static hipError_t rscan_t(const Geometry& g, const void* Q, const BwdChunkWs& w,
   dim3 grid((D / RS_TILE) * (D / RS_TILE), g.B * g.Hkv);
   hipLaunchKernelGGL((rscan_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T*>(Q), w.dnum,
                      w.dden, dM_in, dz_in, dM_out, dz_out, w.dMsnap, w.dzsnap, g.Hq, g.Hkv, g.N,
-                     g.L, s_begin, s_end - s_begin);
+                     g.L, s_begin, s_end - s_begin, g.lens);
   return hipGetLastError();
 }
 
@@ -341,7 +348,7 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_kv_kernel(
     const float* __restrict__ ws_lse, const float* __restrict__ ws_Dd,
     const float* __restrict__ dMsnap, const float* __restrict__ dzsnap,
     T* __restrict__ dK, T* __restrict__ dV,
-    int Hq, int Hkv, int N, int L, int s_begin, int nseg, float scale) {
+    int Hq, int Hkv, int N, int L, int s_begin, int nseg, float scale, const int* __restrict__ lens) {
   using RS = KSplit<D>;
   constexpr int LPR = RS::LPR, DL = RS::DL, ROWS = RS::ROWS;
   constexpr int RST = D + 1;
@@ -362,7 +369,10 @@ __global__ __launch_bounds__(GB_THREADS) void bwd_kv_kernel(
   const int b = blockIdx.z / nseg;
   const int s = s_begin + sl;
   const int G = Hq / Hkv;
-  const int Ls = min(L, N - s * L);           // keys of this segment (the last may be short)
+  // keys of this segment: the last may be short; none past the end of a
+  // sequence of a variable-length batch
+  const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
+  if (Ls <= 0) return;
   const int j_raw = blockIdx.x * ROWS + r;
   const bool valid = j_raw < Ls;
   const int j = valid ? j_raw : Ls - 1;
@@ -469,7 +479,7 @@ static hipError_t bwd_kv_t(const Geometry& g, const void* Q, const void* K, cons
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
                      beta, static_cast<const T*>(dO), w.lse, w.Dd, w.dMsnap, w.dzsnap,
                      static_cast<T*>(dK), static_cast<T*>(dV), g.Hq, g.Hkv, g.N, g.L, s_begin, nseg,
-                     1.f / sqrtf((float)D));
+                     1.f / sqrtf((float)D), g.lens);
   return hipGetLastError();
 }
 

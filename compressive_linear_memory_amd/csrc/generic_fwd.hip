@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(
     const T* __restrict__ K, const T* __restrict__ V,
     const float* M_in, const float* z_in, float* M_out, float* z_out,
     float* __restrict__ Msnap, float* __restrict__ zsnap, bf16_t* __restrict__ MsnapT,
-    int N, int L, int s_begin, int s_end) {
+    int N, int L, int s_begin, int s_end, const int* __restrict__ lens, int Hkv) {
   constexpr int TPR = D / SW_TILE;                 // tiles per row of M
   const int tile = blockIdx.x;
   const int a0 = (tile / TPR) * SW_TILE;
@@ -65,7 +65,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(
       for (int c = 0; c < 4; ++c) MsnapT[tb + (size_t)(c0 + tc + c) * D + a0 + ta] = f32_to_bf16(acc[c]);
     }
     const size_t rowbase = (bh * N + (size_t)s * L) * D;
-    const int Ls = min(L, N - s * L);              // keys of this segment (the last may be short)
+    // keys of this segment: the last may be short, and in a variable-length
+    // batch the segment may lie past its sequence's end (no keys)
+    const int Ls = min(L, seq_len_of(lens, (int)(bh / Hkv), N) - s * L);
     for (int j0 = 0; j0 < Ls; j0 += SW_KEYS) {
       for (int e = t; e < SW_KEYS * SW_TILE; e += 256) {
         const int j = e / SW_TILE, x = e % SW_TILE;
@@ -101,7 +103,7 @@ static hipError_t sweep_t(const Geometry& g, const void* K, const void* V, const
   dim3 grid((D / SW_TILE) * (D / SW_TILE), g.B * g.Hkv);
   hipLaunchKernelGGL((sweep_kernel<T, D>), grid, dim3(256), 0, st,
                      static_cast<const T*>(K), static_cast<const T*>(V), M_in, z_in, M_out, z_out,
-                     Msnap, zsnap, static_cast<bf16_t*>(MsnapT), g.N, g.L, s_begin, s_end);
+                     Msnap, zsnap, static_cast<bf16_t*>(MsnapT), g.N, g.L, s_begin, s_end, g.lens, g.Hkv);
   return hipGetLastError();
 }
 
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(GF_THREADS) void fwd_generic_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ beta, const float* __restrict__ Msnap, const float* __restrict__ zsnap,
     T* __restrict__ O, float* __restrict__ lse,
-    int Hq, int Hkv, int N, int L, int s_begin, int nseg, float scale) {
+    int Hq, int Hkv, int N, int L, int s_begin, int nseg, float scale, const int* __restrict__ lens) {
   using RS = RowSplit<D>;
   constexpr int LPR = RS::LPR, DL = RS::DL, ROWS = RS::ROWS;
   constexpr int LDS_FLOATS = (2 * GF_KT * D > D * D + D) ? 2 * GF_KT * D : D * D + D;
@@ -161,7 +163,10 @@ __global__ __launch_bounds__(GF_THREADS) void fwd_generic_kernel(
   const int b = blockIdx.z / nseg;
   const int s = s_begin + sl;
   const int kvh = h / (Hq / Hkv);
-  const int Ls = min(L, N - s * L);           // rows of this segment (the last may be short)
+  // rows of this segment: the last may be short; none past the end of a
+  // sequence of a variable-length batch
+  const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
+  if (Ls <= 0) return;
   const int i_raw = blockIdx.x * ROWS + r;
   const bool valid = i_raw < Ls;
   const int i = valid ? i_raw : Ls - 1;
@@ -257,7 +262,7 @@ static hipError_t fwd_t(const Geometry& g, const void* Q, const void* K, const v
   hipLaunchKernelGGL((fwd_generic_kernel<T, D>), grid, dim3(GF_THREADS), 0, st,
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
                      beta, Msnap, zsnap, static_cast<T*>(O), lse, g.Hq, g.Hkv, g.N, g.L, s_begin,
-                     nseg, 1.f / sqrtf((float)D));
+                     nseg, 1.f / sqrtf((float)D), g.lens);
   return hipGetLastError();
 }
 
@@ -290,6 +295,24 @@ hipError_t launch_state_copy(float* dst, const float* src, size_t n, hipStream_t
   if (n == 0) return hipSuccess;
   const size_t blocks = std::min<size_t>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dst, src, n);
+  return hipGetLastError();
+}
+
+// Rows [n_b, N) of slot (b, h): one workgroup per (b, h), 32-bit stores.
+__global__ __launch_bounds__(256) void zero_tail_kernel(uint32_t* __restrict__ X, const int* __restrict__ lens,
+                                                       int H, int N, size_t row_words) {
+  const int bh = blockIdx.x;
+  const int nb = seq_len_of(lens, bh / H, N);
+  uint32_t* base = X + (size_t)bh * N * row_words;
+  const size_t first = (size_t)nb * row_words, end = (size_t)N * row_words;
+  for (size_t i = first + threadIdx.x; i < end; i += 256) base[i] = 0u;
+}
+
+hipError_t launch_zero_tail(void* X, const int* lens, int B, int H, int N, size_t row_words, hipStream_t st) {
+  if (!X || !lens || (long long)B * H == 0 || N == 0) return hipSuccess;
+  if ((long long)B * H > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zero_tail_kernel, dim3((unsigned)(B * H)), dim3(256), 0, st, static_cast<uint32_t*>(X), lens,
+                     H, N, row_words);
   return hipGetLastError();
 }
 

@@ -9,10 +9,18 @@ namespace infini {
 
 // One call's geometry, after validation.
 struct Geometry {
-  int B, Hq, Hkv, N, D, L, S;   // S = N / L segments
+  int B, Hq, Hkv, N, D, L, S;   // S = ceil(N / L) segments (of the longest sequence)
   int dtype;                    // 0 fp32, 1 bf16
+  // Variable-length batch: device int32 [B], sequence b holds lens[b] <= N
+  // tokens in the first rows of its N-row slot (clamped to [0, N] where
+  // read).  NULL: every sequence has N tokens.
+  const int* lens = nullptr;
   int G() const { return Hq / Hkv; }
 };
+
+// Zero rows [lens[b], N) of every (b, h) slot of X ([B][H][N][row_words]
+// 32-bit words per row): the rows past each sequence's end.
+hipError_t launch_zero_tail(void* X, const int* lens, int B, int H, int N, size_t row_words, hipStream_t st);
 
 // Memory path over segments [s_begin, s_end) of the call.
 //   M_in/z_in: state before segment s_begin (NULL = empty memory).

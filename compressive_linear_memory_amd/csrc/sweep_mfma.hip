@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                        float* __restrict__ dM, float* __restrict__ dz,
                        int N, int L, int s_begin, int nseg, int nsplit, int split_keys,
-                       FwdCallTable tab, int spc) {
+                       FwdCallTable tab, int spc, const int* __restrict__ lens, int Hkv) {
   using C = DeltaCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[4 * C::TILE];   // 2 buffers x (K^T, V^T)
   static_assert(C::NKG * (D + 1) * 4 <= 4 * C::TILE * 2, "dz reduction must fit the tile buffers");
@@ -68,8 +68,10 @@ void delta_mfma_kernel(const __bf16* __restrict__ K, const __bf16* __restrict__ 
     K = tab.K[c]; V = tab.V[c];
   }
   const size_t base = (bk * N + (size_t)s * L + k_begin) * D;
-  // keys of this split (may be none); the last segment may be short
-  L = max(0, min(min(L, N - s * L) - k_begin, split_keys));
+  // keys of this split (may be none); the last segment may be short, and in
+  // a variable-length batch the segment may lie past its sequence's end
+  const int Nb = seq_len_of(lens, (int)(bk / Hkv), N);
+  L = max(0, min(min(L, Nb - s * L) - k_begin, split_keys));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -269,7 +271,7 @@ static hipError_t sweep_mfma_t(const Geometry& g, const void* K, const void* V, 
   if (parts > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((delta_mfma_kernel<D, false>), dim3((unsigned)parts), dim3(256), 0, st,
                      static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), dM, dz, g.N, g.L,
-                     s_begin, nseg, nsplit, split_keys, FwdCallTable{}, 1);
+                     s_begin, nseg, nsplit, split_keys, FwdCallTable{}, 1, g.lens, g.Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((D / SC_T) * (D / SC_T), g.B * g.Hkv);
@@ -302,7 +304,7 @@ static hipError_t sweep_mfma_group_t(const Geometry& g, const FwdCallTable& tab,
   const long long parts = (long long)g.B * g.Hkv * nseg * nsplit;
   if (parts > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((delta_mfma_kernel<D, true>), dim3((unsigned)parts), dim3(256), 0, st, nullptr, nullptr, dM,
-                     dz, g.N, g.L, 0, nseg, nsplit, split_keys, tab, g.S);
+                     dz, g.N, g.L, 0, nseg, nsplit, split_keys, tab, g.S, nullptr, g.Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((D / SC_T) * (D / SC_T), g.B * g.Hkv);

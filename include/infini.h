@@ -173,6 +173,38 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p,
                                 float* dM0, float* dz0,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* Variable-length batches: the forward and backward above for a batch whose
+ * sequences have different lengths (page "Hugging Face Infini-Attention 재현
+ * 분석", section "Infini-Attention 메커니즘", step Segmentation, applied to
+ * each sequence on its own).
+ *   seq_lens  device int32 [batch]: sequence b holds seq_lens[b] tokens in
+ *             rows 0 .. seq_lens[b]-1 of its seq_len-row slot (p->seq_len is
+ *             the capacity, the longest sequence); 4-byte aligned.  Values
+ *             are read on the device, so they cannot be checked before the
+ *             launch: each is clamped to [0, p->seq_len].  NULL = every
+ *             sequence has p->seq_len tokens (then identical to the calls
+ *             above).
+ * Each sequence is cut into its own segments, the last possibly shorter, and
+ * processed exactly as if it were alone: its state M_S[b], z_S[b] is the one
+ * after its own last segment (M0[b], z0[b] for an empty sequence), and dbeta
+ * sums over the sequences.  Rows past a sequence's end are never read, and
+ * are written as zeros in O, lse, dQ, dK and dV.  Workspace sizes are those of
+ * the same problem without seq_lens; every other argument, layout and error
+ * is as for infini_attn_fwd / infini_attn_bwd. */
+infini_status_t infini_attn_fwd_varlen(const infini_problem_t* p, const int32_t* seq_lens,
+                                       const void* Q, const void* K, const void* V,
+                                       const float* beta, const float* M0, const float* z0,
+                                       void* O, float* M_S, float* z_S, float* lse,
+                                       void* ws, size_t ws_bytes, void* stream);
+infini_status_t infini_attn_bwd_varlen(const infini_problem_t* p, const int32_t* seq_lens,
+                                       const void* Q, const void* K, const void* V,
+                                       const float* beta, const float* M0, const float* z0,
+                                       const float* lse, const void* dO,
+                                       const float* dM_S, const float* dz_S,
+                                       void* dQ, void* dK, void* dV, float* dbeta,
+                                       float* dM0, float* dz0,
+                                       void* ws, size_t ws_bytes, void* stream);
+
 /* Segments whose per-segment state a workspace holds at once.  Longer calls
  * are processed in chunks of this many segments. */
 #define INFINI_CHUNK_SEGMENTS 16

@@ -283,3 +283,21 @@ def test_decode_noalloc_refuses_problems_beyond_its_scratch(L):
     assert L.infini_decode_noalloc(ctypes.byref(small), 0, *a[:11], None) == 4
     assert L.infini_decode_noalloc(ctypes.byref(small), 14, *arr[:11], None) == 2
     assert L.infini_decode_noalloc(None, 0, *arr[:11], None) == 1
+
+
+def test_varlen_entry_points_validate_before_launch(L):
+    """infini_attn_fwd_varlen / infini_attn_bwd_varlen: the length array must
+    be 4-byte aligned (3) and must not overlap an output (4); the other
+    checks are those of the uniform calls."""
+    p = P(B=2, N=64, d=64, L=16, dtype=1)
+    a = [FAKE[i] for i in range(20)]
+    lens_bad = ctypes.c_void_p(FAKE[19].value + 2)
+    # forward: Q K V beta M0 z0 O M_S z_S lse, then ws, ws_bytes, stream
+    assert L.infini_attn_fwd_varlen(ctypes.byref(p), lens_bad, *a[:10], None, 0, None) == 3
+    lens_in_O = ctypes.c_void_p(a[6].value + 16)          # inside O
+    assert L.infini_attn_fwd_varlen(ctypes.byref(p), lens_in_O, *a[:10], None, 0, None) == 4
+    # backward: Q K V beta M0 z0 lse dO dM_S dz_S dQ dK dV dbeta dM0 dz0, then ws, ws_bytes, stream
+    assert L.infini_attn_bwd_varlen(ctypes.byref(p), lens_bad, *a[:16], None, 0, None) == 3
+    lens_in_dQ = ctypes.c_void_p(a[10].value + 16)
+    assert L.infini_attn_bwd_varlen(ctypes.byref(p), lens_in_dQ, *a[:16], FAKE[19], 1 << 30, None) == 4
+    assert L.infini_attn_bwd_varlen(None, FAKE[19], *a[:16], None, 0, None) == 1

@@ -50,7 +50,7 @@ def make(Bn, Hq, Hkv, N, d, dtype, seed, scale=None, with_state=False):
     return Q, K, V, beta, M0, z0
 
 
-def run_fwd(Q, K, V, beta, L, M0, z0, dtype, want_lse=False):
+def run_fwd(Q, K, V, beta, L, M0, z0, dtype, want_lse=False, lens=None):
     """One forward call whose outputs sit inside canary guard bands; the
     bands are checked before the outputs are returned."""
     from gpu_util import torch_dtype
@@ -62,17 +62,21 @@ def run_fwd(Q, K, V, beta, L, M0, z0, dtype, want_lse=False):
         gs.append(guarded((Bn, Hq, N), torch.float32))
     out = tuple(x.t for x in gs) + ((None,) if not want_lse else ())
     r = B().attn_fwd(dev(Q, dtype), dev(K, dtype), dev(V, dtype), dev(beta), L,
-                     dev(M0), dev(z0), want_lse=want_lse, out=out)
+                     dev(M0), dev(z0), want_lse=want_lse, out=out, seq_lens=dev_lens(lens))
     torch.cuda.synchronize()
     for name, x in zip(("O", "M_S", "z_S", "lse"), gs):
         x.check(name)
     return r
 
 
-def check_fwd(Q, K, V, beta, L, M0, z0, dtype, tag=""):
-    log(f"fwd {tag} Q{Q.shape} K{K.shape} L={L} {dtype} state={M0 is not None}")
-    o, M, z = run_fwd(Q, K, V, beta, L, M0, z0, dtype)
-    ro, rM, rz = O.forward(Q, K, V, beta, L, M0, z0)
+def dev_lens(lens):
+    return None if lens is None else torch.tensor(np.asarray(lens, dtype=np.int32), device="cuda")
+
+
+def check_fwd(Q, K, V, beta, L, M0, z0, dtype, tag="", lens=None):
+    log(f"fwd {tag} Q{Q.shape} K{K.shape} L={L} {dtype} state={M0 is not None} lens={lens}")
+    o, M, z = run_fwd(Q, K, V, beta, L, M0, z0, dtype, lens=lens)
+    ro, rM, rz = O.forward(Q, K, V, beta, L, M0, z0, lens=None if lens is None else np.clip(lens, 0, Q.shape[2]))
     eo, eM, ez = rel(host(o), ro), rel(host(M), rM), rel(host(z), rz)
     log(f"   err O {eo:.2e} M {eM:.2e} z {ez:.2e}")
     tol = TOL[dtype]
@@ -88,7 +92,7 @@ def test_tiny_fp32_forward():
     check_fwd(Q, K, V, I.beta(w), w.seg_len, None, None, "fp32", "tiny_fp32")
 
 
-def _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, tag="", lse=None):
+def _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, tag="", lse=None, lens=None):
     log(f"bwd {tag} Q{Q.shape} K{K.shape} L={L} {dtype} state={M0 is not None} dstate={dMS is not None} "
         f"lse={lse is not None}")
     from gpu_util import torch_dtype
@@ -99,11 +103,11 @@ def _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, tag="", lse=None):
           guarded((Bn, Hkv, d, d), torch.float32), guarded((Bn, Hkv, d), torch.float32)]
     g = B().attn_bwd(dev(Q, dtype), dev(K, dtype), dev(V, dtype), dev(beta), L, dev(dO, dtype),
                      dev(M0), dev(z0), dev(lse), dev(dMS), dev(dzS), want_state_grads=True,
-                     out=tuple(x.t for x in gs))
+                     out=tuple(x.t for x in gs), seq_lens=dev_lens(lens))
     torch.cuda.synchronize()
     for name, x in zip(("dQ", "dK", "dV", "dbeta", "dM0", "dz0"), gs):
         x.check(name)
-    ref = O.backward(Q, K, V, beta, L, dO, M0, z0, dMS, dzS)
+    ref = O.backward(Q, K, V, beta, L, dO, M0, z0, dMS, dzS, lens=lens)
     errs = {}
     for name, t in zip(("dQ", "dK", "dV", "dbeta", "dM0", "dz0"), g):
         errs[name] = rel(host(t), ref[name])
@@ -386,6 +390,70 @@ def test_backward_peaked_softmax(case):
         dMS = np.random.default_rng(N).standard_normal(M0.shape).astype(np.float32) * 1e-2
         dzS = np.random.default_rng(N + 1).standard_normal(z0.shape).astype(np.float32) * 1e-2
     _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, f"peaked c={c} grow={grow}")
+
+
+# ------------------------------------------------------------------ variable-length batches
+
+VARLEN_CASES = [
+    # B, Hq, Hkv, N (capacity), d, L, dtype, state, lengths
+    (3, 4, 2, 600, 128, 256, "bf16", True, [600, 0, 345]),       # long path, one empty sequence
+    (2, 8, 2, 1000, 64, 384, "bf16", False, [1000, 130]),        # long path, ragged tails
+    (4, 8, 2, 256, 128, 64, "bf16", True, [256, 100, 1, 0]),     # fused short path
+    (1, 2, 2, 1024, 64, 64, "bf16", True, [700]),                # fused short, segments split over parts
+    (2, 4, 4, 150, 64, 32, "bf16", False, [150, 77]),
+    (3, 2, 2, 100, 32, 16, "fp32", True, [100, 37, 0]),          # generic path
+    (2, 4, 2, 300, 64, 130, "bf16", True, [131, 300]),           # generic backward (bf16 seg_len > 64)
+    (2, 4, 2, 90, 128, 40, "fp32", False, [90, 41]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: "-".join(map(str, c[:8])) + "-" + "_".join(map(str, c[8])))
+def test_varlen_forward_and_backward(case):
+    """infini_attn_fwd_varlen / infini_attn_bwd_varlen against the oracle's
+    variable-length batch (each sequence processed as if alone; rows past its
+    end zero), every output inside canary guard bands."""
+    Bn, Hq, Hkv, N, d, L, dtype, st, lens = case
+    Q, K, V, beta, M0, z0 = make(Bn, Hq, Hkv, N, d, dtype, seed=11 * N + d, with_state=st)
+    check_fwd(Q, K, V, beta, L, M0, z0, dtype, "varlen", lens=lens)
+    o, M, z, lse = run_fwd(Q, K, V, beta, L, M0, z0, dtype, want_lse=True, lens=lens)
+    rl = O.forward(Q, K, V, beta, L, M0, z0, want_lse=True, lens=lens)[3]
+    assert rel(host(lse), rl) < TOL[dtype]
+    dO = rnd(Q.shape, 7 + N, 1.0, dtype)
+    dMS = dzS = None
+    if st:
+        dMS = np.random.default_rng(N).standard_normal(M0.shape).astype(np.float32) * 1e-2
+        dzS = np.random.default_rng(N + 1).standard_normal(z0.shape).astype(np.float32) * 1e-2
+    _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, "varlen", lens=lens)
+    _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, "varlen + saved lse", lens=lens,
+               lse=host(lse).astype(np.float32))
+
+
+def test_varlen_multi_chunk(monkeypatch):
+    """More segments than one workspace chunk holds, with different lengths."""
+    monkeypatch.setenv("INFINI_CHUNK_SEGMENTS", "3")
+    Q, K, V, beta, M0, z0 = make(3, 4, 2, 20 * 16, 64, "fp32", seed=23, with_state=True)
+    lens = [320, 150, 17]
+    check_fwd(Q, K, V, beta, 16, M0, z0, "fp32", "varlen chunks", lens=lens)
+    dO = rnd(Q.shape, 24, 1.0, "fp32")
+    _check_bwd(Q, K, V, beta, 16, M0, z0, dO, None, None, "fp32", "varlen chunks", lens=lens)
+
+
+def test_varlen_lengths_are_clamped():
+    """Lengths below 0 or above the capacity act as 0 and the capacity."""
+    Q, K, V, beta, M0, z0 = make(2, 4, 2, 128, 64, "bf16", seed=31, with_state=True)
+    a = run_fwd(Q, K, V, beta, 64, M0, z0, "bf16", lens=[-5, 1000])
+    b = run_fwd(Q, K, V, beta, 64, M0, z0, "bf16", lens=[0, 128])
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert np.array_equal(host(a[1])[0], M0[0])            # the empty sequence hands its state through
+
+
+def test_varlen_full_lengths_equal_uniform_call():
+    Q, K, V, beta, M0, z0 = make(2, 8, 2, 520, 128, "bf16", seed=37, with_state=True)
+    a = run_fwd(Q, K, V, beta, 256, M0, z0, "bf16")
+    b = run_fwd(Q, K, V, beta, 256, M0, z0, "bf16", lens=[520, 520])
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
 
 
 # ------------------------------------------------------------------ gate limits
