@@ -65,6 +65,20 @@ Readings where the pages leave a step open (each is stated where it is used):
       [HF] Segmentation cuts each input sequence; nothing couples the
       sequences of a batch.
 
+  R15 Pluggable feature map.  The memory path's feature map is ELU + 1 (R4)
+      by default; the alternative is the second-order Taylor map of the
+      page "Based" (cartesia.ai), section "고정 크기 순환 상태를 사용하는
+      방법도 중요합니다": phi is chosen so that phi(q) . phi(k) equals
+      1 + q.k + (q.k)^2 / 2, the Taylor series of exp(q.k) to second order,
+      with the key dimension growing from d to about d^2.  Written out:
+      phi(x) = [1, x_1 .. x_d, x_a x_b / sqrt 2 for a, b = 1 .. d (a major)],
+      D' = 1 + d + d^2 features.  It is applied to Q and K as they arrive
+      (no 1/sqrt(d): the page states the approximation of exp(q k^T)
+      itself), and everything else is unchanged: M is D' x d, z has D'
+      entries, A_mem = phi(Q) M / (phi(Q) z + eps).  Since
+      1 + x + x^2 / 2 >= 1/2 for every real x, the denominator stays
+      positive.  The local attention keeps its exact softmax.
+
 Parity pins: every public function is pinned by tests in tests/test_oracle_pins.py
 against brute force, closed forms, invariants, a library attention routine
 and finite differences.  No function here is "parity unpinned".
@@ -94,6 +108,65 @@ def sigma_grad(x: np.ndarray) -> np.ndarray:
     """Derivative of ELU + 1: 1 for x > 0, exp(x) otherwise (continuous at 0)."""
     x = f64(x)
     return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+class Elu1:
+    """The default feature map sigma = ELU + 1 (R4), D' = d features."""
+    name = "elu1"
+
+    @staticmethod
+    def dim(d):
+        return d
+
+    @staticmethod
+    def phi(x):
+        return sigma(x)
+
+    @staticmethod
+    def vjp(x, g):
+        """d<g, phi(x)>/dx for rows x (n, d) and g (n, D')."""
+        return f64(g) * sigma_grad(x)
+
+    @staticmethod
+    def kernel(q, k):
+        """phi(q) . phi(k) for single vectors."""
+        return float(sigma(q) @ sigma(k))
+
+
+class Taylor2:
+    """Second-order Taylor feature map (R15; page "Based", section
+    "고정 크기 순환 상태를 사용하는 방법도 중요합니다"):
+    phi(x) = [1, x, x_a x_b / sqrt 2 (a major)], D' = 1 + d + d^2, so that
+    phi(q) . phi(k) = 1 + q.k + (q.k)^2 / 2."""
+    name = "taylor2"
+
+    @staticmethod
+    def dim(d):
+        return 1 + d + d * d
+
+    @staticmethod
+    def phi(x):
+        x = f64(x)
+        n, d = x.shape
+        quad = (x[:, :, None] * x[:, None, :]).reshape(n, d * d) / math.sqrt(2.0)
+        return np.concatenate([np.ones((n, 1)), x, quad], axis=1)
+
+    @staticmethod
+    def vjp(x, g):
+        x, g = f64(x), f64(g)
+        n, d = x.shape
+        G = g[:, 1 + d:].reshape(n, d, d)
+        # d(x_a x_b)/dx_c = delta_ac x_b + x_a delta_bc
+        quad = np.einsum("ncb,nb->nc", G, x) + np.einsum("nac,na->nc", G, x)
+        return g[:, 1:1 + d] + quad / math.sqrt(2.0)
+
+    @staticmethod
+    def kernel(q, k):
+        t = float(f64(q) @ f64(k))
+        return 1.0 + t + 0.5 * t * t
+
+
+FEATURE_MAPS = {"elu1": Elu1, "taylor2": Taylor2}
 
 
 def gate(beta) -> np.ndarray:
@@ -132,9 +205,10 @@ def seq_lengths(lens, B, N):
     return out
 
 
-def _state_or_zero(M0, z0, B, Hkv, d):
-    M = np.zeros((B, Hkv, d, d)) if M0 is None else f64(M0).copy()
-    z = np.zeros((B, Hkv, d)) if z0 is None else f64(z0).copy()
+def _state_or_zero(M0, z0, B, Hkv, d, fmap=Elu1):
+    n = fmap.dim(d)
+    M = np.zeros((B, Hkv, n, d)) if M0 is None else f64(M0).copy()
+    z = np.zeros((B, Hkv, n)) if z0 is None else f64(z0).copy()
     return M, z
 
 
@@ -159,11 +233,12 @@ def local_attention(Qs, Ks, Vs, rows=None):
     return P @ Vs, P, (m + np.log(l))[:, 0]
 
 
-def memory_retrieval(Qs, M, z, eps=EPS):
-    """A_mem = sigma(Q) M_{s-1} / (sigma(Q) z_{s-1} + eps) ([HF] Memory Retrieval; R1, R2).
+def memory_retrieval(Qs, M, z, eps=EPS, fmap=Elu1):
+    """A_mem = sigma(Q) M_{s-1} / (sigma(Q) z_{s-1} + eps) ([HF] Memory Retrieval; R1, R2),
+    with fmap.phi in place of sigma (R15).
 
-    Returns (A_mem, num, den, sigma(Q))."""
-    sQ = sigma(Qs)
+    Returns (A_mem, num, den, phi(Q))."""
+    sQ = fmap.phi(Qs)
     num = sQ @ f64(M)
     den = sQ @ f64(z) + eps
     return num / den[:, None], num, den, sQ
@@ -175,16 +250,17 @@ def integrate(A_mem, A_dot, beta_h):
     return g * A_mem + (1.0 - g) * A_dot
 
 
-def memory_update(M, z, Ks, Vs):
+def memory_update(M, z, Ks, Vs, fmap=Elu1):
     """M_s = M_{s-1} + sigma(K)^T V and z_s = z_{s-1} + sum_rows sigma(K)
-    ([HF] Memory Update; R1).  Returns new arrays."""
-    sK = sigma(Ks)
+    ([HF] Memory Update; R1), with fmap.phi in place of sigma (R15).
+    Returns new arrays."""
+    sK = fmap.phi(Ks)
     return f64(M) + sK.T @ f64(Vs), f64(z) + sK.sum(axis=0)
 
 
 # ------------------------------------------------------------------ forward
 
-def state_sweep(K, V, seg_len, M0=None, z0=None, lens=None):
+def state_sweep(K, V, seg_len, M0=None, z0=None, lens=None, fmap=Elu1):
     """Run only the memory path ([HF] Memory Update, State Transfer).
 
     Returns (Msnap, zsnap, M_S, z_S) where Msnap[b, k, s] is M_{s-1}, the state
@@ -195,9 +271,9 @@ def state_sweep(K, V, seg_len, M0=None, z0=None, lens=None):
     B, Hkv, N, d = K.shape
     S = num_segments(N, seg_len)
     nb = seq_lengths(lens, B, N)
-    M, z = _state_or_zero(M0, z0, B, Hkv, d)
-    Msnap = np.empty((B, Hkv, S, d, d))
-    zsnap = np.empty((B, Hkv, S, d))
+    M, z = _state_or_zero(M0, z0, B, Hkv, d, fmap)
+    Msnap = np.empty((B, Hkv, S) + M.shape[2:])
+    zsnap = np.empty((B, Hkv, S) + z.shape[2:])
     for b in range(B):
         for k in range(Hkv):
             for s in range(S):
@@ -206,11 +282,11 @@ def state_sweep(K, V, seg_len, M0=None, z0=None, lens=None):
                 if s >= num_segments(nb[b], seg_len):
                     continue
                 r = seg_rows(s, seg_len, nb[b])
-                M[b, k], z[b, k] = memory_update(M[b, k], z[b, k], K[b, k, r], V[b, k, r])
+                M[b, k], z[b, k] = memory_update(M[b, k], z[b, k], K[b, k, r], V[b, k, r], fmap)
     return Msnap, zsnap, M, z
 
 
-def segment_unit(Qs, Ks, Vs, Mprev, zprev, beta_h, rows=None, eps=EPS):
+def segment_unit(Qs, Ks, Vs, Mprev, zprev, beta_h, rows=None, eps=EPS, fmap=Elu1):
     """Output rows of one (batch, query head, segment) unit given its M_{s-1}, z_{s-1}.
 
     Because the carried state is a prefix sum of per-segment terms, any unit
@@ -219,11 +295,11 @@ def segment_unit(Qs, Ks, Vs, Mprev, zprev, beta_h, rows=None, eps=EPS):
     Qs = f64(Qs)
     rows = np.arange(Qs.shape[0]) if rows is None else np.asarray(rows)
     A_dot, _, _ = local_attention(Qs, Ks, Vs, rows)
-    A_mem, _, _, _ = memory_retrieval(Qs[rows], Mprev, zprev, eps)
+    A_mem, _, _, _ = memory_retrieval(Qs[rows], Mprev, zprev, eps, fmap)
     return integrate(A_mem, A_dot, beta_h)
 
 
-def forward(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS, want_lse=False, lens=None):
+def forward(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS, want_lse=False, lens=None, fmap=Elu1):
     """Infini-attention forward over one call ([HF] all six steps, in order).
 
     Q: [B, Hq, N, d]; K, V: [B, Hkv, N, d]; beta: [Hq]; M0: [B, Hkv, d, d];
@@ -234,7 +310,7 @@ def forward(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS, want_lse=False, l
     Q, K, V = f64(Q), f64(K), f64(V)
     B, Hq, Hkv, N, d, G, _ = _dims(Q, K, seg_len)
     nb = seq_lengths(lens, B, N)
-    M, z = _state_or_zero(M0, z0, B, Hkv, d)
+    M, z = _state_or_zero(M0, z0, B, Hkv, d, fmap)
     O = np.zeros((B, Hq, N, d))
     lse = np.zeros((B, Hq, N))
     beta = f64(beta)
@@ -246,28 +322,40 @@ def forward(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS, want_lse=False, l
                 for h in range(k * G, (k + 1) * G):             # R7
                     Qs = Q[b, h, r]
                     A_dot, _, l = local_attention(Qs, Ks, Vs)   # Local Attention
-                    A_mem, _, _, _ = memory_retrieval(Qs, M[b, k], z[b, k], eps)  # Retrieval
-                    O[b, h, r] = integrate(A_mem, A_dot, beta[h])                  # Integration
+                    A_mem, _, _, _ = memory_retrieval(Qs, M[b, k], z[b, k], eps, fmap)  # Retrieval
+                    O[b, h, r] = integrate(A_mem, A_dot, beta[h])                        # Integration
                     lse[b, h, r] = l
-                M[b, k], z[b, k] = memory_update(M[b, k], z[b, k], Ks, Vs)        # Update
+                M[b, k], z[b, k] = memory_update(M[b, k], z[b, k], Ks, Vs, fmap)        # Update
                 # State Transfer: nothing but (M, z) survives to the next segment.
     return (O, M, z, lse) if want_lse else (O, M, z)
 
 
-def forward_per_token(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS):
+def forward_per_token(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS, fmap=Elu1):
     """Direct per-token evaluation, never forming M (linear-attention view, R1).
 
     For token i of segment s:
       A_dot_i = sum over keys j of segment s with j <= i of softmax_j(q_i.k_j / sqrt d) v_j
-      A_mem_i = (sigma(q_i) M0 + sum_{j before segment s} (sigma(q_i).sigma(k_j)) v_j)
-                / (sigma(q_i) z0 + sum_{j before segment s} sigma(q_i).sigma(k_j) + eps)
-    Written with explicit loops over tokens; for tiny inputs only."""
+      A_mem_i = (phi(q_i) M0 + sum_{j before segment s} kappa(q_i, k_j) v_j)
+                / (phi(q_i) z0 + sum_{j before segment s} kappa(q_i, k_j) + eps)
+    where kappa(q, k) = phi(q).phi(k) is written out without any feature
+    vector: sigma(q).sigma(k) with scalar loops for ELU + 1, and the closed
+    form 1 + q.k + (q.k)^2 / 2 for the Taylor map (R15).  Explicit loops over
+    tokens; for tiny inputs only."""
     Q, K, V = f64(Q), f64(K), f64(V)
     B, Hq, Hkv, N, d, G, S = _dims(Q, K, seg_len)
-    M0 = np.zeros((B, Hkv, d, d)) if M0 is None else f64(M0)
-    z0 = np.zeros((B, Hkv, d)) if z0 is None else f64(z0)
+    n = fmap.dim(d)
+    M0 = np.zeros((B, Hkv, n, d)) if M0 is None else f64(M0)
+    z0 = np.zeros((B, Hkv, n)) if z0 is None else f64(z0)
     O = np.zeros((B, Hq, N, d))
     inv = 1.0 / math.sqrt(d)
+    elu = lambda v: np.array([x + 1.0 if x > 0 else math.exp(x) for x in v])
+
+    def kappa(q, k):
+        if fmap is Taylor2:
+            t = sum(q[c] * k[c] for c in range(d))
+            return 1.0 + t + 0.5 * t * t
+        return float(elu(q) @ elu(k))
+
     for b in range(B):
         for h in range(Hq):
             k = h // G
@@ -285,12 +373,11 @@ def forward_per_token(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS):
                 for t, j in enumerate(range(start, i + 1)):
                     a_dot += (w[t] / tot) * V[b, k, j]
                 # memory as a sum over all earlier segments' tokens
-                sq = np.array([x + 1.0 if x > 0 else math.exp(x) for x in q])
-                num = sq @ M0[b, k]
-                den = float(sq @ z0[b, k]) + eps
+                pq = elu(q) if fmap is Elu1 else fmap.phi(q[None, :])[0]
+                num = pq @ M0[b, k]
+                den = float(pq @ z0[b, k]) + eps
                 for j in range(0, start):
-                    sk = np.array([x + 1.0 if x > 0 else math.exp(x) for x in K[b, k, j]])
-                    a = float(sq @ sk)
+                    a = kappa(q, K[b, k, j])
                     num = num + a * V[b, k, j]
                     den += a
                 O[b, h, i] = g * (num / den) + (1.0 - g) * a_dot
@@ -299,7 +386,8 @@ def forward_per_token(Q, K, V, beta, seg_len, M0=None, z0=None, eps=EPS):
 
 # ------------------------------------------------------------------ backward
 
-def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None, eps=EPS, lens=None):
+def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None, eps=EPS, lens=None,
+             fmap=Elu1):
     """Exact gradient of `forward` (R9) for loss = <dO, O> + <dM_S, M_S> + <dz_S, z_S>.
 
     Returns dict with dQ, dK, dV, dbeta, dM0, dz0.  Steps, per (batch, K/V head),
@@ -314,9 +402,10 @@ def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None,
     Q, K, V, dO = f64(Q), f64(K), f64(V), f64(dO)
     B, Hq, Hkv, N, d, G, _ = _dims(Q, K, seg_len)
     nb = seq_lengths(lens, B, N)
-    Msnap, zsnap, _, _ = state_sweep(K, V, seg_len, M0, z0, lens)
-    dM = np.zeros((B, Hkv, d, d)) if dM_S is None else f64(dM_S).copy()
-    dz = np.zeros((B, Hkv, d)) if dz_S is None else f64(dz_S).copy()
+    Msnap, zsnap, _, _ = state_sweep(K, V, seg_len, M0, z0, lens, fmap)
+    n = fmap.dim(d)
+    dM = np.zeros((B, Hkv, n, d)) if dM_S is None else f64(dM_S).copy()
+    dz = np.zeros((B, Hkv, n)) if dz_S is None else f64(dz_S).copy()
     dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
     dbeta = np.zeros(Hq)
     g_all = gate(beta)
@@ -326,19 +415,19 @@ def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None,
             for s in reversed(range(num_segments(nb[b], seg_len))):
                 r = seg_rows(s, seg_len, nb[b])
                 Ks, Vs = K[b, k, r], V[b, k, r]
-                sK = sigma(Ks)
+                sK = fmap.phi(Ks)
                 # memory update of segment s: M_s = M_{s-1} + sK^T V_s
                 dsK = Vs @ dM[b, k].T + dz[b, k][None, :]
-                dK[b, k, r] += dsK * sigma_grad(Ks)
+                dK[b, k, r] += fmap.vjp(Ks, dsK)
                 dV[b, k, r] += sK @ dM[b, k]
                 Mprev, zprev = Msnap[b, k, s], zsnap[b, k, s]
-                addM = np.zeros((d, d))
-                addz = np.zeros(d)
+                addM = np.zeros((n, d))
+                addz = np.zeros(n)
                 for h in range(k * G, (k + 1) * G):
                     g = g_all[h]
                     Qs, dOs = Q[b, h, r], dO[b, h, r]
                     A_dot, P, _ = local_attention(Qs, Ks, Vs)
-                    A_mem, num, den, sQ = memory_retrieval(Qs, Mprev, zprev, eps)
+                    A_mem, num, den, sQ = memory_retrieval(Qs, Mprev, zprev, eps, fmap)
                     dA_mem = g * dOs
                     dA_dot = (1.0 - g) * dOs
                     dbeta[h] += g * (1.0 - g) * np.sum(dOs * (A_mem - A_dot))
@@ -346,7 +435,7 @@ def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None,
                     dnum = dA_mem / den[:, None]
                     dden = -np.sum(dA_mem * A_mem, axis=1) / den
                     dsQ = dnum @ Mprev.T + dden[:, None] * zprev[None, :]
-                    dQ[b, h, r] += dsQ * sigma_grad(Qs)
+                    dQ[b, h, r] += fmap.vjp(Qs, dsQ)
                     addM += sQ.T @ dnum
                     addz += sQ.T @ dden
                     # local causal attention
@@ -362,9 +451,10 @@ def backward(Q, K, V, beta, seg_len, dO, M0=None, z0=None, dM_S=None, dz_S=None,
 
 # ------------------------------------------------------------------ metrics
 
-def state_bytes(batch, kv_heads, head_dim, seq_len):
+def state_bytes(batch, kv_heads, head_dim, seq_len, fmap=Elu1):
     """Bytes of the carried fp32 state (M, z) for a call of any length ([HF]
     State Transfer: only the fixed-size memory crosses segments).  The
-    sequence length does not enter."""
+    sequence length does not enter; the feature map sets the key dimension."""
     del seq_len
-    return batch * kv_heads * (head_dim * head_dim + head_dim) * 4
+    n = fmap.dim(head_dim)
+    return batch * kv_heads * (n * head_dim + n) * 4

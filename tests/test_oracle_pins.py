@@ -599,3 +599,121 @@ def test_R14_state_sweep_matches_forward_state():
             r = O.seg_rows(S_b - 1, L, n)
             Mn, zn = O.memory_update(Msnap[b, 0, S_b - 1], zsnap[b, 0, S_b - 1], K[b, 0, r], V[b, 0, r])
             assert np.array_equal(Mn, M[b, 0]) and np.array_equal(zn, z[b, 0])
+
+
+# ----------------------------------------------------------- R15 Taylor feature map
+#
+# Page "Based", section "고정 크기 순환 상태를 사용하는 방법도 중요합니다":
+# phi(q) . phi(k) = 1 + q.k + (q.k)^2 / 2, the second-order Taylor series of
+# exp(q.k); the key dimension grows to about d^2.
+
+T2 = O.Taylor2
+
+
+@pytest.mark.parametrize("d", [1, 2, 5, 32])
+def test_R15_taylor_features_give_the_second_order_series(d):
+    q = _rand((7, d), 80 + d)
+    k = _rand((7, d), 90 + d)
+    got = np.sum(T2.phi(q) * T2.phi(k), axis=1)
+    t = np.sum(q * k, axis=1)
+    assert np.max(np.abs(got - (1.0 + t + 0.5 * t * t))) < 1e-12 * max(1.0, np.max(np.abs(got)))
+    assert T2.phi(q).shape == (7, 1 + d + d * d)
+    # and it approximates exp(q.k) to third order for small q.k
+    qs, ks = 1e-2 * q, 1e-2 * k
+    ts = np.sum(qs * ks, axis=1)
+    assert np.max(np.abs(np.sum(T2.phi(qs) * T2.phi(ks), axis=1) - np.exp(ts))) <= np.max(np.abs(ts)) ** 3
+
+
+def test_R15_taylor_vjp_matches_torch_autograd():
+    x = torch.tensor(_rand((5, 4), 81), dtype=torch.float64, requires_grad=True)
+    g = _rand((5, 1 + 4 + 16), 82)
+    # phi written independently in torch: ones, x, and the outer product over sqrt 2
+    phi = torch.cat([torch.ones(5, 1, dtype=torch.float64), x,
+                     torch.einsum("na,nb->nab", x, x).reshape(5, 16) / math.sqrt(2.0)], dim=1)
+    (phi * torch.tensor(g)).sum().backward()
+    assert np.max(np.abs(T2.vjp(x.detach().numpy(), g) - x.grad.numpy())) < 1e-13
+
+
+@pytest.mark.parametrize("state", [False, True])
+def test_R15_taylor_per_token_closed_form_agrees(state):
+    Q, K, V, beta = _problem(1, 2, 1, 10, 3, 83, scale=0.7)
+    M0 = z0 = None
+    if state:
+        Kp, Vp = _rand((1, 1, 4, 3), 84), _rand((1, 1, 4, 3), 85)
+        _, _, M0, z0 = O.state_sweep(Kp, Vp, 4, fmap=T2)
+    a = O.forward(Q, K, V, beta, 4, M0, z0, fmap=T2)[0]
+    b = O.forward_per_token(Q, K, V, beta, 4, M0, z0, fmap=T2)
+    assert max_rel_err(a, b) < 1e-12
+
+
+def test_R15_taylor_state_rows_have_closed_forms():
+    """Row 0 of M sums the values and z[0] counts the tokens (constant
+    feature); rows 1..d hold sum_j k_ja v_j (linear features); the state does
+    not depend on the segment length."""
+    Q, K, V, beta = _problem(2, 2, 2, 12, 3, 86)
+    _, M, z = O.forward(Q, K, V, beta, 5, fmap=T2)
+    assert np.max(np.abs(M[:, :, 0] - V.sum(axis=2))) < 1e-12
+    assert np.max(np.abs(z[:, :, 0] - 12.0)) < 1e-12
+    lin = np.einsum("bhja,bhjc->bhac", K, V)
+    assert np.max(np.abs(M[:, :, 1:4] - lin)) < 1e-12
+    quad = np.einsum("nhja,nhjb,nhjc->nhabc", K, K, V).reshape(2, 2, 9, 3) / math.sqrt(2.0)
+    assert np.max(np.abs(M[:, :, 4:] - quad)) < 1e-12
+    for L in (1, 3, 12):
+        _, M2, z2 = O.forward(Q, K, V, beta, L, fmap=T2)
+        assert max_rel_err(M2, M) < 1e-13 and max_rel_err(z2, z) < 1e-13
+
+
+def test_R15_taylor_denominator_stays_positive():
+    """1 + t + t^2 / 2 >= 1/2: even keys chosen to make q.k = -1 (the minimum)
+    keep sigma(Q) z above half the token count."""
+    d = 4
+    q = np.ones((1, d)) / 2.0
+    k = -q / float((q @ q.T)[0, 0])       # q.k = -1
+    Ks = np.repeat(k, 6, axis=0)
+    Vs = _rand((6, d), 87)
+    M, z = O.memory_update(np.zeros((T2.dim(d), d)), np.zeros(T2.dim(d)), Ks, Vs, T2)
+    _, _, den, _ = O.memory_retrieval(q, M, z, fmap=T2)
+    assert abs(den[0] - (3.0 + O.EPS)) < 1e-12
+
+
+def test_R15_taylor_gate_closed_is_unchanged_local_attention():
+    Q, K, V, beta = _problem(1, 2, 2, 9, 3, 88)
+    b = np.full(2, -np.inf)
+    a = O.forward(Q, K, V, b, 4)[0]
+    c = O.forward(Q, K, V, b, 4, fmap=T2)[0]
+    assert np.array_equal(a, c)
+
+
+def test_R15_taylor_backward_matches_central_differences():
+    Q, K, V, beta = _problem(1, 2, 1, 7, 2, 89, scale=0.8)
+    Kp, Vp = _rand((1, 1, 3, 2), 90), _rand((1, 1, 3, 2), 91)
+    _, _, M0, z0 = O.state_sweep(Kp, Vp, 3, fmap=T2)
+    dO = _rand(Q.shape, 92)
+    dMS = _rand(M0.shape, 93, 0.3)
+    dzS = _rand(z0.shape, 94, 0.3)
+    L = 3
+
+    def loss(Q_, K_, V_, b_, M_, z_):
+        o, m, zz = O.forward(Q_, K_, V_, b_, L, M_, z_, fmap=T2)
+        return float(np.sum(o * dO) + np.sum(m * dMS) + np.sum(zz * dzS))
+
+    g = O.backward(Q, K, V, beta, L, dO, M0, z0, dMS, dzS, fmap=T2)
+    args = [Q, K, V, beta, M0, z0]
+    names = ["dQ", "dK", "dV", "dbeta", "dM0", "dz0"]
+    h = 1e-6
+    for ai, name in enumerate(names):
+        x = args[ai]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(args), list(args)
+            ap[ai], am[ai] = xp, xm
+            fd[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+        assert max_rel_err(g[name], fd) < 1e-6, name
+
+
+def test_R15_taylor_state_size_is_fixed_by_head_dim():
+    for N in (64, 1 << 20):
+        assert O.state_bytes(4, 8, 64, N, fmap=T2) == 4 * 8 * ((1 + 64 + 64 * 64) * 64 + (1 + 64 + 64 * 64)) * 4
