@@ -129,11 +129,12 @@ def main():
                     help="untimed steps; the first few launches run slower while the GPU clocks ramp up")
     ap.add_argument("--workload", default="fwd_llama3_8b", choices=sorted(I.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="fwd", choices=["fwd", "train", "stream", "decode", "copy"],
+    ap.add_argument("--mode", default="fwd", choices=["fwd", "train", "stream", "decode", "copy", "taylor"],
                     help="fwd: forward throughput (default, the headline line); train: forward + "
                          "backward step; stream: chained single-segment launches carrying the state; "
                          "decode: token-by-token streaming decode through one segment; "
-                         "copy: a plain device copy of known size (calibrates HBM byte counters)")
+                         "copy: a plain device copy of known size (calibrates HBM byte counters); "
+                         "taylor: forward with the second-order Taylor feature map (200M-model shape)")
     ap.add_argument("--launches", type=int, default=512, help="stream mode: chained launches per step")
     ap.add_argument("--graph", action="store_true",
                     help="stream mode: capture the chained launches of one step in a HIP graph and replay it")
@@ -150,6 +151,8 @@ def main():
         return bench_copy(args)
     if args.mode == "decode":
         return bench_decode(args)
+    if args.mode == "taylor":
+        return bench_taylor(args)
 
     import torch
     from compressive_linear_memory_amd import binding as Bi
@@ -574,6 +577,59 @@ def bench_decode(args):
                       "us_per_token_eager": round(1e3 * ms_eager / L, 2), "graph": True,
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                       "data": "synthetic", "config": {"workload": "stream_1m", "mode": "decode", "tokens": L},
+                      "roofline": roof}), flush=True)
+
+
+def bench_taylor(args):
+    """Forward with the second-order Taylor feature map on the 200M-model
+    shape (B=8, H=12, d=64, seg_len 64, 16 segments, bf16): the memory path
+    carries 1 + d + d^2 = 4161 features per key, so the update and the
+    retrieval, on fp32 vector kernels, dominate."""
+    import torch
+    from compressive_linear_memory_amd import binding as Bi
+    Bi.lib()
+    w = I.WORKLOADS["fwd_200m"] if args.workload == "fwd_llama3_8b" else I.WORKLOADS[args.workload]
+    say(f"[bench] generating {w.name} inputs (Taylor feature map)")
+    Q, K, V = I.qkv(w)
+    tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    t = lambda x: torch.from_numpy(x).to(dev).to(tdt)
+    q, k, v = t(Q), t(K), t(V)
+    b = torch.from_numpy(I.beta(w)).to(dev)
+    p = Bi.problem(q, k, w.seg_len, "taylor2")
+    ws = torch.empty(Bi.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    B_, Hq, Hkv, N, d, L, S = w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.seg_len, w.segments
+    nf = Bi.feature_dim(d, "taylor2")
+    out = (torch.empty_like(q), torch.empty((B_, Hkv, nf, d), device=dev), torch.empty((B_, Hkv, nf), device=dev),
+           None)
+
+    def step():
+        Bi.attn_fwd(q, k, v, b, L, out=out, ws=ws, feature_map="taylor2")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # algorithmic work: local attention as for ELU + 1, retrieval 2 L D' d + 2 L D'
+    # per (b, query head, segment), update 2 L D' d + L D' per (b, K/V head, segment)
+    local = 2 * 2 * d * L * (L + 1) / 2
+    flop = B_ * Hq * S * (local + 2 * L * nf * d + 2 * L * nf) + B_ * Hkv * S * (2 * L * nf * d + L * nf)
+    ach = flop / (ms / 1e3) / 1e12
+    roof = dict(bound="alu", peak=PEAK_FP32_VECTOR_TFLOPS, unit="TFLOP/s", achieved=round(ach, 3),
+                frac=round(ach / PEAK_FP32_VECTOR_TFLOPS, 5), traffic=None,
+                kernel="infini_attn_fwd (Taylor feature map: sweep + retrieval + attention)", flop_per_step=flop)
+    print(json.dumps({"metric": f"Infini-attention fwd tokens/s, Taylor feature map ({w.name})",
+                      "value": round(B_ * N / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+                      "config": {"workload": w.name, "mode": "taylor", "feature_dim": nf, "io_dtype": w.dtype,
+                                 "kernel_path": Bi.fwd_path(p)},
                       "roofline": roof}), flush=True)
 
 

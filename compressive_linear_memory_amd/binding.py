@@ -18,13 +18,19 @@ LIB_PATH = os.path.join(HERE, "libinfini.so")
 
 INFINI_FP32, INFINI_BF16 = 0, 1
 _DTYPES = {torch.float32: INFINI_FP32, torch.bfloat16: INFINI_BF16}
+FEATURE_MAPS = {"elu1": 0, "taylor2": 1}
+
+
+def feature_dim(head_dim: int, feature_map: str = "elu1") -> int:
+    """Rows of the memory M (features per key) for a feature map."""
+    return head_dim if feature_map == "elu1" else 1 + head_dim + head_dim * head_dim
 
 
 class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32),
                 ("kv_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("seg_len", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("feature_map", ctypes.c_int32)]
 
 
 class InfiniError(RuntimeError):
@@ -79,13 +85,15 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def problem(q: torch.Tensor, k: torch.Tensor, seg_len: int) -> Problem:
+def problem(q: torch.Tensor, k: torch.Tensor, seg_len: int, feature_map: str = "elu1") -> Problem:
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be [batch, heads, seq_len, head_dim]")
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
+    if feature_map not in FEATURE_MAPS:
+        raise ValueError(f"unknown feature map {feature_map}")
     B, Hq, N, d = q.shape
-    return Problem(B, Hq, k.shape[1], N, d, int(seg_len), _DTYPES[q.dtype])
+    return Problem(B, Hq, k.shape[1], N, d, int(seg_len), _DTYPES[q.dtype], FEATURE_MAPS[feature_map])
 
 
 def workspace_bytes(p: Problem, backward: bool = False) -> int:
@@ -114,32 +122,35 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def attn_fwd(q, k, v, beta, seg_len, M0=None, z0=None, want_lse=False, out=None, ws=None, seq_lens=None):
+def attn_fwd(q, k, v, beta, seg_len, M0=None, z0=None, want_lse=False, out=None, ws=None, seq_lens=None,
+             feature_map="elu1"):
     """O, M_S, z_S (and lse if want_lse) of one call; see include/infini.h.
 
     `out` may hold preallocated (O, M_S, z_S, lse) tensors and `ws` a uint8
     workspace tensor, so that a timed loop allocates nothing.  `seq_lens`
     (int32 [batch] on the device) makes it a variable-length batch
-    (infini_attn_fwd_varlen)."""
-    p = problem(q, k, seg_len)
+    (infini_attn_fwd_varlen).  `feature_map` "taylor2" selects the
+    second-order Taylor map: the state then has 1 + d + d^2 rows."""
+    p = problem(q, k, seg_len, feature_map)
     dev = q.device
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
+    nf = feature_dim(d, feature_map)
     for name, t, dt, shp in (("k", k, q.dtype, (B, Hkv, N, d)), ("v", v, q.dtype, (B, Hkv, N, d)),
                              ("beta", beta, torch.float32, (Hq,)),
-                             ("M0", M0, torch.float32, (B, Hkv, d, d)), ("z0", z0, torch.float32, (B, Hkv, d))):
+                             ("M0", M0, torch.float32, (B, Hkv, nf, d)), ("z0", z0, torch.float32, (B, Hkv, nf))):
         _check(name, t, dt, shp, dev)
     _check("q", q, q.dtype, q.shape, dev)
     _check("seq_lens", seq_lens, torch.int32, (B,), dev)
     if out is None:
         O = torch.empty_like(q)
-        M_S = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=dev)
-        z_S = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
+        M_S = torch.empty((B, Hkv, nf, d), dtype=torch.float32, device=dev)
+        z_S = torch.empty((B, Hkv, nf), dtype=torch.float32, device=dev)
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if want_lse else None
     else:
         O, M_S, z_S, lse = out
-        for name, t, dt, shp in (("O", O, q.dtype, q.shape), ("M_S", M_S, torch.float32, (B, Hkv, d, d)),
-                                 ("z_S", z_S, torch.float32, (B, Hkv, d)), ("lse", lse, torch.float32, (B, Hq, N))):
+        for name, t, dt, shp in (("O", O, q.dtype, q.shape), ("M_S", M_S, torch.float32, (B, Hkv, nf, d)),
+                                 ("z_S", z_S, torch.float32, (B, Hkv, nf)), ("lse", lse, torch.float32, (B, Hq, N))):
             _check(name, t, dt, shp, dev)
     if ws is None:
         ws = torch.empty(max(workspace_bytes(p), 1), dtype=torch.uint8, device=dev)

@@ -27,6 +27,9 @@ bool valid_problem(const infini_problem_t* p, infini_status_t* why) {
     *why = INFINI_ERR_UNSUPPORTED; return false;
   }
   if (p->dtype != INFINI_FP32 && p->dtype != INFINI_BF16) { *why = INFINI_ERR_UNSUPPORTED; return false; }
+  if (p->feature_map != INFINI_FEATURE_ELU1 && p->feature_map != INFINI_FEATURE_TAYLOR2) {
+    *why = INFINI_ERR_UNSUPPORTED; return false;
+  }
   // Every index the kernels form must fit comfortably in 64 bits and every
   // per-call count in 32 bits.
   const double elems = (double)p->batch * p->q_heads * p->seq_len * p->head_dim;
@@ -37,7 +40,7 @@ bool valid_problem(const infini_problem_t* p, infini_status_t* why) {
 Geometry geometry(const infini_problem_t* p) {
   Geometry g;
   g.B = p->batch; g.Hq = p->q_heads; g.Hkv = p->kv_heads; g.N = p->seq_len;
-  g.D = p->head_dim; g.L = p->seg_len; g.dtype = p->dtype;
+  g.D = p->head_dim; g.L = p->seg_len; g.dtype = p->dtype; g.fmap = p->feature_map;
   // the last segment may be shorter; formed in 64 bits (seq_len + seg_len
   // can exceed the 32-bit range)
   g.S = (int)(((int64_t)p->seq_len + p->seg_len - 1) / p->seg_len);
@@ -59,14 +62,29 @@ size_t elem_bytes(const Geometry& g) { return g.dtype == INFINI_FP32 ? 4 : 2; }
 
 // ---- workspace layouts (byte offsets, 256-aligned)
 
-struct FwdWs { size_t Msnap, zsnap, MsnapT, dz, total; };
+struct FwdWs { size_t Msnap, zsnap, MsnapT, dz, Amem, total; };
+
+// Features per key of the problem's memory path (the rows of M).
+size_t feature_dim(const Geometry& g) { return g.fmap == INFINI_FEATURE_TAYLOR2 ? infini::taylor_dim(g.D) : g.D; }
+
+// Only the forward entry points take the Taylor feature map.
+bool elu_only(const infini_problem_t* p) { return p && p->feature_map != INFINI_FEATURE_ELU1; }
 // parts: key splits per segment of the matrix-core memory phase (0: the
 // library's choice for g)
 FwdWs fwd_layout(const Geometry& g, int parts_of = 0) {
   const size_t C = (size_t)(g.S < kMaxChunkSegments ? g.S : kMaxChunkSegments);
   const size_t bk = (size_t)g.B * g.Hkv;
-  FwdWs w;
+  FwdWs w{};
   size_t off = 0;
+  if (g.fmap == INFINI_FEATURE_TAYLOR2) {   // fp32 snapshots over D' features, and the retrieved rows
+    const size_t nf = feature_dim(g);
+    w.Msnap = off; off = align_up(off + bk * C * nf * g.D * 4);
+    w.zsnap = off; off = align_up(off + bk * C * nf * 4);
+    w.Amem = off;  off = align_up(off + (size_t)g.B * g.Hq * C * g.L * g.D * 4);
+    w.MsnapT = w.dz = off;
+    w.total = off;
+    return w;
+  }
   // The matrix-core path keeps its per-segment dM parts (one per key split)
   // where the generic path keeps fp32 snapshots.
   const bool mfma = infini::fwd_mfma_supported(g);
@@ -75,6 +93,7 @@ FwdWs fwd_layout(const Geometry& g, int parts_of = 0) {
   w.zsnap = off; off = align_up(off + bk * C * g.D * 4);
   w.MsnapT = off; off = align_up(off + (mfma ? bk * C * g.D * g.D * 2 : 0));
   w.dz = off;     off = align_up(off + (mfma ? bk * C * parts * g.D * 4 : 0));
+  w.Amem = off;
   w.total = off;
   return w;
 }
@@ -86,6 +105,17 @@ hipError_t run_fwd_chunk(const Geometry& g, const FwdWs& lay, char* base, const 
                          int s1, hipStream_t st, bool memory, bool attend) {
   float* Msnap = reinterpret_cast<float*>(base + lay.Msnap);
   float* zsnap = reinterpret_cast<float*>(base + lay.zsnap);
+  if (g.fmap == INFINI_FEATURE_TAYLOR2) {
+    float* Amem = reinterpret_cast<float*>(base + lay.Amem);
+    if (memory) {
+      hipError_t e = infini::launch_taylor_sweep(g, K, V, Min, zin, M_S, z_S, Msnap, zsnap, s0, s1, st);
+      if (e != hipSuccess) return e;
+    }
+    if (!attend) return hipSuccess;
+    hipError_t e = infini::launch_taylor_retrieve(g, Q, Msnap, zsnap, Amem, s0, s1, st);
+    if (e != hipSuccess) return e;
+    return infini::launch_fwd_generic(g, Q, K, V, beta, nullptr, nullptr, O, lse, s0, s1, st, Amem);
+  }
   const bool mfma = infini::fwd_mfma_supported(g);
   void* MsnapT = mfma ? base + lay.MsnapT : nullptr;
   if (memory) {
@@ -226,6 +256,7 @@ const char* infini_fwd_path(const infini_problem_t* p) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return nullptr;
   const Geometry g = geometry(p);
+  if (g.fmap == INFINI_FEATURE_TAYLOR2) return "generic_fp32_taylor2";
   if (infini::fwd_short_supported(g)) return "mfma_bf16_short";
   return infini::fwd_mfma_supported(g) ? "mfma_bf16" : "generic_fp32";
 }
@@ -244,7 +275,7 @@ size_t infini_fwd_saved_bytes(const infini_problem_t* p) {
 
 size_t infini_bwd_workspace_bytes(const infini_problem_t* p) {
   infini_status_t why;
-  if (!valid_problem(p, &why)) return 0;
+  if (!valid_problem(p, &why) || elu_only(p)) return 0;
   return bwd_layout(geometry(p)).total;
 }
 
@@ -261,7 +292,8 @@ static infini_status_t attn_fwd_impl(const infini_problem_t* p, const int32_t* l
   if (reinterpret_cast<uintptr_t>(lens) & 3) return INFINI_ERR_UNSUPPORTED;
   const size_t eb = elem_bytes(g);
   const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
-  const size_t nM = (size_t)g.B * g.Hkv * g.D * g.D * 4, nz = (size_t)g.B * g.Hkv * g.D * 4;
+  const size_t nf = feature_dim(g);
+  const size_t nM = (size_t)g.B * g.Hkv * nf * g.D * 4, nz = (size_t)g.B * g.Hkv * nf * 4;
   // tensors of no elements may be null (torch gives them no storage)
   if ((nq && (!Q || !O)) || (nkv && (!K || !V)) || !beta || (nM && (!M_S || !z_S))) return INFINI_ERR_NULL;
   if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
@@ -321,6 +353,7 @@ infini_status_t infini_fwd_memory(const infini_problem_t* p, const void* K, cons
                                   void* ws, size_t ws_bytes, void* stream) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
+  if (elu_only(p)) return INFINI_ERR_UNSUPPORTED;
   const Geometry g = geometry(p);
   const size_t eb = elem_bytes(g);
   const size_t nkv = (size_t)g.B * g.Hkv * g.N * g.D;
@@ -349,6 +382,7 @@ infini_status_t infini_fwd_attend(const infini_problem_t* p, const void* Q, cons
                                   const void* ws, size_t ws_bytes, void* stream) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
+  if (elu_only(p)) return INFINI_ERR_UNSUPPORTED;
   const Geometry g = geometry(p);
   const size_t eb = elem_bytes(g);
   const size_t nq = (size_t)g.B * g.Hq * g.N * g.D, nkv = (size_t)g.B * g.Hkv * g.N * g.D;
@@ -387,7 +421,7 @@ size_t stream_stage_bytes(const Geometry& g, int group) {
 
 size_t infini_fwd_stream_workspace_bytes(const infini_problem_t* p, int n_pipe, int group) {
   infini_status_t why;
-  if (!valid_problem(p, &why) || n_pipe < 1 || group < 1 || group > INFINI_STREAM_MAX_GROUP) return 0;
+  if (!valid_problem(p, &why) || elu_only(p) || n_pipe < 1 || group < 1 || group > INFINI_STREAM_MAX_GROUP) return 0;
   const Geometry g = geometry(p);
   if (g.S > kMaxChunkSegments) return 0;
   if (infini::fwd_mfma_supported(g) && group * g.S > kMaxChunkSegments) return 0;
@@ -401,6 +435,7 @@ infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, con
                                   void* const* events) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
+  if (elu_only(p)) return INFINI_ERR_UNSUPPORTED;
   if (n_launches < 1 || n_pipe < 1 || group < 1 || group > INFINI_STREAM_MAX_GROUP) return INFINI_ERR_SHAPE;
   if (p->seq_len == 0 || p->batch == 0) return INFINI_OK;  // no tokens: M and z stay as they are
   if (!Q || !K || !V || !O || !beta || !M || !z || !ws || !att_streams || !events) return INFINI_ERR_NULL;
@@ -489,6 +524,7 @@ static infini_status_t attn_bwd_impl(const infini_problem_t* p, const int32_t* l
                                      float* dM0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
+  if (elu_only(p)) return INFINI_ERR_UNSUPPORTED;
   Geometry g = geometry(p);
   g.lens = lens;
   if (reinterpret_cast<uintptr_t>(lens) & 3) return INFINI_ERR_UNSUPPORTED;
@@ -589,6 +625,7 @@ infini_status_t infini_attn_bwd_varlen(const infini_problem_t* p, const int32_t*
 // caches and of the memory update that closes the segment).
 static bool decode_problem(const infini_problem_t* p, int32_t pos, Geometry* seg, infini_status_t* why) {
   if (!valid_problem(p, why)) return false;
+  if (elu_only(p)) { *why = INFINI_ERR_UNSUPPORTED; return false; }
   // a decode step carries at least one token of at least one sequence
   if (p->seq_len < 1 || p->batch < 1 || pos < 0 || (int64_t)pos + p->seq_len > p->seg_len) {
     *why = INFINI_ERR_SHAPE;

@@ -575,7 +575,7 @@ __global__ void dbeta_finish_kernel(const float* __restrict__ beta, const float*
 }
 
 bool bwd_short_supported(const Geometry& g) {
-  return g.dtype == 1 && (g.D == 64 || g.D == 128) && g.L <= 64 && g.G() <= kBwdMaxGroup;
+  return g.fmap == 0 && g.dtype == 1 && (g.D == 64 || g.D == 128) && g.L <= 64 && g.G() <= kBwdMaxGroup;
 }
 
 hipError_t launch_bwd_short(const Geometry& g, const void* Q, const void* K, const void* V,

@@ -442,7 +442,7 @@ hipError_t launch_fwd_mfma_group(const Geometry& g, const FwdCallTable& tab, int
   return hipErrorInvalidValue;
 }
 
-bool fwd_mfma_supported(const Geometry& g) { return g.dtype == 1 && (g.D == 64 || g.D == 128); }
+bool fwd_mfma_supported(const Geometry& g) { return g.fmap == 0 && g.dtype == 1 && (g.D == 64 || g.D == 128); }
 
 hipError_t launch_fwd_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
                            const float* beta, const void* MsnapT, const float* zsnap, void* O,

@@ -321,7 +321,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 }
 
 bool fwd_short_supported(const Geometry& g) {
-  return g.dtype == 1 && (g.D == 64 || g.D == 128) && g.L <= 64;
+  return g.fmap == 0 && g.dtype == 1 && (g.D == 64 || g.D == 128) && g.L <= 64;
 }
 
 hipError_t launch_fwd_short(const Geometry& g, const void* Q, const void* K, const void* V,

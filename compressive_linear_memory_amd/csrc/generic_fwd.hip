@@ -147,7 +147,8 @@ __global__ __launch_bounds__(GF_THREADS) void fwd_generic_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ beta, const float* __restrict__ Msnap, const float* __restrict__ zsnap,
     T* __restrict__ O, float* __restrict__ lse,
-    int Hq, int Hkv, int N, int L, int s_begin, int nseg, float scale, const int* __restrict__ lens) {
+    int Hq, int Hkv, int N, int L, int s_begin, int nseg, float scale, const int* __restrict__ lens,
+    const float* __restrict__ Amem) {
   using RS = RowSplit<D>;
   constexpr int LPR = RS::LPR, DL = RS::DL, ROWS = RS::ROWS;
   constexpr int LDS_FLOATS = (2 * GF_KT * D > D * D + D) ? 2 * GF_KT * D : D * D + D;
@@ -218,29 +219,36 @@ __global__ __launch_bounds__(GF_THREADS) void fwd_generic_kernel(
     __syncthreads();
   }
 
-  // Retrieval from M_{s-1}, z_{s-1} and the gate.
-  const size_t snap = ((size_t)(b * Hkv + kvh) * nseg + sl);
-  for (int e = t; e < D * D; e += GF_THREADS) smem[e] = Msnap[snap * D * D + e];
-  for (int e = t; e < D; e += GF_THREADS) smem[D * D + e] = zsnap[snap * D + e];
-  __syncthreads();
-  const float* sM = smem;
-  const float* sz = smem + D * D;
+  // Retrieval from M_{s-1}, z_{s-1} (or the A_mem rows formed by another
+  // feature map's retrieval kernel) and the gate.
   float num[DL];
+  float inv_den = 1.f;
+  if (Amem) {
+    const float* ar = Amem + (((size_t)b * Hq + h) * ((size_t)nseg * L) + (size_t)sl * L + i) * D + part * DL;
 #pragma unroll
-  for (int c = 0; c < DL; ++c) num[c] = 0.f;
-  float den = 0.f;
-  const size_t qfull = qrow - part * DL;
-  for (int a = 0; a < D; ++a) {
-    const float sq = elu1(io<T>::load(Q, qfull + a));
-    den += sq * sz[a];
-    const float* mr = sM + a * D + part * DL;
+    for (int c = 0; c < DL; ++c) num[c] = ar[c];
+  } else {
+    const size_t snap = ((size_t)(b * Hkv + kvh) * nseg + sl);
+    for (int e = t; e < D * D; e += GF_THREADS) smem[e] = Msnap[snap * D * D + e];
+    for (int e = t; e < D; e += GF_THREADS) smem[D * D + e] = zsnap[snap * D + e];
+    __syncthreads();
+    const float* sM = smem;
+    const float* sz = smem + D * D;
 #pragma unroll
-    for (int c = 0; c < DL; ++c) num[c] += sq * mr[c];
+    for (int c = 0; c < DL; ++c) num[c] = 0.f;
+    float den = 0.f;
+    const size_t qfull = qrow - part * DL;
+    for (int a = 0; a < D; ++a) {
+      const float sq = elu1(io<T>::load(Q, qfull + a));
+      den += sq * sz[a];
+      const float* mr = sM + a * D + part * DL;
+#pragma unroll
+      for (int c = 0; c < DL; ++c) num[c] += sq * mr[c];
+    }
+    inv_den = 1.f / (den + 1e-6f);
   }
-  den += 1e-6f;
   const float gt = sigmoid(beta[h]);
   const float inv_l = 1.f / l;
-  const float inv_den = 1.f / den;
   if (valid) {
 #pragma unroll
     for (int c = 0; c < DL; ++c) {
@@ -255,21 +263,21 @@ __global__ __launch_bounds__(GF_THREADS) void fwd_generic_kernel(
 template <typename T, int D>
 static hipError_t fwd_t(const Geometry& g, const void* Q, const void* K, const void* V,
                         const float* beta, const float* Msnap, const float* zsnap, void* O,
-                        float* lse, int s_begin, int s_end, hipStream_t st) {
+                        float* lse, int s_begin, int s_end, hipStream_t st, const float* Amem) {
   using RS = RowSplit<D>;
   const int nseg = s_end - s_begin;
   dim3 grid((g.L + RS::ROWS - 1) / RS::ROWS, g.Hq, g.B * nseg);
   hipLaunchKernelGGL((fwd_generic_kernel<T, D>), grid, dim3(GF_THREADS), 0, st,
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
                      beta, Msnap, zsnap, static_cast<T*>(O), lse, g.Hq, g.Hkv, g.N, g.L, s_begin,
-                     nseg, 1.f / sqrtf((float)D), g.lens);
+                     nseg, 1.f / sqrtf((float)D), g.lens, Amem);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_generic(const Geometry& g, const void* Q, const void* K, const void* V,
                               const float* beta, const float* Msnap, const float* zsnap, void* O,
-                              float* lse, int s_begin, int s_end, hipStream_t st) {
-#define GF_CASE(T, DD) return fwd_t<T, DD>(g, Q, K, V, beta, Msnap, zsnap, O, lse, s_begin, s_end, st)
+                              float* lse, int s_begin, int s_end, hipStream_t st, const float* Amem) {
+#define GF_CASE(T, DD) return fwd_t<T, DD>(g, Q, K, V, beta, Msnap, zsnap, O, lse, s_begin, s_end, st, Amem)
   if (g.dtype == 0) {
     if (g.D == 32) GF_CASE(float, 32);
     if (g.D == 64) GF_CASE(float, 64);

@@ -15,8 +15,23 @@ struct Geometry {
   // tokens in the first rows of its N-row slot (clamped to [0, N] where
   // read).  NULL: every sequence has N tokens.
   const int* lens = nullptr;
+  // Feature map of the memory path: 0 = ELU + 1 (feature dim D), 1 = the
+  // second-order Taylor map (feature dim 1 + D + D^2).
+  int fmap = 0;
   int G() const { return Hq / Hkv; }
 };
+
+// Second-order Taylor feature map (fp32 vector kernels, any dtype and head
+// dim): the memory path over D' = taylor_dim(D) features, and the retrieval
+// A_mem = phi(Q) M / (phi(Q) z + eps) of every row into Amem
+// ([B][Hq][nseg * L][D] fp32, the layout the generic attention kernel reads).
+// Msnap [B*Hkv][nseg][D'][D], zsnap [B*Hkv][nseg][D'].
+size_t taylor_dim(int D);
+hipError_t launch_taylor_sweep(const Geometry& g, const void* K, const void* V, const float* M_in,
+                               const float* z_in, float* M_out, float* z_out, float* Msnap, float* zsnap,
+                               int s_begin, int s_end, hipStream_t st);
+hipError_t launch_taylor_retrieve(const Geometry& g, const void* Q, const float* Msnap, const float* zsnap,
+                                  float* Amem, int s_begin, int s_end, hipStream_t st);
 
 // Zero rows [lens[b], N) of every (b, h) slot of X ([B][H][N][row_words]
 // 32-bit words per row): the rows past each sequence's end.
@@ -94,9 +109,12 @@ hipError_t launch_bwd_short(const Geometry& g, const void* Q, const void* K, con
 // dst[i] = src ? src[i] : 0 for i < n.
 hipError_t launch_state_copy(float* dst, const float* src, size_t n, hipStream_t st);
 
+// Amem: when not NULL, the retrieved A_mem of every row ([B][Hq][nseg * L][D]
+// fp32) is read from it instead of being formed from Msnap / zsnap.
 hipError_t launch_fwd_generic(const Geometry& g, const void* Q, const void* K, const void* V,
                               const float* beta, const float* Msnap, const float* zsnap,
-                              void* O, float* lse, int s_begin, int s_end, hipStream_t st);
+                              void* O, float* lse, int s_begin, int s_end, hipStream_t st,
+                              const float* Amem = nullptr);
 
 // Generic backward pieces, over segments [s_begin, s_end) (one chunk).
 struct BwdChunkWs {

@@ -31,8 +31,10 @@
  *   Q, O, dQ, dO : [batch][q_heads][seq_len][head_dim]     dtype of the problem
  *   K, V, dK, dV : [batch][kv_heads][seq_len][head_dim]    dtype of the problem
  *   beta, dbeta  : [q_heads]                                float32
- *   M*, dM*      : [batch][kv_heads][head_dim][head_dim]    float32, M[a][c] = key-feature a, value c
- *   z*, dz*      : [batch][kv_heads][head_dim]              float32
+ *   M*, dM*      : [batch][kv_heads][D'][head_dim]          float32, M[a][c] = key-feature a, value c
+ *   z*, dz*      : [batch][kv_heads][D']                    float32
+ *                  (D' = head_dim for the default feature map; see
+ *                  infini_feature_map_t)
  *   lse          : [batch][q_heads][seq_len]                float32, natural-log
  *                  log-sum-exp of each row's scaled local scores
  *
@@ -74,8 +76,9 @@ typedef enum {
   INFINI_ERR_NULL = 1,        /* a required pointer is NULL                                   */
   INFINI_ERR_SHAPE = 2,       /* a negative batch or seq_len, another dim <= 0, or
                                  q_heads % kv_heads != 0                                       */
-  INFINI_ERR_UNSUPPORTED = 3, /* head_dim not 32, 64 or 128, unknown dtype, or a tensor pointer
-                                 (any but beta, dbeta, lse) not 16-byte aligned                */
+  INFINI_ERR_UNSUPPORTED = 3, /* head_dim not 32, 64 or 128, unknown dtype or feature map, a
+                                 feature map the entry point does not support, or a tensor
+                                 pointer (any but beta, dbeta, lse) not 16-byte aligned        */
   INFINI_ERR_ALIAS = 4,       /* an output buffer overlaps an input or another output          */
   INFINI_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returns          */
   INFINI_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed                      */
@@ -84,6 +87,22 @@ typedef enum {
 } infini_status_t;
 
 typedef enum { INFINI_FP32 = 0, INFINI_BF16 = 1 } infini_dtype_t;
+
+/* Feature map of the memory path.
+ *   INFINI_FEATURE_ELU1     sigma(x) = ELU(x) + 1 elementwise; M is
+ *                           [head_dim][head_dim], z has head_dim entries.
+ *   INFINI_FEATURE_TAYLOR2  the second-order Taylor map of the page "Based"
+ *                           (cartesia.ai), section "고정 크기 순환 상태를 사용하는
+ *                           방법도 중요합니다": phi(x) = [1, x_1..x_d,
+ *                           x_a x_b / sqrt(2) for a, b = 1..d, a major], so that
+ *                           phi(q) . phi(k) = 1 + q.k + (q.k)^2 / 2, applied to
+ *                           Q and K as given.  D' = 1 + d + d^2 features: M is
+ *                           [D'][head_dim], z has D' entries, row f of M holding
+ *                           feature f.  Supported by infini_attn_fwd and
+ *                           infini_attn_fwd_varlen (fp32 vector kernels, any
+ *                           dtype and head_dim); every other entry point returns
+ *                           INFINI_ERR_UNSUPPORTED for it. */
+typedef enum { INFINI_FEATURE_ELU1 = 0, INFINI_FEATURE_TAYLOR2 = 1 } infini_feature_map_t;
 
 /* One call's problem.  The carried state is always float32.
  *
@@ -101,6 +120,7 @@ typedef struct {
   int32_t head_dim;   /* 32, 64 or 128; keys, queries and values share it                            */
   int32_t seg_len;    /* tokens per segment                                                          */
   int32_t dtype;      /* infini_dtype_t of Q, K, V, O, dO, dQ, dK, dV                                */
+  int32_t feature_map; /* infini_feature_map_t of the memory path (0 = ELU + 1)                      */
 } infini_problem_t;
 
 /* Workspace bytes for infini_attn_fwd.  Bounded by a constant times

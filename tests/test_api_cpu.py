@@ -301,3 +301,22 @@ def test_varlen_entry_points_validate_before_launch(L):
     lens_in_dQ = ctypes.c_void_p(a[10].value + 16)
     assert L.infini_attn_bwd_varlen(ctypes.byref(p), lens_in_dQ, *a[:16], FAKE[19], 1 << 30, None) == 4
     assert L.infini_attn_bwd_varlen(None, FAKE[19], *a[:16], None, 0, None) == 1
+
+
+def test_taylor_feature_map_only_on_the_forward(L):
+    """The Taylor feature map is taken by infini_attn_fwd(_varlen) only; the
+    other entry points return INFINI_ERR_UNSUPPORTED (3) before any launch,
+    and an unknown feature map is refused everywhere."""
+    p = binding.Problem(1, 2, 2, 64, 32, 16, 0, 1)
+    assert L.infini_fwd_path(ctypes.byref(p)) == b"generic_fp32_taylor2"
+    assert L.infini_fwd_workspace_bytes(ctypes.byref(p)) > 0
+    assert L.infini_bwd_workspace_bytes(ctypes.byref(p)) == 0
+    assert L.infini_fwd_stream_workspace_bytes(ctypes.byref(p), 1, 1) == 0
+    assert L.infini_decode_workspace_bytes(ctypes.byref(binding.Problem(1, 2, 2, 1, 32, 16, 0, 1))) == 0
+    a = [FAKE[i] for i in range(20)]
+    assert L.infini_attn_bwd(ctypes.byref(p), *a[:16], a[16], 1 << 30, None) == 3
+    assert L.infini_fwd_memory(ctypes.byref(p), *a[:6], a[16], 1 << 30, None) == 3
+    assert L.infini_fwd_attend(ctypes.byref(p), *a[:6], a[16], 1 << 30, None) == 3
+    bad = binding.Problem(1, 2, 2, 64, 32, 16, 0, 7)
+    assert L.infini_fwd_path(ctypes.byref(bad)) is None
+    assert L.infini_attn_fwd(ctypes.byref(bad), *a[:10], a[16], 1 << 30, None) == 3

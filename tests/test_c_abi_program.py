@@ -22,7 +22,7 @@ PROGRAM = r"""
 #define CHECK(cond) do { if (!(cond)) { printf("FAILED: %s (line %d)\n", #cond, __LINE__); return 1; } } while (0)
 
 int main(void) {
-  infini_problem_t p = {1, 4, 2, 64, 64, 16, INFINI_BF16};
+  infini_problem_t p = {1, 4, 2, 64, 64, 16, INFINI_BF16, INFINI_FEATURE_ELU1};
   char fake[64];
   void* a = fake;
   const float* fa = (const float*)fake;
@@ -45,7 +45,7 @@ int main(void) {
   CHECK(infini_attn_fwd(&bad, a, a, a, fa, NULL, NULL, a, fo, fo, NULL, a, 0, NULL) == INFINI_ERR_UNSUPPORTED);
   /* a workspace smaller than the query returns (long segments: memory phase
      then attention phase) */
-  infini_problem_t lp = {1, 4, 2, 256, 64, 128, INFINI_BF16};
+  infini_problem_t lp = {1, 4, 2, 256, 64, 128, INFINI_BF16, INFINI_FEATURE_ELU1};
   CHECK(infini_attn_fwd(&lp, a, a, a, fa, NULL, NULL, a, fo, fo, NULL, a,
                         infini_fwd_workspace_bytes(&lp) - 1, NULL) == INFINI_ERR_WORKSPACE);
   /* the fused short-segment forward needs none: with no workspace the call

@@ -456,6 +456,62 @@ def test_varlen_full_lengths_equal_uniform_call():
         assert torch.equal(x, y)
 
 
+# ------------------------------------------------------------------ Taylor feature map
+
+TAYLOR_CASES = [
+    # B, Hq, Hkv, N, d, L, dtype, state, lengths
+    (1, 2, 2, 64, 32, 16, "fp32", True, None),
+    (2, 4, 2, 150, 32, 48, "fp32", False, None),           # GQA, ragged tail
+    (1, 2, 1, 96, 64, 40, "fp32", True, None),
+    (2, 4, 2, 128, 64, 64, "bf16", True, None),
+    (1, 2, 2, 70, 128, 32, "bf16", True, None),             # 16513 features
+    (1, 2, 2, 40, 128, 40, "fp32", False, None),
+    (3, 2, 2, 100, 32, 16, "fp32", True, [100, 0, 57]),     # variable lengths
+]
+
+
+@pytest.mark.parametrize("case", TAYLOR_CASES, ids=lambda c: "-".join(map(str, c[:8])) + (
+    "-" + "_".join(map(str, c[8])) if c[8] else ""))
+def test_taylor_feature_map_forward(case):
+    """The memory path with the second-order Taylor map (state of
+    1 + d + d^2 rows) against the oracle with the same map."""
+    Bn, Hq, Hkv, N, d, L, dtype, st, lens = case
+    Q, K, V, beta, _, _ = make(Bn, Hq, Hkv, N, d, dtype, seed=13 * N + d)
+    M0 = z0 = None
+    if st:
+        Kp = rnd((Bn, Hkv, 24, d), 5 + d, 1.0 / np.sqrt(d), dtype)
+        Vp = rnd((Bn, Hkv, 24, d), 6 + d, 1.0 / np.sqrt(d), dtype)
+        _, _, M0, z0 = O.state_sweep(Kp, Vp, 24, fmap=O.Taylor2)
+        M0, z0 = M0.astype(np.float32), z0.astype(np.float32)
+    log(f"taylor fwd Q{Q.shape} L={L} {dtype} state={st} lens={lens}")
+    Bi = B()
+    nf = Bi.feature_dim(d, "taylor2")
+    td = torch.float32 if dtype == "fp32" else torch.bfloat16
+    from gpu_util import guarded
+    gs = [guarded(Q.shape, td), guarded((Bn, Hkv, nf, d), torch.float32), guarded((Bn, Hkv, nf), torch.float32),
+          guarded((Bn, Hq, N), torch.float32)]
+    q = dev(Q, dtype)
+    assert Bi.fwd_path(Bi.problem(q, dev(K, dtype), L, "taylor2")) == "generic_fp32_taylor2"
+    Bi.attn_fwd(q, dev(K, dtype), dev(V, dtype), dev(beta), L, dev(M0), dev(z0), want_lse=True,
+                out=tuple(x.t for x in gs), seq_lens=dev_lens(lens), feature_map="taylor2")
+    torch.cuda.synchronize()
+    for name, x in zip(("O", "M_S", "z_S", "lse"), gs):
+        x.check(name)
+    ro, rM, rz, rl = O.forward(Q, K, V, beta, L, M0, z0, want_lse=True, lens=lens, fmap=O.Taylor2)
+    errs = [rel(host(x.t), r) for x, r in zip(gs, (ro, rM, rz, rl))]
+    log("   err O {:.2e} M {:.2e} z {:.2e} lse {:.2e}".format(*errs))
+    assert all(e < TOL[dtype] for e in errs), errs
+
+
+def test_taylor_multi_chunk(monkeypatch):
+    monkeypatch.setenv("INFINI_CHUNK_SEGMENTS", "3")
+    Q, K, V, beta, _, _ = make(1, 2, 2, 8 * 8, 32, "fp32", seed=77)
+    o, M, z = B().attn_fwd(dev(Q), dev(K), dev(V), dev(beta), 8, feature_map="taylor2")
+    torch.cuda.synchronize()
+    ro, rM, rz = O.forward(Q, K, V, beta, 8, fmap=O.Taylor2)
+    assert rel(host(o), ro) < 1e-4 and rel(host(M), rM) < 1e-4 and rel(host(z), rz) < 1e-4
+
+
 # ------------------------------------------------------------------ gate limits
 
 def test_kernel_path_selection():
