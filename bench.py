@@ -85,10 +85,13 @@ def recorded_traffic(w, path):
 
 
 def cpu_baseline(w, Q, K, V, beta, o_gpu_host_rows, budget_s=12.0):
-    """Time the fp64 oracle on a bounded sample of the same workload."""
+    """Time the fp64 oracle on a bounded sample of the same workload, with
+    numpy's BLAS given every core this process may run on."""
     import oracle as O
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(limits=cores, user_api="blas")
         threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = 1
@@ -115,7 +118,7 @@ def cpu_baseline(w, Q, K, V, beta, o_gpu_host_rows, budget_s=12.0):
     est = t_sweep + per_unit * total_units
     tok = w.batch * w.seq_len
     err = max(e for e, _ in errs) / max(m for _, m in errs)
-    return dict(value=tok / est, unit="tokens/s", cores=int(threads), kind="oracle",
+    return dict(value=tok / est, unit="tokens/s", cores=int(cores), blas_threads=int(threads), kind="oracle",
                 sample=(f"full fp64 state sweep ({t_sweep:.2f} s) + {units} of {total_units} "
                         f"(batch, head, segment) units in full ({t_units:.2f} s); "
                         f"whole-workload time extrapolated as sweep + per-unit x units = {est:.1f} s")), err
@@ -138,6 +141,9 @@ def main():
     ap.add_argument("--launches", type=int, default=512, help="stream mode: chained launches per step")
     ap.add_argument("--graph", action="store_true",
                     help="stream mode: capture the chained launches of one step in a HIP graph and replay it")
+    ap.add_argument("--decode-tokens", type=int, default=0,
+                    help="decode mode: decode only the last N tokens of the segment (the cache prefilled "
+                         "with the rest); 0 = the whole segment")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the sequence-parallel "
@@ -531,9 +537,13 @@ def bench_decode(args):
                      device=dev)
     rows = [(q[:, :, i:i + 1].contiguous(), k[:, :, i:i + 1].contiguous(), v[:, :, i:i + 1].contiguous(),
              O_[i]) for i in range(L)]
+    first = L - args.decode_tokens if 0 < args.decode_tokens < L else 0
+    if first:   # the cache holds the segment's earlier rows already
+        kc[:, :, :first] = k[:, :, :first]
+        vc[:, :, :first] = v[:, :, :first]
 
     def run():
-        for i in range(L):
+        for i in range(first, L):
             qi, ki, vi, oi = rows[i]
             Bi.decode(qi, ki, vi, b, L, i, kc, vc, M, z, out=oi, state_out=(Mn, zn), ws=ws)
 
@@ -560,23 +570,24 @@ def bench_decode(args):
     graph.replay()
     torch.cuda.synchronize()
     ms = timed(graph.replay)
-    say(f"[bench] decode: {1e3 * ms_eager / L:.2f} us/token eager, {1e3 * ms / L:.2f} us/token graph-replayed")
-    # Algorithmic bytes of one segment decoded token by token: for token i the
+    T = L - first                                   # tokens per step
+    say(f"[bench] decode: {1e3 * ms_eager / T:.2f} us/token eager, {1e3 * ms / T:.2f} us/token graph-replayed")
+    # Algorithmic bytes of the step's tokens decoded one by one: for token i the
     # cached rows 0..i of K and V, its own Q/K/V/O rows and the state read once;
     # the closing update reads the cache once and writes the state.
     eb = 2
-    kv_rows = B_ * H * L * (L + 1) // 2
-    step_bytes = (eb * 2 * d * kv_rows + L * (eb * d * (2 * w.q_heads + 2 * H) + B_ * H * (d * d + d) * 4)
+    kv_rows = B_ * H * (L * (L + 1) // 2 - first * (first + 1) // 2)
+    step_bytes = (eb * 2 * d * kv_rows + T * (eb * d * (2 * w.q_heads + 2 * H) + B_ * H * (d * d + d) * 4)
                   + eb * 2 * B_ * H * L * d + 2 * B_ * H * (d * d + d) * 4)
     ach = step_bytes / (ms / 1e3) / 1e9
     roof = dict(bound="hbm", peak=PEAK_HBM_GBS, unit="GB/s", achieved=round(ach, 1), frac=round(ach / PEAK_HBM_GBS, 5),
                 traffic=None, kernel="infini_decode, one token per call", bytes_per_step=step_bytes)
     print(json.dumps({"metric": "Infini-attention streaming decode tokens/s (stream_1m shape, one token per call)",
-                      "value": round(L / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-                      "warmup": args.warmup, "ms_per_step": round(ms, 4), "us_per_token": round(1e3 * ms / L, 2),
-                      "us_per_token_eager": round(1e3 * ms_eager / L, 2), "graph": True,
+                      "value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": round(ms, 4), "us_per_token": round(1e3 * ms / T, 2),
+                      "us_per_token_eager": round(1e3 * ms_eager / T, 2), "graph": True, "tokens_per_step": T,
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-                      "data": "synthetic", "config": {"workload": "stream_1m", "mode": "decode", "tokens": L},
+                      "data": "synthetic", "config": {"workload": "stream_1m", "mode": "decode", "seg_len": L, "tokens": T},
                       "roofline": roof}), flush=True)
 
 

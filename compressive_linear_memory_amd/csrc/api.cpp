@@ -578,13 +578,18 @@ static infini_status_t attn_bwd_impl(const infini_problem_t* p, const int32_t* l
 
   const int C = chunk_segments(g);
   const int nchunks = (g.S + C - 1) / C;
+  // The chunks are walked last to first.  With more than one, the memory path
+  // runs forward once to the state after the last chunk, and each chunk's
+  // start state is then recovered by taking that chunk's updates away again
+  // (linear in the number of chunks; the first chunk starts from M0 itself).
+  if (nchunks > 1) TRY(infini::launch_sweep(g, K, V, M0, z0, Mst, zst, nullptr, nullptr, 0, g.S, st));
   for (int ci = nchunks - 1; ci >= 0; --ci) {
     const int s0 = ci * C;
     const int s1 = s0 + C < g.S ? s0 + C : g.S;
     const float* Mstart = M0;
     const float* zstart = z0;
-    if (s0 > 0) {   // state at the chunk start: replay the memory path from M0
-      TRY(infini::launch_sweep(g, K, V, M0, z0, Mst, zst, nullptr, nullptr, 0, s0, st));
+    if (s0 > 0) {   // state at the chunk start
+      TRY(infini::launch_sweep(g, K, V, Mst, zst, Mst, zst, nullptr, nullptr, s0, s1, st, nullptr, true));
       Mstart = Mst; zstart = zst;
     }
     TRY(infini::launch_sweep(g, K, V, Mstart, zstart, nullptr, nullptr, Msnap, zsnap, s0, s1, st));

@@ -288,6 +288,20 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     const __bf16* Mlo = dMt;
 
     for (int h = kvh * G; h < (kvh + 1) * G; ++h) {
+      // register classes: the state, its gradient and the dK / dV
+      // accumulators are read only by the matrix cores inside this loop
+#pragma unroll
+      for (int x = 0; x < C::AB; ++x)
+#pragma unroll
+        for (int cb = 0; cb < C::DB; ++cb) {
+          asm volatile("" : "+a"(macc[x][cb]));
+          asm volatile("" : "+a"(dmacc[x][cb]));
+        }
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        asm volatile("" : "+a"(dkacc[db]));
+        asm volatile("" : "+a"(dvacc[db]));
+      }
       const size_t qb = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
       // this lane's dO pieces (row q, columns cb*16 + 4g ..) are read now and
       // used after the score and retrieval products
@@ -433,7 +447,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dap[ks], acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dsp[kb >> 1][(kb & 1) * 4 + i] = (__bf16)(pacc[kb][i] * (acc[i] - Dd));
+        for (int i = 0; i < 4; ++i) dsp[kb >> 1][(kb & 1) * 4 + i] = (__bf16)(scale * pacc[kb][i] * (acc[i] - Dd));
       }
       // dQ per 16 columns a: (dnum M^T + dden z) sigma'(Q) + scale dS K
       __bf16* dqp = dQ + qb + (size_t)q * D;
@@ -457,7 +471,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           bbf16x4 w;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            w[i] = (__bf16)((ret[i] + dden * zs[ab * 16 + 4 * g + i]) * elu1_grad((float)qv[i]) + scale * loc[i]);
+            w[i] = (__bf16)((ret[i] + dden * zs[ab * 16 + 4 * g + i]) * elu1_grad((float)qv[i]) + loc[i]);
           *reinterpret_cast<bbf16x4*>(dqp + ab * 16 + 4 * g) = w;
         }
       }
@@ -472,16 +486,15 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       if (g == 0) dds[q] = qok ? dden : 0.f;
       if (lane == 0) dbacc[h - kvh * G][wave] += bsum;   // each wave owns its slot: fixed order
       __syncthreads();
-      // key side, contracting over the segment's queries: dK^T += scale Q^T dS
+      // key side, contracting over the segment's queries: dK^T += Q^T dS
+      // (dS carries the softmax scale)
 #pragma unroll
       for (int ab = 0; ab < C::DB; ++ab) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const bbf16x8 a = tr_op(Qs, RS, ab * 16, 32 * t + 8 * g, 32 * t + 8 * g + 4, lane);
           const bbf16x8 bb = tr_op(Sb, PS, wave * 16, 32 * t + 8 * g, 32 * t + 8 * g + 4, lane);
-          bf32x4 acc = {};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc, 0, 0, 0);
-          dkacc[ab] += scale * acc;
+          dkacc[ab] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, dkacc[ab], 0, 0, 0);
         }
       }
       // Xb <- dA_dot rows times 1/l of their query row: Pb holds the

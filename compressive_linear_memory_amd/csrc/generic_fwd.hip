@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(
     const T* __restrict__ K, const T* __restrict__ V,
     const float* M_in, const float* z_in, float* M_out, float* z_out,
     float* __restrict__ Msnap, float* __restrict__ zsnap, bf16_t* __restrict__ MsnapT,
-    int N, int L, int s_begin, int s_end, const int* __restrict__ lens, int Hkv) {
+    int N, int L, int s_begin, int s_end, const int* __restrict__ lens, int Hkv, float sign) {
   constexpr int TPR = D / SW_TILE;                 // tiles per row of M
   const int tile = blockIdx.x;
   const int a0 = (tile / TPR) * SW_TILE;
@@ -83,9 +83,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(
       __syncthreads();
       const int jn = min(SW_KEYS, Ls - j0);
       for (int j = 0; j < jn; ++j) {
-        const float k = sK[j][ta];
+        const float k = sign * sK[j][ta];
         for (int c = 0; c < 4; ++c) acc[c] += k * sV[j][tc + c];
-        if (z_lane) zacc += sK[j][t];
+        if (z_lane) zacc += sign * sK[j][t];
       }
       __syncthreads();
     }
@@ -99,18 +99,19 @@ __global__ __launch_bounds__(256) void sweep_kernel(
 template <typename T, int D>
 static hipError_t sweep_t(const Geometry& g, const void* K, const void* V, const float* M_in,
                           const float* z_in, float* M_out, float* z_out, float* Msnap, float* zsnap,
-                          int s_begin, int s_end, hipStream_t st, void* MsnapT) {
+                          int s_begin, int s_end, hipStream_t st, void* MsnapT, float sign) {
   dim3 grid((D / SW_TILE) * (D / SW_TILE), g.B * g.Hkv);
   hipLaunchKernelGGL((sweep_kernel<T, D>), grid, dim3(256), 0, st,
                      static_cast<const T*>(K), static_cast<const T*>(V), M_in, z_in, M_out, z_out,
-                     Msnap, zsnap, static_cast<bf16_t*>(MsnapT), g.N, g.L, s_begin, s_end, g.lens, g.Hkv);
+                     Msnap, zsnap, static_cast<bf16_t*>(MsnapT), g.N, g.L, s_begin, s_end, g.lens, g.Hkv, sign);
   return hipGetLastError();
 }
 
 hipError_t launch_sweep(const Geometry& g, const void* K, const void* V, const float* M_in,
                         const float* z_in, float* M_out, float* z_out, float* Msnap, float* zsnap,
-                        int s_begin, int s_end, hipStream_t st, void* MsnapT) {
-#define SW_CASE(T, DD) return sweep_t<T, DD>(g, K, V, M_in, z_in, M_out, z_out, Msnap, zsnap, s_begin, s_end, st, MsnapT)
+                        int s_begin, int s_end, hipStream_t st, void* MsnapT, bool subtract) {
+  const float sign = subtract ? -1.f : 1.f;
+#define SW_CASE(T, DD) return sweep_t<T, DD>(g, K, V, M_in, z_in, M_out, z_out, Msnap, zsnap, s_begin, s_end, st, MsnapT, sign)
   if (g.dtype == 0) {
     if (g.D == 32) SW_CASE(float, 32);
     if (g.D == 64) SW_CASE(float, 64);

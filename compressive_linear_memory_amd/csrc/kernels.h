@@ -44,10 +44,12 @@ hipError_t launch_zero_tail(void* X, const int* lens, int B, int H, int N, size_
 //   (NULL = not written).
 //   MsnapT: optional bf16 copy of each snapshot, transposed ([c][a]), for the
 //   matrix-core forward (NULL = not written).
+//   subtract: take the segments' updates away instead (M_out = M_in -
+//   sum sigma(K)^T V): walks back from a later state to an earlier one.
 hipError_t launch_sweep(const Geometry& g, const void* K, const void* V,
                         const float* M_in, const float* z_in, float* M_out, float* z_out,
                         float* Msnap, float* zsnap, int s_begin, int s_end, hipStream_t st,
-                        void* MsnapT = nullptr);
+                        void* MsnapT = nullptr, bool subtract = false);
 
 // bf16 matrix-core memory phase (head_dim 64 or 128): per-segment dM, dz into
 // the scratch buffers dM [B*Hkv][nseg][D][D] and dz [B*Hkv][nseg][D], then the
