@@ -1,0 +1,461 @@
+// Backward of the bf16 Infini-attention segment kernel for segments longer
+// than the fused short backward takes, on the matrix cores (gfx950).
+//
+// It is the same derivative as the generic backward (page "Hugging Face
+// Infini-Attention 재현 분석", section "Infini-Attention 메커니즘": Local
+// Attention, Memory Retrieval, Integration, Memory Update; the gradient
+// formulas are listed at the top of generic_bwd.hip) and writes the same
+// per-row workspace, so the pieces of either path can follow each other.
+//
+// bwd_q_mfma_kernel: one workgroup per (query tile, head, segment); each wave
+// owns 32 query rows and every product is transposed so that a lane owns one
+// query row (layouts as in fwd_mfma.hip):
+//   pass 1   S^T = K Q^T, P from the row log-sum-exp (given, or formed by an
+//            online softmax), A_dot^T = V^T P^T
+//   retrieval  A_mem^T = M^T sigma(Q)^T with M_{s-1} as a bf16 hi/lo pair (the
+//            retrieval gradient is a difference of nearly equal terms), den,
+//            dnum = g dO / den, dden, D_i = rowsum(dA_dot * A_dot), the gate
+//            term, and dQ^T = (M dnum^T + z dden^T) * sigma'(Q)^T
+//   pass 2   dP^T = V dA_dot^T, dS = P (dP - D_i) / sqrt(d), dQ^T += K^T dS^T
+// The transposed operands (V^T in pass 1, M and K^T in the gradient
+// products) come from row-major LDS tiles through ds_read_b64_tr_b16.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace infini {
+
+typedef __bf16 lbf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 lbf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 lbf16x2 __attribute__((ext_vector_type(2)));
+typedef short ls16x4 __attribute__((ext_vector_type(4)));
+typedef float lf32x16 __attribute__((ext_vector_type(16)));
+typedef float lf32x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct BqCfg {
+  // 4 waves of 32 query rows; at head_dim 128 the live operands and
+  // accumulators need the whole register file of a SIMD (one wave each)
+  static constexpr int BM = 128;                    // query rows per workgroup
+  static constexpr int WPE = D == 128 ? 1 : 2;      // waves per SIMD
+  static constexpr int NW = BM / 32;                // waves
+  static constexpr int NT = NW * 64;
+  static constexpr int BN = 64;                     // keys per tile
+  static constexpr int KS = D / 16;                 // k-steps over head_dim
+  static constexpr int DB = D / 32;                 // 32-row blocks of head_dim
+  static constexpr int KSTR = D + 8;                // row stride of the K and V tiles
+  static constexpr int KTILE = BN * KSTR;
+  static constexpr int BUF = 2 * KTILE;             // K tile, V tile
+  static constexpr int CPT = BN * D / 8 / NT;       // 16-byte chunks per thread per tile
+  static constexpr int MSTR = D + 8;                // row stride of the M^T hi / lo tiles
+  static constexpr int LDS = (2 * BUF > 2 * D * MSTR) ? 2 * BUF : 2 * D * MSTR;
+};
+
+__device__ __forceinline__ float lpair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float lpair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// gfx950 transposing LDS read: in each group of 16 lanes, lane j receives
+// element j % 4 of the four 4-element pieces addressed by lanes j/4, j/4 + 4,
+// j/4 + 8 and j/4 + 12.
+__device__ __forceinline__ lbf16x4 ltr4(const __bf16* p) {
+  return __builtin_bit_cast(lbf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ls16x4*)(p)));
+}
+
+// A operand (row r = r0 + lane % 16 of X^T, X row-major [k][r] with row stride
+// xs) of a 32x32x16 product whose k-slots hold the keys k0 + e (e < 4) and
+// k1 + e - 4 (e >= 4); r0 and k0 / k1 depend on the lane's group of 16.
+__device__ __forceinline__ lbf16x8 ltr_op(const __bf16* X, int xs, int r0, int k0, int k1, int lane) {
+  const int i = lane & 15;
+  const int e = i >> 2, a = i & 3;
+  const lbf16x4 lo = ltr4(X + (k0 + e) * xs + r0 + 4 * a);
+  const lbf16x4 hi = ltr4(X + (k1 + e) * xs + r0 + 4 * a);
+  return lbf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <int D>
+__global__ __launch_bounds__(BqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(BqCfg<D>::WPE, BqCfg<D>::WPE)))
+void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                       const __bf16* __restrict__ V, const float* __restrict__ beta,
+                       const float* __restrict__ Msnap, const float* __restrict__ zsnap,
+                       const __bf16* __restrict__ dO, __bf16* __restrict__ dQ,
+                       float* __restrict__ ws_lse, float* __restrict__ ws_Dd, float* __restrict__ ws_dden,
+                       float* __restrict__ ws_dnum, float* __restrict__ dbeta_part,
+                       const float* __restrict__ lse_in, int Hq, int Hkv, int N, int L, int s_begin,
+                       int nseg, float sl2, float scale, const int* __restrict__ lens) {
+  using C = BqCfg<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[C::LDS];
+  __shared__ float zs[D];
+  __shared__ float wsum[C::NW];
+
+  const int qt = blockIdx.x, h = blockIdx.y;
+  const int sl = blockIdx.z % nseg, b = blockIdx.z / nseg;
+  const int s = s_begin + sl;
+  const int G = Hq / Hkv, kvh = h / G;
+  const int tid = threadIdx.x;
+  // rows of this segment: the last may be short; none past the end of a
+  // sequence of a variable-length batch (the gate partial is then zero)
+  const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
+  const size_t dbp = (((size_t)b * Hq + h) * nseg + sl) * gridDim.x + qt;
+  if (Ls <= 0 || qt * C::BM >= Ls) {
+    if (tid == 0) dbeta_part[dbp] = 0.f;
+    return;
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hh = lane >> 5;
+  const int g16 = (lane >> 4) & 1;                // half of a 32-row block, for transposing reads
+  const int q0 = qt * C::BM + wave * 32;
+  const int qrow = q0 + lq;
+  const bool qok = qrow < Ls;
+  const int qr = qok ? qrow : Ls - 1;
+  const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
+  const size_t kvbase = (((size_t)b * Hkv + kvh) * N + (size_t)s * L) * D;
+  const size_t crow = ((size_t)b * Hq + h) * ((size_t)nseg * L) + (size_t)sl * L + qrow;   // chunk row
+  const float gt = sigmoid(beta[h]);
+
+  // Q^T operand (lane: column qrow, k = 16 ks + 8 hh + e)
+  lbf16x8 qreg[C::KS];
+  {
+    const __bf16* qp = Q + qbase + (size_t)qr * D + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const lbf16x8 a = *reinterpret_cast<const lbf16x8*>(qp + ks * 16);
+      qreg[ks] = qok ? a : lbf16x8{};
+    }
+  }
+
+  const int kend = min(Ls, qt * C::BM + C::BM);
+  const int ntiles = (kend + C::BN - 1) / C::BN;
+  const bool live = q0 < Ls;
+
+  // ---- staging of K and V tiles (row-major, both), double-buffered
+  lbf16x8 kst[C::CPT], vst[C::CPT];
+  constexpr int KRS = C::NT / (D / 8);
+  const int krow0 = tid / (D / 8), kcol = (tid % (D / 8)) * 8;
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int key = min(k0 + krow0 + i * KRS, Ls - 1);
+      kst[i] = *reinterpret_cast<const lbf16x8*>(K + kvbase + (size_t)key * D + kcol);
+      vst[i] = *reinterpret_cast<const lbf16x8*>(V + kvbase + (size_t)key * D + kcol);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    __bf16* Ks = smem + buf * C::BUF;
+    __bf16* Vs = Ks + C::KTILE;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      *reinterpret_cast<lbf16x8*>(Ks + (krow0 + i * KRS) * C::KSTR + kcol) = kst[i];
+      *reinterpret_cast<lbf16x8*>(Vs + (krow0 + i * KRS) * C::KSTR + kcol) = vst[i];
+    }
+  };
+  // scores of one tile (S^T, C layout: column qrow, element (kb, r) is key
+  // k0 + kb*32 + 8(r/4) + 4hh + r%4), masked past the diagonal and the segment end
+  auto scores = [&](const __bf16* Ks, int k0, lf32x16 (&sacc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = lf32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const lbf16x8 a = *reinterpret_cast<const lbf16x8*>(Ks + (kb * 32 + lq) * C::KSTR + ks * 16 + hh * 8);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[kb], 0, 0, 0);
+      }
+    }
+    if (k0 + C::BN - 1 > q0 || k0 + C::BN > Ls) {
+      const int lim = min(qrow, Ls - 1) - (k0 + 4 * hh);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+    }
+  };
+  // one sweep over the key tiles, `step` called on each tile the wave attends to
+  auto sweep = [&](auto&& step) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    if (ntiles > 1) load_tile(C::BN);
+    for (int j = 0; j < ntiles; ++j) {
+      const int k0 = j * C::BN;
+      const __bf16* Ks = smem + (j & 1) * C::BUF;
+      if (live && k0 <= q0 + 31) step(Ks, Ks + C::KTILE, k0);
+      if (j + 1 < ntiles) store_tile((j + 1) & 1);
+      __syncthreads();
+      if (j + 2 < ntiles) load_tile((j + 2) * C::BN);
+    }
+  };
+
+  // ---- pass 1: A_dot (and the row log-sum-exp unless given), base 2
+  lf32x16 oacc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) oacc[db] = lf32x16{};
+  const bool have_lse = lse_in != nullptr;
+  float m = have_lse ? lse_in[((size_t)b * Hq + h) * N + (size_t)s * L + qr] * 1.4426950408889634f : -INFINITY;
+  float lpart = 0.f;
+  const lbf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  sweep([&](const __bf16* Ks, const __bf16* Vs, int k0) {
+    lf32x16 sacc[2];
+    scores(Ks, k0, sacc);
+    if (!have_lse) {
+      float mt = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+      const float mn = fmaxf(m, lpair_max32(mt) * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      lpart *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+    }
+    lbf16x8 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pb[kb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -m));
+    if (!have_lse) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            lpart = __builtin_amdgcn_fdot2_f32_bf16(lbf16x2{pb[kb][t][2 * x], pb[kb][t][2 * x + 1]}, ones, lpart, false);
+    }
+    // O^T += V^T P^T: k-slot x of half hh <-> key kb*32 + 16t + 8(x/4) + 4hh + x%4
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int kk = kb * 32 + 16 * t + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const lbf16x8 a = ltr_op(Vs, C::KSTR, db * 32 + 16 * g16, kk, kk + 8, lane);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][t], oacc[db], 0, 0, 0);
+        }
+      }
+  });
+  float inv_l = 1.f;
+  if (!have_lse) {
+    const float l = lpair_sum32(lpart);
+    inv_l = 1.f / l;
+    m += __log2f(l);                          // m is now the row's log-sum-exp (base 2)
+  }
+
+  // ---- retrieval: M_{s-1}^T as bf16 hi / lo tiles [c][a], z_{s-1}
+  __bf16* Mhi = smem;
+  __bf16* Mlo = smem + D * C::MSTR;
+  {
+    const size_t snap = ((size_t)(b * Hkv + kvh) * nseg + sl);
+    const float* msrc = Msnap + snap * D * D;
+    for (int e = tid; e < D * D; e += C::NT) {
+      const int a = e / D, c = e % D;
+      const float v = msrc[e];
+      const __bf16 hi = (__bf16)v;
+      Mhi[c * C::MSTR + a] = hi;
+      Mlo[c * C::MSTR + a] = (__bf16)(v - (float)hi);
+    }
+    for (int e = tid; e < D; e += C::NT) zs[e] = zsnap[snap * D + e];
+  }
+  __syncthreads();
+  lbf16x8 sq[C::KS];
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 v = (__bf16)elu1((float)qreg[ks][e]);
+      sq[ks][e] = v;
+      dpart += (float)v * zs[ks * 16 + hh * 8 + e];
+    }
+  }
+  const float den = lpair_sum32(dpart) + 1e-6f;
+  const float inv_den = 1.f / den;
+  // per element (cb, r) of the C layout: column c = cb*32 + 8(r/4) + 4hh + r%4
+  float bsum = 0.f, ddot = 0.f, dmem = 0.f;
+  lbf16x8 dnb[C::DB][2];                      // dnum^T operand, slots like the probabilities
+#pragma unroll
+  for (int cb = 0; cb < C::DB; ++cb) {
+    lf32x16 nacc = {};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const lbf16x8 a = *reinterpret_cast<const lbf16x8*>(Mhi + (cb * 32 + lq) * C::MSTR + ks * 16 + hh * 8);
+      const lbf16x8 al = *reinterpret_cast<const lbf16x8*>(Mlo + (cb * 32 + lq) * C::MSTR + ks * 16 + hh * 8);
+      nacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sq[ks], nacc, 0, 0, 0);
+      nacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, sq[ks], nacc, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c0 = cb * 32 + 8 * u + 4 * hh;
+      const lbf16x4 dv = *reinterpret_cast<const lbf16x4*>(dO + qbase + (size_t)qr * D + c0);
+      lf32x4 dn32;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 4 * u + x;
+        // rows past the segment end (a wave may have no key at all, l = 0)
+        // contribute nothing
+        const float go = qok ? (float)dv[x] : 0.f;
+        const float am = qok ? nacc[r] * inv_den : 0.f;
+        const float ad = qok ? oacc[cb][r] * inv_l : 0.f;
+        // the row sums pair with the rounded operands the products use, so that
+        // dP - D_i and dnum M^T + dden z^T cancel as they do exactly
+        const __bf16 dn = (__bf16)(gt * go * inv_den);
+        const __bf16 da = (__bf16)((1.f - gt) * go);
+        bsum += go * (am - ad);
+        ddot += (float)da * ad;
+        dmem += (float)dn * am;
+        dnb[cb][r >> 3][r & 7] = dn;
+        dn32[x] = gt * go * inv_den;
+      }
+      if (qok) *reinterpret_cast<lf32x4*>(ws_dnum + crow * D + c0) = dn32;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float Dd = lpair_sum32(ddot);
+  const float dden = -lpair_sum32(dmem);
+  if (qok && hh == 0) {
+    ws_lse[crow] = m * 0.69314718055994531f;
+    ws_Dd[crow] = Dd;
+    ws_dden[crow] = dden;
+  }
+  // gate partial of the workgroup (fixed order)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) bsum += __shfl_xor(bsum, o);
+  if (lane == 0) wsum[wave] = bsum;
+
+  // dQ^T (retrieval part): (M dnum^T + z dden) * sigma'(Q), M from M^T by
+  // transposing reads; rows a = ab*32 + 8(r/4) + 4hh + r%4
+  lf32x16 dq[C::DB];
+#pragma unroll
+  for (int ab = 0; ab < C::DB; ++ab) {
+    dq[ab] = lf32x16{};
+#pragma unroll
+    for (int cb = 0; cb < C::DB; ++cb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int kk = cb * 32 + 16 * t + 4 * hh;
+        const lbf16x8 a = ltr_op(Mhi, C::MSTR, ab * 32 + 16 * g16, kk, kk + 8, lane);
+        const lbf16x8 al = ltr_op(Mlo, C::MSTR, ab * 32 + 16 * g16, kk, kk + 8, lane);
+        dq[ab] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dnb[cb][t], dq[ab], 0, 0, 0);
+        dq[ab] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, dnb[cb][t], dq[ab], 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int a0 = ab * 32 + 8 * u + 4 * hh;
+      const lbf16x4 qv = *reinterpret_cast<const lbf16x4*>(Q + qbase + (size_t)qr * D + a0);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        dq[ab][4 * u + x] = (dq[ab][4 * u + x] + dden * zs[a0 + x]) * elu1_grad((float)qv[x]);
+    }
+  }
+  // dA_dot^T operand = (1 - g) dO, rounded once (lane: column qrow)
+  lbf16x8 dreg[C::KS];
+  {
+    const __bf16* dp = dO + qbase + (size_t)qr * D + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const lbf16x8 d = *reinterpret_cast<const lbf16x8*>(dp + ks * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dreg[ks][e] = qok ? (__bf16)((1.f - gt) * (float)d[e]) : (__bf16)0.f;
+    }
+  }
+  __syncthreads();                            // M^T done with; the tiles reuse the LDS
+  if (tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < C::NW; ++w) t += wsum[w];
+    dbeta_part[dbp] = t;
+  }
+
+  // ---- pass 2: dQ^T += K^T dS^T, dS = P (dP - D_i) / sqrt(d) with dP^T = V dA_dot^T
+  sweep([&](const __bf16* Ks, const __bf16* Vs, int k0) {
+    lf32x16 sacc[2];
+    scores(Ks, k0, sacc);
+    lf32x16 pacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      pacc[kb] = lf32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const lbf16x8 a = *reinterpret_cast<const lbf16x8*>(Vs + (kb * 32 + lq) * C::KSTR + ks * 16 + hh * 8);
+        pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dreg[ks], pacc[kb], 0, 0, 0);
+      }
+    }
+    lbf16x8 dsb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -m));
+        dsb[kb][r >> 3][r & 7] = (__bf16)(scale * p * (pacc[kb][r] - Dd));
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int kk = kb * 32 + 16 * t + 4 * hh;
+#pragma unroll
+        for (int ab = 0; ab < C::DB; ++ab) {
+          const lbf16x8 a = ltr_op(Ks, C::KSTR, ab * 32 + 16 * g16, kk, kk + 8, lane);
+          dq[ab] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[kb][t], dq[ab], 0, 0, 0);
+        }
+      }
+  });
+
+  if (qok) {
+    __bf16* qp = dQ + qbase + (size_t)qrow * D;
+#pragma unroll
+    for (int ab = 0; ab < C::DB; ++ab)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<lbf16x4*>(qp + ab * 32 + 8 * u + 4 * hh) =
+            lbf16x4{(__bf16)dq[ab][4 * u], (__bf16)dq[ab][4 * u + 1], (__bf16)dq[ab][4 * u + 2], (__bf16)dq[ab][4 * u + 3]};
+  }
+}
+
+bool bwd_long_mfma_supported(const Geometry& g) {
+  return g.fmap == 0 && g.dtype == 1 && (g.D == 64 || g.D == 128);
+}
+
+int bwd_q_mfma_row_blocks(const Geometry& g) {
+  const int bm = BqCfg<64>::BM;
+  static_assert(BqCfg<64>::BM == BqCfg<128>::BM, "one row-block count for both head dims");
+  return (g.L + bm - 1) / bm;
+}
+
+template <int D>
+static hipError_t bwd_q_mfma_t(const Geometry& g, const void* Q, const void* K, const void* V,
+                               const float* beta, const float* Msnap, const float* zsnap, const void* dO,
+                               void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin, int s_end,
+                               hipStream_t st) {
+  const int nseg = s_end - s_begin;
+  const float scale = 1.f / sqrtf((float)D);
+  dim3 grid((g.L + BqCfg<D>::BM - 1) / BqCfg<D>::BM, g.Hq, g.B * nseg);
+  hipLaunchKernelGGL((bwd_q_mfma_kernel<D>), grid, dim3(BqCfg<D>::NT), 0, st,
+                     static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
+                     static_cast<const __bf16*>(V), beta, Msnap, zsnap, static_cast<const __bf16*>(dO),
+                     static_cast<__bf16*>(dQ), w.lse, w.Dd, w.dden, w.dnum, w.dbeta_part, lse_in, g.Hq,
+                     g.Hkv, g.N, g.L, s_begin, nseg, 1.4426950408889634f * scale, scale, g.lens);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_q_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
+                             const float* beta, const float* Msnap, const float* zsnap, const void* dO,
+                             void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin, int s_end,
+                             hipStream_t st) {
+  if (!bwd_long_mfma_supported(g)) return hipErrorInvalidValue;
+  if (g.D == 128) return bwd_q_mfma_t<128>(g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, lse_in, s_begin, s_end, st);
+  return bwd_q_mfma_t<64>(g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, lse_in, s_begin, s_end, st);
+}
+
+}  // namespace infini

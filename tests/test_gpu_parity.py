@@ -198,6 +198,10 @@ BWD_CASES = [
     # 17 takes the generic backward
     (1, 16, 1, 128, 128, 64, "bf16", True),
     (1, 34, 2, 64, 64, 32, "bf16", False),
+    # bf16 segments longer than 64: matrix-core query side
+    (1, 4, 2, 520, 128, 256, "bf16", True),    # 3 segments, 8-token tail, 2 heads per K/V head
+    (2, 2, 2, 384, 64, 128, "bf16", False),    # 3 full segments
+    (1, 8, 2, 700, 128, 300, "bf16", True),    # seg_len not a multiple of 64, 100-token tail
 ]
 
 
