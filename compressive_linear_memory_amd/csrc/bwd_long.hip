@@ -17,8 +17,16 @@
 //            dnum = g dO / den, dden, D_i = rowsum(dA_dot * A_dot), the gate
 //            term, and dQ^T = (M dnum^T + z dden^T) * sigma'(Q)^T
 //   pass 2   dP^T = V dA_dot^T, dS = P (dP - D_i) / sqrt(d), dQ^T += K^T dS^T
-// The transposed operands (V^T in pass 1, M and K^T in the gradient
-// products) come from row-major LDS tiles through ds_read_b64_tr_b16.
+// bwd_kv_mfma_kernel: one workgroup per (key tile, K/V head, segment); each
+// wave owns 32 keys, a lane one key (the products transposed the other way):
+//   per query head of the group and 64-row query tile at or after the keys:
+//            S = Q K^T, P from the row log-sum-exp, dP = dA_dot V^T,
+//            dS = P (dP - D_i) / sqrt(d), dV^T += dA_dot^T P, dK^T += Q^T dS
+//   update   dV^T += dM^T sigma(K)^T, dK^T += (dM V^T + dz) * sigma'(K)^T with
+//            dM = dL/dM_s (bf16) and dz = dL/dz_s
+// The transposed operands (V^T in pass 1, M, K^T, dA_dot^T, Q^T and dM^T in
+// the gradient products) come from row-major LDS tiles through
+// ds_read_b64_tr_b16.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -423,6 +431,220 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
   }
 }
 
+
+template <int D>
+struct BkCfg {
+  static constexpr int BK = 128;                    // keys per workgroup (4 waves of 32)
+  static constexpr int NT = 256;
+  static constexpr int WPE = D == 128 ? 1 : 2;      // waves per SIMD
+  static constexpr int BQ = 64;                     // query rows per staged tile
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int QSTR = D + 8;                // row stride of the Q and dA_dot tiles
+  static constexpr int QTILE = BQ * QSTR;
+  static constexpr int BUF = 2 * QTILE;             // Q tile, dA_dot tile
+  static constexpr int CPT = BQ * D / 8 / NT;       // 16-byte chunks per thread per tile
+  static constexpr int MSTR = D + 8;                // row stride of the dM tile
+  static constexpr int LDS = (2 * BUF > D * MSTR) ? 2 * BUF : D * MSTR;
+};
+
+template <int D>
+__global__ __launch_bounds__(BkCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(BkCfg<D>::WPE, BkCfg<D>::WPE)))
+void bwd_kv_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                        const __bf16* __restrict__ V, const float* __restrict__ beta,
+                        const __bf16* __restrict__ dO, const float* __restrict__ ws_lse,
+                        const float* __restrict__ ws_Dd, const float* __restrict__ dMsnap,
+                        const float* __restrict__ dzsnap, __bf16* __restrict__ dK, __bf16* __restrict__ dV,
+                        int Hq, int Hkv, int N, int L, int s_begin, int nseg, float sl2, float scale,
+                        const int* __restrict__ lens) {
+  using C = BkCfg<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[C::LDS];
+  __shared__ float rowst[2][2][C::BQ];              // per buffer: lse (base 2), D_i
+  __shared__ float dzs[D];
+
+  const int kt = blockIdx.x, kvh = blockIdx.y;
+  const int sl = blockIdx.z % nseg, b = blockIdx.z / nseg;
+  const int s = s_begin + sl;
+  const int G = Hq / Hkv;
+  // keys (and rows) of this segment: the last may be short; none past the end
+  // of a sequence of a variable-length batch
+  const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
+  const int k0 = kt * C::BK;
+  if (Ls <= 0 || k0 >= Ls) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hh = lane >> 5;
+  const int g16 = (lane >> 4) & 1;
+  const int kw = k0 + wave * 32;                    // this wave's first key
+  const int key = kw + lq;                          // this lane's key (column of the products)
+  const bool kok = key < Ls;
+  const int kr = kok ? key : Ls - 1;
+  const size_t kvbase = (((size_t)b * Hkv + kvh) * N + (size_t)s * L) * D;
+
+  // K^T and V^T operands (lane: column key, k = 16 ks + 8 hh + e)
+  lbf16x8 kreg[C::KS], vreg[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    kreg[ks] = *reinterpret_cast<const lbf16x8*>(K + kvbase + (size_t)kr * D + ks * 16 + hh * 8);
+    vreg[ks] = *reinterpret_cast<const lbf16x8*>(V + kvbase + (size_t)kr * D + ks * 16 + hh * 8);
+  }
+  lf32x16 dka[C::DB], dva[C::DB];                   // dK^T, dV^T: rows a = ab*32 + 8(r/4) + 4hh + r%4
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) { dka[db] = lf32x16{}; dva[db] = lf32x16{}; }
+
+  // the (head, 64-row query tile) sequence: tiles from the one holding key k0
+  const int qfirst = k0 / C::BQ;
+  const int nqt = (Ls + C::BQ - 1) / C::BQ - qfirst;
+  const int ntot = G * nqt;
+  lbf16x8 qst[C::CPT], dst[C::CPT];
+  float rl = 0.f, rd = 0.f;                         // this thread's lse / D_i staging (tid < BQ)
+  constexpr int QRS = C::NT / (D / 8);
+  const int qrow0 = tid / (D / 8), qcol = (tid % (D / 8)) * 8;
+  auto tile_of = [&](int i, int& h, int& q0) {
+    h = kvh * G + i / nqt;
+    q0 = (qfirst + i % nqt) * C::BQ;
+  };
+  auto load_tile = [&](int i) {
+    int h, q0;
+    tile_of(i, h, q0);
+    const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
+    const float og = 1.f - sigmoid(beta[h]);
+#pragma unroll
+    for (int x = 0; x < C::CPT; ++x) {
+      const int row = min(q0 + qrow0 + x * QRS, Ls - 1);
+      qst[x] = *reinterpret_cast<const lbf16x8*>(Q + qbase + (size_t)row * D + qcol);
+      const lbf16x8 d = *reinterpret_cast<const lbf16x8*>(dO + qbase + (size_t)row * D + qcol);
+      // dA_dot = (1 - g) dO, rounded once as the query side rounds it
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[x][e] = (__bf16)(og * (float)d[e]);
+    }
+    if (tid < C::BQ) {
+      const int row = min(q0 + tid, Ls - 1);
+      const size_t crow = ((size_t)b * Hq + h) * ((size_t)nseg * L) + (size_t)sl * L + row;
+      rl = ws_lse[crow] * 1.4426950408889634f;
+      rd = ws_Dd[crow];
+    }
+  };
+  auto store_tile = [&](int buf) {
+    __bf16* Qs = smem + buf * C::BUF;
+    __bf16* As = Qs + C::QTILE;
+#pragma unroll
+    for (int x = 0; x < C::CPT; ++x) {
+      *reinterpret_cast<lbf16x8*>(Qs + (qrow0 + x * QRS) * C::QSTR + qcol) = qst[x];
+      *reinterpret_cast<lbf16x8*>(As + (qrow0 + x * QRS) * C::QSTR + qcol) = dst[x];
+    }
+    if (tid < C::BQ) {
+      rowst[buf][0][tid] = rl;
+      rowst[buf][1][tid] = rd;
+    }
+  };
+
+  if (ntot > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  if (ntot > 1) load_tile(1);
+  for (int i = 0; i < ntot; ++i) {
+    const int buf = i & 1;
+    int h, q0;
+    tile_of(i, h, q0);
+    const __bf16* Qs = smem + buf * C::BUF;
+    const __bf16* As = Qs + C::QTILE;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qb0 = q0 + qb * 32;                 // first row of this 32-row block
+      if (qb0 + 31 < kw || qb0 >= Ls) continue;     // every row before the wave's keys, or past the end
+      // S[q][key] and dP[q][key]: element r holds row qb0 + 8(r/4) + 4hh + r%4
+      lf32x16 sacc = {}, pacc = {};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const lbf16x8 qa = *reinterpret_cast<const lbf16x8*>(Qs + (qb * 32 + lq) * C::QSTR + ks * 16 + hh * 8);
+        const lbf16x8 da = *reinterpret_cast<const lbf16x8*>(As + (qb * 32 + lq) * C::QSTR + ks * 16 + hh * 8);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[ks], pacc, 0, 0, 0);
+      }
+      lbf16x8 pb[2], dsb[2];                        // k-slot x of half hh <-> row 16t + 8(x/4) + 4hh + x%4
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rloc = qb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int row = q0 + rloc;
+        const bool on = row >= key && row < Ls;
+        const float p = on ? __builtin_amdgcn_exp2f(fmaf(sacc[r], sl2, -rowst[buf][0][rloc])) : 0.f;
+        pb[r >> 3][r & 7] = (__bf16)p;
+        dsb[r >> 3][r & 7] = (__bf16)(scale * p * (pacc[r] - rowst[buf][1][rloc]));
+      }
+      // dV^T += dA_dot^T P, dK^T += Q^T dS (contraction over the block's rows)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int rr = qb * 32 + 16 * t + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const lbf16x8 aa = ltr_op(As, C::QSTR, db * 32 + 16 * g16, rr, rr + 8, lane);
+          const lbf16x8 qa = ltr_op(Qs, C::QSTR, db * 32 + 16 * g16, rr, rr + 8, lane);
+          dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, pb[t], dva[db], 0, 0, 0);
+          dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsb[t], dka[db], 0, 0, 0);
+        }
+      }
+    }
+    if (i + 1 < ntot) store_tile((i + 1) & 1);
+    __syncthreads();
+    if (i + 2 < ntot) load_tile(i + 2);
+  }
+
+  // ---- update backward with dM = dL/dM_s: tile [a][c] (bf16), dz
+  __bf16* dMs = smem;
+  {
+    const size_t snap = ((size_t)(b * Hkv + kvh) * nseg + sl);
+    const float* src = dMsnap + snap * D * D;
+    for (int e = tid; e < D * D; e += C::NT) dMs[(e / D) * C::MSTR + (e % D)] = (__bf16)src[e];
+    for (int e = tid; e < D; e += C::NT) dzs[e] = dzsnap[snap * D + e];
+  }
+  __syncthreads();
+  lbf16x8 sk[C::KS];                                // sigma(K)^T operand
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sk[ks][e] = (__bf16)elu1((float)kreg[ks][e]);
+  // dV^T[c][key] += sum_a dM[a][c] sigma(K)[key][a]: A = dM^T rows c through
+  //   transposing reads of the [a][c] tile, k = a = 16 ks + 8 hh + e
+  // (dM V^T)^T[a][key] = sum_c dM[a][c] V[key][c]: A = dM rows a (plain reads)
+  lf32x16 dku[C::DB];
+#pragma unroll
+  for (int cb = 0; cb < C::DB; ++cb) {
+    dku[cb] = lf32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const lbf16x8 a = ltr_op(dMs, C::MSTR, cb * 32 + 16 * g16, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, lane);
+      dva[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sk[ks], dva[cb], 0, 0, 0);
+      const lbf16x8 am = *reinterpret_cast<const lbf16x8*>(dMs + (cb * 32 + lq) * C::MSTR + ks * 16 + hh * 8);
+      dku[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, vreg[ks], dku[cb], 0, 0, 0);
+    }
+  }
+  // dK = Q^T dS (scaled) + (dM V^T + dz) sigma'(K); rows a of the accumulators
+  // are ab*32 + 8(r/4) + 4hh + r%4
+  if (kok) {
+    __bf16* kp = dK + kvbase + (size_t)key * D;
+    __bf16* vp = dV + kvbase + (size_t)key * D;
+#pragma unroll
+    for (int ab = 0; ab < C::DB; ++ab)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int a0 = ab * 32 + 8 * u + 4 * hh;
+        const lbf16x4 kv = *reinterpret_cast<const lbf16x4*>(K + kvbase + (size_t)key * D + a0);
+        lbf16x4 wk, wv;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * u + x;
+          wk[x] = (__bf16)(dka[ab][r] + (dku[ab][r] + dzs[a0 + x]) * elu1_grad((float)kv[x]));
+          wv[x] = (__bf16)dva[ab][r];
+        }
+        *reinterpret_cast<lbf16x4*>(kp + a0) = wk;
+        *reinterpret_cast<lbf16x4*>(vp + a0) = wv;
+      }
+  }
+}
+
 bool bwd_long_mfma_supported(const Geometry& g) {
   return g.fmap == 0 && g.dtype == 1 && (g.D == 64 || g.D == 128);
 }
@@ -447,6 +669,29 @@ static hipError_t bwd_q_mfma_t(const Geometry& g, const void* Q, const void* K, 
                      static_cast<__bf16*>(dQ), w.lse, w.Dd, w.dden, w.dnum, w.dbeta_part, lse_in, g.Hq,
                      g.Hkv, g.N, g.L, s_begin, nseg, 1.4426950408889634f * scale, scale, g.lens);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t bwd_kv_mfma_t(const Geometry& g, const void* Q, const void* K, const void* V,
+                                const float* beta, const void* dO, const BwdChunkWs& w, void* dK, void* dV,
+                                int s_begin, int s_end, hipStream_t st) {
+  const int nseg = s_end - s_begin;
+  const float scale = 1.f / sqrtf((float)D);
+  dim3 grid((g.L + BkCfg<D>::BK - 1) / BkCfg<D>::BK, g.Hkv, g.B * nseg);
+  hipLaunchKernelGGL((bwd_kv_mfma_kernel<D>), grid, dim3(BkCfg<D>::NT), 0, st,
+                     static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
+                     static_cast<const __bf16*>(V), beta, static_cast<const __bf16*>(dO), w.lse, w.Dd,
+                     w.dMsnap, w.dzsnap, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV), g.Hq, g.Hkv,
+                     g.N, g.L, s_begin, nseg, 1.4426950408889634f * scale, scale, g.lens);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
+                              const float* beta, const void* dO, const BwdChunkWs& w, void* dK, void* dV,
+                              int s_begin, int s_end, hipStream_t st) {
+  if (!bwd_long_mfma_supported(g)) return hipErrorInvalidValue;
+  if (g.D == 128) return bwd_kv_mfma_t<128>(g, Q, K, V, beta, dO, w, dK, dV, s_begin, s_end, st);
+  return bwd_kv_mfma_t<64>(g, Q, K, V, beta, dO, w, dK, dV, s_begin, s_end, st);
 }
 
 hipError_t launch_bwd_q_mfma(const Geometry& g, const void* Q, const void* K, const void* V,

@@ -544,6 +544,7 @@ hipError_t launch_rscan(const Geometry& g, const void* Q, const BwdChunkWs& w, c
 hipError_t launch_bwd_kv(const Geometry& g, const void* Q, const void* K, const void* V,
                          const float* beta, const void* dO, const BwdChunkWs& w, void* dK, void* dV,
                          int s_begin, int s_end, hipStream_t st) {
+  if (bwd_long_mfma_supported(g)) return launch_bwd_kv_mfma(g, Q, K, V, beta, dO, w, dK, dV, s_begin, s_end, st);
   DISPATCH_TD(bwd_kv_t, g, Q, K, V, beta, dO, w, dK, dV, s_begin, s_end, st);
 }
 

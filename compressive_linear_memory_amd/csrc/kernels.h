@@ -131,14 +131,17 @@ struct BwdChunkWs {
 
 int bwd_q_row_blocks(const Geometry& g);
 
-// bf16 head_dim 64 / 128: the query-side backward runs on the matrix cores
-// (bwd_long.hip), writing the same workspace as the generic kernel.
+// bf16 head_dim 64 / 128: the query- and key-side backward run on the matrix
+// cores (bwd_long.hip), with the same workspace as the generic kernels.
 bool bwd_long_mfma_supported(const Geometry& g);
 int bwd_q_mfma_row_blocks(const Geometry& g);
 hipError_t launch_bwd_q_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
                              const float* beta, const float* Msnap, const float* zsnap, const void* dO,
                              void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin, int s_end,
                              hipStream_t st);
+hipError_t launch_bwd_kv_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
+                              const float* beta, const void* dO, const BwdChunkWs& w, void* dK, void* dV,
+                              int s_begin, int s_end, hipStream_t st);
 
 // lse_in: the forward's row log-sum-exp [B][Hq][N] (the probabilities are
 // then formed from it directly), or NULL to form it again.
