@@ -134,7 +134,7 @@ hipError_t run_fwd_chunk(const Geometry& g, const FwdWs& lay, char* base, const 
   return hipSuccess;
 }
 
-struct BwdWs { size_t Mst, zst, Msnap, zsnap, dMc, dzc, dMsnap, dzsnap, lse, Dd, dden, dnum, dbp, dbacc, dbs, total; };
+struct BwdWs { size_t Mst, zst, Msnap, zsnap, dMc, dzc, dMsnap, dzsnap, lse, Dd, dden, dnum, dbp, dbacc, dbs, dlt, dltz, total; };
 BwdWs bwd_layout(const Geometry& g) {
   if (infini::bwd_short_supported(g)) {   // the fused backward needs only its dbeta partials
     BwdWs w{};
@@ -163,6 +163,16 @@ BwdWs bwd_layout(const Geometry& g) {
   w.dbp = off;    off = align_up(off + (size_t)g.B * g.Hq * C * infini::bwd_q_row_blocks(g) * 4);
   w.dbacc = off;  off = align_up(off + (size_t)g.Hq * 4);
   w.dbs = off;    off = align_up(off + (size_t)g.B * g.Hq * 4);
+  // matrix-core path: per-segment scratch of the memory phase (its deltas,
+  // key-split parts included), reused by the reverse scan for the segments'
+  // retrieval terms; Msnap then holds the bf16 transposed snapshots and their
+  // bf16 remainders (the same bytes as one fp32 copy)
+  w.dlt = w.dltz = 0;
+  if (infini::bwd_long_mfma_supported(g)) {
+    const size_t ns = (size_t)infini::delta_splits(g);
+    w.dlt = off;  off = align_up(off + bk * C * ns * D * D * 4);
+    w.dltz = off; off = align_up(off + bk * C * ns * D * 4);
+  }
   w.total = off;
   return w;
 }
@@ -578,6 +588,7 @@ static infini_status_t attn_bwd_impl(const infini_problem_t* p, const int32_t* l
 
   const int C = chunk_segments(g);
   const int nchunks = (g.S + C - 1) / C;
+  const bool mf = infini::bwd_long_mfma_supported(g);
   // The chunks are walked last to first.  With more than one, the memory path
   // runs forward once to the state after the last chunk, and each chunk's
   // start state is then recovered by taking that chunk's updates away again
@@ -592,15 +603,24 @@ static infini_status_t attn_bwd_impl(const infini_problem_t* p, const int32_t* l
       TRY(infini::launch_sweep(g, K, V, Mst, zst, Mst, zst, nullptr, nullptr, s0, s1, st, nullptr, true));
       Mstart = Mst; zstart = zst;
     }
-    TRY(infini::launch_sweep(g, K, V, Mstart, zstart, nullptr, nullptr, Msnap, zsnap, s0, s1, st));
-    TRY(infini::launch_bwd_q(g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, lse, s0, s1, st));
+    if (mf) {   // snapshots as bf16 hi / lo pairs, transposed, from the matrix-core memory phase
+      char* hi = base + lay.Msnap;
+      char* lo = hi + (size_t)g.B * g.Hkv * (s1 - s0) * g.D * g.D * 2;
+      TRY(infini::launch_sweep_mfma(g, K, V, Mstart, zstart, nullptr, nullptr, F(lay.dlt), F(lay.dltz), hi,
+                                    zsnap, s0, s1, st, lo));
+      TRY(infini::launch_bwd_q_mfma(g, Q, K, V, beta, hi, lo, zsnap, dO, dQ, w, lse, s0, s1, st));
+    } else {
+      TRY(infini::launch_sweep(g, K, V, Mstart, zstart, nullptr, nullptr, Msnap, zsnap, s0, s1, st));
+      TRY(infini::launch_bwd_q(g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, lse, s0, s1, st));
+    }
     const bool first = ci == nchunks - 1, last = ci == 0;
     TRY(infini::launch_dbeta_reduce(g, beta, w, dbacc, dbeta, s1 - s0, first, last, st));
     const float* dMin = first ? dM_S : dMc;
     const float* dzin = first ? dz_S : dzc;
     float* dMout = last ? dM0 : dMc;
     float* dzout = last ? dz0 : dzc;
-    TRY(infini::launch_rscan(g, Q, w, dMin, dzin, dMout, dzout, s0, s1, st));
+    if (mf) TRY(infini::launch_rscan_mfma(g, Q, w, F(lay.dlt), F(lay.dltz), dMin, dzin, dMout, dzout, s0, s1, st));
+    else TRY(infini::launch_rscan(g, Q, w, dMin, dzin, dMout, dzout, s0, s1, st));
     TRY(infini::launch_bwd_kv(g, Q, K, V, beta, dO, w, dK, dV, s0, s1, st));
   }
   return INFINI_OK;

@@ -24,6 +24,8 @@
 //            dS = P (dP - D_i) / sqrt(d), dV^T += dA_dot^T P, dK^T += Q^T dS
 //   update   dV^T += dM^T sigma(K)^T, dK^T += (dM V^T + dz) * sigma'(K)^T with
 //            dM = dL/dM_s (bf16) and dz = dL/dz_s
+// rdelta_mfma_kernel / rscan_rev_kernel: the gradient with respect to the
+// state after every segment (see below).
 // The transposed operands (V^T in pass 1, M, K^T, dA_dot^T, Q^T and dM^T in
 // the gradient products) come from row-major LDS tiles through
 // ds_read_b64_tr_b16.
@@ -91,8 +93,8 @@ template <int D>
 __global__ __launch_bounds__(BqCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(BqCfg<D>::WPE, BqCfg<D>::WPE)))
 void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                        const __bf16* __restrict__ V, const float* __restrict__ beta,
-                       const float* __restrict__ Msnap, const float* __restrict__ zsnap,
-                       const __bf16* __restrict__ dO, __bf16* __restrict__ dQ,
+                       const __bf16* __restrict__ MhiT, const __bf16* __restrict__ MloT,
+                       const float* __restrict__ zsnap, const __bf16* __restrict__ dO, __bf16* __restrict__ dQ,
                        float* __restrict__ ws_lse, float* __restrict__ ws_Dd, float* __restrict__ ws_dden,
                        float* __restrict__ ws_dnum, float* __restrict__ dbeta_part,
                        const float* __restrict__ lse_in, int Hq, int Hkv, int N, int L, int s_begin,
@@ -259,18 +261,16 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
     m += __log2f(l);                          // m is now the row's log-sum-exp (base 2)
   }
 
-  // ---- retrieval: M_{s-1}^T as bf16 hi / lo tiles [c][a], z_{s-1}
+  // ---- retrieval: M_{s-1}^T as bf16 hi / lo tiles [c][a] (published so by the
+  // memory phase), z_{s-1}
   __bf16* Mhi = smem;
   __bf16* Mlo = smem + D * C::MSTR;
   {
     const size_t snap = ((size_t)(b * Hkv + kvh) * nseg + sl);
-    const float* msrc = Msnap + snap * D * D;
-    for (int e = tid; e < D * D; e += C::NT) {
-      const int a = e / D, c = e % D;
-      const float v = msrc[e];
-      const __bf16 hi = (__bf16)v;
-      Mhi[c * C::MSTR + a] = hi;
-      Mlo[c * C::MSTR + a] = (__bf16)(v - (float)hi);
+    for (int e = tid; e < D * D / 8; e += C::NT) {
+      const int c = e / (D / 8), a = (e % (D / 8)) * 8;
+      *reinterpret_cast<lbf16x8*>(Mhi + c * C::MSTR + a) = *reinterpret_cast<const lbf16x8*>(MhiT + snap * D * D + c * D + a);
+      *reinterpret_cast<lbf16x8*>(Mlo + c * C::MSTR + a) = *reinterpret_cast<const lbf16x8*>(MloT + snap * D * D + c * D + a);
     }
     for (int e = tid; e < D; e += C::NT) zs[e] = zsnap[snap * D + e];
   }
@@ -645,6 +645,169 @@ void bwd_kv_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   }
 }
 
+
+// ---- reverse state scan on the matrix cores
+//
+// dL/dM_s (the state after segment s) is the upstream gradient plus the
+// retrieval terms of every later segment, R_t = sum over the group's heads and
+// the segment's rows of sigma(Q)^T dnum (and r_t = sigma(Q)^T dden for z):
+//   rdelta_mfma_kernel  one workgroup per (batch, K/V head, segment): R_s, r_s
+//   rscan_rev_kernel    one workgroup per 32x32 tile of the state per (batch,
+//                       K/V head): walks the segments last to first, publishing
+//                       dL/dM_s before adding R_s, and writes the gradient
+//                       with respect to the state the chunk started from.
+template <int D>
+struct RdCfg {
+  static constexpr int BR = 64;                     // rows per staged tile
+  static constexpr int STR = D + 8;
+  static constexpr int CPT = BR * D / 8 / 256;      // 8-element chunks per thread per tile
+  static constexpr int WB = D / 64;                 // 32-blocks per wave edge (2x2 waves)
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void rdelta_mfma_kernel(
+    const __bf16* __restrict__ Q, const float* __restrict__ dnum, const float* __restrict__ dden,
+    float* __restrict__ R, float* __restrict__ r, int Hq, int Hkv, int N, int L, int s_begin, int nseg,
+    const int* __restrict__ lens) {
+  using C = RdCfg<D>;
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  __shared__ __attribute__((aligned(16))) __bf16 SQ[C::BR * C::STR];   // sigma(Q) rows
+  __shared__ __attribute__((aligned(16))) __bf16 DN[C::BR * C::STR];   // dnum rows
+  __shared__ float dd[C::BR];
+  const int unit = blockIdx.x;                      // bk * nseg + sl
+  const int sl = unit % nseg;
+  const int bk = unit / nseg;
+  const int b = bk / Hkv, kvh = bk % Hkv;
+  const int G = Hq / Hkv;
+  const int s = s_begin + sl;
+  const int Ls = max(0, min(L, seq_len_of(lens, b, N) - s * L));
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hh = lane >> 5;
+  const int g16 = (lane >> 4) & 1;
+  // this wave's blocks of R: rows a = (2 (wave >> 1) + ..)..., columns c likewise
+  const int a_base = (wave >> 1) * (D / 2), c_base = (wave & 1) * (D / 2);
+  lf32x16 acc[C::WB][C::WB];
+#pragma unroll
+  for (int x = 0; x < C::WB; ++x)
+#pragma unroll
+    for (int y = 0; y < C::WB; ++y) acc[x][y] = lf32x16{};
+  float zacc = 0.f;                                  // r[a] for a = tid (< D)
+  constexpr int RS8 = 256 / (D / 8);
+  const int row0 = tid / (D / 8), col = (tid % (D / 8)) * 8;
+  for (int h = kvh * G; h < (kvh + 1) * G; ++h) {
+    const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
+    const size_t cbase = ((size_t)b * Hq + h) * ((size_t)nseg * L) + (size_t)sl * L;
+    for (int i0 = 0; i0 < Ls; i0 += C::BR) {
+#pragma unroll
+      for (int x = 0; x < C::CPT; ++x) {
+        const int row = row0 + x * RS8;
+        const bool in = i0 + row < Ls;
+        lbf16x8 sq = {}, dn = {};
+        if (in) {
+          const lbf16x8 qv = *reinterpret_cast<const lbf16x8*>(Q + qbase + (size_t)(i0 + row) * D + col);
+          const lf32x4 d0 = *reinterpret_cast<const lf32x4*>(dnum + (cbase + i0 + row) * D + col);
+          const lf32x4 d1 = *reinterpret_cast<const lf32x4*>(dnum + (cbase + i0 + row) * D + col + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sq[e] = (__bf16)elu1((float)qv[e]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { dn[e] = (__bf16)d0[e]; dn[e + 4] = (__bf16)d1[e]; }
+        }
+        *reinterpret_cast<lbf16x8*>(SQ + row * C::STR + col) = sq;
+        *reinterpret_cast<lbf16x8*>(DN + row * C::STR + col) = dn;
+      }
+      if (tid < C::BR) dd[tid] = (i0 + tid < Ls) ? dden[cbase + i0 + tid] : 0.f;
+      __syncthreads();
+      // R[a][c] += sum_q sigma(Q)[q][a] dnum[q][c]; both operands by transposing
+      // reads, k-slot e of half hh <-> row 16 kk + 8 hh + e
+#pragma unroll
+      for (int kk = 0; kk < C::BR / 16; ++kk) {
+        lbf16x8 bo[C::WB];
+#pragma unroll
+        for (int y = 0; y < C::WB; ++y)
+          bo[y] = ltr_op(DN, C::STR, c_base + y * 32 + 16 * g16, kk * 16 + 8 * hh, kk * 16 + 8 * hh + 4, lane);
+#pragma unroll
+        for (int x = 0; x < C::WB; ++x) {
+          const lbf16x8 ao = ltr_op(SQ, C::STR, a_base + x * 32 + 16 * g16, kk * 16 + 8 * hh, kk * 16 + 8 * hh + 4, lane);
+#pragma unroll
+          for (int y = 0; y < C::WB; ++y)
+            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bo[y], acc[x][y], 0, 0, 0);
+        }
+      }
+      if (tid < D) {
+        float t4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int q = 0; q < C::BR; ++q) t4[q & 3] += (float)SQ[q * C::STR + tid] * dd[q];
+        zacc += (t4[0] + t4[1]) + (t4[2] + t4[3]);
+      }
+      __syncthreads();
+    }
+  }
+  // C layout: column c = c_base + y*32 + lq, rows a = a_base + x*32 + 8(e/4) + 4hh + e%4
+  float* Rs = R + (size_t)unit * D * D;
+#pragma unroll
+  for (int x = 0; x < C::WB; ++x)
+#pragma unroll
+    for (int y = 0; y < C::WB; ++y)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        Rs[(size_t)(a_base + x * 32 + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + c_base + y * 32 + lq] = acc[x][y][e];
+  if (tid < D) r[(size_t)unit * D + tid] = zacc;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void rscan_rev_kernel(
+    const float* __restrict__ R, const float* __restrict__ r, const float* dM_in, const float* dz_in,
+    float* dM_out, float* dz_out, float* __restrict__ dMsnap, float* __restrict__ dzsnap, int nseg) {
+  constexpr int T = 32, TPR = D / T;
+  const int a0 = (blockIdx.x / TPR) * T, c0 = (blockIdx.x % TPR) * T;
+  const bool do_z = (blockIdx.x % TPR) == 0;
+  const size_t bk = blockIdx.y;
+  const int tid = threadIdx.x;
+  const size_t eoff = (size_t)(a0 + tid / 8) * D + c0 + (tid % 8) * 4;
+  lf32x4 acc = dM_in ? *reinterpret_cast<const lf32x4*>(dM_in + bk * D * D + eoff) : lf32x4{};
+  float zacc = (do_z && tid < T && dz_in) ? dz_in[bk * D + a0 + tid] : 0.f;
+  for (int sl = nseg - 1; sl >= 0; --sl) {
+    const size_t unit = bk * nseg + sl;
+    *reinterpret_cast<lf32x4*>(dMsnap + unit * D * D + eoff) = acc;
+    acc += *reinterpret_cast<const lf32x4*>(R + unit * D * D + eoff);
+    if (do_z && tid < T) {
+      dzsnap[unit * D + a0 + tid] = zacc;
+      zacc += r[unit * D + a0 + tid];
+    }
+  }
+  if (dM_out) {
+    *reinterpret_cast<lf32x4*>(dM_out + bk * D * D + eoff) = acc;
+    if (do_z && tid < T) dz_out[bk * D + a0 + tid] = zacc;
+  }
+}
+
+hipError_t launch_rscan_mfma(const Geometry& g, const void* Q, const BwdChunkWs& w, float* R, float* r,
+                             const float* dM_in, const float* dz_in, float* dM_out, float* dz_out,
+                             int s_begin, int s_end, hipStream_t st) {
+  if (!bwd_long_mfma_supported(g)) return hipErrorInvalidValue;
+  const int nseg = s_end - s_begin;
+  const long long units = (long long)g.B * g.Hkv * nseg;
+  if (units > 0x7fffffffLL) return hipErrorInvalidValue;
+  const __bf16* q = static_cast<const __bf16*>(Q);
+  if (g.D == 128)
+    hipLaunchKernelGGL(rdelta_mfma_kernel<128>, dim3((unsigned)units), dim3(256), 0, st, q, w.dnum, w.dden, R, r,
+                       g.Hq, g.Hkv, g.N, g.L, s_begin, nseg, g.lens);
+  else
+    hipLaunchKernelGGL(rdelta_mfma_kernel<64>, dim3((unsigned)units), dim3(256), 0, st, q, w.dnum, w.dden, R, r,
+                       g.Hq, g.Hkv, g.N, g.L, s_begin, nseg, g.lens);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int tiles = (g.D / 32) * (g.D / 32);
+  if (g.D == 128)
+    hipLaunchKernelGGL(rscan_rev_kernel<128>, dim3(tiles, g.B * g.Hkv), dim3(256), 0, st, R, r, dM_in, dz_in,
+                       dM_out, dz_out, w.dMsnap, w.dzsnap, nseg);
+  else
+    hipLaunchKernelGGL(rscan_rev_kernel<64>, dim3(tiles, g.B * g.Hkv), dim3(256), 0, st, R, r, dM_in, dz_in,
+                       dM_out, dz_out, w.dMsnap, w.dzsnap, nseg);
+  return hipGetLastError();
+}
+
 bool bwd_long_mfma_supported(const Geometry& g) {
   return g.fmap == 0 && g.dtype == 1 && (g.D == 64 || g.D == 128);
 }
@@ -657,15 +820,16 @@ int bwd_q_mfma_row_blocks(const Geometry& g) {
 
 template <int D>
 static hipError_t bwd_q_mfma_t(const Geometry& g, const void* Q, const void* K, const void* V,
-                               const float* beta, const float* Msnap, const float* zsnap, const void* dO,
-                               void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin, int s_end,
-                               hipStream_t st) {
+                               const float* beta, const void* MhiT, const void* MloT, const float* zsnap,
+                               const void* dO, void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin,
+                               int s_end, hipStream_t st) {
   const int nseg = s_end - s_begin;
   const float scale = 1.f / sqrtf((float)D);
   dim3 grid((g.L + BqCfg<D>::BM - 1) / BqCfg<D>::BM, g.Hq, g.B * nseg);
   hipLaunchKernelGGL((bwd_q_mfma_kernel<D>), grid, dim3(BqCfg<D>::NT), 0, st,
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
-                     static_cast<const __bf16*>(V), beta, Msnap, zsnap, static_cast<const __bf16*>(dO),
+                     static_cast<const __bf16*>(V), beta, static_cast<const __bf16*>(MhiT),
+                     static_cast<const __bf16*>(MloT), zsnap, static_cast<const __bf16*>(dO),
                      static_cast<__bf16*>(dQ), w.lse, w.Dd, w.dden, w.dnum, w.dbeta_part, lse_in, g.Hq,
                      g.Hkv, g.N, g.L, s_begin, nseg, 1.4426950408889634f * scale, scale, g.lens);
   return hipGetLastError();
@@ -695,12 +859,12 @@ hipError_t launch_bwd_kv_mfma(const Geometry& g, const void* Q, const void* K, c
 }
 
 hipError_t launch_bwd_q_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
-                             const float* beta, const float* Msnap, const float* zsnap, const void* dO,
-                             void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin, int s_end,
-                             hipStream_t st) {
+                             const float* beta, const void* MhiT, const void* MloT, const float* zsnap,
+                             const void* dO, void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin,
+                             int s_end, hipStream_t st) {
   if (!bwd_long_mfma_supported(g)) return hipErrorInvalidValue;
-  if (g.D == 128) return bwd_q_mfma_t<128>(g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, lse_in, s_begin, s_end, st);
-  return bwd_q_mfma_t<64>(g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, lse_in, s_begin, s_end, st);
+  if (g.D == 128) return bwd_q_mfma_t<128>(g, Q, K, V, beta, MhiT, MloT, zsnap, dO, dQ, w, lse_in, s_begin, s_end, st);
+  return bwd_q_mfma_t<64>(g, Q, K, V, beta, MhiT, MloT, zsnap, dO, dQ, w, lse_in, s_begin, s_end, st);
 }
 
 }  // namespace infini

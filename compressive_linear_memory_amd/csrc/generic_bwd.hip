@@ -530,8 +530,6 @@ hipError_t launch_bwd_q(const Geometry& g, const void* Q, const void* K, const v
                         const float* beta, const float* Msnap, const float* zsnap, const void* dO,
                         void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin, int s_end,
                         hipStream_t st) {
-  if (bwd_long_mfma_supported(g))
-    return launch_bwd_q_mfma(g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, lse_in, s_begin, s_end, st);
   DISPATCH_TD(bwd_q_t, g, Q, K, V, beta, Msnap, zsnap, dO, dQ, w, lse_in, s_begin, s_end, st);
 }
 

@@ -58,9 +58,11 @@ hipError_t launch_sweep(const Geometry& g, const void* K, const void* V,
 // Key splits per segment of the bf16 memory phase (dM and dz hold that many
 // parts per segment).
 int delta_splits(const Geometry& g);
+// MsnapTlo, when given, receives bf16(M - bf16(M)) in the layout of MsnapT.
 hipError_t launch_sweep_mfma(const Geometry& g, const void* K, const void* V, const float* M_in,
                              const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
-                             void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st);
+                             void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st,
+                             void* MsnapTlo = nullptr);
 
 // bf16 matrix-core forward (head_dim 64 or 128), reading MsnapT / zsnap.
 bool fwd_mfma_supported(const Geometry& g);
@@ -135,10 +137,17 @@ int bwd_q_row_blocks(const Geometry& g);
 // cores (bwd_long.hip), with the same workspace as the generic kernels.
 bool bwd_long_mfma_supported(const Geometry& g);
 int bwd_q_mfma_row_blocks(const Geometry& g);
+// MhiT / MloT: the segments' M_{s-1} transposed, as bf16 and its bf16 rounding
+// remainder ([B*Hkv][nseg][D][D], from launch_sweep_mfma).
 hipError_t launch_bwd_q_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
-                             const float* beta, const float* Msnap, const float* zsnap, const void* dO,
-                             void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin, int s_end,
-                             hipStream_t st);
+                             const float* beta, const void* MhiT, const void* MloT, const float* zsnap,
+                             const void* dO, void* dQ, const BwdChunkWs& w, const float* lse_in, int s_begin,
+                             int s_end, hipStream_t st);
+// R, r: scratch [B*Hkv][nseg][D][D] and [B*Hkv][nseg][D] for the segments'
+// retrieval terms; writes w.dMsnap / w.dzsnap and dM_out / dz_out as launch_rscan.
+hipError_t launch_rscan_mfma(const Geometry& g, const void* Q, const BwdChunkWs& w, float* R, float* r,
+                             const float* dM_in, const float* dz_in, float* dM_out, float* dz_out,
+                             int s_begin, int s_end, hipStream_t st);
 hipError_t launch_bwd_kv_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
                               const float* beta, const void* dO, const BwdChunkWs& w, void* dK, void* dV,
                               int s_begin, int s_end, hipStream_t st);

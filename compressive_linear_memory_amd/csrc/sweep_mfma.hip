@@ -16,8 +16,10 @@
 //   scan_kernel        one workgroup per 64x64 tile of M per (batch, K/V head):
 //                      walks the segments in order with the tile resident in
 //                      registers, publishes each M_{s-1} as a transposed bf16
-//                      copy (the operand layout the attention kernel reads) and
-//                      z_{s-1} in fp32, and writes the final state.
+//                      copy (the operand layout the attention kernel reads;
+//                      optionally also its rounding remainder, for the
+//                      backward's retrieval gradient) and z_{s-1} in fp32, and
+//                      writes the final state.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -195,7 +197,7 @@ template <int D>
 __global__ __launch_bounds__(256) void scan_kernel(
     const float* __restrict__ dM, const float* __restrict__ dz, const float* M_in, const float* z_in,
     float* M_out, float* z_out, __bf16* __restrict__ MsnapT, float* __restrict__ zsnap, int nseg,
-    int nsplit) {
+    int nsplit, __bf16* __restrict__ MsnapTlo) {
   constexpr int TPR = D / SC_T;
   __shared__ float tr[SC_T][SC_T + 1];
   const int a0 = (blockIdx.x / TPR) * SC_T, c0 = (blockIdx.x % TPR) * SC_T;
@@ -247,6 +249,12 @@ __global__ __launch_bounds__(256) void scan_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = (__bf16)tr[aa + e][cc];
       *reinterpret_cast<bf16x4_t*>(dst) = w;
+      if (MsnapTlo) {   // the rounding remainder, for readers that need M beyond bf16
+        bf16x4_t lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lo[e] = (__bf16)(tr[aa + e][cc] - (float)w[e]);
+        *reinterpret_cast<bf16x4_t*>(MsnapTlo + (dst - MsnapT)) = lo;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -263,7 +271,8 @@ __global__ __launch_bounds__(256) void scan_kernel(
 template <int D>
 static hipError_t sweep_mfma_t(const Geometry& g, const void* K, const void* V, const float* M_in,
                                const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
-                               void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st) {
+                               void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st,
+                               void* MsnapTlo) {
   const int nseg = s_end - s_begin;
   const int nsplit = delta_splits(g);
   const int split_keys = (((g.L + nsplit - 1) / nsplit + 63) / 64) * 64;
@@ -276,7 +285,7 @@ static hipError_t sweep_mfma_t(const Geometry& g, const void* K, const void* V, 
   if (e != hipSuccess) return e;
   dim3 grid((D / SC_T) * (D / SC_T), g.B * g.Hkv);
   hipLaunchKernelGGL((scan_kernel<D>), grid, dim3(256), 0, st, dM, dz, M_in, z_in, M_out, z_out,
-                     static_cast<__bf16*>(MsnapT), zsnap, nseg, nsplit);
+                     static_cast<__bf16*>(MsnapT), zsnap, nseg, nsplit, static_cast<__bf16*>(MsnapTlo));
   return hipGetLastError();
 }
 
@@ -309,7 +318,7 @@ static hipError_t sweep_mfma_group_t(const Geometry& g, const FwdCallTable& tab,
   if (e != hipSuccess) return e;
   dim3 grid((D / SC_T) * (D / SC_T), g.B * g.Hkv);
   hipLaunchKernelGGL((scan_kernel<D>), grid, dim3(256), 0, st, dM, dz, M_in, z_in, M_out, z_out,
-                     static_cast<__bf16*>(MsnapT), zsnap, nseg, nsplit);
+                     static_cast<__bf16*>(MsnapT), zsnap, nseg, nsplit, nullptr);
   return hipGetLastError();
 }
 
@@ -324,10 +333,11 @@ hipError_t launch_sweep_mfma_group(const Geometry& g, const FwdCallTable& tab, i
 
 hipError_t launch_sweep_mfma(const Geometry& g, const void* K, const void* V, const float* M_in,
                              const float* z_in, float* M_out, float* z_out, float* dM, float* dz,
-                             void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st) {
+                             void* MsnapT, float* zsnap, int s_begin, int s_end, hipStream_t st,
+                             void* MsnapTlo) {
   if (g.dtype != 1) return hipErrorInvalidValue;
-  if (g.D == 128) return sweep_mfma_t<128>(g, K, V, M_in, z_in, M_out, z_out, dM, dz, MsnapT, zsnap, s_begin, s_end, st);
-  if (g.D == 64) return sweep_mfma_t<64>(g, K, V, M_in, z_in, M_out, z_out, dM, dz, MsnapT, zsnap, s_begin, s_end, st);
+  if (g.D == 128) return sweep_mfma_t<128>(g, K, V, M_in, z_in, M_out, z_out, dM, dz, MsnapT, zsnap, s_begin, s_end, st, MsnapTlo);
+  if (g.D == 64) return sweep_mfma_t<64>(g, K, V, M_in, z_in, M_out, z_out, dM, dz, MsnapT, zsnap, s_begin, s_end, st, MsnapTlo);
   return hipErrorInvalidValue;
 }
 
