@@ -45,10 +45,10 @@ typedef float lf32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct BqCfg {
-  // 4 waves of 32 query rows; at head_dim 128 the live operands and
-  // accumulators need the whole register file of a SIMD (one wave each)
+  // 4 waves of 32 query rows, two workgroups per compute unit (two waves per
+  // SIMD; one wave per SIMD with the whole register file was 1.25x slower)
   static constexpr int BM = 128;                    // query rows per workgroup
-  static constexpr int WPE = D == 128 ? 1 : 2;      // waves per SIMD
+  static constexpr int WPE = 2;                     // waves per SIMD
   static constexpr int NW = BM / 32;                // waves
   static constexpr int NT = NW * 64;
   static constexpr int BN = 64;                     // keys per tile
@@ -436,7 +436,7 @@ template <int D>
 struct BkCfg {
   static constexpr int BK = 128;                    // keys per workgroup (4 waves of 32)
   static constexpr int NT = 256;
-  static constexpr int WPE = D == 128 ? 1 : 2;      // waves per SIMD
+  static constexpr int WPE = 2;                     // waves per SIMD
   static constexpr int BQ = 64;                     // query rows per staged tile
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
