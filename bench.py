@@ -63,6 +63,16 @@ def algorithmic(w: I.Workload):
     )
 
 
+def algorithmic_bwd_flop(w: I.Workload):
+    """Matrix work of one backward call: the local backward's five causal
+    products (recomputed scores, dP, dS K, dS^T Q, P^T dA_dot), the retrieval
+    backward's three (A_mem, dnum M^T, sigma(Q)^T dnum) and the update
+    backward's two (sigma(K) dM, V dM^T)."""
+    B, Hq, Hkv, L, S, d = w.batch, w.q_heads, w.kv_heads, w.seg_len, w.segments, w.head_dim
+    local = 5 * 2 * d * L * (L + 1) / 2
+    return B * Hq * S * (local + 3 * 2 * L * d * d) + B * Hkv * S * 2 * 2 * L * d * d
+
+
 def recorded_traffic(w, path):
     """HBM bytes per launch of the attention kernel from the committed counter
     summary, or None if there is none for this workload or the kernel source
@@ -139,6 +149,8 @@ def main():
                          "copy: a plain device copy of known size (calibrates HBM byte counters); "
                          "taylor: forward with the second-order Taylor feature map (200M-model shape)")
     ap.add_argument("--launches", type=int, default=512, help="stream mode: chained launches per step")
+    ap.add_argument("--long-segments", action="store_true",
+                    help="train mode: the --workload's own shape (default: 64-token training segments)")
     ap.add_argument("--graph", action="store_true",
                     help="stream mode: capture the chained launches of one step in a HIP graph and replay it")
     ap.add_argument("--decode-tokens", type=int, default=0,
@@ -278,7 +290,10 @@ def bench_train(args):
     import torch
     from compressive_linear_memory_amd import binding as Bi
     Bi.lib()
-    w = I.WORKLOADS["train_llama3_8b"] if args.workload == "fwd_llama3_8b" else I.WORKLOADS[args.workload]
+    if args.long_segments:            # the forward workload's shape (2048-token segments)
+        w = I.WORKLOADS[args.workload]
+    else:
+        w = I.WORKLOADS["train_llama3_8b"] if args.workload == "fwd_llama3_8b" else I.WORKLOADS[args.workload]
     say(f"[bench] generating {w.name} inputs")
     Q, K, V = I.qkv(w)
     dO = I.d_out(w)
@@ -321,14 +336,24 @@ def bench_train(args):
     n_q, n_kv = B_ * Hq * N * d, B_ * Hkv * N * d
     bwd_bytes = eb * (2 * n_q + 2 * n_kv) + 4 * B_ * Hq * N + eb * (n_q + 2 * n_kv) + 2 * B_ * Hkv * (d * d + d) * 4
     step_bytes = alg["step_bytes"] + 4 * B_ * Hq * N + bwd_bytes
-    ach = step_bytes / (total / args.steps / 1e3) / 1e9
-    roof = dict(bound="hbm", peak=PEAK_HBM_GBS, unit="GB/s", achieved=round(ach, 1), frac=round(ach / PEAK_HBM_GBS, 5),
-                traffic=None, kernel="infini_attn_fwd + infini_attn_bwd", bytes_per_step=step_bytes)
-    print(json.dumps({"metric": f"Infini-attention fwd+bwd tokens/s ({w.name})", "value": round(tok * args.steps / (total / 1e3), 1),
+    if args.long_segments:
+        # long segments: the causal products dominate and the matrix cores bind
+        flop = alg["step_flop"] + algorithmic_bwd_flop(w)
+        ach = flop / (total / args.steps / 1e3) / 1e12
+        roof = dict(bound="mfma", peak=PEAK_BF16_MFMA_TFLOPS, unit="TFLOP/s", achieved=round(ach, 3),
+                    frac=round(ach / PEAK_BF16_MFMA_TFLOPS, 5), traffic=None,
+                    kernel="infini_attn_fwd + infini_attn_bwd", flop_per_step=flop)
+        name = w.name + "_train"
+    else:
+        ach = step_bytes / (total / args.steps / 1e3) / 1e9
+        roof = dict(bound="hbm", peak=PEAK_HBM_GBS, unit="GB/s", achieved=round(ach, 1), frac=round(ach / PEAK_HBM_GBS, 5),
+                    traffic=None, kernel="infini_attn_fwd + infini_attn_bwd", bytes_per_step=step_bytes)
+        name = w.name
+    print(json.dumps({"metric": f"Infini-attention fwd+bwd tokens/s ({name})", "value": round(tok * args.steps / (total / 1e3), 1),
                       "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "ms_per_step": round(total / args.steps, 4), "higher_is_better": True, "scaling": "weak",
                       "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-                      "config": {"workload": w.name, "mode": "train", "kernel_path": Bi.fwd_path(p)},
+                      "config": {"workload": name, "mode": "train", "kernel_path": Bi.fwd_path(p)},
                       "phases_ms": {"fwd": round(fwd, 4), "bwd": round(bwd, 4)}, "roofline": roof}), flush=True)
 
 
