@@ -98,21 +98,25 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
                        float* __restrict__ ws_lse, float* __restrict__ ws_Dd, float* __restrict__ ws_dden,
                        float* __restrict__ ws_dnum, float* __restrict__ dbeta_part,
                        const float* __restrict__ lse_in, int Hq, int Hkv, int N, int L, int s_begin,
-                       int nseg, float sl2, float scale, const int* __restrict__ lens) {
+                       int nseg, int nqt, float sl2, float scale, const int* __restrict__ lens) {
   using C = BqCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[C::LDS];
   __shared__ float zs[D];
   __shared__ float wsum[C::NW];
 
-  const int qt = blockIdx.x, h = blockIdx.y;
-  const int sl = blockIdx.z % nseg, b = blockIdx.z / nseg;
+  // query tiles with the most keys first
+  const int per_qt = (int)gridDim.x / nqt;           // (head, batch, segment) units per query tile
+  const int qt = nqt - 1 - (int)blockIdx.x / per_qt;
+  const int rem = (int)blockIdx.x % per_qt;
+  const int h = rem % Hq;
+  const int sl = (rem / Hq) % nseg, b = (rem / Hq) / nseg;
   const int s = s_begin + sl;
   const int G = Hq / Hkv, kvh = h / G;
   const int tid = threadIdx.x;
   // rows of this segment: the last may be short; none past the end of a
   // sequence of a variable-length batch (the gate partial is then zero)
   const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
-  const size_t dbp = (((size_t)b * Hq + h) * nseg + sl) * gridDim.x + qt;
+  const size_t dbp = (((size_t)b * Hq + h) * nseg + sl) * nqt + qt;
   if (Ls <= 0 || qt * C::BM >= Ls) {
     if (tid == 0) dbeta_part[dbp] = 0.f;
     return;
@@ -459,11 +463,15 @@ void bwd_kv_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
                         const int* __restrict__ lens) {
   using C = BkCfg<D>;
   __shared__ __attribute__((aligned(16))) __bf16 smem[C::LDS];
-  __shared__ float rowst[2][2][C::BQ];              // per buffer: lse (base 2), D_i
+  __shared__ __attribute__((aligned(16))) float rowst[2][2][C::BQ];   // per buffer: lse (base 2), D_i
   __shared__ float dzs[D];
 
-  const int kt = blockIdx.x, kvh = blockIdx.y;
-  const int sl = blockIdx.z % nseg, b = blockIdx.z / nseg;
+  // key tiles with the most query rows (the first) first
+  const int per_kt = (int)gridDim.x / ((L + C::BK - 1) / C::BK);   // units per key tile
+  const int kt = (int)blockIdx.x / per_kt;
+  const int rem = (int)blockIdx.x % per_kt;
+  const int kvh = rem % Hkv;
+  const int sl = (rem / Hkv) % nseg, b = (rem / Hkv) / nseg;
   const int s = s_begin + sl;
   const int G = Hq / Hkv;
   // keys (and rows) of this segment: the last may be short; none past the end
@@ -566,13 +574,19 @@ void bwd_kv_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       }
       lbf16x8 pb[2], dsb[2];                        // k-slot x of half hh <-> row 16t + 8(x/4) + 4hh + x%4
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rloc = qb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const int row = q0 + rloc;
-        const bool on = row >= key && row < Ls;
-        const float p = on ? __builtin_amdgcn_exp2f(fmaf(sacc[r], sl2, -rowst[buf][0][rloc])) : 0.f;
-        pb[r >> 3][r & 7] = (__bf16)p;
-        dsb[r >> 3][r & 7] = (__bf16)(scale * p * (pacc[r] - rowst[buf][1][rloc]));
+      for (int u = 0; u < 4; ++u) {
+        const int rl0 = qb * 32 + 8 * u + 4 * hh;  // rows of elements 4u .. 4u+3
+        const lf32x4 lse4 = *reinterpret_cast<const lf32x4*>(&rowst[buf][0][rl0]);
+        const lf32x4 dd4 = *reinterpret_cast<const lf32x4*>(&rowst[buf][1][rl0]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * u + x;
+          const int row = q0 + rl0 + x;
+          const bool on = row >= key && row < Ls;
+          const float p = on ? __builtin_amdgcn_exp2f(fmaf(sacc[r], sl2, -lse4[x])) : 0.f;
+          pb[r >> 3][r & 7] = (__bf16)p;
+          dsb[r >> 3][r & 7] = (__bf16)(scale * p * (pacc[r] - dd4[x]));
+        }
       }
       // dV^T += dA_dot^T P, dK^T += Q^T dS (contraction over the block's rows)
 #pragma unroll
@@ -825,13 +839,16 @@ static hipError_t bwd_q_mfma_t(const Geometry& g, const void* Q, const void* K, 
                                int s_end, hipStream_t st) {
   const int nseg = s_end - s_begin;
   const float scale = 1.f / sqrtf((float)D);
-  dim3 grid((g.L + BqCfg<D>::BM - 1) / BqCfg<D>::BM, g.Hq, g.B * nseg);
+  const int nqt = (g.L + BqCfg<D>::BM - 1) / BqCfg<D>::BM;
+  const long long units = (long long)nqt * g.Hq * g.B * nseg;
+  if (units > 0x7fffffffLL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)units);
   hipLaunchKernelGGL((bwd_q_mfma_kernel<D>), grid, dim3(BqCfg<D>::NT), 0, st,
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
                      static_cast<const __bf16*>(V), beta, static_cast<const __bf16*>(MhiT),
                      static_cast<const __bf16*>(MloT), zsnap, static_cast<const __bf16*>(dO),
                      static_cast<__bf16*>(dQ), w.lse, w.Dd, w.dden, w.dnum, w.dbeta_part, lse_in, g.Hq,
-                     g.Hkv, g.N, g.L, s_begin, nseg, 1.4426950408889634f * scale, scale, g.lens);
+                     g.Hkv, g.N, g.L, s_begin, nseg, nqt, 1.4426950408889634f * scale, scale, g.lens);
   return hipGetLastError();
 }
 
@@ -841,7 +858,9 @@ static hipError_t bwd_kv_mfma_t(const Geometry& g, const void* Q, const void* K,
                                 int s_begin, int s_end, hipStream_t st) {
   const int nseg = s_end - s_begin;
   const float scale = 1.f / sqrtf((float)D);
-  dim3 grid((g.L + BkCfg<D>::BK - 1) / BkCfg<D>::BK, g.Hkv, g.B * nseg);
+  const long long units = (long long)((g.L + BkCfg<D>::BK - 1) / BkCfg<D>::BK) * g.Hkv * g.B * nseg;
+  if (units > 0x7fffffffLL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)units);
   hipLaunchKernelGGL((bwd_kv_mfma_kernel<D>), grid, dim3(BkCfg<D>::NT), 0, st,
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K),
                      static_cast<const __bf16*>(V), beta, static_cast<const __bf16*>(dO), w.lse, w.Dd,
