@@ -378,7 +378,8 @@ PEAKED_BWD = [
     (2, 4, 2, 192, 128, 64, "bf16", 4.0, False, True),     # fused short backward
     (1, 2, 2, 130, 64, 64, "bf16", 1.0, True, True),
     (1, 8, 2, 100, 128, 40, "bf16", 4.0, True, False),
-    (1, 2, 2, 300, 64, 150, "bf16", 4.0, True, True),      # generic backward, long bf16 segments
+    (1, 2, 2, 300, 64, 150, "bf16", 4.0, True, True),      # long-segment matrix-core backward
+    (1, 4, 2, 520, 128, 256, "bf16", 4.0, True, True),     # long-segment, head_dim 128, 8-token tail
     (1, 4, 2, 200, 64, 100, "fp32", 4.0, False, True),
     (1, 2, 1, 200, 128, 200, "fp32", 1.0, True, False),
 ]
