@@ -51,7 +51,9 @@ struct BqCfg {
   static constexpr int WPE = 2;                     // waves per SIMD
   static constexpr int NW = BM / 32;                // waves
   static constexpr int NT = NW * 64;
-  static constexpr int BN = 64;                     // keys per tile
+  // keys per tile: at head_dim 128, 32 keep the staging registers down
+  static constexpr int BN = D == 128 ? 32 : 64;
+  static constexpr int NKB = BN / 32;               // 32-key blocks per tile
   static constexpr int KS = D / 16;                 // k-steps over head_dim
   static constexpr int DB = D / 32;                 // 32-row blocks of head_dim
   static constexpr int KSTR = D + 8;                // row stride of the K and V tiles
@@ -171,9 +173,9 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
   };
   // scores of one tile (S^T, C layout: column qrow, element (kb, r) is key
   // k0 + kb*32 + 8(r/4) + 4hh + r%4), masked past the diagonal and the segment end
-  auto scores = [&](const __bf16* Ks, int k0, lf32x16 (&sacc)[2]) {
+  auto scores = [&](const __bf16* Ks, int k0, lf32x16 (&sacc)[C::NKB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::NKB; ++kb) {
       sacc[kb] = lf32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
@@ -184,7 +186,7 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
     if (k0 + C::BN - 1 > q0 || k0 + C::BN > Ls) {
       const int lim = min(qrow, Ls - 1) - (k0 + 4 * hh);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
@@ -215,12 +217,12 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
   float lpart = 0.f;
   const lbf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   sweep([&](const __bf16* Ks, const __bf16* Vs, int k0) {
-    lf32x16 sacc[2];
+    lf32x16 sacc[C::NKB];
     scores(Ks, k0, sacc);
     if (!have_lse) {
       float mt = sacc[0][0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
       const float mn = fmaxf(m, lpair_max32(mt) * sl2);
@@ -230,15 +232,15 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
     }
-    lbf16x8 pb[2][2];
+    lbf16x8 pb[C::NKB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         pb[kb][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -m));
     if (!have_lse) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -247,7 +249,7 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
     }
     // O^T += V^T P^T: k-slot x of half hh <-> key kb*32 + 16t + 8(x/4) + 4hh + x%4
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int kk = kb * 32 + 16 * t + 4 * hh;
@@ -391,11 +393,11 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
 
   // ---- pass 2: dQ^T += K^T dS^T, dS = P (dP - D_i) / sqrt(d) with dP^T = V dA_dot^T
   sweep([&](const __bf16* Ks, const __bf16* Vs, int k0) {
-    lf32x16 sacc[2];
+    lf32x16 sacc[C::NKB];
     scores(Ks, k0, sacc);
-    lf32x16 pacc[2];
+    lf32x16 pacc[C::NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::NKB; ++kb) {
       pacc[kb] = lf32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
@@ -403,16 +405,16 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
         pacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dreg[ks], pacc[kb], 0, 0, 0);
       }
     }
-    lbf16x8 dsb[2][2];
+    lbf16x8 dsb[C::NKB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl2, -m));
         dsb[kb][r >> 3][r & 7] = (__bf16)(scale * p * (pacc[kb][r] - Dd));
       }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int kk = kb * 32 + 16 * t + 4 * hh;
@@ -441,7 +443,9 @@ struct BkCfg {
   static constexpr int BK = 128;                    // keys per workgroup (4 waves of 32)
   static constexpr int NT = 256;
   static constexpr int WPE = 2;                     // waves per SIMD
-  static constexpr int BQ = 64;                     // query rows per staged tile
+  // query rows per staged tile: at head_dim 128, 32 keep the staging registers
+  // (and with them the spills) down
+  static constexpr int BQ = D == 128 ? 32 : 64;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int QSTR = D + 8;                // row stride of the Q and dA_dot tiles
@@ -560,7 +564,7 @@ void bwd_kv_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     const __bf16* Qs = smem + buf * C::BUF;
     const __bf16* As = Qs + C::QTILE;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < C::BQ / 32; ++qb) {
       const int qb0 = q0 + qb * 32;                 // first row of this 32-row block
       if (qb0 + 31 < kw || qb0 >= Ls) continue;     // every row before the wave's keys, or past the end
       // S[q][key] and dP[q][key]: element r holds row qb0 + 8(r/4) + 4hh + r%4
