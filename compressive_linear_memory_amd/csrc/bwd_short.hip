@@ -111,7 +111,8 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   __shared__ __attribute__((aligned(16))) __bf16 Xb[C::BL * RS];   // dA_dot, then dnum, rows q
   __shared__ __attribute__((aligned(16))) __bf16 Pb[C::BL * PS];   // P rows q
   __shared__ __attribute__((aligned(16))) __bf16 Sb[C::BL * PS];   // dS rows q
-  __shared__ float zs[D], dzs[D], dds[C::BL];
+  __shared__ float zs[D], dzs[D];
+  __shared__ __attribute__((aligned(16))) float dds[C::BL];
   __shared__ float dbacc[kBwdMaxGroup][4];
   float (*zred)[D + 1] = reinterpret_cast<float (*)[D + 1]>(Xb);   // staging only
   static_assert(C::NKG * (D + 1) * 4 <= C::BL * RS * 2, "z partials must fit the scratch tile");
@@ -121,9 +122,13 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int G = Hq / Hkv;
   const int Nb = seq_len_of(lens, b, N);    // tokens of this sequence
   const int S = (Nb + L - 1) / L;           // the last segment may be short
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lc = lane & 15, g = lane >> 4;
+  // Lane indices.  They are passed through an empty asm statement at the
+  // top of each segment and head step ("refresh"), so that the compiler
+  // recomputes the addresses derived from them there instead of keeping
+  // dozens of them live (and spilled) across the whole loop.
+  int tid = threadIdx.x;
+  int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int lc = lane & 15, g = lane >> 4;
   const size_t kvbase = ((size_t)b * Hkv + kvh) * N * D;
 
   // ---- resident state: M and dM blocks (a = ab*16 + 4g + i, c = cb*16 + lc)
@@ -144,24 +149,34 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   }
   if (tid < kBwdMaxGroup * 4) dbacc[tid / 4][tid % 4] = 0.f;
 
-  // ---- staging of segment s: K and V rows (V rows past the end are zero)
-  const int kg = tid % C::NKG, dc = tid / C::NKG;
-  auto stage_kv = [&](int s) {
+  // ---- staging of segment s: K and V rows (V rows past the end are zero).
+  // The rows are loaded into registers one segment ahead (load_kv) and
+  // written to LDS when the segment starts (store_kv), so the load latency
+  // hides behind the previous segment's work.
+  int kg = tid % C::NKG, dc = tid / C::NKG;
+  bbf16x8 kst[C::KPT], vst[C::KPT];
+  auto load_kv = [&](int s) {
+    const int Lk = min(L, Nb - s * L);     // keys of this segment
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const size_t off = kvbase + ((size_t)s * L + min(kg * C::KPT + i, Lk - 1)) * D + dc * 8;
+      kst[i] = *reinterpret_cast<const bbf16x8*>(K + off);
+      vst[i] = *reinterpret_cast<const bbf16x8*>(V + off);
+    }
+  };
+  auto store_kv = [&](int s) {
     float zp[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) zp[e] = 0.f;
-    const int Lk = min(L, Nb - s * L);     // keys of this segment
+    const int Lk = min(L, Nb - s * L);
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int key = kg * C::KPT + i;
       const bool in = key < Lk;
-      const size_t off = kvbase + ((size_t)s * L + min(key, Lk - 1)) * D + dc * 8;
-      const bbf16x8 kv = *reinterpret_cast<const bbf16x8*>(K + off);
-      const bbf16x8 vv = *reinterpret_cast<const bbf16x8*>(V + off);
-      *reinterpret_cast<bbf16x8*>(Ks + key * RS + dc * 8) = kv;
-      *reinterpret_cast<bbf16x8*>(Vr + key * RS + dc * 8) = in ? vv : bbf16x8{};
+      *reinterpret_cast<bbf16x8*>(Ks + key * RS + dc * 8) = kst[i];
+      *reinterpret_cast<bbf16x8*>(Vr + key * RS + dc * 8) = in ? vst[i] : bbf16x8{};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) zp[e] += in ? elu1((float)kv[e]) : 0.f;
+      for (int e = 0; e < 8; ++e) zp[e] += in ? elu1((float)kst[i][e]) : 0.f;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) zred[kg][dc * 8 + e] = zp[e];
@@ -206,22 +221,28 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   };
 
   // ---- 1. replay the memory path to M_S, z_S
+  if (S > 0) load_kv(0);
   for (int s = 0; s < S; ++s) {
-    stage_kv(s);
-    __syncthreads();
+    store_kv(s);
+    load_kv(min(s + 1, S - 1));            // the last one is segment S-1 again: phase 2 starts there
+    lds_barrier();
     state_update(false);
     if (tid < D) zs[tid] += seg_zsum();
-    __syncthreads();
+    lds_barrier();
   }
 
-  const int q = wave * 16 + lc;            // query row of this lane (query-side products)
-  const int jk = wave * 16 + lc;           // key row of this lane (key-side products)
+  int q = wave * 16 + lc;                  // query row of this lane (query-side products)
+  int jk = wave * 16 + lc;                 // key row of this lane (key-side products)
+  auto refresh = [&]() {
+    asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(g), "+v"(kg), "+v"(dc), "+v"(q), "+v"(jk), "+s"(wave));
+  };
 
   // ---- 2. segments in reverse
   for (int s = S - 1; s >= 0; --s) {
+    refresh();
     const int Ls = min(L, Nb - s * L);     // rows and keys of this segment
-    stage_kv(s);
-    __syncthreads();
+    store_kv(s);
+    lds_barrier();
     if (s > 0) {
       state_update(true);                  // M_{s-1}
       if (tid < D) zs[tid] -= seg_zsum();  // z_{s-1}
@@ -239,7 +260,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     }
     publish(macc, Mt);
     publish(dmacc, dMt);
-    __syncthreads();
+    lds_barrier();
 
     // update backward (key-side: this wave's 16 keys), with dM = dL/dM_s
     bf32x4 dkacc[C::DB], dvacc[C::DB];
@@ -275,7 +296,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     // nearly equal terms, so M enters it (and A_mem) as a bf16 hi/lo pair:
     // the low part M - bf16(M) replaces dM^T, which the update backward has
     // finished with.
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int x = 0; x < C::AB; ++x)
 #pragma unroll
@@ -287,7 +308,11 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       }
     const __bf16* Mlo = dMt;
 
-    for (int h = kvh * G; h < (kvh + 1) * G; ++h) {
+    // one query head of the group; the last one also issues the loads of the
+    // next segment's K and V rows (a separate inlined copy, so that those
+    // registers are live only from there on)
+    auto head_step = [&](const int h, const bool prefetch) {
+      refresh();
       // register classes: the state, its gradient and the dK / dV
       // accumulators are read only by the matrix cores inside this loop
 #pragma unroll
@@ -324,7 +349,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           *reinterpret_cast<bbf16x8*>(Qs + row * RS + col) = qv[i];
         }
       }
-      __syncthreads();
+      lds_barrier();
 
       const bool qok = q < Ls;
       const float gt = sigmoid(beta[h]);
@@ -483,9 +508,10 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         *reinterpret_cast<bbf16x4*>(Sb + q * PS + 32 * t + 4 * g) = bbf16x4{dsp[t][0], dsp[t][1], dsp[t][2], dsp[t][3]};
         *reinterpret_cast<bbf16x4*>(Sb + q * PS + 32 * t + 16 + 4 * g) = bbf16x4{dsp[t][4], dsp[t][5], dsp[t][6], dsp[t][7]};
       }
+      if (prefetch) load_kv(s - 1);       // the next segment's rows
       if (g == 0) dds[q] = qok ? dden : 0.f;
       if (lane == 0) dbacc[h - kvh * G][wave] += bsum;   // each wave owns its slot: fixed order
-      __syncthreads();
+      lds_barrier();
       // key side, contracting over the segment's queries: dK^T += Q^T dS
       // (dS carries the softmax scale)
 #pragma unroll
@@ -507,7 +533,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         *reinterpret_cast<bbf16x4*>(Xb + q * RS + 32 * ks + 4 * g) = bbf16x4{w[0], w[1], w[2], w[3]};
         *reinterpret_cast<bbf16x4*>(Xb + q * RS + 32 * ks + 16 + 4 * g) = bbf16x4{w[4], w[5], w[6], w[7]};
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int cb = 0; cb < C::DB; ++cb) {
 #pragma unroll
@@ -517,40 +543,43 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           dvacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, dvacc[cb], 0, 0, 0);
         }
       }
-      __syncthreads();
+      lds_barrier();
       // Xb <- dnum rows; dM += sigma(Q)^T dnum, dz += sigma(Q)^T dden
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         *reinterpret_cast<bbf16x4*>(Xb + q * RS + 32 * ks + 4 * g) = bbf16x4{dnp[ks][0], dnp[ks][1], dnp[ks][2], dnp[ks][3]};
         *reinterpret_cast<bbf16x4*>(Xb + q * RS + 32 * ks + 16 + 4 * g) = bbf16x4{dnp[ks][4], dnp[ks][5], dnp[ks][6], dnp[ks][7]};
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int x = 0; x < C::AB; ++x) {
         const int ab = wave * C::AB + x;
+        float zp = 0.f;                    // dz of row a = ab*16 + lc over this lane's 16 queries
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           bbf16x8 a = tr_op(Qs, RS, ab * 16, 32 * t + 8 * g, 32 * t + 8 * g + 4, lane);
           a = sigma8(a);
-          // query rows past the segment end carry zero dnum
+          // query rows past the segment end carry zero dnum and zero dden
 #pragma unroll
           for (int cb = 0; cb < C::DB; ++cb) {
             const bbf16x8 bb = tr_op(Xb, RS, cb * 16, 32 * t + 8 * g, 32 * t + 8 * g + 4, lane);
             dmacc[x][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, dmacc[x][cb], 0, 0, 0);
           }
-        }
-      }
-      if (tid < D) {
-        // four independent partial sums so that the LDS reads overlap
-        float t4[4] = {0.f, 0.f, 0.f, 0.f};
+          const bf32x4 d0 = *reinterpret_cast<const bf32x4*>(dds + 32 * t + 8 * g);
+          const bf32x4 d1 = *reinterpret_cast<const bf32x4*>(dds + 32 * t + 8 * g + 4);
 #pragma unroll
-        for (int r = 0; r < C::BL; ++r) t4[r & 3] += elu1((float)Qs[r * RS + tid]) * dds[r];
-        dzs[tid] += (t4[0] + t4[1]) + (t4[2] + t4[3]);
+          for (int e = 0; e < 4; ++e) zp += (float)a[e] * d0[e] + (float)a[e + 4] * d1[e];
+        }
+        zp = red16x4(zp);
+        if (g == 0) dzs[ab * 16 + lc] += zp;   // each wave owns its rows
       }
-      __syncthreads();
-    }
+      lds_barrier();
+    };
+    for (int h = kvh * G; h < (kvh + 1) * G - 1; ++h) head_step(h, false);
+    head_step((kvh + 1) * G - 1, s > 0);
 
     // dK, dV of this segment's keys
+    refresh();
     if (jk < Ls) {
       const size_t kr = kvbase + ((size_t)s * L + jk) * D;
 #pragma unroll

@@ -37,6 +37,16 @@ __device__ __forceinline__ int seq_len_of(const int* lens, int b, int N) {
   return lens ? min(max(lens[b], 0), N) : N;
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads also waits
+// for every outstanding global load and store of the wave; after this one,
+// global loads issued before it stay in flight (their registers are waited
+// for where they are used) and global stores drain in the background.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ELU(x) + 1 with alpha = 1.
 __device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 // Its derivative: 1 for x > 0, exp(x) otherwise.
