@@ -234,7 +234,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   int q = wave * 16 + lc;                  // query row of this lane (query-side products)
   int jk = wave * 16 + lc;                 // key row of this lane (key-side products)
   auto refresh = [&]() {
-    asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(g), "+v"(kg), "+v"(dc), "+v"(q), "+v"(jk), "+s"(wave));
+    asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(g), "+v"(kg), "+v"(dc), "+v"(q), "+v"(jk));
   };
 
   // ---- 2. segments in reverse

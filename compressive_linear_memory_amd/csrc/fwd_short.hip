@@ -87,9 +87,13 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   };
   const int s_att = bound(part);            // this part attends segments [s_att, s_end)
   const int s_end = bound(part + 1);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lc = lane & 15, g = lane >> 4;
+  // Lane indices, passed through an empty asm statement at the top of each
+  // segment and head ("refresh") so that the addresses derived from them are
+  // recomputed there instead of being kept live (and spilled) across the loop.
+  int tid = threadIdx.x;
+  int lane = tid & 63;
+  const int wave = tid >> 6;
+  int lc = lane & 15, g = lane >> 4;
   const size_t kvbase = ((size_t)b * Hkv + kvh) * N * D;
 
   // ---- state: M block (ab, cb) of this wave in accumulators, z in LDS
@@ -120,7 +124,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   };
 
   // ---- staging of one segment's K and V: KPT keys x 8 columns per thread
-  const int kg = tid % C::NKG, dc = tid / C::NKG;
+  int kg = tid % C::NKG, dc = tid / C::NKG;
   sbf16x8 kst[C::KPT], vst[C::KPT];
   int Lst = L;                             // keys of the staged segment
   auto load_seg = [&](int s) {
@@ -173,16 +177,18 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   load_seg(0);
   store_seg();
   publish_mt();
-  __syncthreads();
+  lds_barrier();
 
-  const int q0 = wave * 16;                // this wave's query rows inside the segment
-  const int qrow = q0 + lc;                // this lane's query row
+  int qrow = wave * 16 + lc;               // this lane's query row (the wave owns 16)
+  auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(g), "+v"(kg), "+v"(dc), "+v"(qrow)); };
 
   for (int s = 0; s < s_end; ++s) {
+    refresh();
     const int Ls = min(L, Nb - s * L);     // rows and keys of this segment
     if (s + 1 < s_end) load_seg(s + 1);    // in flight while this segment computes
 
     for (int h = kvh * G; s >= s_att && h < (kvh + 1) * G; ++h) {
+      refresh();
       const size_t qb = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
       // Q^T operand: lane holds query qrow, k = 32ks + 8g .. +7
       sbf16x8 qreg[C::KS];
@@ -278,7 +284,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       if (lse && g == 0 && qrow < Ls)
         lse[((size_t)b * Hq + h) * N + (size_t)s * L + qrow] = (mref + __log2f(lsum)) * 0.69314718055994531f;
     }
-    __syncthreads();   // every read of M_{s-1}, z_{s-1} and this segment's tiles is done
+    lds_barrier();   // every read of M_{s-1}, z_{s-1} and this segment's tiles is done
 
     // memory update: M += sigma(K)^T V into the accumulators, z += sum sigma(K)
 #pragma unroll
@@ -299,10 +305,10 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       for (int x = 0; x < C::NKG; ++x) t += zred[x][tid];
       zs[tid] += t;
     }
-    __syncthreads();   // tiles and the z partials are consumed
+    lds_barrier();   // tiles and the z partials are consumed
     if (s + 1 < s_end) store_seg();
     publish_mt();
-    __syncthreads();
+    lds_barrier();
   }
   if (part != parts - 1) return;           // the last part holds the final state
 
