@@ -237,10 +237,31 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(g), "+v"(kg), "+v"(dc), "+v"(q), "+v"(jk));
   };
 
+  // Q rows and this lane's dO pieces of a head (the Q rows are staged into
+  // LDS per head step); those of the group's first head are loaded at the
+  // start of the segment, so that they arrive during the state recovery and
+  // the update backward
+  constexpr int QPT = C::BL * D / 8 / 256;
+  bbf16x8 qpre[QPT];
+  bbf16x4 dpre[C::DB];
+  auto load_qdo = [&](int s, int h) {
+    const int Lq = min(L, Nb - s * L);
+    const size_t qb = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
+    const __bf16* dop = dO + qb + (size_t)min(q, Lq - 1) * D;
+#pragma unroll
+    for (int cb = 0; cb < C::DB; ++cb) dpre[cb] = *reinterpret_cast<const bbf16x4*>(dop + cb * 16 + 4 * g);
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int c = tid + i * 256, row = c / (D / 8), col = (c % (D / 8)) * 8;
+      qpre[i] = *reinterpret_cast<const bbf16x8*>(Q + qb + (size_t)min(row, Lq - 1) * D + col);
+    }
+  };
+
   // ---- 2. segments in reverse
   for (int s = S - 1; s >= 0; --s) {
     refresh();
     const int Ls = min(L, Nb - s * L);     // rows and keys of this segment
+    load_qdo(s, kvh * G);                  // the first head's rows
     store_kv(s);
     lds_barrier();
     if (s > 0) {
@@ -279,6 +300,9 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       for (int i = 0; i < 4; ++i) acc[i] = (acc[i] + dzs[ab * 16 + 4 * g + i]) * elu1_grad((float)kv[i]);
       dkacc[ab] = acc;
     }
+    bbf16x8 skr[C::KS];                    // sigma(K) of this lane's key row, k = 32 ks + 8g ..
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) skr[ks] = sigma8(*reinterpret_cast<const bbf16x8*>(Ks + jk * RS + 32 * ks + 8 * g));
 #pragma unroll
     for (int cb = 0; cb < C::DB; ++cb) {
       // (dM^T sigma(K)^T)[c][j]: A = dM^T rows c (k = a), B = sigma(K)[j][a]
@@ -286,8 +310,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const bbf16x8 a = *reinterpret_cast<const bbf16x8*>(dMt + (cb * 16 + lc) * RS + 32 * ks + 8 * g);
-        const bbf16x8 bb = sigma8(*reinterpret_cast<const bbf16x8*>(Ks + jk * RS + 32 * ks + 8 * g));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, skr[ks], acc, 0, 0, 0);
       }
       dvacc[cb] = acc;
     }
@@ -328,26 +351,16 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         asm volatile("" : "+a"(dvacc[db]));
       }
       const size_t qb = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
-      // this lane's dO pieces (row q, columns cb*16 + 4g ..) are read now and
-      // used after the score and retrieval products
-      const __bf16* dop = dO + qb + (size_t)min(q, Ls - 1) * D;
+      // this lane's dO pieces (row q, columns cb*16 + 4g ..) are used after
+      // the score and retrieval products; the Q rows are staged now
+      if (h != kvh * G) load_qdo(s, h);
       bbf16x4 dov[C::DB];
 #pragma unroll
-      for (int cb = 0; cb < C::DB; ++cb) dov[cb] = *reinterpret_cast<const bbf16x4*>(dop + cb * 16 + 4 * g);
-      // stage Q rows of this head: every load issued before the first store
-      {
-        constexpr int QPT = C::BL * D / 8 / 256;
-        bbf16x8 qv[QPT];
+      for (int cb = 0; cb < C::DB; ++cb) dov[cb] = dpre[cb];
 #pragma unroll
-        for (int i = 0; i < QPT; ++i) {
-          const int c = tid + i * 256, row = c / (D / 8), col = (c % (D / 8)) * 8;
-          qv[i] = *reinterpret_cast<const bbf16x8*>(Q + qb + (size_t)min(row, Ls - 1) * D + col);
-        }
-#pragma unroll
-        for (int i = 0; i < QPT; ++i) {
-          const int c = tid + i * 256, row = c / (D / 8), col = (c % (D / 8)) * 8;
-          *reinterpret_cast<bbf16x8*>(Qs + row * RS + col) = qv[i];
-        }
+      for (int i = 0; i < QPT; ++i) {
+        const int c = tid + i * 256, row = c / (D / 8), col = (c % (D / 8)) * 8;
+        *reinterpret_cast<bbf16x8*>(Qs + row * RS + col) = qpre[i];
       }
       lds_barrier();
 
