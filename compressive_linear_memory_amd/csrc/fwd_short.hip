@@ -182,6 +182,18 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   int qrow = wave * 16 + lc;               // this lane's query row (the wave owns 16)
   auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(g), "+v"(kg), "+v"(dc), "+v"(qrow)); };
 
+  // Q^T operand of a head (lane holds query qrow, k = 32ks + 8g .. +7); the
+  // group's first head is loaded one segment ahead, during the memory update
+  sbf16x8 qnext[C::KS];
+  auto load_q = [&](int s, int h, sbf16x8 (&qr8)[C::KS]) {
+    const size_t qb = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
+    const int qr = min(qrow, min(L, Nb - s * L) - 1);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      qr8[ks] = *reinterpret_cast<const sbf16x8*>(Q + qb + (size_t)qr * D + ks * 32 + g * 8);
+  };
+  if (s_att < s_end) load_q(s_att, kvh * G, qnext);
+
   for (int s = 0; s < s_end; ++s) {
     refresh();
     const int Ls = min(L, Nb - s * L);     // rows and keys of this segment
@@ -190,13 +202,12 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     for (int h = kvh * G; s >= s_att && h < (kvh + 1) * G; ++h) {
       refresh();
       const size_t qb = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
-      // Q^T operand: lane holds query qrow, k = 32ks + 8g .. +7
       sbf16x8 qreg[C::KS];
-      {
-        const int qr = min(qrow, Ls - 1);
+      if (h == kvh * G) {
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-          qreg[ks] = *reinterpret_cast<const sbf16x8*>(Q + qb + (size_t)qr * D + ks * 32 + g * 8);
+        for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = qnext[ks];
+      } else {
+        load_q(s, h, qreg);
       }
       // S^T = K Q^T over the 4 key blocks of 16
       sf32x4 sacc[4];
@@ -285,6 +296,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         lse[((size_t)b * Hq + h) * N + (size_t)s * L + qrow] = (mref + __log2f(lsum)) * 0.69314718055994531f;
     }
     lds_barrier();   // every read of M_{s-1}, z_{s-1} and this segment's tiles is done
+    if (s + 1 < s_end && s + 1 >= s_att) load_q(s + 1, kvh * G, qnext);
 
     // memory update: M += sigma(K)^T V into the accumulators, z += sum sigma(K)
 #pragma unroll
