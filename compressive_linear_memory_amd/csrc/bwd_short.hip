@@ -261,15 +261,11 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   for (int s = S - 1; s >= 0; --s) {
     refresh();
     const int Ls = min(L, Nb - s * L);     // rows and keys of this segment
-    load_qdo(s, kvh * G);                  // the first head's rows
-    store_kv(s);
-    lds_barrier();
-    if (s > 0) {
-      state_update(true);                  // M_{s-1}
-      if (tid < D) zs[tid] -= seg_zsum();  // z_{s-1}
-    } else {
-      // the state passed in, exactly: an empty memory must stay exactly empty
-      // (its retrieval denominator is eps alone)
+    if (s == 0) {
+      // M_{-1}, z_{-1}: the state passed in, exactly (an empty memory must
+      // stay exactly empty: its retrieval denominator is eps alone).  Read
+      // before the segment's own loads are issued, so that waiting for it
+      // does not wait for them.
 #pragma unroll
       for (int x = 0; x < C::AB; ++x)
 #pragma unroll
@@ -278,6 +274,13 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           for (int i = 0; i < 4; ++i)
             macc[x][cb][i] = M0 ? M0[(size_t)bk * D * D + (size_t)((wave * C::AB + x) * 16 + 4 * g + i) * D + cb * 16 + lc] : 0.f;
       if (tid < D) zs[tid] = z0 ? z0[(size_t)bk * D + tid] : 0.f;
+    }
+    load_qdo(s, kvh * G);                  // the first head's rows
+    store_kv(s);
+    lds_barrier();
+    if (s > 0) {
+      state_update(true);                  // M_{s-1}
+      if (tid < D) zs[tid] -= seg_zsum();  // z_{s-1}
     }
     publish(macc, Mt);
     publish(dmacc, dMt);
