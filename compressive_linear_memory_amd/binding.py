@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.infini_attn_fwd_varlen.argtypes = [ctypes.POINTER(Problem)] + [_P] * 12 + [ctypes.c_size_t, _P]
         L.infini_attn_bwd_varlen.restype = ctypes.c_int
         L.infini_attn_bwd_varlen.argtypes = [ctypes.POINTER(Problem)] + [_P] * 18 + [ctypes.c_size_t, _P]
+        L.infini_attn_bwd_saved.restype = ctypes.c_int
+        L.infini_attn_bwd_saved.argtypes = [ctypes.POINTER(Problem)] + [_P] * 20 + [ctypes.c_size_t, _P]
         L.infini_fwd_path.restype = ctypes.c_char_p
         L.infini_fwd_path.argtypes = [ctypes.POINTER(Problem)]
         L.infini_fwd_memory.restype = ctypes.c_int
@@ -166,12 +168,14 @@ def attn_fwd(q, k, v, beta, seg_len, M0=None, z0=None, want_lse=False, out=None,
 
 
 def attn_bwd(q, k, v, beta, seg_len, dO, M0=None, z0=None, lse=None, dM_S=None, dz_S=None,
-             want_state_grads=False, ws=None, out=None, seq_lens=None):
+             want_state_grads=False, ws=None, out=None, seq_lens=None, state=None):
     """dQ, dK, dV, dbeta (and dM0, dz0 if want_state_grads); see include/infini.h.
 
     `out` may hold preallocated (dQ, dK, dV, dbeta, dM0, dz0) tensors (dM0 and
     dz0 None unless want_state_grads).  `seq_lens` (int32 [batch] on the
-    device) makes it a variable-length batch (infini_attn_bwd_varlen)."""
+    device) makes it a variable-length batch (infini_attn_bwd_varlen).
+    `state` = (M_S, z_S) returned by the forward for the same inputs calls
+    infini_attn_bwd_saved, which does not rebuild that state."""
     p = problem(q, k, seg_len)
     dev = q.device
     B, Hq, N, d = q.shape
@@ -184,6 +188,10 @@ def attn_bwd(q, k, v, beta, seg_len, dO, M0=None, z0=None, lse=None, dM_S=None, 
                              ("dz_S", dz_S, torch.float32, (B, Hkv, d)),
                              ("seq_lens", seq_lens, torch.int32, (B,))):
         _check(name, t, dt, shp, dev)
+    M_S, z_S = state if state is not None else (None, None)
+    if state is not None:
+        _check("M_S", M_S, torch.float32, (B, Hkv, d, d), dev)
+        _check("z_S", z_S, torch.float32, (B, Hkv, d), dev)
     if out is None:
         dQ = torch.empty_like(q)
         dK = torch.empty_like(k)
@@ -203,12 +211,17 @@ def attn_bwd(q, k, v, beta, seg_len, dO, M0=None, z0=None, lse=None, dM_S=None, 
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0), _ptr(lse), _ptr(dO), _ptr(dM_S),
             _ptr(dz_S), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dbeta), _ptr(dM0), _ptr(dz0), _ptr(ws), ws.numel(),
             _stream())
-    if seq_lens is None:
+    if state is not None:
+        rc = lib().infini_attn_bwd_saved(ctypes.byref(p), _ptr(seq_lens), *args[:6], _ptr(M_S), _ptr(z_S), *args[6:])
+        name = "infini_attn_bwd_saved"
+    elif seq_lens is None:
         rc = lib().infini_attn_bwd(ctypes.byref(p), *args)
+        name = "infini_attn_bwd"
     else:
         rc = lib().infini_attn_bwd_varlen(ctypes.byref(p), _ptr(seq_lens), *args)
+        name = "infini_attn_bwd_varlen"
     if rc != 0:
-        raise InfiniError(rc, "infini_attn_bwd" if seq_lens is None else "infini_attn_bwd_varlen")
+        raise InfiniError(rc, name)
     if want_state_grads:
         return dQ, dK, dV, dbeta, dM0, dz0
     return dQ, dK, dV, dbeta

@@ -527,11 +527,13 @@ infini_status_t infini_fwd_stream(const infini_problem_t* p, int n_launches, con
   return INFINI_OK;
 }
 
+// Ms_in, zs_in: the forward's final state (both NULL: rebuilt from K, V, M0, z0).
 static infini_status_t attn_bwd_impl(const infini_problem_t* p, const int32_t* lens, const void* Q,
                                      const void* K, const void* V, const float* beta, const float* M0,
-                                     const float* z0, const float* lse, const void* dO, const float* dM_S,
-                                     const float* dz_S, void* dQ, void* dK, void* dV, float* dbeta,
-                                     float* dM0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
+                                     const float* z0, const float* Ms_in, const float* zs_in, const float* lse,
+                                     const void* dO, const float* dM_S, const float* dz_S, void* dQ, void* dK,
+                                     void* dV, float* dbeta, float* dM0, float* dz0, void* ws, size_t ws_bytes,
+                                     void* stream) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return why;
   if (elu_only(p)) return INFINI_ERR_UNSUPPORTED;
@@ -544,9 +546,11 @@ static infini_status_t attn_bwd_impl(const infini_problem_t* p, const int32_t* l
   // tensors of no elements may be null (torch gives them no storage)
   if ((nq && (!Q || !dO || !dQ)) || (nkv && (!K || !V || !dK || !dV)) || !beta || !dbeta) return INFINI_ERR_NULL;
   if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
+  if ((Ms_in == nullptr) != (zs_in == nullptr)) return INFINI_ERR_NULL;
   if ((dM_S == nullptr) != (dz_S == nullptr)) return INFINI_ERR_NULL;
   if ((dM0 == nullptr) != (dz0 == nullptr)) return INFINI_ERR_NULL;
-  if (misaligned({Q, K, V, M0, z0, dO, dM_S, dz_S, dQ, dK, dV, dM0, dz0, ws})) return INFINI_ERR_UNSUPPORTED;
+  if (misaligned({Q, K, V, M0, z0, Ms_in, zs_in, dO, dM_S, dz_S, dQ, dK, dV, dM0, dz0, ws}))
+    return INFINI_ERR_UNSUPPORTED;
   const BwdWs lay = bwd_layout(g);
   if ((lay.total && !ws) || ws_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   const Span outs[] = {{dQ, nq * eb}, {dK, nkv * eb}, {dV, nkv * eb}, {dbeta, (size_t)g.Hq * 4},
@@ -554,8 +558,9 @@ static infini_status_t attn_bwd_impl(const infini_problem_t* p, const int32_t* l
   const Span ins[] = {{Q, nq * eb}, {K, nkv * eb}, {V, nkv * eb}, {beta, (size_t)g.Hq * 4},
                       {M0, M0 ? nM : 0}, {z0, z0 ? nz : 0}, {dO, nq * eb},
                       {dM_S, dM_S ? nM : 0}, {dz_S, dz_S ? nz : 0},
-                      {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0}, {lens, lens ? (size_t)g.B * 4 : 0}};
-  if (any_overlap(outs, 7, ins, 11)) return INFINI_ERR_ALIAS;
+                      {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0}, {lens, lens ? (size_t)g.B * 4 : 0},
+                      {Ms_in, Ms_in ? nM : 0}, {zs_in, zs_in ? nz : 0}};
+  if (any_overlap(outs, 7, ins, 13)) return INFINI_ERR_ALIAS;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (g.N == 0 || g.B == 0) {             // no tokens: the state's gradient passes through
@@ -575,7 +580,7 @@ static infini_status_t attn_bwd_impl(const infini_problem_t* p, const int32_t* l
   auto F = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   if (infini::bwd_short_supported(g)) {   // state and its gradient stay on chip
     TRY(infini::launch_bwd_short(g, Q, K, V, beta, M0, z0, dO, dM_S, dz_S, dQ, dK, dV, dbeta, dM0, dz0,
-                                 F(lay.dbs), lse, st));
+                                 F(lay.dbs), lse, st, Ms_in, zs_in));
     return INFINI_OK;
   }
   infini::BwdChunkWs w;
@@ -592,8 +597,16 @@ static infini_status_t attn_bwd_impl(const infini_problem_t* p, const int32_t* l
   // The chunks are walked last to first.  With more than one, the memory path
   // runs forward once to the state after the last chunk, and each chunk's
   // start state is then recovered by taking that chunk's updates away again
-  // (linear in the number of chunks; the first chunk starts from M0 itself).
-  if (nchunks > 1) TRY(infini::launch_sweep(g, K, V, M0, z0, Mst, zst, nullptr, nullptr, 0, g.S, st));
+  // (linear in the number of chunks; the first chunk starts from M0 itself)
+  // (or the forward's, when given).
+  if (nchunks > 1) {
+    if (Ms_in) {
+      TRY(infini::launch_state_copy(Mst, Ms_in, nM / 4, st));
+      TRY(infini::launch_state_copy(zst, zs_in, nz / 4, st));
+    } else {
+      TRY(infini::launch_sweep(g, K, V, M0, z0, Mst, zst, nullptr, nullptr, 0, g.S, st));
+    }
+  }
   for (int ci = nchunks - 1; ci >= 0; --ci) {
     const int s0 = ci * C;
     const int s1 = s0 + C < g.S ? s0 + C : g.S;
@@ -631,8 +644,8 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p, const void* Q, const 
                                 const float* lse, const void* dO, const float* dM_S,
                                 const float* dz_S, void* dQ, void* dK, void* dV, float* dbeta,
                                 float* dM0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
-  return attn_bwd_impl(p, nullptr, Q, K, V, beta, M0, z0, lse, dO, dM_S, dz_S, dQ, dK, dV, dbeta, dM0, dz0, ws,
-                       ws_bytes, stream);
+  return attn_bwd_impl(p, nullptr, Q, K, V, beta, M0, z0, nullptr, nullptr, lse, dO, dM_S, dz_S, dQ, dK, dV, dbeta,
+                       dM0, dz0, ws, ws_bytes, stream);
 }
 
 infini_status_t infini_attn_bwd_varlen(const infini_problem_t* p, const int32_t* seq_lens, const void* Q,
@@ -640,8 +653,18 @@ infini_status_t infini_attn_bwd_varlen(const infini_problem_t* p, const int32_t*
                                        const float* z0, const float* lse, const void* dO, const float* dM_S,
                                        const float* dz_S, void* dQ, void* dK, void* dV, float* dbeta,
                                        float* dM0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
-  return attn_bwd_impl(p, seq_lens, Q, K, V, beta, M0, z0, lse, dO, dM_S, dz_S, dQ, dK, dV, dbeta, dM0, dz0, ws,
-                       ws_bytes, stream);
+  return attn_bwd_impl(p, seq_lens, Q, K, V, beta, M0, z0, nullptr, nullptr, lse, dO, dM_S, dz_S, dQ, dK, dV, dbeta,
+                       dM0, dz0, ws, ws_bytes, stream);
+}
+
+infini_status_t infini_attn_bwd_saved(const infini_problem_t* p, const int32_t* seq_lens, const void* Q,
+                                      const void* K, const void* V, const float* beta, const float* M0,
+                                      const float* z0, const float* M_S, const float* z_S, const float* lse,
+                                      const void* dO, const float* dM_S, const float* dz_S, void* dQ, void* dK,
+                                      void* dV, float* dbeta, float* dM0, float* dz0, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  return attn_bwd_impl(p, seq_lens, Q, K, V, beta, M0, z0, M_S, z_S, lse, dO, dM_S, dz_S, dQ, dK, dV, dbeta, dM0,
+                       dz0, ws, ws_bytes, stream);
 }
 
 // ---- streaming decode

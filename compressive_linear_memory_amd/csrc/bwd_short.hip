@@ -100,7 +100,8 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                       float* __restrict__ dM0, float* __restrict__ dz0,
                       float* __restrict__ dbeta_part, const float* __restrict__ lse,
-                      const int* __restrict__ lens, int Hq, int Hkv, int N, int L, float scale, float sl2) {
+                      const int* __restrict__ lens, const float* __restrict__ Ms_in,
+                      const float* __restrict__ zs_in, int Hq, int Hkv, int N, int L, float scale, float sl2) {
   using C = BwdCfg<D>;
   constexpr int RS = C::RS, PS = C::PS;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[C::BL * RS];
@@ -140,11 +141,13 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const size_t off = (size_t)bk * D * D + (size_t)((wave * C::AB + x) * 16 + 4 * g + i) * D + cb * 16 + lc;
-        macc[x][cb][i] = M0 ? M0[off] : 0.f;
+        // the walk back starts from M_S: the forward's, when given, else
+        // M0 plus the replay below
+        macc[x][cb][i] = Ms_in ? Ms_in[off] : M0 ? M0[off] : 0.f;
         dmacc[x][cb][i] = dM_S ? dM_S[off] : 0.f;
       }
   for (int a = tid; a < D; a += 256) {
-    zs[a] = z0 ? z0[(size_t)bk * D + a] : 0.f;
+    zs[a] = zs_in ? zs_in[(size_t)bk * D + a] : z0 ? z0[(size_t)bk * D + a] : 0.f;
     dzs[a] = dz_S ? dz_S[(size_t)bk * D + a] : 0.f;
   }
   if (tid < kBwdMaxGroup * 4) dbacc[tid / 4][tid % 4] = 0.f;
@@ -220,9 +223,10 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             bbf16x4{(__bf16)acc[x][cb][0], (__bf16)acc[x][cb][1], (__bf16)acc[x][cb][2], (__bf16)acc[x][cb][3]};
   };
 
-  // ---- 1. replay the memory path to M_S, z_S
-  if (S > 0) load_kv(0);
-  for (int s = 0; s < S; ++s) {
+  // ---- 1. replay the memory path to M_S, z_S (unless the forward's was given)
+  const int Sr = Ms_in ? 0 : S;
+  if (S > 0) load_kv(Sr > 0 ? 0 : S - 1);
+  for (int s = 0; s < Sr; ++s) {
     store_kv(s);
     load_kv(min(s + 1, S - 1));            // the last one is segment S-1 again: phase 2 starts there
     lds_barrier();
@@ -640,13 +644,14 @@ hipError_t launch_bwd_short(const Geometry& g, const void* Q, const void* K, con
                             const float* beta, const float* M0, const float* z0, const void* dO,
                             const float* dM_S, const float* dz_S, void* dQ, void* dK, void* dV,
                             float* dbeta, float* dM0, float* dz0, float* dbeta_part, const float* lse,
-                            hipStream_t st) {
+                            hipStream_t st, const float* M_S_in, const float* z_S_in) {
   if (!bwd_short_supported(g)) return hipErrorInvalidValue;
   const float scale = 1.f / sqrtf((float)g.D);
   const float sl2 = 1.4426950408889634f * scale;
 #define BS_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), beta, \
                 M0, z0, static_cast<const __bf16*>(dO), dM_S, dz_S, static_cast<__bf16*>(dQ), static_cast<__bf16*>(dK), \
-                static_cast<__bf16*>(dV), dM0, dz0, dbeta_part, lse, g.lens, g.Hq, g.Hkv, g.N, g.L, scale, sl2
+                static_cast<__bf16*>(dV), dM0, dz0, dbeta_part, lse, g.lens, M_S_in, z_S_in, g.Hq, g.Hkv, g.N, g.L, \
+                scale, sl2
   if (g.D == 128) hipLaunchKernelGGL(bwd_short_kernel<128>, dim3(g.B * g.Hkv), dim3(256), 0, st, BS_ARGS);
   else hipLaunchKernelGGL(bwd_short_kernel<64>, dim3(g.B * g.Hkv), dim3(256), 0, st, BS_ARGS);
 #undef BS_ARGS

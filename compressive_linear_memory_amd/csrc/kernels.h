@@ -100,13 +100,14 @@ hipError_t launch_fwd_short(const Geometry& g, const void* Q, const void* K, con
 // Fused short-segment backward (bf16, head_dim 64 or 128, seg_len <= 64,
 // at most 16 query heads per K/V head).  dbeta_part: [B][Hq] scratch.  lse:
 // the forward's row log-sum-exp [B][Hq][N], or NULL to form the softmax
-// statistics again.
+// statistics again.  M_S_in, z_S_in: the forward's final state, or NULL to
+// rebuild it from K, V, M0, z0.
 bool bwd_short_supported(const Geometry& g);
 hipError_t launch_bwd_short(const Geometry& g, const void* Q, const void* K, const void* V,
                             const float* beta, const float* M0, const float* z0, const void* dO,
                             const float* dM_S, const float* dz_S, void* dQ, void* dK, void* dV,
                             float* dbeta, float* dM0, float* dz0, float* dbeta_part, const float* lse,
-                            hipStream_t st);
+                            hipStream_t st, const float* M_S_in = nullptr, const float* z_S_in = nullptr);
 
 // Generic forward (fp32 vector arithmetic) over segments [s_begin, s_end),
 // reading the per-segment snapshots written by launch_sweep.

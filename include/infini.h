@@ -193,6 +193,31 @@ infini_status_t infini_attn_bwd(const infini_problem_t* p,
                                 float* dM0, float* dz0,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* Backward with the state the forward returned.  Arguments as for
+ * infini_attn_bwd_varlen (seq_lens NULL = every sequence has seq_len tokens),
+ * plus
+ *   M_S, z_S   the forward's M_S, z_S for the same inputs (read only; both
+ *              non-NULL, or both NULL for exactly infini_attn_bwd_varlen).
+ * The backward walks the segments from last to first and needs the state
+ * after the last one: given here, it is not rebuilt from K, V, M0, z0 (one
+ * pass over K and V less on the fused short-segment path; a copy instead of a
+ * memory sweep on the chunked paths).  The gradients equal those of
+ * infini_attn_bwd within rounding when M_S, z_S are the forward's outputs
+ * (on the fused short-segment path they are the same state bit for bit); a
+ * state that does not belong to these inputs gives unspecified gradients (no
+ * fault).  This is the other half of the saved-state contract: a training
+ * step keeps lse (infini_fwd_saved_bytes) and the final state it returns
+ * anyway. */
+infini_status_t infini_attn_bwd_saved(const infini_problem_t* p, const int32_t* seq_lens,
+                                      const void* Q, const void* K, const void* V,
+                                      const float* beta, const float* M0, const float* z0,
+                                      const float* M_S, const float* z_S,
+                                      const float* lse, const void* dO,
+                                      const float* dM_S, const float* dz_S,
+                                      void* dQ, void* dK, void* dV, float* dbeta,
+                                      float* dM0, float* dz0,
+                                      void* ws, size_t ws_bytes, void* stream);
+
 /* Variable-length batches: the forward and backward above for a batch whose
  * sequences have different lengths (page "Hugging Face Infini-Attention 재현
  * 분석", section "Infini-Attention 메커니즘", step Segmentation, applied to

@@ -320,3 +320,23 @@ def test_taylor_feature_map_only_on_the_forward(L):
     bad = binding.Problem(1, 2, 2, 64, 32, 16, 0, 7)
     assert L.infini_fwd_path(ctypes.byref(bad)) is None
     assert L.infini_attn_fwd(ctypes.byref(bad), *a[:10], a[16], 1 << 30, None) == 3
+
+
+def test_bwd_saved_validates_before_launch(L):
+    """infini_attn_bwd_saved: M_S and z_S come as a pair (1), 16-byte aligned
+    (3), and no output may overlap them (4); the other checks are those of
+    infini_attn_bwd_varlen."""
+    p = P(B=2, N=64, d=64, L=16, dtype=1)
+    a = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(22)]   # never dereferenced
+    # Q K V beta M0 z0 | M_S z_S | lse dO dM_S dz_S dQ dK dV dbeta dM0 dz0, then ws, ws_bytes, stream
+    def call(ms, zs, rest=None, lens=None):
+        r = list(rest or a[8:18])
+        return L.infini_attn_bwd_saved(ctypes.byref(p), lens, *a[:6], ms, zs, *r, a[18], 1 << 40, None)
+    assert call(a[6], None) == 1                           # z_S without M_S
+    assert call(None, a[7]) == 1
+    assert call(ctypes.c_void_p(a[6].value + 4), a[7]) == 3
+    r = list(a[8:18]); r[4] = ctypes.c_void_p(a[6].value)  # dQ on M_S
+    assert call(a[6], a[7], r) == 4
+    r = list(a[8:18]); r[8] = a[7]                          # dM0 on z_S
+    assert call(a[6], a[7], r) == 4
+    assert L.infini_attn_bwd_saved(None, None, *a[:18], a[18], 1 << 40, None) == 1

@@ -92,9 +92,12 @@ def test_tiny_fp32_forward():
     check_fwd(Q, K, V, I.beta(w), w.seg_len, None, None, "fp32", "tiny_fp32")
 
 
-def _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, tag="", lse=None, lens=None):
+def _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, tag="", lse=None, lens=None, saved=None):
+    """Backward through the C ABI against the oracle; `saved` = the forward's
+    (M_S, z_S) on the device routes the call through infini_attn_bwd_saved.
+    Returns the gradients (device tensors)."""
     log(f"bwd {tag} Q{Q.shape} K{K.shape} L={L} {dtype} state={M0 is not None} dstate={dMS is not None} "
-        f"lse={lse is not None}")
+        f"lse={lse is not None} saved={saved is not None}")
     from gpu_util import torch_dtype
     Bn, Hq, N, d = Q.shape
     Hkv = K.shape[1]
@@ -103,7 +106,7 @@ def _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, tag="", lse=None, 
           guarded((Bn, Hkv, d, d), torch.float32), guarded((Bn, Hkv, d), torch.float32)]
     g = B().attn_bwd(dev(Q, dtype), dev(K, dtype), dev(V, dtype), dev(beta), L, dev(dO, dtype),
                      dev(M0), dev(z0), dev(lse), dev(dMS), dev(dzS), want_state_grads=True,
-                     out=tuple(x.t for x in gs), seq_lens=dev_lens(lens))
+                     out=tuple(x.t for x in gs), seq_lens=dev_lens(lens), state=saved)
     torch.cuda.synchronize()
     for name, x in zip(("dQ", "dK", "dV", "dbeta", "dM0", "dz0"), gs):
         x.check(name)
@@ -114,6 +117,7 @@ def _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, tag="", lse=None, 
     log("   " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     tol = TOL[dtype]
     assert all(v < tol for v in errs.values()), errs
+    return g
 
 
 def test_tiny_fp32_backward():
@@ -733,6 +737,50 @@ def test_train_llama3_8b_backward_from_gpu_forward_lse():
     _, _, _, lse = run_fwd(Q, K, V, beta, w.seg_len, None, None, "bf16", want_lse=True)
     _check_bwd(Q, K, V, beta, w.seg_len, None, None, I.d_out(w), None, None, "bf16", w.name + " lse",
                lse=host(lse).astype(np.float32))
+
+
+def test_train_llama3_8b_backward_from_saved_state():
+    """The training step as the benchmark runs it: the forward's lse and final
+    state fed to infini_attn_bwd_saved.  Every gradient matches the oracle, and
+    the fused short-segment backward, which would rebuild that very state,
+    gives the same gradients bit for bit."""
+    w = I.WORKLOADS["train_llama3_8b"]
+    Q, K, V = I.qkv(w)
+    beta = I.beta(w)
+    dO = I.d_out(w)
+    _, M, z, lse = run_fwd(Q, K, V, beta, w.seg_len, None, None, "bf16", want_lse=True)
+    lse_h = host(lse).astype(np.float32)
+    a = _check_bwd(Q, K, V, beta, w.seg_len, None, None, dO, None, None, "bf16", w.name + " saved state",
+                   lse=lse_h, saved=(M, z))
+    b = _check_bwd(Q, K, V, beta, w.seg_len, None, None, dO, None, None, "bf16", w.name + " lse", lse=lse_h)
+    for name, x, y in zip(("dQ", "dK", "dV", "dbeta", "dM0", "dz0"), a, b):
+        assert torch.equal(x, y), name
+
+
+SAVED_CASES = [
+    # B, Hq, Hkv, N, d, L, dtype, lens, chunk segments (None = default)
+    (2, 4, 2, 200, 64, 64, "bf16", [200, 130], None),     # fused short path, GQA, ragged, varlen
+    (1, 2, 2, 190, 128, 40, "bf16", None, None),          # fused short path, head_dim 128, ragged
+    (1, 4, 2, 520, 128, 256, "bf16", None, None),         # long-segment matrix-core path
+    (2, 4, 2, 20 * 16, 64, 16, "fp32", [320, 150], "3"),  # generic path, several workspace chunks
+]
+
+
+@pytest.mark.parametrize("case", SAVED_CASES, ids=lambda c: "x".join(map(str, c[:6])) + c[6])
+def test_backward_from_saved_state(case, monkeypatch):
+    """infini_attn_bwd_saved with the forward's final state: every gradient
+    matches the oracle, with a carried state and upstream state gradients."""
+    Bn, Hq, Hkv, N, d, L, dtype, lens, chunks = case
+    if chunks:
+        monkeypatch.setenv("INFINI_CHUNK_SEGMENTS", chunks)
+    Q, K, V, beta, M0, z0 = make(Bn, Hq, Hkv, N, d, dtype, seed=N + d, with_state=True)
+    dO = rnd(Q.shape, N + 5, 1.0, dtype)
+    g = np.random.default_rng(N + 9)
+    dMS = (g.standard_normal(M0.shape) * 1e-2).astype(np.float32)
+    dzS = (g.standard_normal(z0.shape) * 1e-2).astype(np.float32)
+    _, M, z, lse = run_fwd(Q, K, V, beta, L, M0, z0, dtype, want_lse=True, lens=lens)
+    _check_bwd(Q, K, V, beta, L, M0, z0, dO, dMS, dzS, dtype, "saved state", lens=lens,
+               lse=host(lse).astype(np.float32), saved=(M, z))
 
 
 def sampled_units(w, n_units, seed):
