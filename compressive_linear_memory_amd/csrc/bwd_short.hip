@@ -112,11 +112,10 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   __shared__ __attribute__((aligned(16))) __bf16 Xb[C::BL * RS];   // dA_dot, then dnum, rows q
   __shared__ __attribute__((aligned(16))) __bf16 Pb[C::BL * PS];   // P rows q
   __shared__ __attribute__((aligned(16))) __bf16 Sb[C::BL * PS];   // dS rows q
-  __shared__ float zs[D], dzs[D];
+  __shared__ __attribute__((aligned(16))) float zs[D];
+  __shared__ float dzs[D];
   __shared__ __attribute__((aligned(16))) float dds[C::BL];
   __shared__ float dbacc[kBwdMaxGroup][4];
-  float (*zred)[D + 1] = reinterpret_cast<float (*)[D + 1]>(Xb);   // staging only
-  static_assert(C::NKG * (D + 1) * 4 <= C::BL * RS * 2, "z partials must fit the scratch tile");
 
   const int bk = blockIdx.x;
   const int b = bk / Hkv, kvh = bk % Hkv;
@@ -134,6 +133,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 
   // ---- resident state: M and dM blocks (a = ab*16 + 4g + i, c = cb*16 + lc)
   bf32x4 macc[C::AB][C::DB], dmacc[C::AB][C::DB];
+  bf32x4 zacc[C::AB];                      // z rows a = ab*16 + 4g + i (every column lc alike)
 #pragma unroll
   for (int x = 0; x < C::AB; ++x)
 #pragma unroll
@@ -146,10 +146,14 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
         macc[x][cb][i] = Ms_in ? Ms_in[off] : M0 ? M0[off] : 0.f;
         dmacc[x][cb][i] = dM_S ? dM_S[off] : 0.f;
       }
-  for (int a = tid; a < D; a += 256) {
-    zs[a] = zs_in ? zs_in[(size_t)bk * D + a] : z0 ? z0[(size_t)bk * D + a] : 0.f;
-    dzs[a] = dz_S ? dz_S[(size_t)bk * D + a] : 0.f;
-  }
+#pragma unroll
+  for (int x = 0; x < C::AB; ++x)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t off = (size_t)bk * D + (wave * C::AB + x) * 16 + 4 * g + i;
+      zacc[x][i] = zs_in ? zs_in[off] : z0 ? z0[off] : 0.f;
+    }
+  for (int a = tid; a < D; a += 256) dzs[a] = dz_S ? dz_S[(size_t)bk * D + a] : 0.f;
   if (tid < kBwdMaxGroup * 4) dbacc[tid / 4][tid % 4] = 0.f;
 
   // ---- staging of segment s: K and V rows (V rows past the end are zero).
@@ -168,9 +172,6 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     }
   };
   auto store_kv = [&](int s) {
-    float zp[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zp[e] = 0.f;
     const int Lk = min(L, Nb - s * L);
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
@@ -178,33 +179,32 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       const bool in = key < Lk;
       *reinterpret_cast<bbf16x8*>(Ks + key * RS + dc * 8) = kst[i];
       *reinterpret_cast<bbf16x8*>(Vr + key * RS + dc * 8) = in ? vst[i] : bbf16x8{};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) zp[e] += in ? elu1((float)kst[i][e]) : 0.f;
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zred[kg][dc * 8 + e] = zp[e];
   };
-  // dz of the staged segment: sum_keys sigma(K)[key][a], for a = tid (< D)
-  auto seg_zsum = [&]() {
-    float t = 0.f;
-    for (int x = 0; x < C::NKG; ++x) t += zred[x][tid];
-    return t;
-  };
-  // M +=/-= sigma(K)^T V from the staged tiles (keys 32t + 8g + e; keys past
-  // the segment end contribute zero through V)
-  auto state_update = [&](bool subtract) {
+  // M +=/-= sigma(K)^T V and z +=/-= sigma(K)^T 1 from the staged tiles (keys
+  // 32t + 8g + e; keys past the segment end, Lk and on, contribute zero): the
+  // same bf16 products, in the same order, as the forward's update, so that
+  // the state replayed here is the forward's and subtracting recovers the
+  // earlier one step by step
+  const bbf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                        (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  auto state_update = [&](bool subtract, int Lk) {
 #pragma unroll
     for (int x = 0; x < C::AB; ++x) {
       const int ab = wave * C::AB + x;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         bbf16x8 a = sigma8(tr_op(Ks, RS, ab * 16, 32 * t + 8 * g, 32 * t + 8 * g + 4, lane));
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (32 * t + 8 * g + e >= Lk) a[e] = (__bf16)0.f;
         if (subtract) {   // flip the bf16 sign bits
           typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
           u32x4 u = __builtin_bit_cast(u32x4, a);
           u ^= 0x80008000u;
           a = __builtin_bit_cast(bbf16x8, u);
         }
+        zacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, zacc[x], 0, 0, 0);
 #pragma unroll
         for (int cb = 0; cb < C::DB; ++cb) {
           const bbf16x8 bb = tr_op(Vr, RS, cb * 16, 32 * t + 8 * g, 32 * t + 8 * g + 4, lane);
@@ -230,8 +230,7 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     store_kv(s);
     load_kv(min(s + 1, S - 1));            // the last one is segment S-1 again: phase 2 starts there
     lds_barrier();
-    state_update(false);
-    if (tid < D) zs[tid] += seg_zsum();
+    state_update(false, min(L, Nb - s * L));
     lds_barrier();
   }
 
@@ -277,17 +276,21 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             macc[x][cb][i] = M0 ? M0[(size_t)bk * D * D + (size_t)((wave * C::AB + x) * 16 + 4 * g + i) * D + cb * 16 + lc] : 0.f;
-      if (tid < D) zs[tid] = z0 ? z0[(size_t)bk * D + tid] : 0.f;
+#pragma unroll
+      for (int x = 0; x < C::AB; ++x)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          zacc[x][i] = z0 ? z0[(size_t)bk * D + (wave * C::AB + x) * 16 + 4 * g + i] : 0.f;
     }
     load_qdo(s, kvh * G);                  // the first head's rows
     store_kv(s);
     lds_barrier();
-    if (s > 0) {
-      state_update(true);                  // M_{s-1}
-      if (tid < D) zs[tid] -= seg_zsum();  // z_{s-1}
-    }
+    if (s > 0) state_update(true, Ls);     // M_{s-1}, z_{s-1}
     publish(macc, Mt);
     publish(dmacc, dMt);
+#pragma unroll
+    for (int x = 0; x < C::AB; ++x)
+      if (lc == 0) *reinterpret_cast<bf32x4*>(zs + (wave * C::AB + x) * 16 + 4 * g) = zacc[x];
     lds_barrier();
 
     // update backward (key-side: this wave's 16 keys), with dM = dL/dM_s
