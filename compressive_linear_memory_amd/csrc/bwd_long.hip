@@ -129,7 +129,7 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
   const int q0 = qt * C::BM + wave * 32;
   const int qrow = q0 + lq;
   const bool qok = qrow < Ls;
-  const int qr = qok ? qrow : Ls - 1;
+  int qr = qok ? qrow : Ls - 1;
   const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
   const size_t kvbase = (((size_t)b * Hkv + kvh) * N + (size_t)s * L) * D;
   const size_t crow = ((size_t)b * Hq + h) * ((size_t)nseg * L) + (size_t)sl * L + qrow;   // chunk row
@@ -267,112 +267,36 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
     m += __log2f(l);                          // m is now the row's log-sum-exp (base 2)
   }
 
-  // ---- retrieval: M_{s-1}^T as bf16 hi / lo tiles [c][a] (published so by the
-  // memory phase), z_{s-1}
-  __bf16* Mhi = smem;
-  __bf16* Mlo = smem + D * C::MSTR;
+  // ---- the terms that need A_dot: the gate partial's -dO.A_dot part and
+  // D_i = rowsum(dA_dot * A_dot); A_dot is not held past them.  Per element
+  // (cb, r) of the C layout: column c = cb*32 + 8(r/4) + 4hh + r%4
+  float bsum = 0.f;
+  float Dd;
   {
-    const size_t snap = ((size_t)(b * Hkv + kvh) * nseg + sl);
-    for (int e = tid; e < D * D / 8; e += C::NT) {
-      const int c = e / (D / 8), a = (e % (D / 8)) * 8;
-      *reinterpret_cast<lbf16x8*>(Mhi + c * C::MSTR + a) = *reinterpret_cast<const lbf16x8*>(MhiT + snap * D * D + c * D + a);
-      *reinterpret_cast<lbf16x8*>(Mlo + c * C::MSTR + a) = *reinterpret_cast<const lbf16x8*>(MloT + snap * D * D + c * D + a);
-    }
-    for (int e = tid; e < D; e += C::NT) zs[e] = zsnap[snap * D + e];
-  }
-  __syncthreads();
-  lbf16x8 sq[C::KS];
-  float dpart = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const __bf16 v = (__bf16)elu1((float)qreg[ks][e]);
-      sq[ks][e] = v;
-      dpart += (float)v * zs[ks * 16 + hh * 8 + e];
-    }
-  }
-  const float den = lpair_sum32(dpart) + 1e-6f;
-  const float inv_den = 1.f / den;
-  // per element (cb, r) of the C layout: column c = cb*32 + 8(r/4) + 4hh + r%4
-  float bsum = 0.f, ddot = 0.f, dmem = 0.f;
-  lbf16x8 dnb[C::DB][2];                      // dnum^T operand, slots like the probabilities
-#pragma unroll
-  for (int cb = 0; cb < C::DB; ++cb) {
-    lf32x16 nacc = {};
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const lbf16x8 a = *reinterpret_cast<const lbf16x8*>(Mhi + (cb * 32 + lq) * C::MSTR + ks * 16 + hh * 8);
-      const lbf16x8 al = *reinterpret_cast<const lbf16x8*>(Mlo + (cb * 32 + lq) * C::MSTR + ks * 16 + hh * 8);
-      nacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sq[ks], nacc, 0, 0, 0);
-      nacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, sq[ks], nacc, 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c0 = cb * 32 + 8 * u + 4 * hh;
-      const lbf16x4 dv = *reinterpret_cast<const lbf16x4*>(dO + qbase + (size_t)qr * D + c0);
-      lf32x4 dn32;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int r = 4 * u + x;
-        // rows past the segment end (a wave may have no key at all, l = 0)
-        // contribute nothing
-        const float go = qok ? (float)dv[x] : 0.f;
-        const float am = qok ? nacc[r] * inv_den : 0.f;
-        const float ad = qok ? oacc[cb][r] * inv_l : 0.f;
-        // the row sums pair with the rounded operands the products use, so that
-        // dP - D_i and dnum M^T + dden z^T cancel as they do exactly
-        const __bf16 dn = (__bf16)(gt * go * inv_den);
-        const __bf16 da = (__bf16)((1.f - gt) * go);
-        bsum += go * (am - ad);
-        ddot += (float)da * ad;
-        dmem += (float)dn * am;
-        dnb[cb][r >> 3][r & 7] = dn;
-        dn32[x] = gt * go * inv_den;
-      }
-      if (qok) *reinterpret_cast<lf32x4*>(ws_dnum + crow * D + c0) = dn32;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const float Dd = lpair_sum32(ddot);
-  const float dden = -lpair_sum32(dmem);
-  if (qok && hh == 0) {
-    ws_lse[crow] = m * 0.69314718055994531f;
-    ws_Dd[crow] = Dd;
-    ws_dden[crow] = dden;
-  }
-  // gate partial of the workgroup (fixed order)
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) bsum += __shfl_xor(bsum, o);
-  if (lane == 0) wsum[wave] = bsum;
-
-  // dQ^T (retrieval part): (M dnum^T + z dden) * sigma'(Q), M from M^T by
-  // transposing reads; rows a = ab*32 + 8(r/4) + 4hh + r%4
-  lf32x16 dq[C::DB];
-#pragma unroll
-  for (int ab = 0; ab < C::DB; ++ab) {
-    dq[ab] = lf32x16{};
+    float ddot = 0.f;
 #pragma unroll
     for (int cb = 0; cb < C::DB; ++cb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int kk = cb * 32 + 16 * t + 4 * hh;
-        const lbf16x8 a = ltr_op(Mhi, C::MSTR, ab * 32 + 16 * g16, kk, kk + 8, lane);
-        const lbf16x8 al = ltr_op(Mlo, C::MSTR, ab * 32 + 16 * g16, kk, kk + 8, lane);
-        dq[ab] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dnb[cb][t], dq[ab], 0, 0, 0);
-        dq[ab] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, dnb[cb][t], dq[ab], 0, 0, 0);
+      for (int u = 0; u < 4; ++u) {
+        const lbf16x4 dv = *reinterpret_cast<const lbf16x4*>(dO + qbase + (size_t)qr * D + cb * 32 + 8 * u + 4 * hh);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          // rows past the segment end (a wave may have no key at all, l = 0)
+          // contribute nothing
+          const float go = qok ? (float)dv[x] : 0.f;
+          const float ad = qok ? oacc[cb][4 * u + x] * inv_l : 0.f;
+          // the row sum pairs with the rounded operand the dP products use,
+          // so that dP - D_i cancels as it does exactly
+          const __bf16 da = (__bf16)((1.f - gt) * go);
+          bsum -= go * ad;
+          ddot += (float)da * ad;
+        }
       }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int a0 = ab * 32 + 8 * u + 4 * hh;
-      const lbf16x4 qv = *reinterpret_cast<const lbf16x4*>(Q + qbase + (size_t)qr * D + a0);
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-        dq[ab][4 * u + x] = (dq[ab][4 * u + x] + dden * zs[a0 + x]) * elu1_grad((float)qv[x]);
-    }
+    Dd = lpair_sum32(ddot);
   }
+  // (formed here: otherwise the compiler sinks the sum to its next use after
+  // pass 2 and holds, and spills, the 128 terms it needs through the sweep)
+  asm volatile("" : "+v"(bsum));
   // dA_dot^T operand = (1 - g) dO, rounded once (lane: column qrow)
   lbf16x8 dreg[C::KS];
   {
@@ -384,14 +308,12 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
       for (int e = 0; e < 8; ++e) dreg[ks][e] = qok ? (__bf16)((1.f - gt) * (float)d[e]) : (__bf16)0.f;
     }
   }
-  __syncthreads();                            // M^T done with; the tiles reuse the LDS
-  if (tid == 0) {
-    float t = 0.f;
-    for (int w = 0; w < C::NW; ++w) t += wsum[w];
-    dbeta_part[dbp] = t;
-  }
 
-  // ---- pass 2: dQ^T += K^T dS^T, dS = P (dP - D_i) / sqrt(d) with dP^T = V dA_dot^T
+  // ---- pass 2: dQ^T = K^T dS^T, dS = P (dP - D_i) / sqrt(d) with dP^T = V dA_dot^T
+  // (rows a = ab*32 + 8(r/4) + 4hh + r%4)
+  lf32x16 dq[C::DB];
+#pragma unroll
+  for (int ab = 0; ab < C::DB; ++ab) dq[ab] = lf32x16{};
   sweep([&](const __bf16* Ks, const __bf16* Vs, int k0) {
     lf32x16 sacc[C::NKB];
     scores(Ks, k0, sacc);
@@ -426,6 +348,115 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
       }
   });
 
+  // (the retrieval reads dO again: passing the row index through an empty asm
+  // keeps the compiler from holding the 64 unpacked values since the A_dot
+  // terms in registers, and spilling them, instead)
+  asm volatile("" : "+v"(qr));
+  // ---- retrieval: M_{s-1}^T as bf16 hi / lo tiles [c][a] (published so by the
+  // memory phase), z_{s-1}; the sweep's last barrier freed the tile buffers
+  __bf16* Mhi = smem;
+  __bf16* Mlo = smem + D * C::MSTR;
+  {
+    const size_t snap = ((size_t)(b * Hkv + kvh) * nseg + sl);
+    for (int e = tid; e < D * D / 8; e += C::NT) {
+      const int c = e / (D / 8), a = (e % (D / 8)) * 8;
+      *reinterpret_cast<lbf16x8*>(Mhi + c * C::MSTR + a) = *reinterpret_cast<const lbf16x8*>(MhiT + snap * D * D + c * D + a);
+      *reinterpret_cast<lbf16x8*>(Mlo + c * C::MSTR + a) = *reinterpret_cast<const lbf16x8*>(MloT + snap * D * D + c * D + a);
+    }
+    for (int e = tid; e < D; e += C::NT) zs[e] = zsnap[snap * D + e];
+  }
+  __syncthreads();
+  lbf16x8 sq[C::KS];
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 v = (__bf16)elu1((float)qreg[ks][e]);
+      sq[ks][e] = v;
+      dpart += (float)v * zs[ks * 16 + hh * 8 + e];
+    }
+  }
+  const float den = lpair_sum32(dpart) + 1e-6f;
+  const float inv_den = 1.f / den;
+  float dmem = 0.f;
+  lbf16x8 dnb[C::DB][2];                      // dnum^T operand, slots like the probabilities
+#pragma unroll
+  for (int cb = 0; cb < C::DB; ++cb) {
+    lf32x16 nacc = {};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const lbf16x8 a = *reinterpret_cast<const lbf16x8*>(Mhi + (cb * 32 + lq) * C::MSTR + ks * 16 + hh * 8);
+      const lbf16x8 al = *reinterpret_cast<const lbf16x8*>(Mlo + (cb * 32 + lq) * C::MSTR + ks * 16 + hh * 8);
+      nacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sq[ks], nacc, 0, 0, 0);
+      nacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, sq[ks], nacc, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c0 = cb * 32 + 8 * u + 4 * hh;
+      const lbf16x4 dv = *reinterpret_cast<const lbf16x4*>(dO + qbase + (size_t)qr * D + c0);
+      lf32x4 dn32;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 4 * u + x;
+        const float go = qok ? (float)dv[x] : 0.f;
+        const float am = qok ? nacc[r] * inv_den : 0.f;
+        // the row sum pairs with the rounded operand the products use, so that
+        // dnum M^T + dden z^T cancel as they do exactly
+        const __bf16 dn = (__bf16)(gt * go * inv_den);
+        bsum += go * am;
+        dmem += (float)dn * am;
+        dnb[cb][r >> 3][r & 7] = dn;
+        dn32[x] = gt * go * inv_den;
+      }
+      if (qok) *reinterpret_cast<lf32x4*>(ws_dnum + crow * D + c0) = dn32;
+    }
+    asm volatile("" : "+v"(bsum), "+v"(dmem));   // summed per block, not sunk to the end
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float dden = -lpair_sum32(dmem);
+  if (qok && hh == 0) {
+    ws_lse[crow] = m * 0.69314718055994531f;
+    ws_Dd[crow] = Dd;
+    ws_dden[crow] = dden;
+  }
+  // gate partial of the workgroup (fixed order)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) bsum += __shfl_xor(bsum, o);
+  if (lane == 0) wsum[wave] = bsum;
+
+  // dQ^T += (M dnum^T + z dden) * sigma'(Q), M from M^T by transposing reads
+#pragma unroll
+  for (int ab = 0; ab < C::DB; ++ab) {
+    lf32x16 ret = {};
+#pragma unroll
+    for (int cb = 0; cb < C::DB; ++cb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int kk = cb * 32 + 16 * t + 4 * hh;
+        const lbf16x8 a = ltr_op(Mhi, C::MSTR, ab * 32 + 16 * g16, kk, kk + 8, lane);
+        const lbf16x8 al = ltr_op(Mlo, C::MSTR, ab * 32 + 16 * g16, kk, kk + 8, lane);
+        ret = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dnb[cb][t], ret, 0, 0, 0);
+        ret = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, dnb[cb][t], ret, 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int a0 = ab * 32 + 8 * u + 4 * hh;
+      const lbf16x4 qv = *reinterpret_cast<const lbf16x4*>(Q + qbase + (size_t)qr * D + a0);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        dq[ab][4 * u + x] += (ret[4 * u + x] + dden * zs[a0 + x]) * elu1_grad((float)qv[x]);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < C::NW; ++w) t += wsum[w];
+    dbeta_part[dbp] = t;
+  }
+
   if (qok) {
     __bf16* qp = dQ + qbase + (size_t)qrow * D;
 #pragma unroll
@@ -454,6 +485,11 @@ struct BkCfg {
   static constexpr int CPT = BQ * D / 8 / NT;       // 16-byte chunks per thread per tile
   static constexpr int MSTR = D + 8;                // row stride of the dM tile
   static constexpr int LDS = (2 * BUF > D * MSTR) ? 2 * BUF : D * MSTR;
+  // at head_dim 128 the V^T operand is kept in LDS (lane-private, 16 bytes per
+  // k-step and lane) rather than in registers, which the K^T operand and the
+  // dK / dV accumulators fill
+  static constexpr bool VSTASH = D == 128;
+  static constexpr int VST = VSTASH ? NT * KS * 8 : 8;
 };
 
 template <int D>
@@ -469,6 +505,7 @@ void bwd_kv_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   __shared__ __attribute__((aligned(16))) __bf16 smem[C::LDS];
   __shared__ __attribute__((aligned(16))) float rowst[2][2][C::BQ];   // per buffer: lse (base 2), D_i
   __shared__ float dzs[D];
+  __shared__ __attribute__((aligned(16))) __bf16 vstash[C::VST];
 
   // key tiles with the most query rows (the first) first
   const int per_kt = (int)gridDim.x / ((L + C::BK - 1) / C::BK);   // units per key tile
@@ -499,7 +536,13 @@ void bwd_kv_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   for (int ks = 0; ks < C::KS; ++ks) {
     kreg[ks] = *reinterpret_cast<const lbf16x8*>(K + kvbase + (size_t)kr * D + ks * 16 + hh * 8);
     vreg[ks] = *reinterpret_cast<const lbf16x8*>(V + kvbase + (size_t)kr * D + ks * 16 + hh * 8);
+    if constexpr (C::VSTASH) *reinterpret_cast<lbf16x8*>(vstash + (ks * C::NT + tid) * 8) = vreg[ks];
   }
+  // V^T operand k-step ks (lane-private: the lane reads back what it wrote)
+  auto vop = [&](int ks) -> lbf16x8 {
+    if constexpr (C::VSTASH) return *reinterpret_cast<const lbf16x8*>(vstash + (ks * C::NT + tid) * 8);
+    else return vreg[ks];
+  };
   lf32x16 dka[C::DB], dva[C::DB];                   // dK^T, dV^T: rows a = ab*32 + 8(r/4) + 4hh + r%4
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) { dka[db] = lf32x16{}; dva[db] = lf32x16{}; }
@@ -574,7 +617,7 @@ void bwd_kv_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         const lbf16x8 qa = *reinterpret_cast<const lbf16x8*>(Qs + (qb * 32 + lq) * C::QSTR + ks * 16 + hh * 8);
         const lbf16x8 da = *reinterpret_cast<const lbf16x8*>(As + (qb * 32 + lq) * C::QSTR + ks * 16 + hh * 8);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[ks], pacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vop(ks), pacc, 0, 0, 0);
       }
       lbf16x8 pb[2], dsb[2];                        // k-slot x of half hh <-> row 16t + 8(x/4) + 4hh + x%4
 #pragma unroll
@@ -636,7 +679,7 @@ void bwd_kv_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       const lbf16x8 a = ltr_op(dMs, C::MSTR, cb * 32 + 16 * g16, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, lane);
       dva[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sk[ks], dva[cb], 0, 0, 0);
       const lbf16x8 am = *reinterpret_cast<const lbf16x8*>(dMs + (cb * 32 + lq) * C::MSTR + ks * 16 + hh * 8);
-      dku[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, vreg[ks], dku[cb], 0, 0, 0);
+      dku[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, vop(ks), dku[cb], 0, 0, 0);
     }
   }
   // dK = Q^T dS (scaled) + (dM V^T + dz) sigma'(K); rows a of the accumulators
