@@ -601,16 +601,34 @@ void bwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     for (int h = kvh * G; h < (kvh + 1) * G - 1; ++h) head_step(h, false);
     head_step((kvh + 1) * G - 1, s > 0);
 
-    // dK, dV of this segment's keys
+    // dK, dV of this segment's keys.  Each wave passes its 16 rows through
+    // LDS (rows of Xb and Qs, free here; every other wave is done with them,
+    // and the next writes come after the next segment's first barrier), so
+    // that the global stores are whole 16-byte row pieces, 1 KB per
+    // instruction, instead of 32-byte pieces of 16 rows
     refresh();
-    if (jk < Ls) {
-      const size_t kr = kvbase + ((size_t)s * L + jk) * D;
+    {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        *reinterpret_cast<bbf16x4*>(dK + kr + db * 16 + 4 * g) =
+        *reinterpret_cast<bbf16x4*>(Xb + jk * RS + db * 16 + 4 * g) =
             bbf16x4{(__bf16)dkacc[db][0], (__bf16)dkacc[db][1], (__bf16)dkacc[db][2], (__bf16)dkacc[db][3]};
-        *reinterpret_cast<bbf16x4*>(dV + kr + db * 16 + 4 * g) =
+        *reinterpret_cast<bbf16x4*>(Qs + jk * RS + db * 16 + 4 * g) =
             bbf16x4{(__bf16)dvacc[db][0], (__bf16)dvacc[db][1], (__bf16)dvacc[db][2], (__bf16)dvacc[db][3]};
+      }
+      // the wave reads back rows other lanes of it wrote (LDS is in order
+      // within a wave; the fences keep the compiler from reordering)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      constexpr int CPR = D / 8;                   // 16-byte pieces per row
+#pragma unroll
+      for (int i = 0; i < 16 * CPR / 64; ++i) {
+        const int c = lane + 64 * i, key = wave * 16 + c / CPR, col = (c % CPR) * 8;
+        if (key < Ls) {
+          const size_t kr = kvbase + ((size_t)s * L + key) * D + col;
+          *reinterpret_cast<bbf16x8*>(dK + kr) = *reinterpret_cast<const bbf16x8*>(Xb + key * RS + col);
+          *reinterpret_cast<bbf16x8*>(dV + kr) = *reinterpret_cast<const bbf16x8*>(Qs + key * RS + col);
+        }
       }
     }
   }
