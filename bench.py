@@ -620,9 +620,11 @@ def bench_decode(args):
 
 def bench_taylor(args):
     """Forward with the second-order Taylor feature map on the 200M-model
-    shape (B=8, H=12, d=64, seg_len 64, 16 segments, bf16): the memory path
-    carries 1 + d + d^2 = 4161 features per key, so the update and the
-    retrieval, on fp32 vector kernels, dominate."""
+    shape (B=8, H=12, d=64, seg_len 64, 16 segments, bf16).  The memory path
+    carries 1 + d + d^2 = 4161 features per key.  With no starting state the
+    matrix-core path forms the retrieval as polynomial-weighted attention over
+    the earlier segments' keys and the final state from K and V; otherwise the
+    fp32 vector kernels sweep the per-segment states."""
     import torch
     from compressive_linear_memory_amd import binding as Bi
     Bi.lib()
@@ -654,20 +656,32 @@ def bench_taylor(args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    # algorithmic work: local attention as for ELU + 1, retrieval 2 L D' d + 2 L D'
-    # per (b, query head, segment), update 2 L D' d + L D' per (b, K/V head, segment)
+    path = Bi.fwd_path(p)
     local = 2 * 2 * d * L * (L + 1) / 2
-    flop = B_ * Hq * S * (local + 2 * L * nf * d + 2 * L * nf) + B_ * Hkv * S * (2 * L * nf * d + L * nf)
+    if path == "mfma_bf16_taylor2":
+        # algorithmic work of the kernel form: per (b, query head) the local
+        # causal attention of every segment and the products with the earlier
+        # segments' keys (segment s: s L keys for each of its L queries, score
+        # and value products, 2 * 2 d per pair); per (b, K/V head) the state,
+        # 2 N D' d for M and 2 N D' for z.  All on bf16 matrix cores.
+        poly = 2 * 2 * d * L * L * S * (S - 1) / 2
+        flop = B_ * Hq * (S * local + poly) + B_ * Hkv * (2 * N * nf * d + 2 * N * nf)
+        bound, peak, kern = "mfma", PEAK_BF16_MFMA_TFLOPS, "infini_attn_fwd (Taylor map: state + polynomial attention)"
+    else:
+        # state form: local attention as for ELU + 1, retrieval 2 L D' d + 2 L D'
+        # per (b, query head, segment), update 2 L D' d + L D' per (b, K/V head, segment)
+        flop = B_ * Hq * S * (local + 2 * L * nf * d + 2 * L * nf) + B_ * Hkv * S * (2 * L * nf * d + L * nf)
+        bound, peak, kern = "alu", PEAK_FP32_VECTOR_TFLOPS, "infini_attn_fwd (Taylor map: sweep + retrieval + attention)"
     ach = flop / (ms / 1e3) / 1e12
-    roof = dict(bound="alu", peak=PEAK_FP32_VECTOR_TFLOPS, unit="TFLOP/s", achieved=round(ach, 3),
-                frac=round(ach / PEAK_FP32_VECTOR_TFLOPS, 5), traffic=None,
-                kernel="infini_attn_fwd (Taylor feature map: sweep + retrieval + attention)", flop_per_step=flop)
+    roof = dict(bound=bound, peak=peak, unit="TFLOP/s", achieved=round(ach, 3), frac=round(ach / peak, 5),
+                traffic=None, kernel=kern, flop_per_step=flop)
     print(json.dumps({"metric": f"Infini-attention fwd tokens/s, Taylor feature map ({w.name})",
                       "value": round(B_ * N / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
                       "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-                      "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+                      "scaling": "weak", "vs_baseline": None,
+                      "dtype": "bf16" if path == "mfma_bf16_taylor2" else "f32", "data": "synthetic",
                       "config": {"workload": w.name, "mode": "taylor", "feature_dim": nf, "io_dtype": w.dtype,
-                                 "kernel_path": Bi.fwd_path(p)},
+                                 "kernel_path": path},
                       "roofline": roof}), flush=True)
 
 

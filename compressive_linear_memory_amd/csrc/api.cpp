@@ -266,7 +266,8 @@ const char* infini_fwd_path(const infini_problem_t* p) {
   infini_status_t why;
   if (!valid_problem(p, &why)) return nullptr;
   const Geometry g = geometry(p);
-  if (g.fmap == INFINI_FEATURE_TAYLOR2) return "generic_fp32_taylor2";
+  if (g.fmap == INFINI_FEATURE_TAYLOR2)
+    return infini::taylor_mfma_supported(g) ? "mfma_bf16_taylor2" : "generic_fp32_taylor2";
   if (infini::fwd_short_supported(g)) return "mfma_bf16_short";
   return infini::fwd_mfma_supported(g) ? "mfma_bf16" : "generic_fp32";
 }
@@ -309,8 +310,10 @@ static infini_status_t attn_fwd_impl(const infini_problem_t* p, const int32_t* l
   if ((M0 == nullptr) != (z0 == nullptr)) return INFINI_ERR_NULL;
   if (misaligned({Q, K, V, M0, z0, O, M_S, z_S, ws})) return INFINI_ERR_UNSUPPORTED;
   const FwdWs lay = fwd_layout(g);
-  // the fused short-segment kernel keeps its state on chip and needs none
-  const size_t need = infini::fwd_short_supported(g) ? 0 : lay.total;
+  // the fused short-segment kernel keeps its state on chip and needs none;
+  // the matrix-core Taylor forward (empty starting memory) forms no states
+  const bool taylor_fast = infini::taylor_mfma_supported(g) && !M0;
+  const size_t need = infini::fwd_short_supported(g) || taylor_fast ? 0 : lay.total;
   if ((need && !ws) || ws_bytes < need) return INFINI_ERR_WORKSPACE;
   const Span outs[] = {{O, nq * eb}, {M_S, nM}, {z_S, nz}, {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0},
                        {ws, need}};
@@ -331,6 +334,10 @@ static infini_status_t attn_fwd_impl(const infini_problem_t* p, const int32_t* l
   }
   if (infini::fwd_short_supported(g)) {   // state stays on chip for the whole call
     TRY(infini::launch_fwd_short(g, Q, K, V, beta, M0, z0, O, M_S, z_S, lse, st));
+    return INFINI_OK;
+  }
+  if (taylor_fast) {
+    TRY(infini::launch_taylor_mfma(g, Q, K, V, beta, O, M_S, z_S, lse, st));
     return INFINI_OK;
   }
   char* base = static_cast<char*>(ws);

@@ -33,6 +33,15 @@ hipError_t launch_taylor_sweep(const Geometry& g, const void* K, const void* V, 
 hipError_t launch_taylor_retrieve(const Geometry& g, const void* Q, const float* Msnap, const float* zsnap,
                                   float* Amem, int s_begin, int s_end, hipStream_t st);
 
+// Matrix-core Taylor forward (bf16, head_dim 64 or 128) for a call that
+// starts from an empty memory: the retrieval as polynomial-weighted attention
+// over the earlier segments' keys (no per-segment state), the local attention
+// and gate in the same kernel, and the final M_S ([B*Hkv][D'][D]) and z_S
+// from K and V in a second one.  Needs no workspace.
+bool taylor_mfma_supported(const Geometry& g);
+hipError_t launch_taylor_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
+                              const float* beta, void* O, float* M_S, float* z_S, float* lse, hipStream_t st);
+
 // Zero rows [lens[b], N) of every (b, h) slot of X ([B][H][N][row_words]
 // 32-bit words per row): the rows past each sequence's end.
 hipError_t launch_zero_tail(void* X, const int* lens, int B, int H, int N, size_t row_words, hipStream_t st);

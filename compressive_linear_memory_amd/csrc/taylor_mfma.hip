@@ -1,0 +1,438 @@
+// Matrix-core forward for the second-order Taylor feature map (bf16, head
+// dim 64 or 128, empty starting memory).
+//
+// Page "Based" (cartesia.ai), section "고정 크기 순환 상태를 사용하는 방법도
+// 중요합니다": phi is chosen so that phi(q) . phi(k) = 1 + q.k + (q.k)^2 / 2,
+// and the key dimension grows to about d^2; section "I/O와 데이터 흐름을
+// 고려한 구현" notes that the resulting O(N d'^2 d) state makes a plain
+// implementation slow.  This file never forms the per-segment states at
+// all.  With M_0 = 0, z_0 = 0 the memory before segment s is the sum over the
+// earlier tokens j of phi(k_j)^T v_j and phi(k_j), so the retrieval of page
+// "Hugging Face Infini-Attention 재현 분석", section "Infini-Attention
+// 메커니즘" (Memory Retrieval) is, for a query q of segment s,
+//   A_mem = sum_j kappa(q.k_j) v_j / (sum_j kappa(q.k_j) + eps),
+//   kappa(t) = phi(q) . phi(k) = 1 + t + t^2 / 2,
+// over the keys j before the segment's first token: an attention over the
+// earlier segments with polynomial weights instead of exponentials, the
+// same order of work as the local attention itself.
+//
+//   taylor_attn_kernel   one workgroup of 4 waves per 64 query rows of a
+//                        (batch, query head, segment): key tiles of 64 staged
+//                        in LDS (K row-major, V^T), S^T = K Q^T and
+//                        O^T = V^T P^T on v_mfma_f32_16x16x32_bf16; the tiles
+//                        before the segment take the weights kappa(S), the
+//                        segment's own tiles the causal online softmax of
+//                        S / sqrt d; then the gate, one bf16 store.
+//   taylor_state_kernel  the state after the call, M_S = sum_j phi(k_j)^T v_j
+//                        and z_S = sum_j phi(k_j) (D' = 1 + d + d^2 rows),
+//                        which the call returns: one wave per group of d
+//                        feature rows (the linear rows k_b, or the quadratic
+//                        rows k_a k_b / sqrt 2 of one a) and 64 value
+//                        columns; the operand k_a * k_b is formed in
+//                        registers from the staged K^T, z as one more product
+//                        against a ones operand.
+//
+// 16x16x32 bf16 operand layout (gfx950): A lane l holds row l%16, k = 8(l/16)..+7;
+// B lane l holds column l%16, same k; C/D lane l holds column l%16,
+// rows 4(l/16) + i, i = 0..3.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace infini {
+
+namespace {
+
+typedef __bf16 tbf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 tbf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 tbf16x2 __attribute__((ext_vector_type(2)));
+typedef float tf32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kTRsqrt2 = 0.70710678118654752f;
+
+template <int D>
+struct TaCfg {
+  static constexpr int BQ = 64;          // query rows per workgroup (4 waves x 16)
+  static constexpr int BK = 64;          // keys per staged tile
+  static constexpr int KS = D / 32;      // k-steps of the score products
+  static constexpr int DB = D / 16;      // 16-row blocks of the value dim
+  static constexpr int KSTR = D + 8;     // staged K row stride (bf16)
+  static constexpr int TSTR = BK + 8;    // staged V^T / K^T row stride
+  static constexpr int KPT = D / 32;     // keys per thread in staging (256 threads)
+  static constexpr int NKG = BK / KPT;
+  static constexpr int KTILE = BK * KSTR;
+  static constexpr int TTILE = D * TSTR;
+};
+
+}  // namespace
+
+// Work item w (longest first: the latest segments carry the most earlier
+// keys) -> (segment, batch, query head, query tile).
+template <int D>
+__global__ __launch_bounds__(256) void taylor_attn_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const float* __restrict__ beta, __bf16* __restrict__ O, float* __restrict__ lse,
+    const int* __restrict__ lens, int B, int Hq, int Hkv, int N, int L, int S, int T, float sl2) {
+  using C = TaCfg<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C::KTILE];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][C::TTILE];
+
+  const int per_s = B * Hq * T;
+  const int s = S - 1 - (int)blockIdx.x / per_s;
+  int r = (int)blockIdx.x % per_s;
+  const int t = r % T;
+  r /= T;
+  const int h = r % Hq, b = r / Hq;
+  const int G = Hq / Hkv, kvh = h / G;
+  const int Nb = seq_len_of(lens, b, N);
+  const int seg0 = s * L;
+  if (seg0 >= Nb) return;                          // uniform: the whole workgroup leaves
+  const int Ls = min(L, Nb - seg0);
+  const int q0 = t * C::BQ;                        // first query row of the tile in the segment
+  if (q0 >= Ls) return;
+  const int qn = min(C::BQ, Ls - q0);
+  const int np = (seg0 + C::BK - 1) / C::BK;       // tiles of earlier keys
+  const int nl = (min(Ls, q0 + qn) + C::BK - 1) / C::BK;   // causal tiles of the segment
+  const int ntiles = np + nl;
+
+  int tid = threadIdx.x;
+  int lane = tid & 63;
+  const int wave = tid >> 6;
+  int lc = lane & 15, g = lane >> 4;
+  const size_t kvbase = ((size_t)b * Hkv + kvh) * N * D;
+
+  // staging: thread holds KPT keys x 8 columns of K and V
+  int kg = tid % C::NKG, dc = tid / C::NKG;
+  tbf16x8 kst[C::KPT], vst[C::KPT];
+  auto tile_key0 = [&](int j) { return j < np ? j * C::BK : seg0 + (j - np) * C::BK; };
+  auto tile_end = [&](int j) { return j < np ? seg0 : seg0 + Ls; };
+  auto load_tile = [&](int j) {
+    const int k0 = tile_key0(j), kl = tile_end(j) - 1;
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int key = min(k0 + kg * C::KPT + i, kl);
+      const size_t off = kvbase + (size_t)key * D + dc * 8;
+      kst[i] = *reinterpret_cast<const tbf16x8*>(K + off);
+      vst[i] = *reinterpret_cast<const tbf16x8*>(V + off);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i)
+      *reinterpret_cast<tbf16x8*>(Ks[buf] + (kg * C::KPT + i) * C::KSTR + dc * 8) = kst[i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16* vd = Vt[buf] + (dc * 8 + e) * C::TSTR + kg * C::KPT;
+      if constexpr (C::KPT == 2) {
+        *reinterpret_cast<tbf16x2*>(vd) = tbf16x2{vst[0][e], vst[1][e]};
+      } else {
+        *reinterpret_cast<tbf16x4*>(vd) = tbf16x4{vst[0][e], vst[1][e], vst[2][e], vst[3][e]};
+      }
+    }
+  };
+
+  int qrow = q0 + wave * 16 + lc;                  // this lane's query row in the segment
+  auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(g), "+v"(kg), "+v"(dc), "+v"(qrow)); };
+  const size_t qb = (((size_t)b * Hq + h) * N + seg0) * D;
+  tbf16x8 qreg[C::KS];
+  {
+    const int qr = min(qrow, Ls - 1);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      qreg[ks] = *reinterpret_cast<const tbf16x8*>(Q + qb + (size_t)qr * D + ks * 32 + g * 8);
+  }
+
+  tf32x4 omem[C::DB], odot[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) omem[db] = odot[db] = tf32x4{};
+  float den = 0.f, lsum = 0.f, mref = -INFINITY;   // lane partials; mref in base-2 units
+
+  load_tile(0);
+  store_tile(0);
+  lds_barrier();
+  for (int j = 0; j < ntiles; ++j) {
+    refresh();
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);          // in flight while this tile computes
+    const __bf16* Kb = Ks[buf];
+    const __bf16* Vb = Vt[buf];
+    tf32x4 sacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[kb] = tf32x4{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const tbf16x8 a = *reinterpret_cast<const tbf16x8*>(Kb + (kb * 16 + lc) * C::KSTR + ks * 32 + g * 8);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], sacc[kb], 0, 0, 0);
+      }
+    }
+    const int k0 = tile_key0(j);
+    tbf16x8 pb[2];
+    if (j < np) {
+      // earlier segments: weight kappa(q.k), keys at or past the segment start excluded
+      const int lim = seg0 - k0;                   // keys of the tile below it
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = sacc[kb][i];
+          const float w = kb * 16 + 4 * g + i < lim ? fmaf(x, fmaf(x, 0.5f, 1.f), 1.f) : 0.f;
+          const __bf16 wr = (__bf16)w;
+          den += (float)wr;
+          pb[kb >> 1][(kb & 1) * 4 + i] = wr;
+        }
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const __bf16* vp = Vb + (db * 16 + lc) * C::TSTR + 32 * tt + 4 * g;
+          const tbf16x4 lo = *reinterpret_cast<const tbf16x4*>(vp);
+          const tbf16x4 hi = *reinterpret_cast<const tbf16x4*>(vp + 16);
+          const tbf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          omem[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[tt], omem[db], 0, 0, 0);
+        }
+    } else {
+      // the segment itself: causal online softmax of S / sqrt d
+      const int lim = min(qrow, Ls - 1) - (k0 - seg0);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (kb * 16 + 4 * g + i > lim) sacc[kb][i] = -INFINITY;
+          mx = fmaxf(mx, sacc[kb][i]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mref, mx * sl2);    // finite from the segment's first tile on
+      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+      mref = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) odot[db] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const __bf16 pr = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2, -mnew));
+          lsum += (float)pr;
+          pb[kb >> 1][(kb & 1) * 4 + i] = pr;
+        }
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const __bf16* vp = Vb + (db * 16 + lc) * C::TSTR + 32 * tt + 4 * g;
+          const tbf16x4 lo = *reinterpret_cast<const tbf16x4*>(vp);
+          const tbf16x4 hi = *reinterpret_cast<const tbf16x4*>(vp + 16);
+          const tbf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          odot[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[tt], odot[db], 0, 0, 0);
+        }
+    }
+    // the other buffer was last read in step j - 1, which every wave has left
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    lds_barrier();
+  }
+
+  den += __shfl_xor(den, 16);
+  den += __shfl_xor(den, 32);
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  const float gt = sigmoid(beta[h]);
+  const float wm = gt / (den + 1e-6f), wd = (1.f - gt) / lsum;
+  if (qrow < Ls) {
+    __bf16* op = O + qb + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      tbf16x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (__bf16)(wm * omem[db][i] + wd * odot[db][i]);
+      *reinterpret_cast<tbf16x4*>(op + db * 16 + 4 * g) = w;
+    }
+    if (lse && g == 0) lse[((size_t)b * Hq + h) * N + seg0 + qrow] = (mref + __log2f(lsum)) * 0.69314718055994531f;
+  }
+}
+
+// Feature rows of the state, in the order of phi: row 0 the constant 1, rows
+// 1..D the linear features k_b, rows 1 + D + a D + b the quadratic features
+// k_a k_b / sqrt 2.  Unit u of a (batch, K/V head): feature group a = u / NCH
+// - 1 (-1: the constant and linear rows; a >= 0: quadratic row group a) and
+// value-column block u % NCH of 64 columns.  One wave per unit, 4 per
+// workgroup, over every key of the sequence in staged tiles of 64.
+template <int D>
+__global__ __launch_bounds__(256) void taylor_state_kernel(
+    const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ M_S,
+    float* __restrict__ z_S, const int* __restrict__ lens, int Hkv, int N, int wg_per_bk) {
+  using C = TaCfg<D>;
+  constexpr int NCH = D / 64;                      // 64-column value blocks
+  constexpr int CB = 4;                            // 16-column blocks per wave
+  constexpr int NU = (D + 1) * NCH;                // units per (batch, K/V head)
+  constexpr size_t DF = 1 + (size_t)D + (size_t)D * D;
+  __shared__ __attribute__((aligned(16))) __bf16 KT[2][(D + 1) * C::TSTR];   // row D: 1 for keys in range
+  __shared__ __attribute__((aligned(16))) __bf16 VT[2][C::TTILE];
+
+  const int bk = blockIdx.x / wg_per_bk;
+  const int b = bk / Hkv;
+  const int Nb = seq_len_of(lens, b, N);
+  int tid = threadIdx.x;
+  int lane = tid & 63;
+  const int wave = tid >> 6;
+  int lc = lane & 15, g = lane >> 4;
+  const int u = (blockIdx.x % wg_per_bk) * 4 + wave;
+  const bool active = u < NU;                      // uniform per wave
+  const int a = u / NCH - 1;
+  const int c0 = (u % NCH) * 64;
+  const size_t kvbase = (size_t)bk * N * D;
+
+  int kg = tid % C::NKG, dc = tid / C::NKG;
+  tbf16x8 kst[C::KPT], vst[C::KPT];
+  int kvalid = 0;
+  auto load_tile = [&](int j) {
+    const int k0 = j * C::BK;
+    kvalid = Nb - k0;
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int key = min(k0 + kg * C::KPT + i, Nb - 1);
+      const size_t off = kvbase + (size_t)key * D + dc * 8;
+      kst[i] = *reinterpret_cast<const tbf16x8*>(K + off);
+      vst[i] = *reinterpret_cast<const tbf16x8*>(V + off);
+    }
+  };
+  // keys past the sequence end carry zero K^T and V^T rows and a 0 in the
+  // ones row, so they add nothing to any sum
+  auto store_tile = [&](int buf) {
+    bool in[C::KPT];
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) in[i] = kg * C::KPT + i < kvalid;
+    const __bf16 zero = (__bf16)0.f, one = (__bf16)1.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16* vd = VT[buf] + (dc * 8 + e) * C::TSTR + kg * C::KPT;
+      __bf16* kd = KT[buf] + (dc * 8 + e) * C::TSTR + kg * C::KPT;
+      if constexpr (C::KPT == 2) {
+        *reinterpret_cast<tbf16x2*>(vd) = tbf16x2{in[0] ? vst[0][e] : zero, in[1] ? vst[1][e] : zero};
+        *reinterpret_cast<tbf16x2*>(kd) = tbf16x2{in[0] ? kst[0][e] : zero, in[1] ? kst[1][e] : zero};
+      } else {
+        *reinterpret_cast<tbf16x4*>(vd) = tbf16x4{in[0] ? vst[0][e] : zero, in[1] ? vst[1][e] : zero,
+                                                  in[2] ? vst[2][e] : zero, in[3] ? vst[3][e] : zero};
+        *reinterpret_cast<tbf16x4*>(kd) = tbf16x4{in[0] ? kst[0][e] : zero, in[1] ? kst[1][e] : zero,
+                                                  in[2] ? kst[2][e] : zero, in[3] ? kst[3][e] : zero};
+      }
+    }
+    if (dc == 0) {
+      __bf16* od = KT[buf] + D * C::TSTR + kg * C::KPT;
+      if constexpr (C::KPT == 2) {
+        *reinterpret_cast<tbf16x2*>(od) = tbf16x2{in[0] ? one : zero, in[1] ? one : zero};
+      } else {
+        *reinterpret_cast<tbf16x4*>(od) = tbf16x4{in[0] ? one : zero, in[1] ? one : zero, in[2] ? one : zero,
+                                                  in[3] ? one : zero};
+      }
+    }
+  };
+  auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(g), "+v"(kg), "+v"(dc)); };
+
+  tf32x4 macc[C::DB][CB], zacc[C::DB], cacc[CB];
+#pragma unroll
+  for (int bb = 0; bb < C::DB; ++bb) {
+    zacc[bb] = tf32x4{};
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) macc[bb][cb] = tf32x4{};
+  }
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) cacc[cb] = tf32x4{};
+  const tbf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                        (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  const int arow = a < 0 ? D : a;                  // multiplier row: the ones row for the linear group
+
+  const int ntiles = (Nb + C::BK - 1) / C::BK;
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  lds_barrier();
+  for (int j = 0; j < ntiles; ++j) {
+    refresh();
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);
+    if (active) {
+      const __bf16* KTb = KT[buf];
+      const __bf16* VTb = VT[buf];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const tbf16x8 ka = *reinterpret_cast<const tbf16x8*>(KTb + arow * C::TSTR + 32 * tt + 8 * g);
+        tbf16x8 vb[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          vb[cb] = *reinterpret_cast<const tbf16x8*>(VTb + (c0 + cb * 16 + lc) * C::TSTR + 32 * tt + 8 * g);
+        if (a < 0) {                               // constant row: the ones row against V
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            cacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, vb[cb], cacc[cb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int bb = 0; bb < C::DB; ++bb) {
+          const tbf16x8 kr = *reinterpret_cast<const tbf16x8*>(KTb + (bb * 16 + lc) * C::TSTR + 32 * tt + 8 * g);
+          tbf16x8 op;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) op[e] = (__bf16)((float)kr[e] * (float)ka[e]);   // exact product, one rounding
+          if (c0 == 0) zacc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, ones, zacc[bb], 0, 0, 0);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            macc[bb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, vb[cb], macc[bb][cb], 0, 0, 0);
+        }
+      }
+    }
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    lds_barrier();
+  }
+  if (!active) return;
+  const float sc = a < 0 ? 1.f : kTRsqrt2;
+  const size_t row0 = (size_t)bk * DF + (a < 0 ? 1 : 1 + D + (size_t)a * D);
+#pragma unroll
+  for (int bb = 0; bb < C::DB; ++bb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t row = row0 + bb * 16 + 4 * g + i;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) M_S[row * D + c0 + cb * 16 + lc] = sc * macc[bb][cb][i];
+      if (c0 == 0 && lc == 0) z_S[row] = sc * zacc[bb][i];
+    }
+  if (a < 0 && g == 0) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) M_S[(size_t)bk * DF * D + c0 + cb * 16 + lc] = cacc[cb][0];
+    if (c0 == 0 && lc == 0) z_S[(size_t)bk * DF] = (float)Nb;
+  }
+}
+
+bool taylor_mfma_supported(const Geometry& g) {
+  return g.fmap == 1 && g.dtype == 1 && (g.D == 64 || g.D == 128);
+}
+
+hipError_t launch_taylor_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
+                              const float* beta, void* O, float* M_S, float* z_S, float* lse, hipStream_t st) {
+  if (!taylor_mfma_supported(g)) return hipErrorInvalidValue;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)g.D);
+  const int T = (g.L + 63) / 64;
+  const long long items = (long long)g.S * g.B * g.Hq * T;
+  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int nch = g.D / 64;
+  const int wg_per_bk = ((g.D + 1) * nch + 3) / 4;
+  const long long sitems = (long long)g.B * g.Hkv * wg_per_bk;
+  if (sitems > 0x7fffffffLL) return hipErrorInvalidValue;
+#define TA_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), \
+                beta, static_cast<__bf16*>(O), lse, g.lens, g.B, g.Hq, g.Hkv, g.N, g.L, g.S, T, sl2
+#define TS_ARGS static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), M_S, z_S, g.lens, g.Hkv, g.N, wg_per_bk
+  if (g.D == 128) {
+    hipLaunchKernelGGL(taylor_state_kernel<128>, dim3((unsigned)sitems), dim3(256), 0, st, TS_ARGS);
+    hipLaunchKernelGGL(taylor_attn_kernel<128>, dim3((unsigned)items), dim3(256), 0, st, TA_ARGS);
+  } else {
+    hipLaunchKernelGGL(taylor_state_kernel<64>, dim3((unsigned)sitems), dim3(256), 0, st, TS_ARGS);
+    hipLaunchKernelGGL(taylor_attn_kernel<64>, dim3((unsigned)items), dim3(256), 0, st, TA_ARGS);
+  }
+#undef TA_ARGS
+#undef TS_ARGS
+  return hipGetLastError();
+}
+
+}  // namespace infini

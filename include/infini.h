@@ -99,9 +99,17 @@ typedef enum { INFINI_FP32 = 0, INFINI_BF16 = 1 } infini_dtype_t;
  *                           Q and K as given.  D' = 1 + d + d^2 features: M is
  *                           [D'][head_dim], z has D' entries, row f of M holding
  *                           feature f.  Supported by infini_attn_fwd and
- *                           infini_attn_fwd_varlen (fp32 vector kernels, any
- *                           dtype and head_dim); every other entry point returns
- *                           INFINI_ERR_UNSUPPORTED for it. */
+ *                           infini_attn_fwd_varlen, every dtype and head_dim;
+ *                           every other entry point returns
+ *                           INFINI_ERR_UNSUPPORTED for it.  bf16 with head_dim
+ *                           64 or 128 and no starting state (M0 = z0 = NULL)
+ *                           runs on the matrix cores without forming any
+ *                           per-segment state: the retrieval for a query of
+ *                           segment s is the attention over the keys before
+ *                           the segment with weights 1 + q.k + (q.k)^2 / 2,
+ *                           which equals phi(q) M_{s-1} / (phi(q) z_{s-1} +
+ *                           eps) when M_0 = 0; other calls take fp32 vector
+ *                           kernels over the D'-row states. */
 typedef enum { INFINI_FEATURE_ELU1 = 0, INFINI_FEATURE_TAYLOR2 = 1 } infini_feature_map_t;
 
 /* One call's problem.  The carried state is always float32.
@@ -156,9 +164,10 @@ size_t infini_fwd_saved_bytes(const infini_problem_t* p);
  *             NULL to skip
  *   ws        device workspace of at least infini_fwd_workspace_bytes(p); on
  *             the fused short-segment path (infini_fwd_path(p) returns
- *             "mfma_bf16_short") the call uses none and ws may be NULL with
- *             ws_bytes 0 (the size query still returns what the phased entry
- *             points below need for the same problem)
+ *             "mfma_bf16_short"), and on the matrix-core Taylor path
+ *             ("mfma_bf16_taylor2") when M0 is NULL, the call uses none and
+ *             ws may be NULL with ws_bytes 0 (the size query still returns
+ *             what the other paths need for the same problem)
  */
 infini_status_t infini_attn_fwd(const infini_problem_t* p,
                                 const void* Q, const void* K, const void* V,
@@ -386,7 +395,11 @@ infini_status_t infini_decode_noalloc(const infini_problem_t* p, int32_t pos, co
  * ("generic_fp32": fp32 vector-ALU path; "mfma_bf16": bf16 matrix-core
  * path, memory phase then attention phase; "mfma_bf16_short": bf16
  * matrix-core path for seg_len <= 64 that keeps the memory on chip in one
- * fused kernel).  NULL for an invalid problem.  Static storage. */
+ * fused kernel; with the Taylor feature map "mfma_bf16_taylor2", the
+ * matrix-core Taylor path, which a call with M0 = NULL takes while a call
+ * with a starting state takes "generic_fp32_taylor2", the fp32 vector
+ * kernels that every other Taylor problem takes).  NULL for an invalid
+ * problem.  Static storage. */
 const char* infini_fwd_path(const infini_problem_t* p);
 
 /* Static description of a status code. */

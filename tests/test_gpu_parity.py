@@ -479,6 +479,28 @@ TAYLOR_CASES = [
 ]
 
 
+def _taylor_fwd(Q, K, V, beta, L, M0, z0, dtype, lens, path):
+    Bn, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    Bi = B()
+    nf = Bi.feature_dim(d, "taylor2")
+    td = torch.float32 if dtype == "fp32" else torch.bfloat16
+    from gpu_util import guarded
+    gs = [guarded(Q.shape, td), guarded((Bn, Hkv, nf, d), torch.float32), guarded((Bn, Hkv, nf), torch.float32),
+          guarded((Bn, Hq, N), torch.float32)]
+    q = dev(Q, dtype)
+    assert Bi.fwd_path(Bi.problem(q, dev(K, dtype), L, "taylor2")) == path
+    Bi.attn_fwd(q, dev(K, dtype), dev(V, dtype), dev(beta), L, dev(M0), dev(z0), want_lse=True,
+                out=tuple(x.t for x in gs), seq_lens=dev_lens(lens), feature_map="taylor2")
+    torch.cuda.synchronize()
+    for name, x in zip(("O", "M_S", "z_S", "lse"), gs):
+        x.check(name)
+    ro, rM, rz, rl = O.forward(Q, K, V, beta, L, M0, z0, want_lse=True, lens=lens, fmap=O.Taylor2)
+    errs = [rel(host(x.t), r) for x, r in zip(gs, (ro, rM, rz, rl))]
+    log("   err O {:.2e} M {:.2e} z {:.2e} lse {:.2e}".format(*errs))
+    assert all(e < TOL[dtype] for e in errs), errs
+
+
 @pytest.mark.parametrize("case", TAYLOR_CASES, ids=lambda c: "-".join(map(str, c[:8])) + (
     "-" + "_".join(map(str, c[8])) if c[8] else ""))
 def test_taylor_feature_map_forward(case):
@@ -493,23 +515,38 @@ def test_taylor_feature_map_forward(case):
         _, _, M0, z0 = O.state_sweep(Kp, Vp, 24, fmap=O.Taylor2)
         M0, z0 = M0.astype(np.float32), z0.astype(np.float32)
     log(f"taylor fwd Q{Q.shape} L={L} {dtype} state={st} lens={lens}")
-    Bi = B()
-    nf = Bi.feature_dim(d, "taylor2")
-    td = torch.float32 if dtype == "fp32" else torch.bfloat16
-    from gpu_util import guarded
-    gs = [guarded(Q.shape, td), guarded((Bn, Hkv, nf, d), torch.float32), guarded((Bn, Hkv, nf), torch.float32),
-          guarded((Bn, Hq, N), torch.float32)]
-    q = dev(Q, dtype)
-    assert Bi.fwd_path(Bi.problem(q, dev(K, dtype), L, "taylor2")) == "generic_fp32_taylor2"
-    Bi.attn_fwd(q, dev(K, dtype), dev(V, dtype), dev(beta), L, dev(M0), dev(z0), want_lse=True,
-                out=tuple(x.t for x in gs), seq_lens=dev_lens(lens), feature_map="taylor2")
-    torch.cuda.synchronize()
-    for name, x in zip(("O", "M_S", "z_S", "lse"), gs):
-        x.check(name)
-    ro, rM, rz, rl = O.forward(Q, K, V, beta, L, M0, z0, want_lse=True, lens=lens, fmap=O.Taylor2)
-    errs = [rel(host(x.t), r) for x, r in zip(gs, (ro, rM, rz, rl))]
-    log("   err O {:.2e} M {:.2e} z {:.2e} lse {:.2e}".format(*errs))
-    assert all(e < TOL[dtype] for e in errs), errs
+    fast = dtype == "bf16" and d in (64, 128)
+    _taylor_fwd(Q, K, V, beta, L, M0, z0, dtype, lens, "mfma_bf16_taylor2" if fast else "generic_fp32_taylor2")
+
+
+# Matrix-core Taylor path (bf16, head_dim 64/128, no starting state): the
+# scale sets q.k, so that at 0.4 and above the quadratic term of
+# 1 + q.k + (q.k)^2 / 2 carries the weights (at 1/sqrt(d) it is ~1/(2 d^2)).
+TAYLOR_FAST_CASES = [
+    # B, Hq, Hkv, N, d, L, scale, lengths
+    (2, 4, 2, 256, 64, 64, 0.125, None),
+    (2, 4, 2, 300, 64, 64, 1.0, None),                      # ragged tail, peaked weights
+    (1, 4, 1, 333, 64, 100, 0.4, None),                     # segments not on 64-key tiles, 2 query tiles
+    (2, 2, 2, 260, 128, 48, 0.5, None),                     # seg_len < 64, tiles straddling segments
+    (1, 2, 2, 520, 128, 200, 1.0, None),                    # 4 query tiles, online softmax over 4 key tiles
+    (1, 2, 2, 400, 128, 200, 4.0, None),                    # very peaked scores and weights
+    (3, 4, 2, 200, 64, 64, 0.5, [200, 0, 77]),              # variable lengths, one empty
+    (1, 2, 1, 64, 64, 64, 1.0, None),                       # one segment: no earlier keys
+    (1, 2, 2, 40, 128, 64, 1.0, None),                      # one short segment
+    (2, 12, 12, 1024, 64, 64, 0.125, None),                 # the 200M-model shape at batch 2
+]
+
+
+@pytest.mark.parametrize("case", TAYLOR_FAST_CASES, ids=lambda c: "-".join(map(str, c[:7])) + (
+    "-" + "_".join(map(str, c[7])) if c[7] else ""))
+def test_taylor_matrix_core_forward(case):
+    """bf16 Taylor forward on the matrix cores (polynomial-weighted attention
+    over the earlier segments, state from K and V) against the oracle's
+    segment-by-segment state path."""
+    Bn, Hq, Hkv, N, d, L, sc, lens = case
+    Q, K, V, beta, _, _ = make(Bn, Hq, Hkv, N, d, "bf16", seed=17 * N + d, scale=sc)
+    log(f"taylor mfma fwd Q{Q.shape} L={L} scale={sc} lens={lens}")
+    _taylor_fwd(Q, K, V, beta, L, None, None, "bf16", lens, "mfma_bf16_taylor2")
 
 
 def test_taylor_multi_chunk(monkeypatch):
