@@ -254,42 +254,168 @@ __global__ __launch_bounds__(256) void taylor_attn_kernel(
   }
 }
 
-// Feature rows of the state, in the order of phi: row 0 the constant 1, rows
+// The state after the call, row order of phi: row 0 the constant 1, rows
 // 1..D the linear features k_b, rows 1 + D + a D + b the quadratic features
-// k_a k_b / sqrt 2.  Unit u of a (batch, K/V head): feature group a = u / NCH
-// - 1 (-1: the constant and linear rows; a >= 0: quadratic row group a) and
-// value-column block u % NCH of 64 columns.  One wave per unit, 4 per
-// workgroup, over every key of the sequence in staged tiles of 64.
+// k_a k_b / sqrt 2.  Quadratic rows (a, b) and (b, a) hold the same sums, so
+// only the 16-row blocks with b at or above the 16-block of a are formed
+// and the rest are written as their mirror.
+//
+// One wave per task and 64 value columns, 4 waves per workgroup, every key of
+// the sequence in staged tiles of 64 (K^T and V^T in LDS; K^T row D holds 1
+// for keys in range, 0 past the end).  Task p < D/2 of a (batch, K/V head)
+// owns the quadratic rows of a0 = p (blocks a0/16 .. DB-1) and of
+// a1 = D-1-p (blocks a1/16 .. DB-1): DB + 1 blocks of 16 rows.  Task D/2
+// owns the linear rows (DB blocks) and the constant row (one block whose
+// operand rows are all the ones row): DB + 1 blocks as well, so every wave
+// does the same work.  The operand k_a k_b of a block is formed in registers
+// from the staged K^T with v_dot2_f32_bf16 against (k_a, 0) and (0, k_a)
+// pairs (each result is one exact product, rounded once to bf16); z is one
+// more product against a ones operand.
 template <int D>
-__global__ __launch_bounds__(256) void taylor_state_kernel(
-    const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ M_S,
-    float* __restrict__ z_S, const int* __restrict__ lens, int Hkv, int N, int wg_per_bk) {
-  using C = TaCfg<D>;
-  constexpr int NCH = D / 64;                      // 64-column value blocks
-  constexpr int CB = 4;                            // 16-column blocks per wave
-  constexpr int NU = (D + 1) * NCH;                // units per (batch, K/V head)
-  constexpr size_t DF = 1 + (size_t)D + (size_t)D * D;
-  __shared__ __attribute__((aligned(16))) __bf16 KT[2][(D + 1) * C::TSTR];   // row D: 1 for keys in range
-  __shared__ __attribute__((aligned(16))) __bf16 VT[2][C::TTILE];
+struct TsCfg {
+  static constexpr int DB = D / 16;
+  static constexpr int NX = DB + 1;                // 16-row blocks per task
+  static constexpr int CB = 4;                     // 16-column blocks per task (64 columns)
+  static constexpr int NCH = D / 64;               // 64-column halves of the value dim
+  static constexpr int NTASK = (D / 2 + 1) * NCH;  // tasks per (batch, K/V head)
+  static constexpr int TSTR = 72;                  // staged K^T / V^T row stride (bf16)
+  static constexpr int KPT = D / 32;               // keys per thread in staging (256 threads)
+  static constexpr int NKG = 64 / KPT;
+};
 
-  const int bk = blockIdx.x / wg_per_bk;
-  const int b = bk / Hkv;
-  const int Nb = seq_len_of(lens, b, N);
+// One 64-key tile of a task.  P: 16-block index of a0 (0 .. DB/2 - 1), or -1
+// for the linear task.
+template <int D, int P>
+__device__ __forceinline__ void state_tile(const __bf16* __restrict__ KTb, const __bf16* __restrict__ VTb, int a0,
+                                           int a1, int c0, bool do_z, int lc, int g,
+                                           tf32x4 (&macc)[TsCfg<D>::NX][TsCfg<D>::CB],
+                                           tf32x4 (&zacc)[TsCfg<D>::NX]) {
+  using C = TsCfg<D>;
+  constexpr int NA = P < 0 ? C::DB : C::DB - P;    // blocks of a0 (or the linear blocks)
+  constexpr int B1 = C::DB - 1 - P;                // 16-block of a1
+  const tbf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                        (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+#pragma nounroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int kc = 32 * tt + 8 * g;
+    tbf16x8 vb[C::CB];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+      vb[cb] = *reinterpret_cast<const tbf16x8*>(VTb + (c0 + cb * 16 + lc) * C::TSTR + kc);
+    // (k_a, 0) and (0, k_a) pairs of the multiplier rows
+    tbf16x2 m0[8], m1[8];
+    if constexpr (P >= 0) {
+      const tbf16x8 r0 = *reinterpret_cast<const tbf16x8*>(KTb + a0 * C::TSTR + kc);
+      const tbf16x8 r1 = *reinterpret_cast<const tbf16x8*>(KTb + a1 * C::TSTR + kc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 z = (__bf16)0.f;
+        m0[2 * e] = tbf16x2{r0[2 * e], z};
+        m0[2 * e + 1] = tbf16x2{z, r0[2 * e + 1]};
+        m1[2 * e] = tbf16x2{r1[2 * e], z};
+        m1[2 * e + 1] = tbf16x2{z, r1[2 * e + 1]};
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < C::NX; ++x) {
+      int krow;
+      if constexpr (P < 0) krow = x < C::DB ? x * 16 + lc : D;
+      else krow = (x < NA ? (P + x) * 16 : (B1 + x - NA) * 16) + lc;
+      const tbf16x8 kr = *reinterpret_cast<const tbf16x8*>(KTb + krow * C::TSTR + kc);
+      tbf16x8 op;
+      if constexpr (P < 0) {
+        op = kr;                                   // times the ones row: the linear features themselves
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const tbf16x2 kp = {kr[2 * e], kr[2 * e + 1]};
+          const float lo = __builtin_amdgcn_fdot2_f32_bf16(kp, x < NA ? m0[2 * e] : m1[2 * e], 0.f, false);
+          const float hi = __builtin_amdgcn_fdot2_f32_bf16(kp, x < NA ? m0[2 * e + 1] : m1[2 * e + 1], 0.f, false);
+          op[2 * e] = (__bf16)lo;
+          op[2 * e + 1] = (__bf16)hi;
+        }
+      }
+      if (do_z) zacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, ones, zacc[x], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+        macc[x][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, vb[cb], macc[x][cb], 0, 0, 0);
+    }
+  }
+}
+
+// Writes a task's blocks (and their mirrors) into M_S / z_S of one (batch, K/V head).
+template <int D, int P>
+__device__ __forceinline__ void state_store(float* __restrict__ Mb, float* __restrict__ zb, int a0, int a1, int c0,
+                                            int Nb, int lc, int g, const tf32x4 (&macc)[TsCfg<D>::NX][TsCfg<D>::CB],
+                                            const tf32x4 (&zacc)[TsCfg<D>::NX]) {
+  using C = TsCfg<D>;
+  constexpr int NA = P < 0 ? C::DB : C::DB - P;
+  constexpr int B1 = C::DB - 1 - P;
+  const bool zl = c0 == 0 && lc == 0;
+#pragma unroll
+  for (int x = 0; x < C::NX; ++x) {
+    if constexpr (P < 0) {
+      if (x < C::DB) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 1 + x * 16 + 4 * g + i;
+#pragma unroll
+          for (int cb = 0; cb < C::CB; ++cb) Mb[(size_t)row * D + c0 + cb * 16 + lc] = macc[x][cb][i];
+          if (zl) zb[row] = zacc[x][i];
+        }
+      } else if (g == 0) {                         // constant row: every row of the block holds it
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) Mb[c0 + cb * 16 + lc] = macc[x][cb][0];
+        if (zl) zb[0] = (float)Nb;
+      }
+    } else {
+      const int a = x < NA ? a0 : a1;
+      const int bb = x < NA ? P + x : B1 + x - NA;
+      const bool mirror = x < NA ? x > 0 : x > NA;  // block above the diagonal block of a
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = bb * 16 + 4 * g + i;
+        const size_t r1 = 1 + D + (size_t)a * D + b, r2 = 1 + D + (size_t)b * D + a;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) {
+          const float v = kTRsqrt2 * macc[x][cb][i];
+          Mb[r1 * D + c0 + cb * 16 + lc] = v;
+          if (mirror) Mb[r2 * D + c0 + cb * 16 + lc] = v;
+        }
+        if (zl) {
+          const float v = kTRsqrt2 * zacc[x][i];
+          zb[r1] = v;
+          if (mirror) zb[r2] = v;
+        }
+      }
+    }
+  }
+}
+
+// The whole pass of one workgroup whose tasks all have variant P (so every
+// wave of it runs the same code and the same barriers).  task: this wave's
+// task (pair index and column half), or -1 for an idle wave.
+template <int D, int P>
+__device__ __forceinline__ void state_pass(const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                                           float* __restrict__ Mb, float* __restrict__ zb, int Nb, size_t kvbase,
+                                           int task, __bf16 (*KT)[(D + 1) * TsCfg<D>::TSTR],
+                                           __bf16 (*VT)[D * TsCfg<D>::TSTR]) {
+  using C = TsCfg<D>;
+
   int tid = threadIdx.x;
   int lane = tid & 63;
-  const int wave = tid >> 6;
   int lc = lane & 15, g = lane >> 4;
-  const int u = (blockIdx.x % wg_per_bk) * 4 + wave;
-  const bool active = u < NU;                      // uniform per wave
-  const int a = u / NCH - 1;
-  const int c0 = (u % NCH) * 64;
-  const size_t kvbase = (size_t)bk * N * D;
+  const bool active = task >= 0;                    // uniform per wave
+  const int pt = task / C::NCH;
+  const int c0 = (task % C::NCH) * 64;
+  const bool do_z = c0 == 0;
+  const int a0 = P < 0 ? 0 : pt, a1 = P < 0 ? 0 : D - 1 - pt;
 
   int kg = tid % C::NKG, dc = tid / C::NKG;
   tbf16x8 kst[C::KPT], vst[C::KPT];
   int kvalid = 0;
   auto load_tile = [&](int j) {
-    const int k0 = j * C::BK;
+    const int k0 = j * 64;
     kvalid = Nb - k0;
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
@@ -299,7 +425,7 @@ __global__ __launch_bounds__(256) void taylor_state_kernel(
       vst[i] = *reinterpret_cast<const tbf16x8*>(V + off);
     }
   };
-  // keys past the sequence end carry zero K^T and V^T rows and a 0 in the
+  // keys past the sequence end carry zero K^T and V^T columns and a 0 in the
   // ones row, so they add nothing to any sum
   auto store_tile = [&](int buf) {
     bool in[C::KPT];
@@ -332,20 +458,15 @@ __global__ __launch_bounds__(256) void taylor_state_kernel(
   };
   auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lc), "+v"(g), "+v"(kg), "+v"(dc)); };
 
-  tf32x4 macc[C::DB][CB], zacc[C::DB], cacc[CB];
+  tf32x4 macc[C::NX][C::CB], zacc[C::NX];
 #pragma unroll
-  for (int bb = 0; bb < C::DB; ++bb) {
-    zacc[bb] = tf32x4{};
+  for (int x = 0; x < C::NX; ++x) {
+    zacc[x] = tf32x4{};
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) macc[bb][cb] = tf32x4{};
+    for (int cb = 0; cb < C::CB; ++cb) macc[x][cb] = tf32x4{};
   }
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) cacc[cb] = tf32x4{};
-  const tbf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
-                        (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-  const int arow = a < 0 ? D : a;                  // multiplier row: the ones row for the linear group
 
-  const int ntiles = (Nb + C::BK - 1) / C::BK;
+  const int ntiles = (Nb + 63) / 64;
   if (ntiles > 0) {
     load_tile(0);
     store_tile(0);
@@ -354,54 +475,48 @@ __global__ __launch_bounds__(256) void taylor_state_kernel(
   for (int j = 0; j < ntiles; ++j) {
     refresh();
     const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
-    if (active) {
-      const __bf16* KTb = KT[buf];
-      const __bf16* VTb = VT[buf];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const tbf16x8 ka = *reinterpret_cast<const tbf16x8*>(KTb + arow * C::TSTR + 32 * tt + 8 * g);
-        tbf16x8 vb[CB];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          vb[cb] = *reinterpret_cast<const tbf16x8*>(VTb + (c0 + cb * 16 + lc) * C::TSTR + 32 * tt + 8 * g);
-        if (a < 0) {                               // constant row: the ones row against V
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-            cacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, vb[cb], cacc[cb], 0, 0, 0);
-        }
-#pragma unroll
-        for (int bb = 0; bb < C::DB; ++bb) {
-          const tbf16x8 kr = *reinterpret_cast<const tbf16x8*>(KTb + (bb * 16 + lc) * C::TSTR + 32 * tt + 8 * g);
-          tbf16x8 op;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) op[e] = (__bf16)((float)kr[e] * (float)ka[e]);   // exact product, one rounding
-          if (c0 == 0) zacc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, ones, zacc[bb], 0, 0, 0);
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-            macc[bb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, vb[cb], macc[bb][cb], 0, 0, 0);
-        }
-      }
+    if (active) state_tile<D, P>(KT[buf], VT[buf], a0, a1, c0, do_z, lc, g, macc, zacc);
+    // the other buffer was last read in step j - 1, which every wave has left
+    if (j + 1 < ntiles) {
+      load_tile(j + 1);
+      store_tile(buf ^ 1);
     }
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
     lds_barrier();
   }
-  if (!active) return;
-  const float sc = a < 0 ? 1.f : kTRsqrt2;
-  const size_t row0 = (size_t)bk * DF + (a < 0 ? 1 : 1 + D + (size_t)a * D);
-#pragma unroll
-  for (int bb = 0; bb < C::DB; ++bb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t row = row0 + bb * 16 + 4 * g + i;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) M_S[row * D + c0 + cb * 16 + lc] = sc * macc[bb][cb][i];
-      if (c0 == 0 && lc == 0) z_S[row] = sc * zacc[bb][i];
-    }
-  if (a < 0 && g == 0) {
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) M_S[(size_t)bk * DF * D + c0 + cb * 16 + lc] = cacc[cb][0];
-    if (c0 == 0 && lc == 0) z_S[(size_t)bk * DF] = (float)Nb;
+  if (active) state_store<D, P>(Mb, zb, a0, a1, c0, Nb, lc, g, macc, zacc);
+}
+
+// Workgroups of a (batch, K/V head): for each 16-block P of the pair index,
+// 4 * NCH workgroups of 4 pair tasks (16 pairs x NCH column halves), then one
+// workgroup for the linear task's NCH column halves.
+template <int D>
+__global__ __launch_bounds__(256) void taylor_state_kernel(
+    const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ M_S,
+    float* __restrict__ z_S, const int* __restrict__ lens, int Hkv, int N, int wg_per_bk) {
+  using C = TsCfg<D>;
+  constexpr size_t DF = 1 + (size_t)D + (size_t)D * D;
+  constexpr int WP = 4 * C::NCH;                    // workgroups per 16-block of pairs
+  __shared__ __attribute__((aligned(16))) __bf16 KT[2][(D + 1) * C::TSTR];   // row D: 1 for keys in range
+  __shared__ __attribute__((aligned(16))) __bf16 VT[2][D * C::TSTR];
+  const int bk = blockIdx.x / wg_per_bk;
+  const int wg = blockIdx.x % wg_per_bk;
+  const int Nb = seq_len_of(lens, bk / Hkv, N);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  float* Mb = M_S + (size_t)bk * DF * D;
+  float* zb = z_S + (size_t)bk * DF;
+  const size_t kvbase = (size_t)bk * N * D;
+  const int P = wg / WP;                            // D/32 for the linear workgroup
+  if (P >= D / 32) {
+    state_pass<D, -1>(K, V, Mb, zb, Nb, kvbase, wave < C::NCH ? (D / 2) * C::NCH + wave : -1, KT, VT);
+    return;
+  }
+  const int task = (P * 16) * C::NCH + (wg % WP) * 4 + wave;   // pair P*16 + l / NCH, half l % NCH
+  switch (P) {
+    case 0: state_pass<D, 0>(K, V, Mb, zb, Nb, kvbase, task, KT, VT); break;
+    case 1: state_pass<D, 1>(K, V, Mb, zb, Nb, kvbase, task, KT, VT); break;
+    case 2: if constexpr (D >= 128) state_pass<D, 2>(K, V, Mb, zb, Nb, kvbase, task, KT, VT); break;
+    case 3: if constexpr (D >= 128) state_pass<D, 3>(K, V, Mb, zb, Nb, kvbase, task, KT, VT); break;
+    default: break;
   }
 }
 
@@ -416,8 +531,7 @@ hipError_t launch_taylor_mfma(const Geometry& g, const void* Q, const void* K, c
   const int T = (g.L + 63) / 64;
   const long long items = (long long)g.S * g.B * g.Hq * T;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int nch = g.D / 64;
-  const int wg_per_bk = ((g.D + 1) * nch + 3) / 4;
+  const int wg_per_bk = g.D / 32 * 4 * (g.D / 64) + 1;   // pair workgroups + the linear one
   const long long sitems = (long long)g.B * g.Hkv * wg_per_bk;
   if (sitems > 0x7fffffffLL) return hipErrorInvalidValue;
 #define TA_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), \
