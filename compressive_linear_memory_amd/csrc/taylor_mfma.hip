@@ -60,7 +60,7 @@ struct TaCfg {
   static constexpr int KSTR = D + 8;     // staged K row stride (bf16)
   static constexpr int TSTR = BK + 8;    // staged V^T / K^T row stride
   static constexpr int KPT = D / 32;     // keys per thread in staging (256 threads)
-  static constexpr int NKG = BK / KPT;
+  static constexpr int CH = D / 8;       // 16-byte chunks per key row
   static constexpr int KTILE = BK * KSTR;
   static constexpr int TTILE = D * TSTR;
 };
@@ -102,8 +102,9 @@ __global__ __launch_bounds__(256) void taylor_attn_kernel(
   int lc = lane & 15, g = lane >> 4;
   const size_t kvbase = ((size_t)b * Hkv + kvh) * N * D;
 
-  // staging: thread holds KPT keys x 8 columns of K and V
-  int kg = tid % C::NKG, dc = tid / C::NKG;
+  // staging: thread holds 8 columns (chunk dc) of keys kg*KPT .. +KPT-1 of K
+  // and V; a wave's load covers whole key rows
+  int dc = tid % C::CH, kg = tid / C::CH;
   tbf16x8 kst[C::KPT], vst[C::KPT];
   auto tile_key0 = [&](int j) { return j < np ? j * C::BK : seg0 + (j - np) * C::BK; };
   auto tile_end = [&](int j) { return j < np ? seg0 : seg0 + Ls; };
@@ -172,16 +173,28 @@ __global__ __launch_bounds__(256) void taylor_attn_kernel(
     if (j < np) {
       // earlier segments: weight kappa(q.k), keys at or past the segment start excluded
       const int lim = seg0 - k0;                   // keys of the tile below it
+      if (lim >= C::BK) {                          // uniform: a whole tile of earlier keys
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = sacc[kb][i];
-          const float w = kb * 16 + 4 * g + i < lim ? fmaf(x, fmaf(x, 0.5f, 1.f), 1.f) : 0.f;
-          const __bf16 wr = (__bf16)w;
-          den += (float)wr;
-          pb[kb >> 1][(kb & 1) * 4 + i] = wr;
-        }
+          for (int i = 0; i < 4; ++i) {
+            const float x = sacc[kb][i];
+            const __bf16 wr = (__bf16)fmaf(x, fmaf(x, 0.5f, 1.f), 1.f);
+            den += (float)wr;
+            pb[kb >> 1][(kb & 1) * 4 + i] = wr;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = sacc[kb][i];
+            const float w = kb * 16 + 4 * g + i < lim ? fmaf(x, fmaf(x, 0.5f, 1.f), 1.f) : 0.f;
+            const __bf16 wr = (__bf16)w;
+            den += (float)wr;
+            pb[kb >> 1][(kb & 1) * 4 + i] = wr;
+          }
+      }
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -280,8 +293,15 @@ struct TsCfg {
   static constexpr int NTASK = (D / 2 + 1) * NCH;  // tasks per (batch, K/V head)
   static constexpr int TSTR = 72;                  // staged K^T / V^T row stride (bf16)
   static constexpr int KPT = D / 32;               // keys per thread in staging (256 threads)
-  static constexpr int NKG = 64 / KPT;
+  static constexpr int CH = D / 8;                 // 16-byte chunks per key row
+  static constexpr bool PREFETCH = D == 64;
 };
+
+// a.x b.x + a.y b.y in fp32 (v_dot2_f32_bf16) with a zero addend: with one
+// of b's halves zero it is one exact product.
+__device__ __forceinline__ float dot2_exact(tbf16x2 a, tbf16x2 b) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, 0.f, false);
+}
 
 // One 64-key tile of a task.  P: 16-block index of a0 (0 .. DB/2 - 1), or -1
 // for the linear task.
@@ -316,29 +336,55 @@ __device__ __forceinline__ void state_tile(const __bf16* __restrict__ KTb, const
         m1[2 * e + 1] = tbf16x2{z, r1[2 * e + 1]};
       }
     }
+    auto krow_of = [&](int x) {
+      if constexpr (P < 0) return x < C::DB ? x * 16 + lc : D;
+      else return (x < NA ? (P + x) * 16 : (B1 + x - NA) * 16) + lc;
+    };
+    if constexpr (P < 0) {
 #pragma unroll
-    for (int x = 0; x < C::NX; ++x) {
-      int krow;
-      if constexpr (P < 0) krow = x < C::DB ? x * 16 + lc : D;
-      else krow = (x < NA ? (P + x) * 16 : (B1 + x - NA) * 16) + lc;
-      const tbf16x8 kr = *reinterpret_cast<const tbf16x8*>(KTb + krow * C::TSTR + kc);
-      tbf16x8 op;
-      if constexpr (P < 0) {
-        op = kr;                                   // times the ones row: the linear features themselves
-      } else {
+      for (int x = 0; x < C::NX; ++x) {
+        // times the ones row: the linear features themselves
+        const tbf16x8 op = *reinterpret_cast<const tbf16x8*>(KTb + krow_of(x) * C::TSTR + kc);
+        if (do_z) zacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, ones, zacc[x], 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const tbf16x2 kp = {kr[2 * e], kr[2 * e + 1]};
-          const float lo = __builtin_amdgcn_fdot2_f32_bf16(kp, x < NA ? m0[2 * e] : m1[2 * e], 0.f, false);
-          const float hi = __builtin_amdgcn_fdot2_f32_bf16(kp, x < NA ? m0[2 * e + 1] : m1[2 * e + 1], 0.f, false);
-          op[2 * e] = (__bf16)lo;
-          op[2 * e + 1] = (__bf16)hi;
-        }
+        for (int cb = 0; cb < C::CB; ++cb)
+          macc[x][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, vb[cb], macc[x][cb], 0, 0, 0);
       }
-      if (do_z) zacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, ones, zacc[x], 0, 0, 0);
+    } else {
+      tbf16x8 kr[C::NX];
 #pragma unroll
-      for (int cb = 0; cb < C::CB; ++cb)
-        macc[x][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, vb[cb], macc[x][cb], 0, 0, 0);
+      for (int x = 0; x < C::NX; ++x) kr[x] = *reinterpret_cast<const tbf16x8*>(KTb + krow_of(x) * C::TSTR + kc);
+      // products k_a k_b of pair e of block x
+      auto form = [&](int x, int e) {
+        const tbf16x2 kp = {kr[x][2 * e], kr[x][2 * e + 1]};
+        const float lo = dot2_exact(kp, x < NA ? m0[2 * e] : m1[2 * e]);
+        const float hi = dot2_exact(kp, x < NA ? m0[2 * e + 1] : m1[2 * e + 1]);
+        return tbf16x2{(__bf16)lo, (__bf16)hi};
+      };
+      tbf16x8 op;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const tbf16x2 w = form(0, e);
+        op[2 * e] = w[0];
+        op[2 * e + 1] = w[1];
+      }
+      // the matrix products of block x, with block x + 1's operand formed
+      // beside them
+#pragma unroll
+      for (int x = 0; x < C::NX; ++x) {
+        tbf16x8 nop = op;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) {
+          macc[x][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, vb[cb], macc[x][cb], 0, 0, 0);
+          if (x + 1 < C::NX) {
+            const tbf16x2 w = form(x + 1, cb);
+            nop[2 * cb] = w[0];
+            nop[2 * cb + 1] = w[1];
+          }
+        }
+        if (do_z) zacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, ones, zacc[x], 0, 0, 0);
+        op = nop;
+      }
     }
   }
 }
@@ -411,7 +457,7 @@ __device__ __forceinline__ void state_pass(const __bf16* __restrict__ K, const _
   const bool do_z = c0 == 0;
   const int a0 = P < 0 ? 0 : pt, a1 = P < 0 ? 0 : D - 1 - pt;
 
-  int kg = tid % C::NKG, dc = tid / C::NKG;
+  int dc = tid % C::CH, kg = tid / C::CH;           // chunk dc of keys kg*KPT ..: whole rows per wave
   tbf16x8 kst[C::KPT], vst[C::KPT];
   int kvalid = 0;
   auto load_tile = [&](int j) {
@@ -429,8 +475,9 @@ __device__ __forceinline__ void state_pass(const __bf16* __restrict__ K, const _
   // ones row, so they add nothing to any sum
   auto store_tile = [&](int buf) {
     bool in[C::KPT];
+    const bool full = kvalid >= 64;                 // uniform: no key of the tile past the end
 #pragma unroll
-    for (int i = 0; i < C::KPT; ++i) in[i] = kg * C::KPT + i < kvalid;
+    for (int i = 0; i < C::KPT; ++i) in[i] = full || kg * C::KPT + i < kvalid;
     const __bf16 zero = (__bf16)0.f, one = (__bf16)1.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -475,10 +522,13 @@ __device__ __forceinline__ void state_pass(const __bf16* __restrict__ K, const _
   for (int j = 0; j < ntiles; ++j) {
     refresh();
     const int buf = j & 1;
+    // head_dim 64 has the registers to keep the next tile's loads in flight
+    // during this tile's products; head_dim 128 issues them afterwards
+    if (C::PREFETCH && j + 1 < ntiles) load_tile(j + 1);
     if (active) state_tile<D, P>(KT[buf], VT[buf], a0, a1, c0, do_z, lc, g, macc, zacc);
     // the other buffer was last read in step j - 1, which every wave has left
     if (j + 1 < ntiles) {
-      load_tile(j + 1);
+      if (!C::PREFETCH) load_tile(j + 1);
       store_tile(buf ^ 1);
     }
     lds_barrier();
