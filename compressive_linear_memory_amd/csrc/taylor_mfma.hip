@@ -542,14 +542,20 @@ __device__ __forceinline__ void state_pass(const __bf16* __restrict__ K, const _
 template <int D>
 __global__ __launch_bounds__(256) void taylor_state_kernel(
     const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ M_S,
-    float* __restrict__ z_S, const int* __restrict__ lens, int Hkv, int N, int wg_per_bk) {
+    float* __restrict__ z_S, const int* __restrict__ lens, int Hkv, int N, int wg_per_bk, int items,
+    int per_xcd) {
   using C = TsCfg<D>;
   constexpr size_t DF = 1 + (size_t)D + (size_t)D * D;
   constexpr int WP = 4 * C::NCH;                    // workgroups per 16-block of pairs
   __shared__ __attribute__((aligned(16))) __bf16 KT[2][(D + 1) * C::TSTR];   // row D: 1 for keys in range
   __shared__ __attribute__((aligned(16))) __bf16 VT[2][D * C::TSTR];
-  const int bk = blockIdx.x / wg_per_bk;
-  const int wg = blockIdx.x % wg_per_bk;
+  // workgroups go to the 8 XCDs in turn (blockIdx % 8); item numbers are
+  // contiguous per XCD, so the workgroups of one (batch, K/V head), which all
+  // read its K and V, share one XCD's L2
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (item >= items) return;                        // uniform
+  const int bk = item / wg_per_bk;
+  const int wg = item % wg_per_bk;
   const int Nb = seq_len_of(lens, bk / Hkv, N);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   float* Mb = M_S + (size_t)bk * DF * D;
@@ -583,15 +589,17 @@ hipError_t launch_taylor_mfma(const Geometry& g, const void* Q, const void* K, c
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   const int wg_per_bk = g.D / 32 * 4 * (g.D / 64) + 1;   // pair workgroups + the linear one
   const long long sitems = (long long)g.B * g.Hkv * wg_per_bk;
-  if (sitems > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (sitems > 0x7fffffffLL - 8) return hipErrorInvalidValue;
+  const int per_xcd = (int)((sitems + 7) / 8);
 #define TA_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), \
                 beta, static_cast<__bf16*>(O), lse, g.lens, g.B, g.Hq, g.Hkv, g.N, g.L, g.S, T, sl2
-#define TS_ARGS static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), M_S, z_S, g.lens, g.Hkv, g.N, wg_per_bk
+#define TS_ARGS static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), M_S, z_S, g.lens, g.Hkv, g.N, wg_per_bk, \
+                (int)sitems, per_xcd
   if (g.D == 128) {
-    hipLaunchKernelGGL(taylor_state_kernel<128>, dim3((unsigned)sitems), dim3(256), 0, st, TS_ARGS);
+    hipLaunchKernelGGL(taylor_state_kernel<128>, dim3(8u * per_xcd), dim3(256), 0, st, TS_ARGS);
     hipLaunchKernelGGL(taylor_attn_kernel<128>, dim3((unsigned)items), dim3(256), 0, st, TA_ARGS);
   } else {
-    hipLaunchKernelGGL(taylor_state_kernel<64>, dim3((unsigned)sitems), dim3(256), 0, st, TS_ARGS);
+    hipLaunchKernelGGL(taylor_state_kernel<64>, dim3(8u * per_xcd), dim3(256), 0, st, TS_ARGS);
     hipLaunchKernelGGL(taylor_attn_kernel<64>, dim3((unsigned)items), dim3(256), 0, st, TA_ARGS);
   }
 #undef TA_ARGS
