@@ -67,20 +67,18 @@ struct TaCfg {
 
 }  // namespace
 
-// Work item w (longest first: the latest segments carry the most earlier
-// keys) -> (segment, batch, query head, query tile).
+// Attention work item w (longest first: the latest segments carry the most
+// earlier keys) -> (segment, batch, query head, query tile).
 template <int D>
-__global__ __launch_bounds__(256) void taylor_attn_kernel(
+__device__ __forceinline__ void taylor_attn_item(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const float* __restrict__ beta, __bf16* __restrict__ O, float* __restrict__ lse,
-    const int* __restrict__ lens, int B, int Hq, int Hkv, int N, int L, int S, int T, float sl2) {
+    const int* __restrict__ lens, int B, int Hq, int Hkv, int N, int L, int S, int T, float sl2, int w,
+    __bf16 (*Ks)[TaCfg<D>::KTILE], __bf16 (*Vt)[TaCfg<D>::TTILE]) {
   using C = TaCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C::KTILE];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][C::TTILE];
-
   const int per_s = B * Hq * T;
-  const int s = S - 1 - (int)blockIdx.x / per_s;
-  int r = (int)blockIdx.x % per_s;
+  const int s = S - 1 - w / per_s;
+  int r = w % per_s;
   const int t = r % T;
   r /= T;
   const int h = r % Hq, b = r / Hq;
@@ -536,23 +534,22 @@ __device__ __forceinline__ void state_pass(const __bf16* __restrict__ K, const _
   if (active) state_store<D, P>(Mb, zb, a0, a1, c0, Nb, lc, g, macc, zacc);
 }
 
-// Workgroups of a (batch, K/V head): for each 16-block P of the pair index,
-// 4 * NCH workgroups of 4 pair tasks (16 pairs x NCH column halves), then one
-// workgroup for the linear task's NCH column halves.
+// State workgroup of launch index wid.  Workgroups of a (batch, K/V head):
+// for each 16-block P of the pair index, 4 * NCH workgroups of 4 pair tasks
+// (16 pairs x NCH column halves), then one workgroup for the linear task's
+// NCH column halves.
 template <int D>
-__global__ __launch_bounds__(256) void taylor_state_kernel(
+__device__ __forceinline__ void taylor_state_item(
     const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ M_S,
     float* __restrict__ z_S, const int* __restrict__ lens, int Hkv, int N, int wg_per_bk, int items,
-    int per_xcd) {
+    int per_xcd, int wid, __bf16 (*KT)[(D + 1) * TsCfg<D>::TSTR], __bf16 (*VT)[D * TsCfg<D>::TSTR]) {
   using C = TsCfg<D>;
   constexpr size_t DF = 1 + (size_t)D + (size_t)D * D;
   constexpr int WP = 4 * C::NCH;                    // workgroups per 16-block of pairs
-  __shared__ __attribute__((aligned(16))) __bf16 KT[2][(D + 1) * C::TSTR];   // row D: 1 for keys in range
-  __shared__ __attribute__((aligned(16))) __bf16 VT[2][D * C::TSTR];
-  // workgroups go to the 8 XCDs in turn (blockIdx % 8); item numbers are
+  // workgroups go to the 8 XCDs in turn (launch index % 8); item numbers are
   // contiguous per XCD, so the workgroups of one (batch, K/V head), which all
   // read its K and V, share one XCD's L2
-  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  const int item = (wid % 8) * per_xcd + wid / 8;
   if (item >= items) return;                        // uniform
   const int bk = item / wg_per_bk;
   const int wg = item % wg_per_bk;
@@ -576,6 +573,36 @@ __global__ __launch_bounds__(256) void taylor_state_kernel(
   }
 }
 
+// One launch for both: the state workgroups first (8 * per_xcd of them,
+// the longest), then the attention items; the two kinds run side by side.
+template <int D>
+struct TfLds {
+  static constexpr size_t ATT = 2 * (TaCfg<D>::KTILE + TaCfg<D>::TTILE) * sizeof(__bf16);
+  static constexpr size_t ST = 2 * ((D + 1) * TsCfg<D>::TSTR + D * TsCfg<D>::TSTR) * sizeof(__bf16);
+  static constexpr size_t BYTES = ATT > ST ? ATT : ST;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void taylor_fwd_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const float* __restrict__ beta, __bf16* __restrict__ O, float* __restrict__ lse, float* __restrict__ M_S,
+    float* __restrict__ z_S, const int* __restrict__ lens, int B, int Hq, int Hkv, int N, int L, int S, int T,
+    float sl2, int wg_per_bk, int sitems, int per_xcd) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[TfLds<D>::BYTES];
+  const int nst = 8 * per_xcd;
+  if ((int)blockIdx.x < nst) {
+    using C = TsCfg<D>;
+    taylor_state_item<D>(K, V, M_S, z_S, lens, Hkv, N, wg_per_bk, sitems, per_xcd, (int)blockIdx.x,
+                         reinterpret_cast<__bf16 (*)[(D + 1) * C::TSTR]>(lds),
+                         reinterpret_cast<__bf16 (*)[D * C::TSTR]>(lds + 2 * (D + 1) * C::TSTR * sizeof(__bf16)));
+  } else {
+    using C = TaCfg<D>;
+    taylor_attn_item<D>(Q, K, V, beta, O, lse, lens, B, Hq, Hkv, N, L, S, T, sl2, (int)blockIdx.x - nst,
+                        reinterpret_cast<__bf16 (*)[C::KTILE]>(lds),
+                        reinterpret_cast<__bf16 (*)[C::TTILE]>(lds + 2 * C::KTILE * sizeof(__bf16)));
+  }
+}
+
 bool taylor_mfma_supported(const Geometry& g) {
   return g.fmap == 1 && g.dtype == 1 && (g.D == 64 || g.D == 128);
 }
@@ -591,19 +618,14 @@ hipError_t launch_taylor_mfma(const Geometry& g, const void* Q, const void* K, c
   const long long sitems = (long long)g.B * g.Hkv * wg_per_bk;
   if (sitems > 0x7fffffffLL - 8) return hipErrorInvalidValue;
   const int per_xcd = (int)((sitems + 7) / 8);
-#define TA_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), \
-                beta, static_cast<__bf16*>(O), lse, g.lens, g.B, g.Hq, g.Hkv, g.N, g.L, g.S, T, sl2
-#define TS_ARGS static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), M_S, z_S, g.lens, g.Hkv, g.N, wg_per_bk, \
-                (int)sitems, per_xcd
-  if (g.D == 128) {
-    hipLaunchKernelGGL(taylor_state_kernel<128>, dim3(8u * per_xcd), dim3(256), 0, st, TS_ARGS);
-    hipLaunchKernelGGL(taylor_attn_kernel<128>, dim3((unsigned)items), dim3(256), 0, st, TA_ARGS);
-  } else {
-    hipLaunchKernelGGL(taylor_state_kernel<64>, dim3(8u * per_xcd), dim3(256), 0, st, TS_ARGS);
-    hipLaunchKernelGGL(taylor_attn_kernel<64>, dim3((unsigned)items), dim3(256), 0, st, TA_ARGS);
-  }
-#undef TA_ARGS
-#undef TS_ARGS
+  if (items + 8LL * per_xcd > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(items + 8LL * per_xcd));
+#define TF_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), \
+                beta, static_cast<__bf16*>(O), lse, M_S, z_S, g.lens, g.B, g.Hq, g.Hkv, g.N, g.L, g.S, T, sl2, \
+                wg_per_bk, (int)sitems, per_xcd
+  if (g.D == 128) hipLaunchKernelGGL(taylor_fwd_kernel<128>, grid, dim3(256), 0, st, TF_ARGS);
+  else hipLaunchKernelGGL(taylor_fwd_kernel<64>, grid, dim3(256), 0, st, TF_ARGS);
+#undef TF_ARGS
   return hipGetLastError();
 }
 
