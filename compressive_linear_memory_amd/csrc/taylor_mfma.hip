@@ -16,14 +16,15 @@
 // earlier segments with polynomial weights instead of exponentials, the
 // same order of work as the local attention itself.
 //
-//   taylor_attn_kernel   one workgroup of 4 waves per 64 query rows of a
+// One launch, taylor_fwd_kernel, with two kinds of workgroup side by side:
+//   attention items      one workgroup of 4 waves per 64 query rows of a
 //                        (batch, query head, segment): key tiles of 64 staged
 //                        in LDS (K row-major, V^T), S^T = K Q^T and
 //                        O^T = V^T P^T on v_mfma_f32_16x16x32_bf16; the tiles
 //                        before the segment take the weights kappa(S), the
 //                        segment's own tiles the causal online softmax of
 //                        S / sqrt d; then the gate, one bf16 store.
-//   taylor_state_kernel  the state after the call, M_S = sum_j phi(k_j)^T v_j
+//   state workgroups     the state after the call, M_S = sum_j phi(k_j)^T v_j
 //                        and z_S = sum_j phi(k_j) (D' = 1 + d + d^2 rows),
 //                        which the call returns: one wave per group of d
 //                        feature rows (the linear rows k_b, or the quadratic
