@@ -26,12 +26,14 @@
 //                        S / sqrt d; then the gate, one bf16 store.
 //   state workgroups     the state after the call, M_S = sum_j phi(k_j)^T v_j
 //                        and z_S = sum_j phi(k_j) (D' = 1 + d + d^2 rows),
-//                        which the call returns: one wave per group of d
-//                        feature rows (the linear rows k_b, or the quadratic
-//                        rows k_a k_b / sqrt 2 of one a) and 64 value
-//                        columns; the operand k_a * k_b is formed in
-//                        registers from the staged K^T, z as one more product
-//                        against a ones operand.
+//                        which the call returns: one wave per task and 64
+//                        value columns, a task being the quadratic rows
+//                        k_a k_b / sqrt 2 of a and of d-1-a from the 16-row
+//                        block of each upwards (the rows below are written
+//                        as their mirrors), or the constant and linear rows;
+//                        the operand k_a * k_b is formed in registers from
+//                        the staged K^T, z as one more product against a
+//                        ones operand.
 //
 // 16x16x32 bf16 operand layout (gfx950): A lane l holds row l%16, k = 8(l/16)..+7;
 // B lane l holds column l%16, same k; C/D lane l holds column l%16,
