@@ -606,8 +606,13 @@ __global__ __launch_bounds__(256) void taylor_fwd_kernel(
   }
 }
 
+// The kernel form costs 4 d per earlier key per query, so its work grows as
+// N^2; the state sweep (fp32 vector kernels) costs about 4 D' d per token on a
+// unit some ten times slower per flop.  Up to N = 16 D' tokens (66576 at
+// d = 64, 264208 at d = 128) the kernel form is the cheaper one.
 bool taylor_mfma_supported(const Geometry& g) {
-  return g.fmap == 1 && g.dtype == 1 && (g.D == 64 || g.D == 128);
+  return g.fmap == 1 && g.dtype == 1 && (g.D == 64 || g.D == 128) &&
+         (long long)g.N <= 16LL * (long long)taylor_dim(g.D);
 }
 
 hipError_t launch_taylor_mfma(const Geometry& g, const void* Q, const void* K, const void* V,

@@ -102,9 +102,10 @@ typedef enum { INFINI_FP32 = 0, INFINI_BF16 = 1 } infini_dtype_t;
  *                           infini_attn_fwd_varlen, every dtype and head_dim;
  *                           every other entry point returns
  *                           INFINI_ERR_UNSUPPORTED for it.  bf16 with head_dim
- *                           64 or 128 and no starting state (M0 = z0 = NULL)
- *                           runs on the matrix cores without forming any
- *                           per-segment state: the retrieval for a query of
+ *                           64 or 128, seq_len <= 16 D' and no starting state
+ *                           (M0 = z0 = NULL) runs on the matrix cores without
+ *                           forming any per-segment state: the retrieval for
+ *                           a query of
  *                           segment s is the attention over the keys before
  *                           the segment with weights 1 + q.k + (q.k)^2 / 2,
  *                           which equals phi(q) M_{s-1} / (phi(q) z_{s-1} +

@@ -317,6 +317,12 @@ def test_taylor_feature_map_only_on_the_forward(L):
     assert L.infini_attn_bwd(ctypes.byref(p), *a[:16], a[16], 1 << 30, None) == 3
     assert L.infini_fwd_memory(ctypes.byref(p), *a[:6], a[16], 1 << 30, None) == 3
     assert L.infini_fwd_attend(ctypes.byref(p), *a[:6], a[16], 1 << 30, None) == 3
+    # bf16, head_dim 64/128: the matrix-core kernel form up to 16 D' tokens
+    # (D' = 4161 at 64), the fp32 state sweep beyond
+    assert L.infini_fwd_path(ctypes.byref(binding.Problem(1, 2, 2, 16 * 4161, 64, 64, 1, 1))) == b"mfma_bf16_taylor2"
+    assert L.infini_fwd_path(ctypes.byref(binding.Problem(1, 2, 2, 16 * 4161 + 1, 64, 64, 1, 1))) == \
+        b"generic_fp32_taylor2"
+    assert L.infini_fwd_path(ctypes.byref(binding.Problem(1, 2, 2, 64, 32, 16, 1, 1))) == b"generic_fp32_taylor2"
     bad = binding.Problem(1, 2, 2, 64, 32, 16, 0, 7)
     assert L.infini_fwd_path(ctypes.byref(bad)) is None
     assert L.infini_attn_fwd(ctypes.byref(bad), *a[:10], a[16], 1 << 30, None) == 3
