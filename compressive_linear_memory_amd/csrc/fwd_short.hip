@@ -16,9 +16,13 @@
 //   M_{s-1}^T sigma(Q)^T, den = sigma(Q) z_{s-1} + eps and the gate, one bf16
 //   store.
 // Both roles run at once on the same staged K and V, so a step costs the
-// longer of the two, not their sum; all eight waves stage the next segment's
-// K and V, whose loads are in flight while this one computes.  Nothing but
-// (M, z) crosses segments and nothing but the final state leaves the chip.
+// longer of the two, not their sum.  The update waves, whose products are
+// the shorter part, also stage: after folding segment s in they write
+// segment s + 1's K and V^T into the other half of double-buffered tiles
+// (and its sigma(K)^T, which only they read, over segment s's) and issue the
+// loads of segment s + 2, so the attention waves never stage and one barrier
+// per segment suffices.  Nothing but (M, z) crosses segments and nothing but
+// the final state leaves the chip.
 //
 // When few (batch, K/V head) pairs are in flight the segments of a pair are
 // dealt to `parts` workgroups in consecutive ranges; part p first replays the
@@ -44,7 +48,27 @@ typedef __bf16 sbf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 sbf16x2 __attribute__((ext_vector_type(2)));
 typedef float sf32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kReplayCost = 0.45f;      // replayed segment / fully processed segment
+constexpr float kReplayCost = 0.6f;       // replayed segment / fully processed segment
+
+// max / sum over the four lanes l, l^16, l^32, l^48 of the query column, by
+// v_permlane16_swap (rows 0<->1, 2<->3) and v_permlane32_swap (the two wave
+// halves); each returns the lane's own value and its partner's.
+__device__ __forceinline__ float pair_max16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int D>
 struct ShortCfg {
@@ -54,8 +78,8 @@ struct ShortCfg {
   static constexpr int KSTR = D + 8;
   static constexpr int TSTR = BL + 8;
   static constexpr int MSTR = D + 8;
-  static constexpr int KPT = D / 64;      // keys per thread in staging (2 or 1), 512 threads
-  static constexpr int NKG = BL / KPT;
+  static constexpr int KPT = D / 32;      // keys per thread in staging (2 or 4), by the 256 update threads
+  static constexpr int CH = D / 8;        // 16-byte chunks per key row
   static constexpr int AB = DB / 4;       // M row blocks per update wave
   static constexpr int KTILE = BL * KSTR;
   static constexpr int TTILE = D * TSTR;
@@ -71,9 +95,9 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                          float* __restrict__ lse, const int* __restrict__ lens, int Hq, int Hkv, int N, int L,
                          int parts, float sl2) {
   using C = ShortCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[C::KTILE];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[C::TTILE];
-  __shared__ __attribute__((aligned(16))) __bf16 SKt[C::TTILE];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][C::KTILE];   // segment s in buffer s % 2
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][C::TTILE];
+  __shared__ __attribute__((aligned(16))) __bf16 SKt[C::TTILE];     // read by its own writers only
   __shared__ __attribute__((aligned(16))) __bf16 Mt[2][C::MTILE];
   __shared__ __attribute__((aligned(16))) float zs[2][D];
 
@@ -125,8 +149,14 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     }
   };
 
-  // ---- staging of one segment's K and V by all 512 threads
-  int kg = tid % C::NKG, dc = tid / C::NKG;
+  // ---- staging of one segment's K and V by the 256 update threads; the
+  // attention waves never stage.  Update wave uw stages the columns
+  // (chunks dc) of K and V that hold the rows of sigma(K)^T it reads itself,
+  // so sigma(K)^T needs one buffer: a wave's own LDS reads of segment s are
+  // done before its writes of segment s + 1.  Thread j of the wave holds
+  // chunk dc = KPT uw + j % KPT of keys kg KPT .. +KPT-1, kg = j / KPT.
+  const int ut = tid - 256, uj = ut & 63;
+  int dc = (ut >> 6) * C::KPT + uj % C::KPT, kg = uj / C::KPT;
   sbf16x8 kst[C::KPT], vst[C::KPT];
   int Lst = L;
   auto load_seg = [&](int s) {
@@ -139,25 +169,32 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       vst[i] = *reinterpret_cast<const sbf16x8*>(V + off);
     }
   };
-  auto store_seg = [&]() {
+  auto store_seg = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i)
-      *reinterpret_cast<sbf16x8*>(Ks + (kg * C::KPT + i) * C::KSTR + dc * 8) = kst[i];
+      *reinterpret_cast<sbf16x8*>(Ks[buf] + (kg * C::KPT + i) * C::KSTR + dc * 8) = kst[i];
+    bool in[C::KPT];
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) in[i] = kg * C::KPT + i < Lst;
+    const __bf16 zero = (__bf16)0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      __bf16* vd = Vt + (dc * 8 + e) * C::TSTR + kg * C::KPT;
+      __bf16* vd = Vt[buf] + (dc * 8 + e) * C::TSTR + kg * C::KPT;
       __bf16* kd = SKt + (dc * 8 + e) * C::TSTR + kg * C::KPT;
       // keys past the segment end carry zero V and zero sigma(K): they meet
       // zero probability and must not enter the memory update
+      __bf16 vv[C::KPT], kk[C::KPT];
+#pragma unroll
+      for (int i = 0; i < C::KPT; ++i) {
+        vv[i] = in[i] ? vst[i][e] : zero;
+        kk[i] = in[i] ? (__bf16)elu1((float)kst[i][e]) : zero;
+      }
       if constexpr (C::KPT == 2) {
-        const bool in0 = kg * 2 + 0 < Lst, in1 = kg * 2 + 1 < Lst;
-        *reinterpret_cast<sbf16x2*>(vd) = sbf16x2{in0 ? vst[0][e] : (__bf16)0.f, in1 ? vst[1][e] : (__bf16)0.f};
-        *reinterpret_cast<sbf16x2*>(kd) = sbf16x2{in0 ? (__bf16)elu1((float)kst[0][e]) : (__bf16)0.f,
-                                                  in1 ? (__bf16)elu1((float)kst[1][e]) : (__bf16)0.f};
+        *reinterpret_cast<sbf16x2*>(vd) = sbf16x2{vv[0], vv[1]};
+        *reinterpret_cast<sbf16x2*>(kd) = sbf16x2{kk[0], kk[1]};
       } else {
-        const bool in0 = kg < Lst;
-        *vd = in0 ? vst[0][e] : (__bf16)0.f;
-        *kd = in0 ? (__bf16)elu1((float)kst[0][e]) : (__bf16)0.f;
+        *reinterpret_cast<sbf16x4*>(vd) = sbf16x4{vv[0], vv[1], vv[2], vv[3]};
+        *reinterpret_cast<sbf16x4*>(kd) = sbf16x4{kk[0], kk[1], kk[2], kk[3]};
       }
     }
   };
@@ -175,18 +212,24 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const sbf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
-  if (s_end > 0) load_seg(0);
-  if (attend_wave && s_att < s_end) load_q(s_att, kvh * G, qnext);
-  if (s_end > 0) store_seg();
-  if (!attend_wave) publish(0);
+  if (attend_wave) {
+    if (s_att < s_end) load_q(s_att, kvh * G, qnext);
+  } else {
+    if (s_end > 0) {
+      load_seg(0);
+      store_seg(0);
+    }
+    if (s_end > 1) load_seg(1);            // in flight during segment 0
+    publish(0);
+  }
   lds_barrier();
 
   for (int s = 0; s < s_end; ++s) {
     refresh();
     const int Ls = min(L, Nb - s * L);
-    if (s + 1 < s_end) load_seg(s + 1);    // in flight while this segment computes
-    const __bf16* Mts = Mt[s & 1];
-    const float* zss = zs[s & 1];
+    const int cur = s & 1;
+    const __bf16* Mts = Mt[cur];
+    const float* zss = zs[cur];
     if (attend_wave) {
       for (int h = kvh * G; s >= s_att && h < (kvh + 1) * G; ++h) {
         refresh();
@@ -204,7 +247,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           sacc[kb] = sf32x4{};
 #pragma unroll
           for (int ks = 0; ks < C::KS; ++ks) {
-            const sbf16x8 a = *reinterpret_cast<const sbf16x8*>(Ks + (kb * 16 + lc) * C::KSTR + ks * 32 + g * 8);
+            const sbf16x8 a = *reinterpret_cast<const sbf16x8*>(Ks[cur] + (kb * 16 + lc) * C::KSTR + ks * 32 + g * 8);
             sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], sacc[kb], 0, 0, 0);
           }
         }
@@ -217,8 +260,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             if (kb * 16 + 4 * g + i > lim) sacc[kb][i] = -INFINITY;
             mx = fmaxf(mx, sacc[kb][i]);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = pair_max32(pair_max16(mx));
         const float mref = mx * sl2;
         sbf16x8 pb[2];
         float lsum = 0.f;
@@ -231,15 +273,14 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             lsum += (float)pr;
             pb[kb >> 1][(kb & 1) * 4 + i] = pr;
           }
-        lsum += __shfl_xor(lsum, 16);
-        lsum += __shfl_xor(lsum, 32);
+        lsum = pair_sum32(pair_sum16(lsum));
         sf32x4 oacc[C::DB];
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           oacc[db] = sf32x4{};
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const __bf16* vp = Vt + (db * 16 + lc) * C::TSTR + 32 * t + 4 * g;
+            const __bf16* vp = Vt[cur] + (db * 16 + lc) * C::TSTR + 32 * t + 4 * g;
             const sbf16x4 lo = *reinterpret_cast<const sbf16x4*>(vp);
             const sbf16x4 hi = *reinterpret_cast<const sbf16x4*>(vp + 16);
             const sbf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -256,8 +297,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             sq[ks][e] = v;
             dpart += (float)v * zss[ks * 32 + g * 8 + e];
           }
-        dpart += __shfl_xor(dpart, 16);
-        dpart += __shfl_xor(dpart, 32);
+        dpart = pair_sum32(pair_sum16(dpart));
         const float den = dpart + 1e-6f;
         const float gt = sigmoid(beta[h]);
         const float wm = gt / den, wd = (1.f - gt) / lsum;
@@ -293,16 +333,20 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
           zacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, zacc[x], 0, 0, 0);
 #pragma unroll
           for (int cb = 0; cb < C::DB; ++cb) {
-            const sbf16x8 bb = *reinterpret_cast<const sbf16x8*>(Vt + (cb * 16 + lc) * C::TSTR + 32 * t + 8 * g);
+            const sbf16x8 bb = *reinterpret_cast<const sbf16x8*>(Vt[cur] + (cb * 16 + lc) * C::TSTR + 32 * t + 8 * g);
             macc[x][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, macc[x][cb], 0, 0, 0);
           }
         }
       }
       publish((s + 1) & 1);
     }
-    lds_barrier();   // this segment's tiles and M_{s-1}^T are consumed; M_s^T is published
-    if (s + 1 < s_end) store_seg();
-    lds_barrier();
+    if (!attend_wave && s + 1 < s_end) {
+      // segment s + 1 into the other buffers (last read in step s - 1, which
+      // every wave has left), then the loads of segment s + 2
+      store_seg(cur ^ 1);
+      if (s + 2 < s_end) load_seg(s + 2);
+    }
+    lds_barrier();   // segment s's tiles and M_{s-1}^T are consumed; M_s^T and segment s + 1 are in place
   }
   if (part != parts - 1 || attend_wave) return;    // the last part's update waves hold the final state
 #pragma unroll
