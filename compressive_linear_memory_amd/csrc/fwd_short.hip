@@ -50,26 +50,6 @@ typedef float sf32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kReplayCost = 0.6f;       // replayed segment / fully processed segment
 
-// max / sum over the four lanes l, l^16, l^32, l^48 of the query column, by
-// v_permlane16_swap (rows 0<->1, 2<->3) and v_permlane32_swap (the two wave
-// halves); each returns the lane's own value and its partner's.
-__device__ __forceinline__ float pair_max16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float pair_max32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 template <int D>
 struct ShortCfg {
   static constexpr int BL = 64;
@@ -260,7 +240,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             if (kb * 16 + 4 * g + i > lim) sacc[kb][i] = -INFINITY;
             mx = fmaxf(mx, sacc[kb][i]);
           }
-        mx = pair_max32(pair_max16(mx));
+        mx = quad_max(mx);
         const float mref = mx * sl2;
         sbf16x8 pb[2];
         float lsum = 0.f;
@@ -273,7 +253,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             lsum += (float)pr;
             pb[kb >> 1][(kb & 1) * 4 + i] = pr;
           }
-        lsum = pair_sum32(pair_sum16(lsum));
+        lsum = quad_sum(lsum);
         sf32x4 oacc[C::DB];
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
@@ -297,7 +277,7 @@ void fwd_short_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
             sq[ks][e] = v;
             dpart += (float)v * zss[ks * 32 + g * 8 + e];
           }
-        dpart = pair_sum32(pair_sum16(dpart));
+        dpart = quad_sum(dpart);
         const float den = dpart + 1e-6f;
         const float gt = sigmoid(beta[h]);
         const float wm = gt / den, wd = (1.f - gt) / lsum;

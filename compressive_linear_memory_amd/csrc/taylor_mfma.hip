@@ -217,8 +217,7 @@ __device__ __forceinline__ void taylor_attn_item(
           if (kb * 16 + 4 * g + i > lim) sacc[kb][i] = -INFINITY;
           mx = fmaxf(mx, sacc[kb][i]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = quad_max(mx);
       const float mnew = fmaxf(mref, mx * sl2);    // finite from the segment's first tile on
       const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
       mref = mnew;
@@ -249,10 +248,8 @@ __device__ __forceinline__ void taylor_attn_item(
     lds_barrier();
   }
 
-  den += __shfl_xor(den, 16);
-  den += __shfl_xor(den, 32);
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  den = quad_sum(den);
+  lsum = quad_sum(lsum);
   const float gt = sigmoid(beta[h]);
   const float wm = gt / (den + 1e-6f), wd = (1.f - gt) / lsum;
   if (qrow < Ls) {
