@@ -549,6 +549,35 @@ def test_taylor_matrix_core_forward(case):
     _taylor_fwd(Q, K, V, beta, L, None, None, "bf16", lens, "mfma_bf16_taylor2")
 
 
+def _random_taylor_cases(n, seed):
+    """Seeded shapes for the matrix-core Taylor path: head dims 64/128, GQA,
+    seg_len from 1 past the sequence length, ragged tails, input scales from
+    1/sqrt(d) to 2, and variable lengths (some empty)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.integers(1, 3))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        Bn = int(rng.integers(1, 4))
+        N = int(rng.integers(1, 360))
+        L = int(rng.choice([1, 5, 33, 64, 65, 100, 128, 300, 512]))
+        sc = float(rng.choice([1.0 / np.sqrt(d), 0.5, 1.0, 2.0]))
+        lens = [int(x) for x in rng.integers(0, N + 1, Bn)] if rng.random() < 0.4 else None
+        out.append((Bn, Hq, Hkv, N, d, L, round(sc, 4), lens))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_taylor_cases(10, 2027), ids=lambda c: "-".join(map(str, c[:7])) + (
+    "-" + "_".join(map(str, c[7])) if c[7] else ""))
+def test_taylor_matrix_core_random_shapes(case):
+    """The matrix-core Taylor forward on seeded random shapes against the oracle."""
+    Bn, Hq, Hkv, N, d, L, sc, lens = case
+    Q, K, V, beta, _, _ = make(Bn, Hq, Hkv, N, d, "bf16", seed=31 * N + d, scale=sc)
+    log(f"taylor mfma random Q{Q.shape} L={L} scale={sc} lens={lens}")
+    _taylor_fwd(Q, K, V, beta, L, None, None, "bf16", lens, "mfma_bf16_taylor2")
+
+
 def test_taylor_multi_chunk(monkeypatch):
     monkeypatch.setenv("INFINI_CHUNK_SEGMENTS", "3")
     Q, K, V, beta, _, _ = make(1, 2, 2, 8 * 8, 32, "fp32", seed=77)
