@@ -83,6 +83,8 @@ FwdWs fwd_layout(const Geometry& g, int parts_of = 0) {
     w.Amem = off;  off = align_up(off + (size_t)g.B * g.Hq * C * g.L * g.D * 4);
     w.MsnapT = w.dz = off;
     w.total = off;
+    // the matrix-core path needs only the starting state's retrieval terms
+    if (infini::taylor_mfma_supported(g)) w.total = std::max(w.total, infini::taylor_mfma_m0_bytes(g));
     return w;
   }
   // The matrix-core path keeps its per-segment dM parts (one per key split)
@@ -312,8 +314,10 @@ static infini_status_t attn_fwd_impl(const infini_problem_t* p, const int32_t* l
   const FwdWs lay = fwd_layout(g);
   // the fused short-segment kernel keeps its state on chip and needs none;
   // the matrix-core Taylor forward (empty starting memory) forms no states
-  const bool taylor_fast = infini::taylor_mfma_supported(g) && !M0;
-  const size_t need = infini::fwd_short_supported(g) || taylor_fast ? 0 : lay.total;
+  const bool taylor_fast = infini::taylor_mfma_supported(g);
+  const size_t need = infini::fwd_short_supported(g) ? 0
+                      : taylor_fast                  ? (M0 ? infini::taylor_mfma_m0_bytes(g) : 0)
+                                                     : lay.total;
   if ((need && !ws) || ws_bytes < need) return INFINI_ERR_WORKSPACE;
   const Span outs[] = {{O, nq * eb}, {M_S, nM}, {z_S, nz}, {lse, lse ? (size_t)g.B * g.Hq * g.N * 4 : 0},
                        {ws, need}};
@@ -337,7 +341,7 @@ static infini_status_t attn_fwd_impl(const infini_problem_t* p, const int32_t* l
     return INFINI_OK;
   }
   if (taylor_fast) {
-    TRY(infini::launch_taylor_mfma(g, Q, K, V, beta, O, M_S, z_S, lse, st));
+    TRY(infini::launch_taylor_mfma(g, Q, K, V, beta, M0, z0, O, M_S, z_S, lse, ws, st));
     return INFINI_OK;
   }
   char* base = static_cast<char*>(ws);

@@ -33,14 +33,17 @@ hipError_t launch_taylor_sweep(const Geometry& g, const void* K, const void* V, 
 hipError_t launch_taylor_retrieve(const Geometry& g, const void* Q, const float* Msnap, const float* zsnap,
                                   float* Amem, int s_begin, int s_end, hipStream_t st);
 
-// Matrix-core Taylor forward (bf16, head_dim 64 or 128) for a call that
-// starts from an empty memory: the retrieval as polynomial-weighted attention
-// over the earlier segments' keys (no per-segment state), the local attention
-// and gate in the same kernel, and the final M_S ([B*Hkv][D'][D]) and z_S
-// from K and V in a second one.  Needs no workspace.
+// Matrix-core Taylor forward (bf16, head_dim 64 or 128): the retrieval as
+// polynomial-weighted attention over the earlier segments' keys (no
+// per-segment state) plus, with a starting state, phi(q) M0 / phi(q) z0 per
+// query; the local attention and gate; the final M_S ([B*Hkv][D'][D]) and
+// z_S from K, V (and M0, z0).  m0ws: taylor_mfma_m0_bytes(g) bytes of
+// scratch when M0 is given, else unused.
 bool taylor_mfma_supported(const Geometry& g);
+size_t taylor_mfma_m0_bytes(const Geometry& g);
 hipError_t launch_taylor_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
-                              const float* beta, void* O, float* M_S, float* z_S, float* lse, hipStream_t st);
+                              const float* beta, const float* M0, const float* z0, void* O, float* M_S, float* z_S,
+                              float* lse, void* m0ws, hipStream_t st);
 
 // Zero rows [lens[b], N) of every (b, h) slot of X ([B][H][N][row_words]
 // 32-bit words per row): the rows past each sequence's end.

@@ -76,8 +76,9 @@ template <int D>
 __device__ __forceinline__ void taylor_attn_item(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const float* __restrict__ beta, __bf16* __restrict__ O, float* __restrict__ lse,
-    const int* __restrict__ lens, int B, int Hq, int Hkv, int N, int L, int S, int T, float sl2, int w,
-    __bf16 (*Ks)[TaCfg<D>::KTILE], __bf16 (*Vt)[TaCfg<D>::TTILE]) {
+    const int* __restrict__ lens, const float* __restrict__ num0, const float* __restrict__ den0, int B, int Hq,
+    int Hkv, int N, int L, int S, int T, float sl2, int w, __bf16 (*Ks)[TaCfg<D>::KTILE],
+    __bf16 (*Vt)[TaCfg<D>::TTILE]) {
   using C = TaCfg<D>;
   const int per_s = B * Hq * T;
   const int s = S - 1 - w / per_s;
@@ -250,6 +251,15 @@ __device__ __forceinline__ void taylor_attn_item(
 
   den = quad_sum(den);
   lsum = quad_sum(lsum);
+  if (num0 && qrow < Ls) {                         // the starting state's part of the retrieval
+    const size_t r = ((size_t)b * Hq + h) * N + seg0 + qrow;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const float4 n4 = *reinterpret_cast<const float4*>(num0 + r * D + db * 16 + 4 * g);
+      omem[db] += tf32x4{n4.x, n4.y, n4.z, n4.w};
+    }
+    den += den0[r];
+  }
   const float gt = sigmoid(beta[h]);
   const float wm = gt / (den + 1e-6f), wd = (1.f - gt) / lsum;
   if (qrow < Ls) {
@@ -389,10 +399,16 @@ __device__ __forceinline__ void state_tile(const __bf16* __restrict__ KTb, const
 
 // Writes a task's blocks (and their mirrors) into M_S / z_S of one (batch, K/V head).
 template <int D, int P>
-__device__ __forceinline__ void state_store(float* __restrict__ Mb, float* __restrict__ zb, int a0, int a1, int c0,
-                                            int Nb, int lc, int g, const tf32x4 (&macc)[TsCfg<D>::NX][TsCfg<D>::CB],
+// M0b / z0b: the starting state of the same (batch, K/V head), added to
+// every entry, or NULL.
+__device__ __forceinline__ void state_store(float* __restrict__ Mb, float* __restrict__ zb,
+                                            const float* __restrict__ M0b, const float* __restrict__ z0b, int a0,
+                                            int a1, int c0, int Nb, int lc, int g,
+                                            const tf32x4 (&macc)[TsCfg<D>::NX][TsCfg<D>::CB],
                                             const tf32x4 (&zacc)[TsCfg<D>::NX]) {
   using C = TsCfg<D>;
+  auto m0 = [&](size_t i) { return M0b ? M0b[i] : 0.f; };
+  auto z0 = [&](size_t i) { return z0b ? z0b[i] : 0.f; };
   constexpr int NA = P < 0 ? C::DB : C::DB - P;
   constexpr int B1 = C::DB - 1 - P;
   const bool zl = c0 == 0 && lc == 0;
@@ -404,13 +420,16 @@ __device__ __forceinline__ void state_store(float* __restrict__ Mb, float* __res
         for (int i = 0; i < 4; ++i) {
           const int row = 1 + x * 16 + 4 * g + i;
 #pragma unroll
-          for (int cb = 0; cb < C::CB; ++cb) Mb[(size_t)row * D + c0 + cb * 16 + lc] = macc[x][cb][i];
-          if (zl) zb[row] = zacc[x][i];
+          for (int cb = 0; cb < C::CB; ++cb) {
+            const size_t o = (size_t)row * D + c0 + cb * 16 + lc;
+            Mb[o] = m0(o) + macc[x][cb][i];
+          }
+          if (zl) zb[row] = z0(row) + zacc[x][i];
         }
       } else if (g == 0) {                         // constant row: every row of the block holds it
 #pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb) Mb[c0 + cb * 16 + lc] = macc[x][cb][0];
-        if (zl) zb[0] = (float)Nb;
+        for (int cb = 0; cb < C::CB; ++cb) Mb[c0 + cb * 16 + lc] = m0(c0 + cb * 16 + lc) + macc[x][cb][0];
+        if (zl) zb[0] = z0(0) + (float)Nb;
       }
     } else {
       const int a = x < NA ? a0 : a1;
@@ -423,13 +442,14 @@ __device__ __forceinline__ void state_store(float* __restrict__ Mb, float* __res
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb) {
           const float v = kTRsqrt2 * macc[x][cb][i];
-          Mb[r1 * D + c0 + cb * 16 + lc] = v;
-          if (mirror) Mb[r2 * D + c0 + cb * 16 + lc] = v;
+          const size_t o1 = r1 * D + c0 + cb * 16 + lc, o2 = r2 * D + c0 + cb * 16 + lc;
+          Mb[o1] = m0(o1) + v;
+          if (mirror) Mb[o2] = m0(o2) + v;
         }
         if (zl) {
           const float v = kTRsqrt2 * zacc[x][i];
-          zb[r1] = v;
-          if (mirror) zb[r2] = v;
+          zb[r1] = z0(r1) + v;
+          if (mirror) zb[r2] = z0(r2) + v;
         }
       }
     }
@@ -441,8 +461,9 @@ __device__ __forceinline__ void state_store(float* __restrict__ Mb, float* __res
 // task (pair index and column half), or -1 for an idle wave.
 template <int D, int P>
 __device__ __forceinline__ void state_pass(const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                                           float* __restrict__ Mb, float* __restrict__ zb, int Nb, size_t kvbase,
-                                           int task, __bf16 (*KT)[(D + 1) * TsCfg<D>::TSTR],
+                                           float* __restrict__ Mb, float* __restrict__ zb,
+                                           const float* __restrict__ M0b, const float* __restrict__ z0b, int Nb,
+                                           size_t kvbase, int task, __bf16 (*KT)[(D + 1) * TsCfg<D>::TSTR],
                                            __bf16 (*VT)[D * TsCfg<D>::TSTR]) {
   using C = TsCfg<D>;
 
@@ -531,7 +552,7 @@ __device__ __forceinline__ void state_pass(const __bf16* __restrict__ K, const _
     }
     lds_barrier();
   }
-  if (active) state_store<D, P>(Mb, zb, a0, a1, c0, Nb, lc, g, macc, zacc);
+  if (active) state_store<D, P>(Mb, zb, M0b, z0b, a0, a1, c0, Nb, lc, g, macc, zacc);
 }
 
 // State workgroup of launch index wid.  Workgroups of a (batch, K/V head):
@@ -540,9 +561,10 @@ __device__ __forceinline__ void state_pass(const __bf16* __restrict__ K, const _
 // NCH column halves.
 template <int D>
 __device__ __forceinline__ void taylor_state_item(
-    const __bf16* __restrict__ K, const __bf16* __restrict__ V, float* __restrict__ M_S,
-    float* __restrict__ z_S, const int* __restrict__ lens, int Hkv, int N, int wg_per_bk, int items,
-    int per_xcd, int wid, __bf16 (*KT)[(D + 1) * TsCfg<D>::TSTR], __bf16 (*VT)[D * TsCfg<D>::TSTR]) {
+    const __bf16* __restrict__ K, const __bf16* __restrict__ V, const float* __restrict__ M0,
+    const float* __restrict__ z0, float* __restrict__ M_S, float* __restrict__ z_S, const int* __restrict__ lens,
+    int Hkv, int N, int wg_per_bk, int items, int per_xcd, int wid, __bf16 (*KT)[(D + 1) * TsCfg<D>::TSTR],
+    __bf16 (*VT)[D * TsCfg<D>::TSTR]) {
   using C = TsCfg<D>;
   constexpr size_t DF = 1 + (size_t)D + (size_t)D * D;
   constexpr int WP = 4 * C::NCH;                    // workgroups per 16-block of pairs
@@ -557,19 +579,141 @@ __device__ __forceinline__ void taylor_state_item(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   float* Mb = M_S + (size_t)bk * DF * D;
   float* zb = z_S + (size_t)bk * DF;
+  const float* M0b = M0 ? M0 + (size_t)bk * DF * D : nullptr;
+  const float* z0b = z0 ? z0 + (size_t)bk * DF : nullptr;
   const size_t kvbase = (size_t)bk * N * D;
   const int P = wg / WP;                            // D/32 for the linear workgroup
   if (P >= D / 32) {
-    state_pass<D, -1>(K, V, Mb, zb, Nb, kvbase, wave < C::NCH ? (D / 2) * C::NCH + wave : -1, KT, VT);
+    state_pass<D, -1>(K, V, Mb, zb, M0b, z0b, Nb, kvbase, wave < C::NCH ? (D / 2) * C::NCH + wave : -1, KT, VT);
     return;
   }
   const int task = (P * 16) * C::NCH + (wg % WP) * 4 + wave;   // pair P*16 + l / NCH, half l % NCH
   switch (P) {
-    case 0: state_pass<D, 0>(K, V, Mb, zb, Nb, kvbase, task, KT, VT); break;
-    case 1: state_pass<D, 1>(K, V, Mb, zb, Nb, kvbase, task, KT, VT); break;
-    case 2: if constexpr (D >= 128) state_pass<D, 2>(K, V, Mb, zb, Nb, kvbase, task, KT, VT); break;
-    case 3: if constexpr (D >= 128) state_pass<D, 3>(K, V, Mb, zb, Nb, kvbase, task, KT, VT); break;
+    case 0: state_pass<D, 0>(K, V, Mb, zb, M0b, z0b, Nb, kvbase, task, KT, VT); break;
+    case 1: state_pass<D, 1>(K, V, Mb, zb, M0b, z0b, Nb, kvbase, task, KT, VT); break;
+    case 2: if constexpr (D >= 128) state_pass<D, 2>(K, V, Mb, zb, M0b, z0b, Nb, kvbase, task, KT, VT); break;
+    case 3: if constexpr (D >= 128) state_pass<D, 3>(K, V, Mb, zb, M0b, z0b, Nb, kvbase, task, KT, VT); break;
     default: break;
+  }
+}
+
+// The starting state's part of the retrieval, phi(q) M_0 and phi(q) z_0, of
+// every query row, into num0 [B][Hq][N][D] and den0 [B][Hq][N] (fp32) for
+// the attention items to add.  One workgroup of 4 waves per 256 query rows
+// of a (batch, query head), each wave 4 blocks of 16 rows.  The state is
+// walked one feature group at a time, each group staged in LDS as bf16
+// [value column][feature]: the linear rows 1..D, then quadratic group a
+// (rows 1 + D + a D + b, scaled by 1/sqrt 2 before rounding).  The operand
+// phi(q) of a group is formed in registers: q_b itself, or q_a q_b by
+// v_dot2_f32_bf16 against (q_a, 0) / (0, q_a) pairs; the den part is one
+// more product whose A rows all hold the group's z entries.  The constant
+// row is added in fp32.
+template <int D>
+struct TmCfg {
+  static constexpr int QB = 4;                     // 16-row query blocks per wave
+  static constexpr int ROWS = 64 * QB;             // query rows per workgroup
+  static constexpr int DB = D / 16, KS = D / 32;
+  static constexpr int MSTR = D + 8;               // staged group: rows = value columns, bf16
+  static constexpr int QSTR = D + 8;               // staged query rows
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void taylor_m0_kernel(
+    const __bf16* __restrict__ Q, const float* __restrict__ M0, const float* __restrict__ z0,
+    float* __restrict__ num0, float* __restrict__ den0, const int* __restrict__ lens, int Hq, int Hkv, int N,
+    int tiles) {
+  using C = TmCfg<D>;
+  constexpr size_t DF = 1 + (size_t)D + (size_t)D * D;
+  __shared__ __attribute__((aligned(16))) __bf16 Mt[D * C::MSTR];
+  __shared__ __attribute__((aligned(16))) __bf16 zt[D];
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[C::ROWS * C::QSTR];
+  const int bh = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int b = bh / Hq, h = bh % Hq;
+  const int bk = b * Hkv + h / (Hq / Hkv);
+  const int Nb = seq_len_of(lens, b, N);
+  const int r0 = tile * C::ROWS;
+  if (r0 >= Nb) return;                            // uniform
+  const float* M0b = M0 + (size_t)bk * DF * D;
+  const float* z0b = z0 + (size_t)bk * DF;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lc = lane & 15, g = lane >> 4;
+  const size_t qbase = (size_t)bh * N * D;
+  // the tile's query rows (rows past the sequence repeat its last row)
+  for (int idx = tid; idx < C::ROWS * (D / 8); idx += 256) {
+    const int r = idx / (D / 8), c8 = idx % (D / 8);
+    const int q = min(r0 + r, Nb - 1);
+    *reinterpret_cast<tbf16x8*>(Qs + r * C::QSTR + c8 * 8) =
+        *reinterpret_cast<const tbf16x8*>(Q + qbase + (size_t)q * D + c8 * 8);
+  }
+  tf32x4 acc[C::QB][C::DB], zac[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    zac[qb] = tf32x4{};
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[qb][db] = tf32x4{};
+  }
+  const __bf16 zero = (__bf16)0.f;
+  for (int grp = 0; grp <= D; ++grp) {             // 0: linear rows; 1 + a: quadratic group a
+    const size_t frow = grp == 0 ? 1 : 1 + D + (size_t)(grp - 1) * D;
+    const float sc = grp == 0 ? 1.f : kTRsqrt2;
+    lds_barrier();                                  // the previous group's reads are done
+    for (int idx = tid; idx < (D / 4) * (D / 4); idx += 256) {
+      const int f4 = idx / (D / 4), c4 = idx % (D / 4);
+      float4 rw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rw[j] = *reinterpret_cast<const float4*>(M0b + (frow + f4 * 4 + j) * D + c4 * 4);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const float v0 = cc == 0 ? rw[0].x : cc == 1 ? rw[0].y : cc == 2 ? rw[0].z : rw[0].w;
+        const float v1 = cc == 0 ? rw[1].x : cc == 1 ? rw[1].y : cc == 2 ? rw[1].z : rw[1].w;
+        const float v2 = cc == 0 ? rw[2].x : cc == 1 ? rw[2].y : cc == 2 ? rw[2].z : rw[2].w;
+        const float v3 = cc == 0 ? rw[3].x : cc == 1 ? rw[3].y : cc == 2 ? rw[3].z : rw[3].w;
+        *reinterpret_cast<tbf16x4*>(Mt + (c4 * 4 + cc) * C::MSTR + f4 * 4) =
+            tbf16x4{(__bf16)(sc * v0), (__bf16)(sc * v1), (__bf16)(sc * v2), (__bf16)(sc * v3)};
+      }
+    }
+    if (tid < D) zt[tid] = (__bf16)(sc * z0b[frow + tid]);
+    lds_barrier();
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const int qr = wave * 64 + qb * 16 + lc;
+      const __bf16 qa = grp == 0 ? zero : Qs[qr * C::QSTR + grp - 1];
+      const tbf16x2 mlo = {qa, zero}, mhi = {zero, qa};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const tbf16x8 qv = *reinterpret_cast<const tbf16x8*>(Qs + qr * C::QSTR + ks * 32 + 8 * g);
+        tbf16x8 op = qv;
+        if (grp > 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const tbf16x2 kp = {qv[2 * e], qv[2 * e + 1]};
+            op[2 * e] = (__bf16)dot2_exact(kp, mlo);
+            op[2 * e + 1] = (__bf16)dot2_exact(kp, mhi);
+          }
+        }
+        const tbf16x8 za = *reinterpret_cast<const tbf16x8*>(zt + ks * 32 + 8 * g);
+        zac[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za, op, zac[qb], 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const tbf16x8 a = *reinterpret_cast<const tbf16x8*>(Mt + (db * 16 + lc) * C::MSTR + ks * 32 + 8 * g);
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, op, acc[qb][db], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // the constant row, then the stores
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int q = r0 + wave * 64 + qb * 16 + lc;
+    if (q >= Nb) continue;
+    const size_t r = (size_t)bh * N + q;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const float4 m = *reinterpret_cast<const float4*>(M0b + db * 16 + 4 * g);
+      *reinterpret_cast<float4*>(num0 + r * D + db * 16 + 4 * g) =
+          float4{acc[qb][db][0] + m.x, acc[qb][db][1] + m.y, acc[qb][db][2] + m.z, acc[qb][db][3] + m.w};
+    }
+    if (g == 0) den0[r] = zac[qb][0] + z0b[0];
   }
 }
 
@@ -585,19 +729,20 @@ struct TfLds {
 template <int D>
 __global__ __launch_bounds__(256) void taylor_fwd_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const float* __restrict__ beta, __bf16* __restrict__ O, float* __restrict__ lse, float* __restrict__ M_S,
-    float* __restrict__ z_S, const int* __restrict__ lens, int B, int Hq, int Hkv, int N, int L, int S, int T,
-    float sl2, int wg_per_bk, int sitems, int per_xcd) {
+    const float* __restrict__ beta, const float* __restrict__ M0, const float* __restrict__ z0,
+    const float* __restrict__ num0, const float* __restrict__ den0, __bf16* __restrict__ O, float* __restrict__ lse,
+    float* __restrict__ M_S, float* __restrict__ z_S, const int* __restrict__ lens, int B, int Hq, int Hkv, int N,
+    int L, int S, int T, float sl2, int wg_per_bk, int sitems, int per_xcd) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[TfLds<D>::BYTES];
   const int nst = 8 * per_xcd;
   if ((int)blockIdx.x < nst) {
     using C = TsCfg<D>;
-    taylor_state_item<D>(K, V, M_S, z_S, lens, Hkv, N, wg_per_bk, sitems, per_xcd, (int)blockIdx.x,
+    taylor_state_item<D>(K, V, M0, z0, M_S, z_S, lens, Hkv, N, wg_per_bk, sitems, per_xcd, (int)blockIdx.x,
                          reinterpret_cast<__bf16 (*)[(D + 1) * C::TSTR]>(lds),
                          reinterpret_cast<__bf16 (*)[D * C::TSTR]>(lds + 2 * (D + 1) * C::TSTR * sizeof(__bf16)));
   } else {
     using C = TaCfg<D>;
-    taylor_attn_item<D>(Q, K, V, beta, O, lse, lens, B, Hq, Hkv, N, L, S, T, sl2, (int)blockIdx.x - nst,
+    taylor_attn_item<D>(Q, K, V, beta, O, lse, lens, num0, den0, B, Hq, Hkv, N, L, S, T, sl2, (int)blockIdx.x - nst,
                         reinterpret_cast<__bf16 (*)[C::KTILE]>(lds),
                         reinterpret_cast<__bf16 (*)[C::TTILE]>(lds + 2 * C::KTILE * sizeof(__bf16)));
   }
@@ -612,9 +757,30 @@ bool taylor_mfma_supported(const Geometry& g) {
          (long long)g.N <= 16LL * (long long)taylor_dim(g.D);
 }
 
+size_t taylor_mfma_m0_bytes(const Geometry& g) {
+  const size_t rows = (size_t)g.B * g.Hq * g.N;
+  return ((rows * g.D * 4 + 255) / 256) * 256 + ((rows * 4 + 255) / 256) * 256;
+}
+
 hipError_t launch_taylor_mfma(const Geometry& g, const void* Q, const void* K, const void* V,
-                              const float* beta, void* O, float* M_S, float* z_S, float* lse, hipStream_t st) {
+                              const float* beta, const float* M0, const float* z0, void* O, float* M_S, float* z_S,
+                              float* lse, void* m0ws, hipStream_t st) {
   if (!taylor_mfma_supported(g)) return hipErrorInvalidValue;
+  if ((M0 == nullptr) != (z0 == nullptr) || (M0 && !m0ws)) return hipErrorInvalidValue;
+  float* num0 = nullptr;
+  float* den0 = nullptr;
+  if (M0) {
+    const size_t rows = (size_t)g.B * g.Hq * g.N;
+    num0 = static_cast<float*>(m0ws);
+    den0 = reinterpret_cast<float*>(static_cast<char*>(m0ws) + ((rows * g.D * 4 + 255) / 256) * 256);
+    const int tiles = (g.N + 255) / 256;
+    const long long wgs = (long long)g.B * g.Hq * tiles;
+    if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+#define TM_ARGS static_cast<const __bf16*>(Q), M0, z0, num0, den0, g.lens, g.Hq, g.Hkv, g.N, tiles
+    if (g.D == 128) hipLaunchKernelGGL(taylor_m0_kernel<128>, dim3((unsigned)wgs), dim3(256), 0, st, TM_ARGS);
+    else hipLaunchKernelGGL(taylor_m0_kernel<64>, dim3((unsigned)wgs), dim3(256), 0, st, TM_ARGS);
+#undef TM_ARGS
+  }
   const float sl2 = 1.4426950408889634f / sqrtf((float)g.D);
   const int T = (g.L + 63) / 64;
   const long long items = (long long)g.S * g.B * g.Hq * T;
@@ -626,8 +792,8 @@ hipError_t launch_taylor_mfma(const Geometry& g, const void* Q, const void* K, c
   if (items + 8LL * per_xcd > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(items + 8LL * per_xcd));
 #define TF_ARGS static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V), \
-                beta, static_cast<__bf16*>(O), lse, M_S, z_S, g.lens, g.B, g.Hq, g.Hkv, g.N, g.L, g.S, T, sl2, \
-                wg_per_bk, (int)sitems, per_xcd
+                beta, M0, z0, num0, den0, static_cast<__bf16*>(O), lse, M_S, z_S, g.lens, g.B, g.Hq, g.Hkv, g.N, \
+                g.L, g.S, T, sl2, wg_per_bk, (int)sitems, per_xcd
   if (g.D == 128) hipLaunchKernelGGL(taylor_fwd_kernel<128>, grid, dim3(256), 0, st, TF_ARGS);
   else hipLaunchKernelGGL(taylor_fwd_kernel<64>, grid, dim3(256), 0, st, TF_ARGS);
 #undef TF_ARGS

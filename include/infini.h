@@ -102,15 +102,15 @@ typedef enum { INFINI_FP32 = 0, INFINI_BF16 = 1 } infini_dtype_t;
  *                           infini_attn_fwd_varlen, every dtype and head_dim;
  *                           every other entry point returns
  *                           INFINI_ERR_UNSUPPORTED for it.  bf16 with head_dim
- *                           64 or 128, seq_len <= 16 D' and no starting state
- *                           (M0 = z0 = NULL) runs on the matrix cores without
- *                           forming any per-segment state: the retrieval for
- *                           a query of
- *                           segment s is the attention over the keys before
- *                           the segment with weights 1 + q.k + (q.k)^2 / 2,
- *                           which equals phi(q) M_{s-1} / (phi(q) z_{s-1} +
- *                           eps) when M_0 = 0; other calls take fp32 vector
- *                           kernels over the D'-row states. */
+ *                           64 or 128 and seq_len <= 16 D' runs on the matrix
+ *                           cores without forming any per-segment state: the
+ *                           retrieval for a query of segment s is the
+ *                           attention over the keys before the segment with
+ *                           weights 1 + q.k + (q.k)^2 / 2, plus phi(q) M0 and
+ *                           phi(q) z0 for a starting state, which equals
+ *                           phi(q) M_{s-1} / (phi(q) z_{s-1} + eps); other
+ *                           calls take fp32 vector kernels over the D'-row
+ *                           states. */
 typedef enum { INFINI_FEATURE_ELU1 = 0, INFINI_FEATURE_TAYLOR2 = 1 } infini_feature_map_t;
 
 /* One call's problem.  The carried state is always float32.
@@ -168,7 +168,9 @@ size_t infini_fwd_saved_bytes(const infini_problem_t* p);
  *             "mfma_bf16_short"), and on the matrix-core Taylor path
  *             ("mfma_bf16_taylor2") when M0 is NULL, the call uses none and
  *             ws may be NULL with ws_bytes 0 (the size query still returns
- *             what the other paths need for the same problem)
+ *             what the other paths need for the same problem); with M0 the
+ *             matrix-core Taylor path uses batch * q_heads * seq_len *
+ *             (head_dim + 1) floats of it
  */
 infini_status_t infini_attn_fwd(const infini_problem_t* p,
                                 const void* Q, const void* K, const void* V,
@@ -397,10 +399,8 @@ infini_status_t infini_decode_noalloc(const infini_problem_t* p, int32_t pos, co
  * path, memory phase then attention phase; "mfma_bf16_short": bf16
  * matrix-core path for seg_len <= 64 that keeps the memory on chip in one
  * fused kernel; with the Taylor feature map "mfma_bf16_taylor2", the
- * matrix-core Taylor path, which a call with M0 = NULL takes while a call
- * with a starting state takes "generic_fp32_taylor2", the fp32 vector
- * kernels that every other Taylor problem takes).  NULL for an invalid
- * problem.  Static storage. */
+ * matrix-core Taylor path, or "generic_fp32_taylor2", the fp32 vector
+ * kernels).  NULL for an invalid problem.  Static storage. */
 const char* infini_fwd_path(const infini_problem_t* p);
 
 /* Static description of a status code. */

@@ -549,6 +549,34 @@ def test_taylor_matrix_core_forward(case):
     _taylor_fwd(Q, K, V, beta, L, None, None, "bf16", lens, "mfma_bf16_taylor2")
 
 
+# The same path with a starting state M0, z0 (the Taylor state of earlier
+# tokens, from the oracle): phi(q) M0 / phi(q) z0 join every query's retrieval
+# and M0, z0 the final state.
+TAYLOR_FAST_STATE_CASES = [
+    # B, Hq, Hkv, N, d, L, scale, lengths
+    (2, 4, 2, 200, 64, 64, 0.5, None),
+    (1, 2, 2, 130, 128, 48, 1.0, None),
+    (3, 4, 2, 150, 64, 100, 0.4, [150, 0, 61]),                 # variable lengths, one empty
+    (1, 2, 1, 64, 64, 64, 1.0, None),                           # one segment: the state is all the memory
+    (1, 4, 4, 300, 128, 256, 0.125, None),                      # 2 query-row tiles of the state kernel
+]
+
+
+@pytest.mark.parametrize("case", TAYLOR_FAST_STATE_CASES, ids=lambda c: "-".join(map(str, c[:7])) + (
+    "-" + "_".join(map(str, c[7])) if c[7] else ""))
+def test_taylor_matrix_core_forward_with_state(case):
+    """bf16 Taylor forward on the matrix cores from a carried state against the
+    oracle's state path."""
+    Bn, Hq, Hkv, N, d, L, sc, lens = case
+    Q, K, V, beta, _, _ = make(Bn, Hq, Hkv, N, d, "bf16", seed=19 * N + d, scale=sc)
+    Kp = rnd((Bn, Hkv, 40, d), 7 + d, sc, "bf16")
+    Vp = rnd((Bn, Hkv, 40, d), 8 + d, sc, "bf16")
+    _, _, M0, z0 = O.state_sweep(Kp, Vp, 40, fmap=O.Taylor2)
+    M0, z0 = M0.astype(np.float32), z0.astype(np.float32)
+    log(f"taylor mfma fwd with state Q{Q.shape} L={L} scale={sc} lens={lens}")
+    _taylor_fwd(Q, K, V, beta, L, M0, z0, "bf16", lens, "mfma_bf16_taylor2")
+
+
 def _random_taylor_cases(n, seed):
     """Seeded shapes for the matrix-core Taylor path: head dims 64/128, GQA,
     seg_len from 1 past the sequence length, ragged tails, input scales from
