@@ -1,20 +1,23 @@
 // Matrix-core forward for the second-order Taylor feature map (bf16, head
-// dim 64 or 128, empty starting memory).
+// dim 64 or 128).
 //
 // Page "Based" (cartesia.ai), section "고정 크기 순환 상태를 사용하는 방법도
 // 중요합니다": phi is chosen so that phi(q) . phi(k) = 1 + q.k + (q.k)^2 / 2,
 // and the key dimension grows to about d^2; section "I/O와 데이터 흐름을
 // 고려한 구현" notes that the resulting O(N d'^2 d) state makes a plain
 // implementation slow.  This file never forms the per-segment states at
-// all.  With M_0 = 0, z_0 = 0 the memory before segment s is the sum over the
-// earlier tokens j of phi(k_j)^T v_j and phi(k_j), so the retrieval of page
-// "Hugging Face Infini-Attention 재현 분석", section "Infini-Attention
-// 메커니즘" (Memory Retrieval) is, for a query q of segment s,
-//   A_mem = sum_j kappa(q.k_j) v_j / (sum_j kappa(q.k_j) + eps),
+// all.  The memory before segment s is M_0 plus the sum over the earlier
+// tokens j of phi(k_j)^T v_j (and z_0 plus the sum of phi(k_j)), so the
+// retrieval of page "Hugging Face Infini-Attention 재현 분석", section
+// "Infini-Attention 메커니즘" (Memory Retrieval) is, for a query q of
+// segment s,
+//   A_mem = (phi(q) M_0 + sum_j kappa(q.k_j) v_j)
+//           / (phi(q) z_0 + sum_j kappa(q.k_j) + eps),
 //   kappa(t) = phi(q) . phi(k) = 1 + t + t^2 / 2,
 // over the keys j before the segment's first token: an attention over the
 // earlier segments with polynomial weights instead of exponentials, the
-// same order of work as the local attention itself.
+// same order of work as the local attention itself, plus, with a starting
+// state, one product of phi(q) with it per query (taylor_m0_kernel).
 //
 // One launch, taylor_fwd_kernel, with two kinds of workgroup side by side:
 //   attention items      one workgroup of 4 waves per 64 query rows of a
