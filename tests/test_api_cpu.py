@@ -328,6 +328,22 @@ def test_taylor_feature_map_only_on_the_forward(L):
     assert L.infini_attn_fwd(ctypes.byref(bad), *a[:10], a[16], 1 << 30, None) == 3
 
 
+def test_taylor_matrix_core_workspace(L):
+    """The matrix-core Taylor forward needs workspace only for a starting
+    state: batch * q_heads * seq_len * (head_dim + 1) floats (rounded to 256
+    bytes per part), which the size query covers; a call with M0 and no
+    workspace is refused before any launch."""
+    p = binding.Problem(1, 2, 1, 64, 64, 64, 1, 1)
+    assert L.infini_fwd_path(ctypes.byref(p)) == b"mfma_bf16_taylor2"
+    rows = 1 * 2 * 64
+    need = -(-rows * 64 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert L.infini_fwd_workspace_bytes(ctypes.byref(p)) >= need
+    a = [FAKE[i] for i in range(11)]
+    a[10] = None                                              # no workspace
+    assert L.infini_attn_fwd(ctypes.byref(p), *a[:10], None, 0, None) == 5
+    assert L.infini_attn_fwd(ctypes.byref(p), *a[:10], FAKE[10], need - 1, None) == 5
+
+
 def test_bwd_saved_validates_before_launch(L):
     """infini_attn_bwd_saved: M_S and z_S come as a pair (1), 16-byte aligned
     (3), and no output may overlap them (4); the other checks are those of
