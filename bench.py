@@ -152,7 +152,9 @@ def main():
     ap.add_argument("--long-segments", action="store_true",
                     help="train mode: the --workload's own shape (default: 64-token training segments)")
     ap.add_argument("--graph", action="store_true",
-                    help="stream mode: capture the chained launches of one step in a HIP graph and replay it")
+                    help="stream mode: capture the chained launches of one step in a HIP graph and replay it; "
+                         "fwd mode: also time the step replayed from a HIP graph (no per-call host work), "
+                         "reported beside the eager step")
     ap.add_argument("--decode-tokens", type=int, default=0,
                     help="decode mode: decode only the last N tokens of the segment (the cache prefilled "
                          "with the rest); 0 = the whole segment")
@@ -233,6 +235,25 @@ def main():
     value = tokens * args.steps / (total_ms / 1e3)
     say(f"[bench] {ms_step:.3f} ms/step (memory {mem_ms:.3f} ms, attend {att_ms:.3f} ms); wall {wall:.2f} s")
 
+    graph_ms = None
+    if args.graph:
+        # the same step's launches recorded once and replayed: the GPU time of
+        # the step without the binding's per-call host work
+        import torch
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = _events(2)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        say(f"[bench] graph-replayed step {graph_ms:.4f} ms")
+
     alg = algorithmic(w)
     if fused:   # the one kernel does the whole step
         alg["attend_flop"] = alg["step_flop"]
@@ -262,6 +283,7 @@ def main():
         "pct_bf16_mfma_peak": round(100 * step_tflops / PEAK_BF16_MFMA_TFLOPS, 3),
         "step_tflops": round(step_tflops, 3),
         "phases_ms": {"memory": round(mem_ms, 4), "attend": round(att_ms, 4)},
+        "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 4),
         "memory_phase_gbs": round(alg["memory_bytes"] / (mem_ms / 1e3) / 1e9, 1),
         "roofline": roof,
     }
