@@ -55,7 +55,8 @@ struct FwdCfg {
   static constexpr int CPT = BN * D / 8 / NT;   // 16-byte K chunks per thread per tile
   static constexpr int MSTR = D + 8;      // M^T stage row stride
   static constexpr int BUF = KTILE + VTILE;
-  static constexpr int LDS_ELEMS = (2 * BUF > D * MSTR) ? 2 * BUF : D * MSTR;
+  static constexpr int MT = 2 * BUF;      // M^T region, after the two tile buffers
+  static constexpr int LDS_ELEMS = 2 * BUF + D * D;
 };
 
 // max / sum of x over lanes l and l^32 (v_permlane32_swap exchanges the two
@@ -92,10 +93,14 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   int work = blockIdx.x;
   if ((nwg & 7) == 0) work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
   const int G = Hq / Hkv;
-  const int per_group = G * nqt;
+  // Each workgroup attends two query tiles of one (batch, head, segment),
+  // nqt - 1 - p and p, so every workgroup walks the same number of key tiles
+  // (the middle tile of an odd nqt goes alone).
+  const int npair = (nqt + 1) / 2;
+  const int per_group = G * npair;
   const int grp = work / per_group;
   const int rem = work % per_group;
-  const int qt = nqt - 1 - rem / G;           // longest (most keys) tiles first
+  const int pr = rem / G;
   const int h_in = rem % G;
   const int sl = grp % nseg;
   const int bk = grp / nseg;                  // b * Hkv + kvh
@@ -114,29 +119,37 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // waves w and w + 4 share a SIMD: they take row blocks w and 7 - w, so
   // that each SIMD's pair attends to the same number of diagonal tiles
   const int rblk = (C::NW == 8 && wave >= 4) ? 11 - wave : wave;
-  const int q0 = qt * C::BM + rblk * C::WM;   // wave's first row (segment-relative)
-  const int qrow = q0 + lq;                   // this lane's query row
   const size_t qbase = (((size_t)b * Hq + h) * N + (size_t)s * L) * D;
   const size_t kvbase = (((size_t)b * Hkv + kvh) * N + (size_t)s * L) * D;
   // rows and keys of this segment: the last may be short, and in a
   // variable-length batch the segment may lie past its sequence's end
   const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
-  if (qt * C::BM >= Ls) return;               // a query tile past the end of a short segment
+  // query tiles of this workgroup that hold rows of the segment (a short
+  // segment may end before them)
+  int qtA = nqt - 1 - pr, qtB = pr, nq = 0;
+  if (qtA * C::BM < Ls) ++nq;
+  else qtA = qtB;
+  if (qtB != nqt - 1 - pr && qtB * C::BM < Ls) ++nq;
+  if (nq == 0) return;
+  auto tiles_of = [&](int qt) { return (min(Ls, qt * C::BM + C::BM) + C::BN - 1) / C::BN; };
+  const int nA = tiles_of(qtA);
+  const int nsteps = nA + (nq > 1 ? tiles_of(qtB) : 0);   // key tiles of both query tiles, in order
+  auto kofs = [&](int i) { return (i < nA ? i : i - nA) * C::BN; };
 
-  // ---- Q^T operand in registers for the whole key loop
+  // ---- Q^T operand of a query tile in registers for its whole key loop
   bf16x8_t qreg[C::KS];
-  {
-    const bool ok = qrow < Ls;
-    const __bf16* qp = Q + qbase + (size_t)(ok ? qrow : 0) * D + hh * 8;
+  auto load_q = [&](int qt) {
+    const int r = qt * C::BM + rblk * C::WM + lq;
+    const bool ok = r < Ls;
+    const __bf16* qp = Q + qbase + (size_t)(ok ? r : 0) * D + hh * 8;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
       qreg[ks] = ok ? v : bf16x8_t{};
     }
-  }
-
-  const int kend = min(Ls, qt * C::BM + C::BM);
-  const int ntiles = (kend + C::BN - 1) / C::BN;
+  };
+  load_q(qtA);
+  int q0 = 0, qrow = 0;   // wave's first row and this lane's query row in the current query tile
 
   // ---- global -> register staging of K and V tiles
   //
@@ -202,15 +215,11 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
   };
 
-  // The retrieval operand M_{s-1}^T (bf16) is loaded into registers while
-  // the last tile computes (the staging registers are free by
-  // then) and stored after the key loop into the tile buffer the last tile
-  // does not use.  M^T rows are unpadded; 16-byte chunk c of row r sits at
-  // chunk c ^ (r & 7), which keeps the epilogue's row reads conflict-free.
-  // (Loads straight into LDS would make the compiler wait for every
-  // outstanding global load before each tile's LDS reads.)
+  // The retrieval operand M_{s-1}^T (bf16), shared by both query tiles, is
+  // staged once, with the first K/V tile, into an LDS region of its own.
+  // M^T rows are unpadded; 16-byte chunk c of row r sits at chunk
+  // c ^ (r & 7), which keeps the epilogue's row reads conflict-free.
   constexpr int MPT = D * D / 8 / C::NT;  // 16-byte chunks of M^T per thread
-  static_assert(D * D <= C::BUF, "M^T stage must fit one tile buffer");
   const __bf16* msrc = MsnapT + ((size_t)bk * nseg + sl) * D * D;
   const float* zsrc = zsnap + ((size_t)bk * nseg + sl) * D;
   // Chunk i of a thread in wave w covers 1 KB block i*NW + w, i.e. rows
@@ -219,21 +228,7 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   constexpr int RPB = 64 / (D / 8);               // M^T rows per 1 KB block
   const int mrow0 = wave * RPB + lane / (D / 8);
   const __bf16* msrc0 = msrc + (size_t)mrow0 * D + (((lane % (D / 8)) ^ (mrow0 & 7)) * 8);
-  // The chunks live in the K/V staging registers (kst, then vst).
-  static_assert(MPT <= C::CPT + C::KPT, "M^T chunks must fit the staging registers");
-  auto load_m = [&]() {
-#pragma unroll
-    for (int i = 0; i < MPT; ++i) {
-      const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(msrc0 + (size_t)i * C::NW * RPB * D);
-      if (i < C::CPT) kst[i] = v;
-      else vst[i - C::CPT] = v;
-    }
-  };
-  auto store_m = [&](__bf16* dst) {
-#pragma unroll
-    for (int i = 0; i < MPT; ++i)
-      *reinterpret_cast<bf16x8_t*>(dst + (i * C::NW + wave) * 512 + lane * 8) = i < C::CPT ? kst[i] : vst[i - C::CPT];
-  };
+  __bf16* const Mts = smem + C::MT;
 
   f32x16_t oacc[C::DB];
 #pragma unroll
@@ -330,76 +325,91 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // every tile's first LDS wait a full wait.
   asm volatile("" ::"s"(beta), "s"(O), "s"(lse), "s"(msrc));
   load_tile(0);
-  // z_{s-1} has an LDS array of its own, written once before the first barrier
-  if (wave < D / 64) zs[wave * 64 + lane] = zsrc[wave * 64 + lane];
-  store_tile(0);
-  __syncthreads();
-  if (ntiles > 1) load_tile(C::BN);
-  else load_m();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int k0 = j * C::BN;
-    const __bf16* Ks = smem + (j & 1) * C::BUF;
-    const __bf16* Vt = Ks + C::KTILE;
-    const bool active = k0 <= q0 + C::WM - 1 && q0 < Ls;
-    const bool masked = (k0 + C::BN - 1 > q0) || (k0 + C::BN > Ls);
-    if (active) {
-      tile_step(Ks, Vt, k0, masked);
-    }
-    if (j + 1 < ntiles) store_tile((j + 1) & 1);
-    __syncthreads();
-    if (j + 2 < ntiles) load_tile((j + 2) * C::BN);
-    else if (j + 2 == ntiles) load_m();
+  {
+    bf16x8_t mst[MPT];
+#pragma unroll
+    for (int i = 0; i < MPT; ++i) mst[i] = *reinterpret_cast<const bf16x8_t*>(msrc0 + (size_t)i * C::NW * RPB * D);
+    // z_{s-1} has an LDS array of its own, written once before the first barrier
+    if (wave < D / 64) zs[wave * 64 + lane] = zsrc[wave * 64 + lane];
+    store_tile(0);
+#pragma unroll
+    for (int i = 0; i < MPT; ++i)
+      *reinterpret_cast<bf16x8_t*>(Mts + (i * C::NW + wave) * 512 + lane * 8) = mst[i];
   }
-  // M^T goes to the buffer the last tile did not use: every wave has passed
-  // the barrier after the tile that used it last.
-  __bf16* Mts = smem + (ntiles & 1) * C::BUF;
-  store_m(Mts);
   __syncthreads();
+  if (nsteps > 1) load_tile(kofs(1));
 
-  // ---- retrieval from M_{s-1}, z_{s-1} (staged in a tile buffer) and the gate
-  const float l = pair_sum32(lpart);
+  const float gt = sigmoid(beta[h]);
+  int step = 0;   // key tiles walked so far (both query tiles); tile buffer step & 1
+  for (int t = 0; t < nq; ++t) {
+    const int qt = t == 0 ? qtA : qtB;
+    q0 = qt * C::BM + rblk * C::WM;
+    qrow = q0 + lq;
+    const int ntiles = t == 0 ? nA : nsteps - nA;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16_t{};
+    m = -INFINITY;
+    lpart = 0.f;
 
-  bf16x8_t sq[C::KS];
-  float dpart = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const __bf16 v = (__bf16)elu1((float)qreg[ks][e]);
-      sq[ks][e] = v;
-      dpart += (float)v * zs[ks * 16 + hh * 8 + e];
+    for (int j = 0; j < ntiles; ++j, ++step) {
+      const int k0 = j * C::BN;
+      const __bf16* Ks = smem + (step & 1) * C::BUF;
+      const __bf16* Vt = Ks + C::KTILE;
+      const bool active = k0 <= q0 + C::WM - 1 && q0 < Ls;
+      const bool masked = (k0 + C::BN - 1 > q0) || (k0 + C::BN > Ls);
+      if (active) {
+        tile_step(Ks, Vt, k0, masked);
+      }
+      if (step + 1 < nsteps) store_tile((step + 1) & 1);
+      __syncthreads();
+      if (step + 2 < nsteps) load_tile(kofs(step + 2));
     }
-  }
-  const float den = pair_sum32(dpart) + 1e-6f;
-  f32x16_t nacc[C::DB];
-#pragma unroll
-  for (int cb = 0; cb < C::DB; ++cb) {
-    nacc[cb] = f32x16_t{};
+
+    // ---- retrieval from M_{s-1}, z_{s-1} (staged in their own LDS) and the gate
+    const float l = pair_sum32(lpart);
+
+    bf16x8_t sq[C::KS];
+    float dpart = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const int r = cb * 32 + lq;
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Mts + r * D + (((ks * 2 + hh) ^ (r & 7)) * 8));
-      nacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sq[ks], nacc[cb], 0, 0, 0);
-    }
-  }
-  const float gt = sigmoid(beta[h]);
-  const float wm = gt / den;
-  const float wd = (1.f - gt) / l;
-  if (qrow < Ls) {
-    __bf16* op = O + qbase + (size_t)qrow * D;
 #pragma unroll
-    for (int cb = 0; cb < C::DB; ++cb) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        bf16x4_t w;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) w[x] = (__bf16)(wm * nacc[cb][4 * u + x] + wd * oacc[cb][4 * u + x]);
-        *reinterpret_cast<bf16x4_t*>(op + cb * 32 + 8 * u + 4 * hh) = w;
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 v = (__bf16)elu1((float)qreg[ks][e]);
+        sq[ks][e] = v;
+        dpart += (float)v * zs[ks * 16 + hh * 8 + e];
       }
     }
-    if (lse && hh == 0)
-      lse[((size_t)b * Hq + h) * N + (size_t)s * L + qrow] = (m + __log2f(l)) * 0.69314718055994531f;
+    const float den = pair_sum32(dpart) + 1e-6f;
+    f32x16_t nacc[C::DB];
+#pragma unroll
+    for (int cb = 0; cb < C::DB; ++cb) {
+      nacc[cb] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int r = cb * 32 + lq;
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Mts + r * D + (((ks * 2 + hh) ^ (r & 7)) * 8));
+        nacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sq[ks], nacc[cb], 0, 0, 0);
+      }
+    }
+    // the next query tile's Q rows arrive during this tile's output stores
+    if (t + 1 < nq) load_q(qtB);
+    const float wm = gt / den;
+    const float wd = (1.f - gt) / l;
+    if (qrow < Ls) {
+      __bf16* op = O + qbase + (size_t)qrow * D;
+#pragma unroll
+      for (int cb = 0; cb < C::DB; ++cb) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          bf16x4_t w;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) w[x] = (__bf16)(wm * nacc[cb][4 * u + x] + wd * oacc[cb][4 * u + x]);
+          *reinterpret_cast<bf16x4_t*>(op + cb * 32 + 8 * u + 4 * hh) = w;
+        }
+      }
+      if (lse && hh == 0)
+        lse[((size_t)b * Hq + h) * N + (size_t)s * L + qrow] = (m + __log2f(l)) * 0.69314718055994531f;
+    }
   }
 }
 
@@ -409,7 +419,7 @@ static hipError_t fwd_mfma_t(const Geometry& g, const void* Q, const void* K, co
                              float* lse, int s_begin, int s_end, hipStream_t st) {
   const int nseg = s_end - s_begin;
   const int nqt = (g.L + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
-  const long long nwg = (long long)g.B * g.Hq * nseg * nqt;
+  const long long nwg = (long long)g.B * g.Hq * nseg * ((nqt + 1) / 2);
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL((fwd_mfma_kernel<D, false>), dim3((unsigned)nwg), dim3(FwdCfg<D>::NT), 0, st,
@@ -425,7 +435,7 @@ static hipError_t fwd_mfma_group_t(const Geometry& g, const FwdCallTable& tab, i
                                    const void* MsnapT, const float* zsnap, hipStream_t st) {
   const int nseg = ncalls * g.S;
   const int nqt = (g.L + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
-  const long long nwg = (long long)g.B * g.Hq * nseg * nqt;
+  const long long nwg = (long long)g.B * g.Hq * nseg * ((nqt + 1) / 2);
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL((fwd_mfma_kernel<D, true>), dim3((unsigned)nwg), dim3(FwdCfg<D>::NT), 0, st,
