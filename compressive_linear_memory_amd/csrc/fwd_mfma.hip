@@ -125,11 +125,11 @@ void fwd_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // variable-length batch the segment may lie past its sequence's end
   const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
   // query tiles of this workgroup that hold rows of the segment (a short
-  // segment may end before them)
-  int qtA = nqt - 1 - pr, qtB = pr, nq = 0;
-  if (qtA * C::BM < Ls) ++nq;
-  else qtA = qtB;
-  if (qtB != nqt - 1 - pr && qtB * C::BM < Ls) ++nq;
+  // segment may end before them); the shorter one first, so that the longer
+  // one's first key tiles are still in L2 when it reads them
+  const int qtA = pr, qtB = nqt - 1 - pr;
+  int nq = 0;
+  if (qtA * C::BM < Ls) nq = (qtB != qtA && qtB * C::BM < Ls) ? 2 : 1;
   if (nq == 0) return;
   auto tiles_of = [&](int qt) { return (min(Ls, qt * C::BM + C::BM) + C::BN - 1) / C::BN; };
   const int nA = tiles_of(qtA);
