@@ -2,7 +2,9 @@
 //
 // One workgroup = 8 waves = 256 query rows (head_dim 128; 4 waves = 128 rows
 // for head_dim 64) of one (batch, query head, segment); each wave owns 32
-// query rows, and all waves share each staged K/V tile.  Per 64-key tile:
+// query rows, and all waves share each staged K/V tile.  A workgroup attends
+// two such query tiles, p and nqt-1-p, one after the other, so that all
+// workgroups walk the same number of key tiles.  Per 64-key tile:
 //   S^T = K Q^T          v_mfma_f32_32x32x16_bf16, K from LDS, Q^T in registers
 //   online softmax       base-2, row max/sum inside the lane plus one swap with
 //                        the lane 32 apart (page "Context Memorization for
