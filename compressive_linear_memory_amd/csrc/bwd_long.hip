@@ -106,22 +106,33 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
   __shared__ float zs[D];
   __shared__ float wsum[C::NW];
 
-  // query tiles with the most keys first
-  const int per_qt = (int)gridDim.x / nqt;           // (head, batch, segment) units per query tile
-  const int qt = nqt - 1 - (int)blockIdx.x / per_qt;
+  // a workgroup takes query tiles p and nqt - 1 - p, the shorter first, so
+  // that every workgroup walks the same number of key tiles
+  const int npair = (nqt + 1) / 2;
+  const int per_qt = (int)gridDim.x / npair;         // (head, batch, segment) units per tile pair
+  const int pr = (int)blockIdx.x / per_qt;
   const int rem = (int)blockIdx.x % per_qt;
   const int h = rem % Hq;
   const int sl = (rem / Hq) % nseg, b = (rem / Hq) / nseg;
   const int s = s_begin + sl;
   const int G = Hq / Hkv, kvh = h / G;
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
   // rows of this segment: the last may be short; none past the end of a
   // sequence of a variable-length batch (the gate partial is then zero)
   const int Ls = min(L, seq_len_of(lens, b, N) - s * L);
+  for (int t = 0; t < 2; ++t) {
+  // the lane-derived addresses are recomputed per tile instead of being held
+  // (and spilled) across both
+  asm volatile("" : "+v"(tid));
+  const int qt = t == 0 ? pr : nqt - 1 - pr;
+  if (t == 1) {
+    if (qt == pr) break;          // the middle tile of an odd nqt goes alone
+    __syncthreads();              // the first tile's LDS reads are done
+  }
   const size_t dbp = (((size_t)b * Hq + h) * nseg + sl) * nqt + qt;
   if (Ls <= 0 || qt * C::BM >= Ls) {
     if (tid == 0) dbeta_part[dbp] = 0.f;
-    return;
+    continue;
   }
   const int lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 31, hh = lane >> 5;
@@ -466,6 +477,7 @@ void bwd_q_mfma_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ 
         *reinterpret_cast<lbf16x4*>(qp + ab * 32 + 8 * u + 4 * hh) =
             lbf16x4{(__bf16)dq[ab][4 * u], (__bf16)dq[ab][4 * u + 1], (__bf16)dq[ab][4 * u + 2], (__bf16)dq[ab][4 * u + 3]};
   }
+  }   // query tiles of the pair
 }
 
 
@@ -887,7 +899,7 @@ static hipError_t bwd_q_mfma_t(const Geometry& g, const void* Q, const void* K, 
   const int nseg = s_end - s_begin;
   const float scale = 1.f / sqrtf((float)D);
   const int nqt = (g.L + BqCfg<D>::BM - 1) / BqCfg<D>::BM;
-  const long long units = (long long)nqt * g.Hq * g.B * nseg;
+  const long long units = (long long)((nqt + 1) / 2) * g.Hq * g.B * nseg;
   if (units > 0x7fffffffLL) return hipErrorInvalidValue;
   dim3 grid((unsigned)units);
   hipLaunchKernelGGL((bwd_q_mfma_kernel<D>), grid, dim3(BqCfg<D>::NT), 0, st,
